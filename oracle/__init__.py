@@ -1,0 +1,20 @@
+"""Float64 CPU oracle of the pre-LN ViT encoder block (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path never does.
+"""
+
+from .block import (  # noqa: F401
+    attention_scores,
+    attention_weights,
+    gelu_tanh,
+    layer_norm,
+    merge_heads,
+    mlp,
+    multi_head_attention,
+    project,
+    softmax_rows,
+    split_heads,
+    vit_block,
+    vit_block_stages,
+)

@@ -1,0 +1,212 @@
+"""Float64 CPU oracle for the forward pass of one pre-LayerNorm ViT encoder block.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, header,
+constant or helper with the HIP library in ``vision_transformer_encoder_amd``;
+the only thing both sides consume is the seeded input arrays.
+
+It is the plain definition of the block, written out step by step in float64
+NumPy, vectorised over sequences and heads (no blocking, fusion or reordering
+beyond what the definition states).  Matrix products use ``numpy.matmul``.
+
+Sources (the pages this follows; each function names the section it restates):
+
+  [CAC]  crackedaicode.com, "ViT Encoder Block" (PyTorch track) -- sections
+         "Inputs and output", "Normalize before each stage",
+         "Multi-head attention", "Feed-forward stage".
+  [TT]   tensortonic.com, "ViT Encoder Block" -- the block equations,
+         "Requirements" (population variance, eps 1e-6), "Examples".
+  [AEE]  ai-engineer-exhaustive.pages.dev, "ViT Encoder Block" --
+         "Key Equations" steps 1-6, "Numerical Example".
+  [MLG]  mlgrind.dev, "E2E: Tiny Vision Transformer" -- "Details" (MHA, GELU).
+  [NB]   nipunbatra.github.io, vision1 lecture transcript -- Page 70
+         (head h owns features h*d_h .. (h+1)*d_h-1), Pages 106-110 (code).
+
+Readings taken where the pages differ (all fixed by the block definition in
+[CAC]): no LayerNorm scale/shift, no projection biases, tanh-GELU, and a
+caller-supplied eps (1e-5 in [CAC], 1e-6 in [TT]).
+
+Every function here has pins in ``tests/test_oracle.py`` that do not reuse
+this code: the printed worked examples of [TT] "Examples" and the hand trace
+of [AEE] "Numerical Example", closed forms, invariants and a brute-force
+scalar loop.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "layer_norm",
+    "project",
+    "split_heads",
+    "merge_heads",
+    "attention_scores",
+    "softmax_rows",
+    "attention_weights",
+    "multi_head_attention",
+    "gelu_tanh",
+    "mlp",
+    "vit_block",
+    "vit_block_stages",
+]
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+def layer_norm(x, eps: float) -> np.ndarray:
+    """Normalise every token over its last (feature) axis.
+
+    [CAC] "Normalize before each stage": subtract the token mean and divide by
+    sqrt(population variance + eps), the variance dividing by D (not D-1);
+    there is no learned scale or shift.  [AEE] "Key Equations" step 1 gives the
+    same mean/variance with gamma = 1, beta = 0.
+    """
+    x = _f64(x)
+    mean = x.mean(axis=-1, keepdims=True)
+    dev = x - mean
+    var = (dev * dev).mean(axis=-1, keepdims=True)
+    return dev / np.sqrt(var + eps)
+
+
+def project(a, w) -> np.ndarray:
+    """Row-vector projection ``a @ w`` with ``w`` stored (in_features, out_features).
+
+    [CAC] "Multi-head attention": Q = LN(x) @ w_q with w_q of shape (D, D);
+    "Inputs and output": w_mlp1 is (D, F) and w_mlp2 is (F, D).
+    """
+    return np.matmul(_f64(a), _f64(w))
+
+
+def split_heads(t, num_heads: int) -> np.ndarray:
+    """(N, T, D) -> (N, H, T, D/H): head h takes the h-th run of D/H consecutive features.
+
+    [CAC] "Multi-head attention" (split into H consecutive chunks of width D/H);
+    [NB] Page 70 (the first 64 features belong to head 1).
+    """
+    t = _f64(t)
+    n, tt, d = t.shape
+    dh = d // num_heads
+    return t.reshape(n, tt, num_heads, dh).transpose(0, 2, 1, 3)
+
+
+def merge_heads(o) -> np.ndarray:
+    """(N, H, T, d_h) -> (N, T, H*d_h), heads concatenated in their original order.
+
+    [CAC] "Multi-head attention" (concatenate head outputs in original order).
+    """
+    o = _f64(o)
+    n, h, tt, dh = o.shape
+    return o.transpose(0, 2, 1, 3).reshape(n, tt, h * dh)
+
+
+def attention_scores(qh, kh) -> np.ndarray:
+    """Q_h K_h^T / sqrt(d_h) for every sequence and head: (N, H, T, T).
+
+    [CAC] "Multi-head attention" (scores scaled by 1/sqrt(D/H));
+    [AEE] "Key Equations" step 2 (divide by sqrt(d_k)).
+    """
+    qh = _f64(qh)
+    kh = _f64(kh)
+    dh = qh.shape[-1]
+    return np.matmul(qh, np.swapaxes(kh, -1, -2)) / math.sqrt(dh)
+
+
+def softmax_rows(s) -> np.ndarray:
+    """Stable softmax over the last (key) axis; no mask of any kind.
+
+    [CAC] "Multi-head attention" (stable softmax across key positions, every
+    token sees every token of its sequence); [AEE] "No Causal Mask".
+    The row maximum is subtracted before exponentiating.
+    """
+    s = _f64(s)
+    m = s.max(axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def attention_weights(xn, w_q, w_k, num_heads: int) -> np.ndarray:
+    """softmax(Q_h K_h^T / sqrt(d_h)) for every sequence and head: (N, H, T, T)."""
+    qh = split_heads(project(xn, w_q), num_heads)
+    kh = split_heads(project(xn, w_k), num_heads)
+    return softmax_rows(attention_scores(qh, kh))
+
+
+def multi_head_attention(xn, w_q, w_k, w_v, num_heads: int) -> np.ndarray:
+    """Concatenated head outputs before the output projection: (N, T, D).
+
+    [CAC] "Multi-head attention": per sequence and head,
+    head_output = softmax(Q_h K_h^T / sqrt(D/H)) @ V_h; heads concatenated.
+    """
+    a = attention_weights(xn, w_q, w_k, num_heads)
+    vh = split_heads(project(xn, w_v), num_heads)
+    return merge_heads(np.matmul(a, vh))
+
+
+def gelu_tanh(z) -> np.ndarray:
+    """GELU, tanh form: 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).
+
+    [CAC] "Feed-forward stage"; [MLG] "Details"; [AEE] "Key Equations" step 5.
+    sqrt(2/pi) is evaluated, not the rounded 0.7979 of [AEE]'s hand trace.
+    """
+    z = _f64(z)
+    return 0.5 * z * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (z + 0.044715 * z ** 3)))
+
+
+def mlp(yn, w_mlp1, w_mlp2) -> np.ndarray:
+    """GELU(yn @ w_mlp1) @ w_mlp2, no biases ([CAC] "Feed-forward stage")."""
+    return project(gelu_tanh(project(yn, w_mlp1)), w_mlp2)
+
+
+def vit_block_stages(x, w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, num_heads: int,
+                     eps: float) -> dict:
+    """Every intermediate of the block for a batch of sequences, float64.
+
+    Keys: xn = LN(x); q, k, v = xn @ w_{q,k,v}; att = concatenated heads;
+    y = x + att @ w_o; yn = LN(y); z = yn @ w_mlp1; h = GELU(z);
+    out = y + h @ w_mlp2.
+
+    [CAC] "Multi-head attention" and "Feed-forward stage": the first residual
+    adds the un-normalised x, the second LayerNorm normalises y (not x).
+    [AEE] "Key Equations" steps 1-6 give the same order.
+    """
+    x = _f64(x)
+    if x.ndim != 3:
+        raise ValueError("x must be (N, T, D)")
+    d = x.shape[-1]
+    if num_heads <= 0 or d % num_heads:
+        raise ValueError("num_heads must be positive and divide D")
+    xn = layer_norm(x, eps)
+    q = project(xn, w_q)
+    k = project(xn, w_k)
+    v = project(xn, w_v)
+    a = softmax_rows(attention_scores(split_heads(q, num_heads), split_heads(k, num_heads)))
+    att = merge_heads(np.matmul(a, split_heads(v, num_heads)))
+    y = x + project(att, w_o)
+    yn = layer_norm(y, eps)
+    z = project(yn, w_mlp1)
+    h = gelu_tanh(z)
+    out = y + project(h, w_mlp2)
+    return dict(xn=xn, q=q, k=k, v=v, weights=a, att=att, y=y, yn=yn, z=z, h=h, out=out)
+
+
+def vit_block(x, w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, num_heads: int, eps: float,
+              chunk: int = 8) -> np.ndarray:
+    """Output of one pre-LN encoder block, (N, T, D) float64.
+
+    Sequences never interact ([CAC] "Inputs and output": N independent
+    sequences), so they are processed ``chunk`` at a time to bound memory;
+    this changes no arithmetic.
+    """
+    x = _f64(x)
+    out = np.empty_like(x)
+    for s in range(0, x.shape[0], max(1, int(chunk))):
+        st = vit_block_stages(x[s:s + chunk], w_q, w_k, w_v, w_o, w_mlp1, w_mlp2,
+                              num_heads, eps)
+        out[s:s + chunk] = st["out"]
+    return out

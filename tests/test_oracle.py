@@ -1,0 +1,391 @@
+"""Pins for the float64 oracle (CPU only).
+
+The oracle is trusted only through checks that do not reuse its code:
+
+* the three worked examples printed on tensortonic.com "ViT Encoder Block",
+  section "Examples" (6 printed decimals);
+* the hand trace of ai-engineer-exhaustive.pages.dev "ViT Encoder Block",
+  section "Numerical Example" (4 printed decimals, hand-rounded: 1e-3);
+* closed forms (GELU odd part, two-way softmax as a logistic, uniform
+  attention when the queries vanish, T = 1) and invariants (zero update,
+  LayerNorm moments, row-stochastic weights, token-permutation equivariance,
+  batch independence);
+* a brute-force scalar loop written from the block's definition on
+  crackedaicode.com "ViT Encoder Block" (sections "Normalize before each
+  stage", "Multi-head attention", "Feed-forward stage"), run on tiny inputs;
+* float64 library cross-checks (torch's layer_norm, tanh-GELU and
+  scaled-dot-product attention), used here only, never by the oracle.
+
+The last group plants plausible mistakes into one oracle step at a time and
+asserts that the pins above catch every one of them.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import block as ob
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _tt_case_args(c):
+    a = lambda k: np.array(c[k], dtype=np.float64)  # noqa: E731
+    return (a("x"), a("Wq"), a("Wk"), a("Wv"), a("Wo"), a("W1"), a("W2"), c["num_heads"])
+
+
+def _tt_max_err():
+    """Largest |oracle - printed| over the three printed worked examples."""
+    g = _load("tt_worked_examples.json")
+    worst = 0.0
+    for c in g["cases"]:
+        x, wq, wk, wv, wo, w1, w2, h = _tt_case_args(c)
+        out = oracle.vit_block(x, wq, wk, wv, wo, w1, w2, h, g["eps"])
+        worst = max(worst, float(np.abs(out - np.array(c["out"])).max()))
+    return worst
+
+
+# 6 printed decimals: half a unit in the last place, plus float64 slack.
+TT_TOL = 5e-7 + 1e-12
+
+
+# ---------------------------------------------------------------- brute force
+
+def _brute_ln(row, eps):
+    d = len(row)
+    mu = sum(row) / d
+    var = sum((v - mu) ** 2 for v in row) / d
+    return [(v - mu) / math.sqrt(var + eps) for v in row]
+
+
+def _brute_gelu(z):
+    return 0.5 * z * (1.0 + math.tanh(math.sqrt(2.0 / math.pi) * (z + 0.044715 * z * z * z)))
+
+
+def brute_force_block(x, wq, wk, wv, wo, w1, w2, H, eps):
+    """Scalar loops over (sequence, token, head, key, feature); tiny inputs only."""
+    x = np.asarray(x).tolist()
+    wq, wk, wv, wo, w1, w2 = (np.asarray(w).tolist() for w in (wq, wk, wv, wo, w1, w2))
+    N, T, D = len(x), len(x[0]), len(x[0][0])
+    F = len(w1[0])
+    dh = D // H
+    out = [[[0.0] * D for _ in range(T)] for _ in range(N)]
+    for n in range(N):
+        xn = [_brute_ln(x[n][t], eps) for t in range(T)]
+
+        def mat(a, w, cols):
+            return [[sum(a[t][i] * w[i][j] for i in range(len(w))) for j in range(cols)]
+                    for t in range(len(a))]
+
+        q, k, v = mat(xn, wq, D), mat(xn, wk, D), mat(xn, wv, D)
+        att = [[0.0] * D for _ in range(T)]
+        for h in range(H):
+            c0 = h * dh
+            for i in range(T):
+                s = [sum(q[i][c0 + c] * k[j][c0 + c] for c in range(dh)) / math.sqrt(dh)
+                     for j in range(T)]
+                m = max(s)
+                e = [math.exp(sj - m) for sj in s]
+                z = sum(e)
+                for c in range(dh):
+                    att[i][c0 + c] = sum(e[j] / z * v[j][c0 + c] for j in range(T))
+        proj = mat(att, wo, D)
+        y = [[x[n][t][j] + proj[t][j] for j in range(D)] for t in range(T)]
+        yn = [_brute_ln(y[t], eps) for t in range(T)]
+        hid = [[_brute_gelu(val) for val in row] for row in mat(yn, w1, F)]
+        upd = mat(hid, w2, D)
+        for t in range(T):
+            for j in range(D):
+                out[n][t][j] = y[t][j] + upd[t][j]
+    return np.array(out)
+
+
+def _rand_block(rng, N, T, D, F):
+    x = rng.standard_normal((N, T, D))
+    ws = [rng.standard_normal(s) / math.sqrt(s[0]) for s in
+          [(D, D), (D, D), (D, D), (D, D), (D, F), (F, D)]]
+    return [x] + ws
+
+
+BRUTE_SHAPES = [(2, 3, 4, 1, 6), (2, 3, 4, 2, 6), (1, 4, 4, 4, 5), (2, 2, 6, 3, 7)]
+
+
+def _brute_max_err():
+    rng = np.random.default_rng(1234)
+    worst = 0.0
+    for (N, T, D, H, F) in BRUTE_SHAPES:
+        args = _rand_block(rng, N, T, D, F)
+        ref = brute_force_block(*args, H, 1e-5)
+        got = oracle.vit_block(*args, H, 1e-5)
+        worst = max(worst, float(np.abs(ref - got).max()))
+    return worst
+
+
+# ------------------------------------------------------------------ the pins
+
+def test_tt_worked_examples():
+    assert _tt_max_err() <= TT_TOL
+
+
+def test_tt_example2_constant_token_passes_through():
+    # A constant token normalises to zero, so both updates vanish for it and
+    # its output row equals its input row (example 2, third token).
+    g = _load("tt_worked_examples.json")
+    c = g["cases"][1]
+    x, wq, wk, wv, wo, w1, w2, h = _tt_case_args(c)
+    out = oracle.vit_block(x, wq, wk, wv, wo, w1, w2, h, g["eps"])
+    np.testing.assert_array_equal(out[0, 2], x[0, 2])
+
+
+def test_brute_force_agrees():
+    assert _brute_max_err() <= 1e-12
+
+
+def test_aee_layer_norm_trace():
+    g = _load("aee_hand_trace.json")
+    ln = g["layer_norm"]
+    x = np.array(ln["x"])
+    np.testing.assert_allclose(x.mean(-1), ln["mean"], atol=1e-15)
+    np.testing.assert_allclose(x.var(-1), ln["variance"], atol=1e-15)
+    got = oracle.layer_norm(x, 1e-6)
+    assert np.abs(got - np.array(ln["normalized"])).max() <= g["tolerance"]
+
+
+def test_aee_softmax_trace():
+    g = _load("aee_hand_trace.json")
+    s = np.array(g["softmax"]["scaled_scores"])
+    got = oracle.softmax_rows(s)
+    assert np.abs(got - np.array(g["softmax"]["weights"])).max() <= g["tolerance"]
+    # Two-way softmax is the logistic function of the score difference.
+    for r in range(2):
+        p0 = 1.0 / (1.0 + math.exp(s[r, 1] - s[r, 0]))
+        assert abs(got[r, 0] - p0) < 1e-15 and abs(got[r, 1] - (1.0 - p0)) < 1e-15
+
+
+def test_aee_gelu_trace():
+    g = _load("aee_hand_trace.json")
+    got = float(oracle.gelu_tanh(np.array(g["gelu"]["z"])))
+    assert abs(got - g["gelu"]["value"]) <= g["tolerance"]
+
+
+def test_aee_residual_trace():
+    g = _load("aee_hand_trace.json")["residual"]
+    x = np.array(_load("aee_hand_trace.json")["layer_norm"]["x"])
+    np.testing.assert_allclose(x + np.array(g["msa_out"]), g["x_prime"], atol=1e-15)
+
+
+def test_gelu_closed_forms():
+    z = np.linspace(-8, 8, 2001)
+    gz = oracle.gelu_tanh(z)
+    # tanh is odd, so GELU(z) - GELU(-z) = z exactly in real arithmetic.
+    np.testing.assert_allclose(gz - oracle.gelu_tanh(-z), z, atol=1e-14)
+    assert oracle.gelu_tanh(np.array(0.0)) == 0.0
+    assert oracle.gelu_tanh(np.array(30.0)) == 30.0
+    assert abs(float(oracle.gelu_tanh(np.array(-30.0)))) < 1e-300
+    # It is the tanh form, not the erf form: they differ by up to ~5e-4.
+    erf_form = np.array([0.5 * v * (1.0 + math.erf(v / math.sqrt(2.0))) for v in z])
+    diff = np.abs(gz - erf_form).max()
+    assert 1e-4 < diff < 1e-3
+
+
+def test_gelu_matches_torch_tanh_gelu():
+    torch = pytest.importorskip("torch")
+    z = np.random.default_rng(0).standard_normal(4096) * 4
+    ref = torch.nn.functional.gelu(torch.from_numpy(z), approximate="tanh").numpy()
+    np.testing.assert_allclose(oracle.gelu_tanh(z), ref, rtol=1e-14, atol=1e-15)
+
+
+def test_layer_norm_moments_and_constant_row():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((7, 33)) * rng.uniform(0.1, 10, (7, 1)) + rng.uniform(-5, 5, (7, 1))
+    eps = 1e-5
+    y = oracle.layer_norm(x, eps)
+    np.testing.assert_allclose(y.mean(-1), 0.0, atol=1e-14)
+    var = x.var(-1)
+    np.testing.assert_allclose(y.var(-1), var / (var + eps), rtol=1e-12)
+    c = np.full((1, 16), 3.25)
+    assert np.all(oracle.layer_norm(c, 1e-6) == 0.0)
+
+
+def test_layer_norm_matches_torch():
+    torch = pytest.importorskip("torch")
+    x = np.random.default_rng(4).standard_normal((9, 48)) * 3 + 1
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(x), (48,), eps=1e-6).numpy()
+    np.testing.assert_allclose(oracle.layer_norm(x, 1e-6), ref, rtol=1e-12, atol=1e-13)
+
+
+def test_attention_rows_are_stochastic():
+    rng = np.random.default_rng(5)
+    x, wq, wk, *_ = _rand_block(rng, 3, 9, 12, 8)
+    a = oracle.attention_weights(oracle.layer_norm(x, 1e-6), wq, wk, 3)
+    assert a.shape == (3, 3, 9, 9)
+    assert np.all(a >= 0)
+    np.testing.assert_allclose(a.sum(-1), 1.0, atol=1e-14)
+    # Columns need not sum to one (no symmetry between queries and keys).
+    assert np.abs(a.sum(-2) - 1.0).max() > 1e-3
+
+
+def test_attention_closed_forms():
+    rng = np.random.default_rng(6)
+    x, wq, wk, wv, *_ = _rand_block(rng, 2, 6, 8, 8)
+    xn = oracle.layer_norm(x, 1e-6)
+    v = xn @ wv
+    # Zero queries: every score is 0, weights are uniform, output = token mean of V.
+    att = oracle.multi_head_attention(xn, np.zeros_like(wq), wk, wv, 4)
+    np.testing.assert_allclose(att, np.broadcast_to(v.mean(1, keepdims=True), att.shape),
+                               atol=1e-14)
+    # One token: it attends only to itself, output = V.
+    att1 = oracle.multi_head_attention(xn[:, :1], wq, wk, wv, 4)
+    np.testing.assert_allclose(att1, v[:, :1], atol=1e-15)
+
+
+def test_attention_matches_torch_sdpa():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(7)
+    N, T, D, H = 2, 11, 24, 3
+    x, wq, wk, wv, *_ = _rand_block(rng, N, T, D, 8)
+    xn = oracle.layer_norm(x, 1e-6)
+    q, k, v = (torch.from_numpy(xn @ w).view(N, T, H, D // H).transpose(1, 2).contiguous()
+               for w in (wq, wk, wv))
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v)
+    ref = ref.transpose(1, 2).reshape(N, T, D).numpy()
+    np.testing.assert_allclose(oracle.multi_head_attention(xn, wq, wk, wv, H), ref,
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_zero_update_identity():
+    rng = np.random.default_rng(8)
+    x, wq, wk, wv, wo, w1, w2 = _rand_block(rng, 3, 5, 8, 12)
+    out = oracle.vit_block(x, wq, wk, wv, np.zeros_like(wo), w1, np.zeros_like(w2), 2, 1e-5)
+    np.testing.assert_array_equal(out, x)
+    # Only the MLP branch, or only the attention branch.
+    st = oracle.vit_block_stages(x, wq, wk, wv, wo, w1, w2, 2, 1e-5)
+    out_no_mlp = oracle.vit_block(x, wq, wk, wv, wo, w1, np.zeros_like(w2), 2, 1e-5)
+    np.testing.assert_array_equal(out_no_mlp, st["y"])
+    out_no_att = oracle.vit_block(x, wq, wk, wv, np.zeros_like(wo), w1, w2, 2, 1e-5)
+    xn = oracle.layer_norm(x, 1e-5)
+    mlp_x = oracle.gelu_tanh(xn @ w1) @ w2
+    np.testing.assert_allclose(out_no_att, x + mlp_x, atol=1e-14)
+
+
+def test_token_permutation_equivariance():
+    rng = np.random.default_rng(9)
+    args = _rand_block(rng, 2, 7, 8, 16)
+    out = oracle.vit_block(*args, 2, 1e-6)
+    perm = rng.permutation(7)
+    args_p = [args[0][:, perm]] + args[1:]
+    out_p = oracle.vit_block(*args_p, 2, 1e-6)
+    np.testing.assert_allclose(out_p, out[:, perm], atol=1e-13)
+
+
+def test_batch_independence_and_chunking():
+    rng = np.random.default_rng(10)
+    args = _rand_block(rng, 5, 4, 8, 16)
+    out = oracle.vit_block(*args, 4, 1e-6, chunk=8)
+    x2 = args[0].copy()
+    x2[3] = rng.standard_normal(x2[3].shape)
+    out2 = oracle.vit_block(*([x2] + args[1:]), 4, 1e-6, chunk=8)
+    np.testing.assert_allclose(np.delete(out2, 3, 0), np.delete(out, 3, 0), atol=1e-14)
+    out_c1 = oracle.vit_block(*args, 4, 1e-6, chunk=1)
+    np.testing.assert_allclose(out_c1, out, atol=1e-14)
+
+
+def test_shape_checks():
+    x = np.zeros((1, 2, 6))
+    w = np.zeros((6, 6))
+    with pytest.raises(ValueError):
+        oracle.vit_block(x, w, w, w, w, w, w, 4, 1e-6)
+    with pytest.raises(ValueError):
+        oracle.vit_block(x[0], w, w, w, w, w, w, 2, 1e-6)
+
+
+# ------------------------------------------------------- planted mistakes
+
+def _ln_unbiased(x, eps):
+    x = np.asarray(x, dtype=np.float64)
+    return (x - x.mean(-1, keepdims=True)) / np.sqrt(x.var(-1, ddof=1, keepdims=True) + eps)
+
+
+def _ln_eps_outside(x, eps):
+    x = np.asarray(x, dtype=np.float64)
+    return (x - x.mean(-1, keepdims=True)) / (np.sqrt(x.var(-1, keepdims=True)) + eps)
+
+
+def _scores_unscaled(qh, kh):
+    return np.matmul(qh, np.swapaxes(kh, -1, -2))
+
+
+def _scores_over_dh(qh, kh):
+    return np.matmul(qh, np.swapaxes(kh, -1, -2)) / qh.shape[-1]
+
+
+def _project_transposed(a, w):
+    w = np.asarray(w, dtype=np.float64)
+    return np.matmul(a, w.T) if w.shape[0] == w.shape[1] else np.matmul(a, w)
+
+
+def _gelu_erf(z):
+    z = np.asarray(z, dtype=np.float64)
+    return np.vectorize(lambda v: 0.5 * v * (1.0 + math.erf(v / math.sqrt(2.0))))(z)
+
+
+def _gelu_bad_constant(z):
+    z = np.asarray(z, dtype=np.float64)
+    return 0.5 * z * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (z + 0.04471 * z ** 3)))
+
+
+def _split_interleaved(t, num_heads):
+    n, tt, d = t.shape
+    return t.reshape(n, tt, d // num_heads, num_heads).transpose(0, 3, 1, 2)
+
+
+def _softmax_wrong_axis(s):
+    e = np.exp(s - s.max(-2, keepdims=True))
+    return e / e.sum(-2, keepdims=True)
+
+
+def _softmax_causal(s):
+    t = s.shape[-1]
+    s = np.where(np.triu(np.ones((t, t), bool), 1), -np.inf, s)
+    e = np.exp(s - s.max(-1, keepdims=True))
+    return e / e.sum(-1, keepdims=True)
+
+
+_MERGE = ob.merge_heads
+
+
+def _merge_reversed(o):
+    return _MERGE(np.asarray(o)[:, ::-1])
+
+
+MUTANTS = {
+    "unbiased variance": ("layer_norm", _ln_unbiased),
+    "eps outside sqrt": ("layer_norm", _ln_eps_outside),
+    "no score scale": ("attention_scores", _scores_unscaled),
+    "scale 1/d_h": ("attention_scores", _scores_over_dh),
+    "nn.Linear weight layout": ("project", _project_transposed),
+    "erf GELU": ("gelu_tanh", _gelu_erf),
+    "GELU constant 0.04471": ("gelu_tanh", _gelu_bad_constant),
+    "interleaved heads": ("split_heads", _split_interleaved),
+    "softmax over queries": ("softmax_rows", _softmax_wrong_axis),
+    "causal mask": ("softmax_rows", _softmax_causal),
+    "heads merged in reverse": ("merge_heads", _merge_reversed),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(ob, attr, fn)
+    caught_tt = _tt_max_err() > TT_TOL
+    caught_brute = _brute_max_err() > 1e-9
+    assert caught_tt or caught_brute, f"pins did not catch: {name}"
