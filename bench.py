@@ -1,0 +1,233 @@
+"""Throughput of one pre-LN ViT encoder block forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload vit_l16]
+
+A step is one full block forward (7 kernels through vitblk_forward) over one
+batch of synthetic inputs already resident in HBM.  Prints ONE JSON line:
+tokens/s for the whole job, ms per step, the block's achieved TFLOP/s and
+fraction of the bf16 dense MFMA peak, per-kernel times (each step's kernel
+timed alone with HIP events on the launch stream), the roofline of the
+dominant kernel, a parity check of the timed output against the float64
+oracle on sampled sequences, and the oracle's own throughput on the host
+cores (cpu_baseline).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "encoder-block fwd tokens/sec + % bf16 MFMA peak, ViT-L/16 shape N=256"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+
+
+def block_flops(N, T, D, F):
+    """Matmul FLOPs of one block: N*T*(8 D^2 + 4 D F + 4 T D)."""
+    return N * T * (8 * D * D + 4 * D * F + 4 * T * D)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="vit_l16")
+    ap.add_argument("--kernel-reps", type=int, default=20,
+                    help="launches per step kernel in the per-kernel timing")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target host time for the oracle baseline sample (0 = skip)")
+    ap.add_argument("--seed", type=int, default=0)
+    return ap.parse_args()
+
+
+def time_launches(fn, reps, torch):
+    """Average duration of fn() (one kernel launch) over reps, HIP events on the launch stream."""
+    s = torch.cuda.current_stream()
+    fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(s)
+    for _ in range(reps):
+        fn()
+    e1.record(s)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            return int(info[0]["num_threads"]), info[0].get("internal_api", "blas")
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0)), "unknown"
+
+
+def cpu_baseline(inp, w, target_s, got_out):
+    """Time the float64 oracle on a bounded sample of sequences; also check parity there."""
+    import oracle
+    args = (inp["w_q"], inp["w_k"], inp["w_v"], inp["w_o"], inp["w_mlp1"], inp["w_mlp2"],
+            w.H, w.eps)
+    t0 = time.perf_counter()
+    ref0 = oracle.vit_block(inp["x"][:1], *args)
+    t1 = time.perf_counter() - t0
+    n = int(max(1, min(w.N, math.floor(target_s / max(t1, 1e-6)))))
+    seqs = sorted(set(np.linspace(0, w.N - 1, n).astype(int).tolist()))
+    t0 = time.perf_counter()
+    ref = oracle.vit_block(inp["x"][seqs], *args)
+    dt = time.perf_counter() - t0
+    got = got_out[seqs]
+    err = np.abs(got - ref)
+    viol = float((err / (1.0 + np.abs(ref))).max())
+    threads, api = blas_threads()
+    del ref0
+    return ({"value": len(seqs) * w.T / dt, "unit": "tokens/s", "cores": threads,
+             "kind": "oracle",
+             "sample": f"{len(seqs)} of {w.N} sequences ({len(seqs) * w.T} tokens), float64 "
+                       f"NumPy ({api} BLAS, {threads} threads), {dt:.1f} s",
+             "host_cpus": len(os.sched_getaffinity(0))},
+            {"violation": viol, "bar": 3e-2 if w.dtype == "bf16" else 2e-4,
+             "mean_abs_err": float(err.mean()), "sequences": len(seqs)})
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(--gpus {a.gpus} requested). Under data parallelism each GPU would run "
+              "this same block on its own share of the sequences.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import vision_transformer_encoder_amd as vb
+    from vision_transformer_encoder_amd.inputs import WORKLOADS, make_block_inputs
+
+    w = WORKLOADS[a.workload]
+    tdt = {"fp32": torch.float32, "bf16": torch.bfloat16}[w.dtype]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_block_inputs(w.N, w.T, w.D, w.F, w.dtype, seed=a.seed)
+    g = {k: torch.from_numpy(v.astype(np.float32)).to(dev, tdt) for k, v in inp.items()}
+    out = torch.empty_like(g["x"])
+    ws = torch.empty(vb.workspace_bytes(w.N, w.T, w.D, w.F, w.H, tdt), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        vb.forward(g["x"], g["w_q"], g["w_k"], g["w_v"], g["w_o"], g["w_mlp1"], g["w_mlp2"],
+                   w.H, w.eps, out=out, workspace=ws)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(s)
+    for _ in range(a.steps):
+        step()
+    e1.record(s)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / a.steps
+    got = out.to("cpu", torch.float64).numpy()
+
+    # Each step's kernel alone, on the same shapes (separate buffers per step).
+    M, D, F = w.M, w.D, w.F
+    x2 = g["x"].view(M, D)
+    xn = torch.empty_like(x2)
+    qkv = torch.empty((M, 3 * D), dtype=tdt, device=dev)
+    att = torch.empty_like(x2)
+    y = torch.empty_like(x2)
+    yn = torch.empty_like(x2)
+    hid = torch.empty((M, F), dtype=tdt, device=dev)
+    o2 = torch.empty_like(x2)
+    vb.layernorm(x2, w.eps, out=xn)
+    vb.qkv_projection(xn, g["w_q"], g["w_k"], g["w_v"], out=qkv)
+    vb.attention(qkv, w.N, w.T, w.H, out=att)
+    vb.linear(att, g["w_o"], vb.EPI_RESIDUAL, residual=x2, out=y)
+    vb.layernorm(y, w.eps, out=yn)
+    vb.linear(yn, g["w_mlp1"], vb.EPI_GELU, out=hid)
+    es = 2 if w.dtype == "bf16" else 4
+    kern = {
+        "ln1": (lambda: vb.layernorm(x2, w.eps, out=xn), "hbm", 2 * M * D * es),
+        "qkv_gemm": (lambda: vb.qkv_projection(xn, g["w_q"], g["w_k"], g["w_v"], out=qkv),
+                     "mfma", 2 * M * D * 3 * D),
+        "attention": (lambda: vb.attention(qkv, w.N, w.T, w.H, out=att), "mfma",
+                      4 * w.N * w.T * w.T * D),
+        "oproj_residual": (lambda: vb.linear(att, g["w_o"], vb.EPI_RESIDUAL, residual=x2,
+                                             out=y), "mfma", 2 * M * D * D),
+        "ln2": (lambda: vb.layernorm(y, w.eps, out=yn), "hbm", 2 * M * D * es),
+        "mlp1_gelu": (lambda: vb.linear(yn, g["w_mlp1"], vb.EPI_GELU, out=hid), "mfma",
+                      2 * M * D * F),
+        "mlp2_residual": (lambda: vb.linear(hid, g["w_mlp2"], vb.EPI_RESIDUAL, residual=y,
+                                            out=o2), "mfma", 2 * M * F * D),
+    }
+    per = {}
+    for name, (fn, bound, work) in kern.items():
+        kms = time_launches(fn, a.kernel_reps, torch)
+        rate = work / (kms * 1e-3)
+        per[name] = {"ms": round(kms, 5), "bound": bound,
+                     ("tflops" if bound == "mfma" else "gbs"):
+                     round(rate / (1e12 if bound == "mfma" else 1e9), 2)}
+    dom = max(per, key=lambda k: per[k]["ms"])
+    fn, bound, work = kern[dom]
+    dms = per[dom]["ms"]
+    if bound == "mfma":
+        ach = work / (dms * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "work_per_launch": f"{work / 1e9:.2f} GFLOP"}
+    else:
+        ach = work / (dms * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                "work_per_launch": f"{work / 1e6:.1f} MB"}
+
+    flops = block_flops(w.N, w.T, w.D, w.F)
+    tflops = flops / (ms * 1e-3) / 1e12
+    res = {
+        "metric": METRIC,
+        "value": round(w.M / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) weights)",
+        "config": {"workload": w.name, "N": w.N, "T": w.T, "D": w.D, "H": w.H, "F": w.F,
+                   "eps": w.eps, "global_batch": w.N, "seq_len": w.T, "parallelism": "none"},
+        "block_tflops": round(tflops, 2),
+        "block_frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "wall_s_timed": round(t_wall, 3),
+        "kernels": per,
+        "roofline": roof,
+    }
+    if a.cpu_seconds > 0:
+        cb, par = cpu_baseline(inp, w, a.cpu_seconds, got)
+        res["cpu_baseline"] = cb
+        res["parity"] = par
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

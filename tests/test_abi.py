@@ -1,0 +1,157 @@
+"""C-ABI tests that run without a GPU.
+
+They load libvitblk.so, check that it exports every function include/vitblk.h
+declares, and drive every argument-error path with fake (never dereferenced)
+device addresses: all checks run on the host before any HIP call, so no
+kernel is launched here.
+"""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import vision_transformer_encoder_amd as vb
+from vision_transformer_encoder_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vitblk.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, ALIAS = 0, -1, -2, -3, -4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return vb.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(vitblk_\w+)\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert names, "no declarations parsed from the header"
+    assert sorted(_lib.SIGNATURES) == names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code, name in _lib.STATUS.items():
+        assert vb.status_string(code).startswith(name)
+    assert "unknown" in vb.status_string(12345)
+
+
+def test_workspace_bytes():
+    # three 256-B aligned regions: [M, max(3D, F)], [M, D], [M, D]
+    def expect(N, T, D, F, es):
+        r = lambda b: (b + 255) // 256 * 256  # noqa: E731
+        M = N * T
+        return r(M * max(3 * D, F) * es) + 2 * r(M * D * es)
+    assert vb.workspace_bytes(256, 197, 1024, 4096, 16, vb.VITBLK_BF16) == expect(256, 197, 1024, 4096, 2)
+    assert vb.workspace_bytes(4, 5, 16, 32, 2, vb.VITBLK_FP32) == expect(4, 5, 16, 32, 4)
+    assert vb.workspace_bytes(2, 3, 8, 8, 2, vb.VITBLK_FP32) == expect(2, 3, 8, 8, 4)  # 3D > F
+    assert vb.workspace_bytes(1, 1, 6, 4, 4, vb.VITBLK_BF16) == 0       # H does not divide D
+    assert vb.workspace_bytes(0, 1, 8, 8, 1, vb.VITBLK_BF16) == 0       # empty batch
+    assert vb.workspace_bytes(1, 1, 8, 8, 1, 7) == 0                    # unknown dtype
+    assert vb.workspace_bytes(1, 1, 2048 * 2, 8, 2, vb.VITBLK_BF16) == 0  # head width 2048
+
+
+# Fake device addresses, 16-byte aligned and far apart (never dereferenced).
+GAP = 1 << 36
+
+
+def _addr(i):
+    return ctypes.c_void_p((i + 1) * GAP)
+
+
+def _fwd(lib, N=2, T=5, D=16, F=32, H=2, eps=1e-6, dtype=1, ptrs=None, ws=None, ws_bytes=None):
+    p = [_addr(i) for i in range(8)] if ptrs is None else ptrs
+    if ws is None:
+        ws = _addr(20)
+    if ws_bytes is None:
+        ws_bytes = max(vb.workspace_bytes(max(N, 1), max(T, 1), max(D, 1), max(F, 1),
+                                          max(H, 1), 1), 1 << 20)
+    return lib.vitblk_forward(*p, N, T, D, F, H, eps, dtype, ws, ws_bytes, None)
+
+
+def test_forward_invalid_args(lib):
+    assert _fwd(lib, N=0) == INVALID
+    assert _fwd(lib, T=-1) == INVALID
+    assert _fwd(lib, D=0) == INVALID
+    assert _fwd(lib, F=0) == INVALID
+    assert _fwd(lib, H=0) == INVALID
+    assert _fwd(lib, D=16, H=3) == INVALID
+    assert _fwd(lib, eps=-1e-6) == INVALID
+    assert _fwd(lib, eps=math.nan) == INVALID
+    assert _fwd(lib, eps=math.inf) == INVALID
+    assert _fwd(lib, dtype=2) == INVALID
+    for i in range(8):
+        p = [_addr(j) for j in range(8)]
+        p[i] = None
+        assert _fwd(lib, ptrs=p) == INVALID, i
+        p[i] = ctypes.c_void_p((i + 1) * GAP + 2)  # misaligned
+        assert _fwd(lib, ptrs=p) == INVALID, i
+
+
+def test_forward_unsupported_sizes(lib):
+    assert _fwd(lib, N=1 << 20, T=1 << 12, ws_bytes=1) == UNSUPPORTED  # N*T > 2^31-1
+    assert _fwd(lib, D=4096, H=2, F=8) == UNSUPPORTED                   # head width 2048
+
+
+def test_forward_workspace_errors(lib):
+    need = vb.workspace_bytes(2, 5, 16, 32, 2, 1)
+    assert _fwd(lib, ws_bytes=need - 1) == WORKSPACE
+    assert _fwd(lib, ws=ctypes.c_void_p(0)) == WORKSPACE
+
+
+def test_forward_alias_errors(lib):
+    # out overlapping x
+    p = [_addr(i) for i in range(8)]
+    p[7] = ctypes.c_void_p(p[0].value + 64)
+    assert _fwd(lib, ptrs=p) == ALIAS
+    # out overlapping w_mlp2
+    p = [_addr(i) for i in range(8)]
+    p[7] = ctypes.c_void_p(p[6].value)
+    assert _fwd(lib, ptrs=p) == ALIAS
+    # workspace overlapping out, and workspace overlapping an input
+    assert _fwd(lib, ws=ctypes.c_void_p(_addr(7).value + 16)) == ALIAS
+    assert _fwd(lib, ws=ctypes.c_void_p(_addr(3).value)) == ALIAS
+    # (Calls whose arguments all pass the checks would launch kernels, so the
+    # accepting side of these checks is covered by the GPU tests only.)
+
+
+def test_step_entry_points_errors(lib):
+    a, b, c, d, e = (_addr(i) for i in range(5))
+    # layernorm
+    assert lib.vitblk_layernorm(None, b, 4, 8, 1e-5, 1, None) == INVALID
+    assert lib.vitblk_layernorm(a, b, 0, 8, 1e-5, 1, None) == INVALID
+    assert lib.vitblk_layernorm(a, b, 4, 8, -1.0, 1, None) == INVALID
+    assert lib.vitblk_layernorm(a, b, 4, 8, 1e-5, 9, None) == INVALID
+    assert lib.vitblk_layernorm(a, a, 4, 8, 1e-5, 1, None) == ALIAS
+    # qkv
+    assert lib.vitblk_qkv_projection(a, b, c, d, None, 4, 8, 1, None) == INVALID
+    assert lib.vitblk_qkv_projection(a, b, c, d, a, 4, 8, 1, None) == ALIAS
+    assert lib.vitblk_qkv_projection(a, b, c, d, e, 4, 0, 1, None) == INVALID
+    # attention
+    assert lib.vitblk_attention(a, b, 2, 3, 8, 3, 1, None) == INVALID   # H does not divide D
+    assert lib.vitblk_attention(a, a, 2, 3, 8, 2, 1, None) == ALIAS
+    assert lib.vitblk_attention(a, b, 1, 1, 4096, 2, 1, None) == UNSUPPORTED
+    # linear
+    assert lib.vitblk_linear(a, b, None, c, 4, 8, 8, vb.EPI_RESIDUAL, 1, None) == INVALID
+    assert lib.vitblk_linear(a, b, None, c, 4, 8, 8, 7, 1, None) == INVALID
+    assert lib.vitblk_linear(a, b, c, c, 4, 8, 8, vb.EPI_RESIDUAL, 1, None) == ALIAS
+    assert lib.vitblk_linear(a, b, None, a, 4, 8, 8, vb.EPI_NONE, 1, None) == ALIAS
+    assert lib.vitblk_linear(a, b, None, c, 4, -8, 8, vb.EPI_GELU, 1, None) == INVALID
+
+
+def test_python_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 2, 8)
+    w = torch.zeros(8, 8)
+    with pytest.raises(ValueError):
+        vb.forward(x, w, w, w, w, w, w, 2, 1e-6)

@@ -1,0 +1,203 @@
+"""GPU parity: every step and the whole block against the float64 oracle.
+
+All inputs are seeded and synthetic (vision_transformer_encoder_amd.inputs),
+rounded to the device dtype; the oracle consumes exactly the same values.
+Bars (elementwise): fp32 |g - o| <= 2e-4 (1 + |o|), bf16 <= 3e-2 (1 + |o|).
+Full-size workloads run on the GPU in full; the oracle checks sampled
+sequences, which is exact because sequences never interact.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import vision_transformer_encoder_amd as vb
+from vision_transformer_encoder_amd.inputs import WORKLOADS, make_block_inputs, round_to
+
+from gpu_util import TOL, assert_close, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _rand(rng, shape, dtype, scale=1.0, offset=0.0):
+    return round_to(rng.standard_normal(shape) * scale + offset, dtype)
+
+
+# ------------------------------------------------------------------ steps
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("rows,D", [(37, 768), (5, 1280), (64, 1024), (3, 20), (2, 4104),
+                                    (9, 16)])
+def test_layernorm(dtype, rows, D):
+    rng = np.random.default_rng(rows * 1000 + D)
+    x = _rand(rng, (rows, D), dtype, scale=3.0, offset=1.5)
+    x[0] = round_to(np.full(D, 2.5), dtype)  # constant token -> exactly 0
+    got = to_host(vb.layernorm(to_dev(x, dtype), 1e-6))
+    assert np.all(got[0] == 0.0)
+    assert_close(got, oracle.layer_norm(x, 1e-6), dtype, f"LN rows={rows} D={D}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("M,D", [(300, 256), (515, 768), (50, 24), (7, 64)])
+def test_qkv_projection(dtype, M, D):
+    rng = np.random.default_rng(M + D)
+    xn = _rand(rng, (M, D), dtype)
+    ws = [_rand(rng, (D, D), dtype, scale=1 / math.sqrt(D)) for _ in range(3)]
+    got = to_host(vb.qkv_projection(to_dev(xn, dtype), *(to_dev(w, dtype) for w in ws)))
+    ref = np.concatenate([oracle.project(xn, w) for w in ws], axis=1)
+    assert_close(got, ref, dtype, f"QKV M={M} D={D}")
+
+
+EPIS = {"none": vb.EPI_NONE, "residual": vb.EPI_RESIDUAL, "gelu": vb.EPI_GELU}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("epi", sorted(EPIS))
+@pytest.mark.parametrize("M,K,N", [(300, 256, 512), (129, 1024, 200), (33, 40, 24),
+                                   (600, 4096, 256)])
+def test_linear(dtype, epi, M, K, N):
+    rng = np.random.default_rng(M * 7 + K * 3 + N)
+    a = _rand(rng, (M, K), dtype)
+    w = _rand(rng, (K, N), dtype, scale=1 / math.sqrt(K))
+    r = _rand(rng, (M, N), dtype)
+    res = to_dev(r, dtype) if epi == "residual" else None
+    got = to_host(vb.linear(to_dev(a, dtype), to_dev(w, dtype), EPIS[epi], residual=res))
+    ref = oracle.project(a, w)
+    if epi == "residual":
+        ref = r + ref
+    elif epi == "gelu":
+        ref = oracle.gelu_tanh(ref)
+    assert_close(got, ref, dtype, f"linear {epi} M={M} K={K} N={N}")
+
+
+def _attention_ref(q, k, v, H):
+    a = oracle.softmax_rows(oracle.attention_scores(oracle.split_heads(q, H),
+                                                    oracle.split_heads(k, H)))
+    return oracle.merge_heads(np.matmul(a, oracle.split_heads(v, H)))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("N,T,D,H", [
+    (2, 197, 128, 2),    # d_h 64, ViT token count
+    (2, 257, 160, 2),    # d_h 80
+    (1, 1025, 64, 1),    # long sequence
+    (3, 1, 128, 2),      # single token: output = V
+    (2, 33, 96, 3),      # d_h 32, one key past a 32-block
+    (2, 65, 256, 2),     # d_h 128
+    (2, 96, 192, 2),     # d_h 96, T a multiple of 32 but not 64
+    (2, 50, 24, 3),      # d_h 8 (generic kernel)
+    (1, 7, 48, 1),       # d_h 48 (generic kernel)
+])
+def test_attention(dtype, N, T, D, H):
+    rng = np.random.default_rng(N * 100000 + T * 100 + D)
+    q, k, v = (_rand(rng, (N, T, D), dtype, scale=1.5) for _ in range(3))
+    qkv = np.concatenate([q, k, v], axis=-1).reshape(N * T, 3 * D)
+    got = to_host(vb.attention(to_dev(qkv, dtype), N, T, H)).reshape(N, T, D)
+    ref = _attention_ref(q, k, v, H)
+    assert_close(got, ref, dtype, f"attention N={N} T={T} D={D} H={H}")
+
+
+# ------------------------------------------------------------------ whole block
+
+def _run_block(inp, H, eps, dtype, stream=None):
+    dev = {k: to_dev(v, dtype) for k, v in inp.items()}
+    out = vb.forward(dev["x"], dev["w_q"], dev["w_k"], dev["w_v"], dev["w_o"], dev["w_mlp1"],
+                     dev["w_mlp2"], H, eps, stream=stream)
+    return out, dev
+
+
+def _oracle(inp, H, eps, seqs=None):
+    x = inp["x"] if seqs is None else inp["x"][seqs]
+    return oracle.vit_block(x, inp["w_q"], inp["w_k"], inp["w_v"], inp["w_o"], inp["w_mlp1"],
+                            inp["w_mlp2"], H, eps)
+
+
+SMALL_BLOCKS = [
+    # (N, T, D, H, F, eps, dtype)
+    (4, 5, 16, 2, 32, 1e-5, "fp32"),       # the tiny workload
+    (2, 50, 64, 4, 256, 1e-6, "fp32"),
+    (3, 197, 256, 4, 1024, 1e-6, "bf16"),  # several tiles, ragged M tail
+    (2, 257, 320, 4, 1280, 1e-6, "bf16"),  # d_h 80
+    (2, 65, 128, 2, 512, 1e-5, "bf16"),
+    (2, 9, 24, 3, 40, 1e-6, "bf16"),       # shapes only the generic kernels take
+    (1, 3, 8, 8, 8, 1e-6, "bf16"),         # H = D (head width 1)
+]
+
+
+@pytest.mark.parametrize("N,T,D,H,F,eps,dtype", SMALL_BLOCKS)
+def test_block_small(N, T, D, H, F, eps, dtype):
+    inp = make_block_inputs(N, T, D, F, dtype, seed=0)
+    out, _ = _run_block(inp, H, eps, dtype)
+    assert_close(to_host(out), _oracle(inp, H, eps), dtype, f"block N={N} T={T} D={D}")
+
+
+@pytest.mark.parametrize("name", ["vit_b16", "vit_l16", "vit_h14", "long_t1025"])
+def test_block_full_size(name):
+    w = WORKLOADS[name]
+    inp = make_block_inputs(w.N, w.T, w.D, w.F, w.dtype, seed=0)
+    out, _ = _run_block(inp, w.H, w.eps, w.dtype)
+    got = to_host(out)
+    assert np.all(np.isfinite(got))
+    seqs = sorted({0, w.N // 2, w.N - 1})
+    assert_close(got[seqs], _oracle(inp, w.H, w.eps, seqs), w.dtype,
+                 f"{name} sequences {seqs}")
+
+
+def test_tiny_workload_seed0():
+    w = WORKLOADS["tiny"]
+    inp = make_block_inputs(w.N, w.T, w.D, w.F, w.dtype, seed=0)
+    out, _ = _run_block(inp, w.H, w.eps, w.dtype)
+    assert_close(to_host(out), _oracle(inp, w.H, w.eps), "fp32", "tiny")
+
+
+# ------------------------------------------------------------------ invariants
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_zero_update_identity_is_exact(dtype):
+    inp = make_block_inputs(2, 197, 256, 1024, dtype, seed=3)
+    inp["w_o"] = np.zeros_like(inp["w_o"])
+    inp["w_mlp2"] = np.zeros_like(inp["w_mlp2"])
+    out, dev = _run_block(inp, 4, 1e-6, dtype)
+    import torch
+    assert torch.equal(out, dev["x"])
+
+
+def test_batch_independence_and_determinism():
+    import torch
+    inp = make_block_inputs(4, 197, 256, 1024, "bf16", seed=4)
+    out1, _ = _run_block(inp, 4, 1e-6, "bf16")
+    out2, _ = _run_block(inp, 4, 1e-6, "bf16")
+    assert torch.equal(out1, out2)
+    inp2 = dict(inp)
+    inp2["x"] = inp["x"].copy()
+    inp2["x"][2] = round_to(np.random.default_rng(5).standard_normal(inp["x"][2].shape), "bf16")
+    out3, _ = _run_block(inp2, 4, 1e-6, "bf16")
+    keep = [0, 1, 3]
+    assert torch.equal(out1[keep], out3[keep])
+    assert not torch.equal(out1[2], out3[2])
+
+
+def test_token_permutation_equivariance():
+    inp = make_block_inputs(2, 197, 256, 1024, "bf16", seed=6)
+    perm = np.random.default_rng(7).permutation(197)
+    out, _ = _run_block(inp, 4, 1e-6, "bf16")
+    inp_p = dict(inp)
+    inp_p["x"] = inp["x"][:, perm]
+    out_p, _ = _run_block(inp_p, 4, 1e-6, "bf16")
+    assert_close(to_host(out_p), to_host(out)[:, perm], "bf16", "permuted tokens")
+
+
+def test_side_stream():
+    import torch
+    inp = make_block_inputs(2, 65, 128, 512, "bf16", seed=8)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out, _ = _run_block(inp, 2, 1e-6, "bf16", stream=s)
+    s.synchronize()
+    assert_close(to_host(out), _oracle(inp, 2, 1e-6), "bf16", "side stream")
+
+
+def test_tolerance_bars_are_the_stated_ones():
+    assert TOL == {"fp32": 2e-4, "bf16": 3e-2}

@@ -2,7 +2,24 @@
 
 The computation runs in hand-written HIP kernels for gfx950 inside
 ``libvitblk.so`` (C ABI declared in ``include/vitblk.h``); this package is the
-thin ctypes binding over it plus the seeded synthetic-input generator.
-Importing the package does not load the library; the first call does, and it
-raises if the library has not been built.
+thin ctypes binding over it plus the seeded synthetic-input generator
+(``inputs``).  Importing the package loads neither torch nor the library; the
+first call does, and it raises if the library has not been built.
 """
+
+from ._lib import (  # noqa: F401
+    EPI_GELU,
+    EPI_NONE,
+    EPI_RESIDUAL,
+    VITBLK_BF16,
+    VITBLK_FP32,
+    VitblkError,
+    attention,
+    forward,
+    layernorm,
+    linear,
+    load,
+    qkv_projection,
+    status_string,
+    workspace_bytes,
+)

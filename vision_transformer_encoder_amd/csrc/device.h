@@ -1,0 +1,129 @@
+// Device-side helpers shared by the vitblk kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vitblk {
+
+typedef uint16_t bf16_t;  // bfloat16 bit pattern as stored in memory
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------- conversions
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even float -> bfloat16 (NaN stays NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+// Two floats -> two packed bf16 in one dword (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+}
+
+// Element load/store of the storage type T (float or bf16_t) as float.
+template <typename T> __device__ __forceinline__ float load_f32(const T* p);
+template <> __device__ __forceinline__ float load_f32<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float load_f32<bf16_t>(const bf16_t* p) {
+  return bf16_to_f32(*p);
+}
+template <typename T> __device__ __forceinline__ void store_f32(T* p, float v);
+template <> __device__ __forceinline__ void store_f32<float>(float* p, float v) { *p = v; }
+template <> __device__ __forceinline__ void store_f32<bf16_t>(bf16_t* p, float v) {
+  *p = f32_to_bf16(v);
+}
+
+// ------------------------------------------------------------- math
+
+// GELU, tanh form: 0.5 z (1 + tanh(u)) with u = sqrt(2/pi) (z + 0.044715 z^3).
+// Uses 0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)), evaluated with the hardware
+// base-2 exponential; exact limits z -> +inf (z) and z -> -inf (-0).
+__device__ __forceinline__ float gelu_tanh_fast(float z) {
+  const float k0 = 0.7978845608028654f;        // sqrt(2/pi)
+  const float k1 = 0.044715f;
+  const float m2log2e = -2.8853900817779268f;  // -2 * log2(e)
+  float u = k0 * (z + k1 * z * z * z);
+  float e = __builtin_amdgcn_exp2f(m2log2e * u);
+  return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// Same function through the library tanh, for the fp32 path.
+__device__ __forceinline__ float gelu_tanh_precise(float z) {
+  const float k0 = 0.7978845608028654f;
+  return 0.5f * z * (1.0f + tanhf(k0 * (z + 0.044715f * z * z * z)));
+}
+
+// ------------------------------------------------------------- wave reductions
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over all 64 lanes of the wave; every lane receives the total.
+// Inside each 16-lane row: two quad permutes and two row rotations (DPP);
+// across the four rows: read one lane of each row.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_mov<0x124>(v);  // row_ror:4
+  v += dpp_mov<0x128>(v);  // row_ror:8
+  float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_mov<0xB1>(v));
+  v = fmaxf(v, dpp_mov<0x4E>(v));
+  v = fmaxf(v, dpp_mov<0x124>(v));
+  v = fmaxf(v, dpp_mov<0x128>(v));
+  float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// ------------------------------------------------------------- 16-byte memory ops
+
+__device__ __forceinline__ uint4 ld_global16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+__device__ __forceinline__ void st_global16(void* p, uint4 v) {
+  *reinterpret_cast<uint4*>(p) = v;
+}
+
+// 8x8 transpose of 16-bit elements held as 8 rows of 8 (one uint4 per row):
+// out[j] holds element j of every input row, row 0 in the lowest half-word.
+__device__ __forceinline__ void transpose8x8_b16(const uint4 in[8], uint4 out[8]) {
+  const uint32_t* w[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) w[r] = reinterpret_cast<const uint32_t*>(&in[r]);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    // element c of row r lives in dword c/2 of row r, half (c & 1)
+    uint32_t o[4];
+#pragma unroll
+    for (int rp = 0; rp < 4; ++rp) {
+      const uint32_t a = w[2 * rp][c >> 1];
+      const uint32_t b = w[2 * rp + 1][c >> 1];
+      o[rp] = (c & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+    }
+    out[c] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+}  // namespace vitblk

@@ -1,0 +1,130 @@
+// Row-wise LayerNorm without affine terms (crackedaicode.com "ViT Encoder
+// Block", "Normalize before each stage"): per token, the mean and the
+// population variance over its D features, then (x - mean) / sqrt(var + eps).
+//
+// One wave per row, four rows per 256-thread workgroup.  Each lane loads its
+// share of the row as 16-byte vectors and keeps it in registers, so the row
+// is read from HBM once and written once: the kernel is bound by HBM
+// bandwidth (2 * D * element size bytes per row).  Statistics are fp32 and
+// two-pass over the registers (mean, then the squared deviations), reduced
+// across the wave with DPP row operations and lane reads.
+#include <math.h>
+
+#include "device.h"
+#include "kernels.h"
+#include "vitblk.h"
+
+namespace vitblk {
+namespace {
+
+constexpr int kRowsPerBlock = 4;
+
+// 8 consecutive elements <-> 8 floats.
+__device__ __forceinline__ void load8(const bf16_t* p, float v[8]) {
+  const uint4 u = ld_global16(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float v[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void store8(bf16_t* p, const float v[8]) {
+  st_global16(p, make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                            pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])));
+}
+__device__ __forceinline__ void store8(float* p, const float v[8]) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+// NCH = upper bound on 8-element chunks per lane (D <= 512 * NCH).
+template <typename T, int NCH>
+__global__ __launch_bounds__(64 * kRowsPerBlock) void ln_rows_kernel(const T* __restrict__ x,
+                                                                     T* __restrict__ y,
+                                                                     int64_t rows, int D,
+                                                                     float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;  // whole wave leaves; no workgroup barrier follows
+  const int nchunks = D >> 3;
+  const T* xr = x + row * D;
+  T* yr = y + row * D;
+  float v[NCH][8];
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int idx = lane + 64 * c;
+    if (idx < nchunks) {
+      load8(xr + idx * 8, v[c]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += v[c][e];
+    }
+  }
+  const float inv_d = 1.0f / static_cast<float>(D);
+  const float mean = wave_sum(s) * inv_d;
+  float q = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    if (lane + 64 * c < nchunks) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float d = v[c][e] - mean;
+        q += d * d;
+      }
+    }
+  }
+  const float var = wave_sum(q) * inv_d;
+  const float rstd = 1.0f / sqrtf(var + eps);
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int idx = lane + 64 * c;
+    if (idx < nchunks) {
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (v[c][e] - mean) * rstd;
+      store8(yr + idx * 8, o);
+    }
+  }
+}
+
+template <typename T>
+hipError_t ln_fast_typed(const T* x, T* y, int64_t rows, int D, float eps, hipStream_t s) {
+  const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  const dim3 grid(static_cast<unsigned>(blocks)), block(64 * kRowsPerBlock);
+  const int cpl = (D / 8 + 63) / 64;  // chunks per lane
+  if (cpl <= 1)
+    hipLaunchKernelGGL((ln_rows_kernel<T, 1>), grid, block, 0, s, x, y, rows, D, eps);
+  else if (cpl <= 2)
+    hipLaunchKernelGGL((ln_rows_kernel<T, 2>), grid, block, 0, s, x, y, rows, D, eps);
+  else if (cpl <= 3)
+    hipLaunchKernelGGL((ln_rows_kernel<T, 3>), grid, block, 0, s, x, y, rows, D, eps);
+  else if (cpl <= 4)
+    hipLaunchKernelGGL((ln_rows_kernel<T, 4>), grid, block, 0, s, x, y, rows, D, eps);
+  else
+    hipLaunchKernelGGL((ln_rows_kernel<T, 8>), grid, block, 0, s, x, y, rows, D, eps);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_layernorm(const void* x, void* y, int64_t rows, int64_t D, float eps,
+                            int dtype, hipStream_t s) {
+  // Register-resident rows: D a multiple of 8 (16-byte bf16 vectors), at most
+  // 8 chunks of 8 per lane.
+  const bool fast = (D % 8 == 0) && (D <= 64 * 8 * 8);
+  if (!fast) return launch_layernorm_generic(x, y, rows, D, eps, dtype, s);
+  if (dtype == VITBLK_BF16)
+    return ln_fast_typed(static_cast<const bf16_t*>(x), static_cast<bf16_t*>(y), rows,
+                         static_cast<int>(D), eps, s);
+  return ln_fast_typed(static_cast<const float*>(x), static_cast<float*>(y), rows,
+                       static_cast<int>(D), eps, s);
+}
+
+}  // namespace vitblk

@@ -1,0 +1,46 @@
+// Host-side argument validation and workspace planning for the vitblk C ABI.
+// HIP-free: this interface and validate.cpp build with a plain C++ compiler,
+// so every error path can be exercised on a machine without a GPU.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+namespace vitblk {
+
+constexpr size_t kRegionAlign = 256;
+constexpr int64_t kMaxDim = 2147483647;   // every dim and N*T fit in int32
+constexpr int64_t kMaxHeadDim = 1024;
+
+size_t elem_size(int dtype);  // 0 for an unknown dtype
+
+struct WorkspacePlan {
+  size_t off_big;    // [M, max(3D, F)]: packed qkv, later the MLP hidden
+  size_t off_act;    // [M, D]: LN(x), then concatenated heads, then LN(y)
+  size_t off_y;      // [M, D]: first residual output
+  size_t total;
+};
+
+// Returns VITBLK_OK and fills *plan, or an error status.
+int plan_workspace(int64_t N, int64_t T, int64_t D, int64_t F, int64_t H, int dtype,
+                   WorkspacePlan* plan);
+
+int validate_forward(const void* x, const void* w_q, const void* w_k, const void* w_v,
+                     const void* w_o, const void* w_mlp1, const void* w_mlp2,
+                     const void* out, int64_t N, int64_t T, int64_t D, int64_t F,
+                     int64_t H, double eps, int dtype, const void* workspace,
+                     size_t workspace_bytes, WorkspacePlan* plan);
+
+int validate_layernorm(const void* x, const void* out, int64_t rows, int64_t D,
+                       double eps, int dtype);
+
+int validate_qkv(const void* xn, const void* w_q, const void* w_k, const void* w_v,
+                 const void* qkv, int64_t M, int64_t D, int dtype);
+
+int validate_attention(const void* qkv, const void* att, int64_t N, int64_t T, int64_t D,
+                       int64_t H, int dtype);
+
+int validate_linear(const void* a, const void* w, const void* residual, const void* out,
+                    int64_t M, int64_t K, int64_t Nout, int epilogue, int dtype);
+
+}  // namespace vitblk
