@@ -2,7 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload vit_l16]
 
-A step is one full block forward (7 kernels through vitblk_forward) over one
+A step is one full block forward (8 kernels through vitblk_forward: weight packing
+and the seven steps of the block) over one
 batch of synthetic inputs already resident in HBM.  Prints ONE JSON line:
 tokens/s for the whole job, ms per step, the block's achieved TFLOP/s and
 fraction of the bf16 dense MFMA peak, per-kernel times (each step's kernel
@@ -146,6 +147,8 @@ def main():
 
     # Each step's kernel alone, on the same shapes (separate buffers per step).
     M, D, F = w.M, w.D, w.F
+    packed = vb.pack_weights(g["w_q"], g["w_k"], g["w_v"], g["w_o"], g["w_mlp1"], g["w_mlp2"])
+    wqkv_t, wo_t, w1_t, w2_t = vb.packed_views(packed, D, F, tdt)
     x2 = g["x"].view(M, D)
     xn = torch.empty_like(x2)
     qkv = torch.empty((M, 3 * D), dtype=tdt, device=dev)
@@ -155,25 +158,27 @@ def main():
     hid = torch.empty((M, F), dtype=tdt, device=dev)
     o2 = torch.empty_like(x2)
     vb.layernorm(x2, w.eps, out=xn)
-    vb.qkv_projection(xn, g["w_q"], g["w_k"], g["w_v"], out=qkv)
+    vb.qkv_projection(xn, wqkv_t, out=qkv)
     vb.attention(qkv, w.N, w.T, w.H, out=att)
-    vb.linear(att, g["w_o"], vb.EPI_RESIDUAL, residual=x2, out=y)
+    vb.linear(att, wo_t, vb.EPI_RESIDUAL, residual=x2, out=y)
     vb.layernorm(y, w.eps, out=yn)
-    vb.linear(yn, g["w_mlp1"], vb.EPI_GELU, out=hid)
+    vb.linear(yn, w1_t, vb.EPI_GELU, out=hid)
     es = 2 if w.dtype == "bf16" else 4
+    wbytes = (4 * D * D + 2 * D * F) * es
     kern = {
+        "pack_weights": (lambda: vb.pack_weights(g["w_q"], g["w_k"], g["w_v"], g["w_o"],
+                                                 g["w_mlp1"], g["w_mlp2"], packed=packed),
+                         "hbm", 2 * wbytes),
         "ln1": (lambda: vb.layernorm(x2, w.eps, out=xn), "hbm", 2 * M * D * es),
-        "qkv_gemm": (lambda: vb.qkv_projection(xn, g["w_q"], g["w_k"], g["w_v"], out=qkv),
-                     "mfma", 2 * M * D * 3 * D),
+        "qkv_gemm": (lambda: vb.qkv_projection(xn, wqkv_t, out=qkv), "mfma", 2 * M * D * 3 * D),
         "attention": (lambda: vb.attention(qkv, w.N, w.T, w.H, out=att), "mfma",
                       4 * w.N * w.T * w.T * D),
-        "oproj_residual": (lambda: vb.linear(att, g["w_o"], vb.EPI_RESIDUAL, residual=x2,
-                                             out=y), "mfma", 2 * M * D * D),
+        "oproj_residual": (lambda: vb.linear(att, wo_t, vb.EPI_RESIDUAL, residual=x2, out=y),
+                           "mfma", 2 * M * D * D),
         "ln2": (lambda: vb.layernorm(y, w.eps, out=yn), "hbm", 2 * M * D * es),
-        "mlp1_gelu": (lambda: vb.linear(yn, g["w_mlp1"], vb.EPI_GELU, out=hid), "mfma",
-                      2 * M * D * F),
-        "mlp2_residual": (lambda: vb.linear(hid, g["w_mlp2"], vb.EPI_RESIDUAL, residual=y,
-                                            out=o2), "mfma", 2 * M * F * D),
+        "mlp1_gelu": (lambda: vb.linear(yn, w1_t, vb.EPI_GELU, out=hid), "mfma", 2 * M * D * F),
+        "mlp2_residual": (lambda: vb.linear(hid, w2_t, vb.EPI_RESIDUAL, residual=y, out=o2),
+                          "mfma", 2 * M * F * D),
     }
     per = {}
     for name, (fn, bound, work) in kern.items():

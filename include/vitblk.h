@@ -86,15 +86,40 @@ const char* vitblk_status_string(int status);
  * Bytes of device workspace vitblk_forward() needs for these sizes, or 0 if
  * the arguments are invalid.  Pure host function: no HIP call.
  *
- * Layout (each region starts on a 256-byte boundary), es = element size:
- *   region 0: M x max(3D, F) elements: packed Q|K|V [M, 3D], later the
- *             MLP hidden activations [M, F]
- *   region 1: M x D elements: LN(x), later the concatenated heads, later LN(y)
- *   region 2: M x D elements: y = x + att @ w_o
- * with M = N*T.  (ViT-L/16, N = 256, bf16: about 620 MB.)
+ * Layout (each region starts on a 256-byte boundary), es = element size,
+ * M = N*T:
+ *   packed weights, vitblk_packed_weights_bytes(D, F, dtype) bytes
+ *   activations:
+ *     region 0: M x max(3D, F) elements: packed Q|K|V [M, 3D], later the
+ *               MLP hidden activations [M, F]
+ *     region 1: M x D elements: LN(x), later the concatenated heads, later LN(y)
+ *     region 2: M x D elements: y = x + att @ w_o
+ * (ViT-L/16, N = 256, bf16: about 645 MB.)  vitblk_forward_packed() needs
+ * only the activations: vitblk_workspace_bytes() minus
+ * vitblk_packed_weights_bytes().
  */
 size_t vitblk_workspace_bytes(int64_t N, int64_t T, int64_t D, int64_t F, int64_t H,
                               int dtype);
+
+/*
+ * Out-major ("packed") copies of the six weights, the layout the GEMM kernels
+ * read: both operands of every product contiguous along the reduction axis.
+ * Regions, each on a 256-byte boundary, in this order:
+ *   Wqkv^T [3D, D]  row n < D is column n of w_q, rows D..2D-1 columns of
+ *                   w_k, rows 2D..3D-1 columns of w_v
+ *   Wo^T   [D, D]
+ *   W1^T   [F, D]   (w_mlp1 is [D, F])
+ *   W2^T   [D, F]   (w_mlp2 is [F, D])
+ * vitblk_packed_weights_bytes() returns the size (0 for invalid arguments;
+ * host only).  vitblk_pack_weights() writes it on `stream` (one launch); the
+ * buffer must not overlap a weight.  Callers that run many blocks with the
+ * same weights pack once and call vitblk_forward_packed().
+ */
+size_t vitblk_packed_weights_bytes(int64_t D, int64_t F, int dtype);
+
+int vitblk_pack_weights(const void* w_q, const void* w_k, const void* w_v, const void* w_o,
+                        const void* w_mlp1, const void* w_mlp2, void* packed, int64_t D,
+                        int64_t F, int dtype, vitblk_stream_t stream);
 
 /*
  * One encoder block forward: out = block(x).
@@ -111,14 +136,25 @@ size_t vitblk_workspace_bytes(int64_t N, int64_t T, int64_t D, int64_t F, int64_
  *          vitblk_workspace_bytes(N, T, D, F, H, dtype) bytes; its contents
  *          on entry are ignored and on return are unspecified
  *
- * Seven kernels run in order on `stream`: LN, fused QKV projection,
- * attention, output projection + residual, LN, MLP1 + GELU, MLP2 + residual.
+ * Eight kernels run in order on `stream`: weight packing, LN, fused QKV
+ * projection, attention, output projection + residual, LN, MLP1 + GELU,
+ * MLP2 + residual.
  */
 int vitblk_forward(const void* x, const void* w_q, const void* w_k, const void* w_v,
                    const void* w_o, const void* w_mlp1, const void* w_mlp2, void* out,
                    int64_t N, int64_t T, int64_t D, int64_t F, int64_t H, double eps,
                    int dtype, void* workspace, size_t workspace_bytes,
                    vitblk_stream_t stream);
+
+/*
+ * The same block on weights already packed by vitblk_pack_weights() (the
+ * seven kernels after packing).  workspace must hold at least
+ * vitblk_workspace_bytes() - vitblk_packed_weights_bytes() bytes and must not
+ * overlap x, packed or out.
+ */
+int vitblk_forward_packed(const void* x, const void* packed, void* out, int64_t N, int64_t T,
+                          int64_t D, int64_t F, int64_t H, double eps, int dtype,
+                          void* workspace, size_t workspace_bytes, vitblk_stream_t stream);
 
 /*
  * The steps of the block, one call each, on the same kernels vitblk_forward
@@ -132,15 +168,14 @@ int vitblk_forward(const void* x, const void* w_q, const void* w_k, const void* 
 int vitblk_layernorm(const void* x, void* out, int64_t rows, int64_t D, double eps,
                      int dtype, vitblk_stream_t stream);
 
-/* qkv[:, 0:D] = xn @ w_q, qkv[:, D:2D] = xn @ w_k, qkv[:, 2D:3D] = xn @ w_v;
- * xn [M, D], w_* [D, D], qkv [M, 3D] (one row holds a token's Q, K and V,
- * each as H consecutive head chunks).  crackedaicode.com "ViT Encoder Block",
- * "Multi-head attention" (the three projections); mlgrind.dev "E2E: Tiny
- * Vision Transformer", "Details" (one product with a concatenated weight).
- * qkv must not overlap an input. */
-int vitblk_qkv_projection(const void* xn, const void* w_q, const void* w_k,
-                          const void* w_v, void* qkv, int64_t M, int64_t D, int dtype,
-                          vitblk_stream_t stream);
+/* qkv = xn @ [w_q | w_k | w_v]: xn [M, D], w_qkv_t [3D, D] (the first
+ * region of the packed weights), qkv [M, 3D] (one row holds a token's Q, K
+ * and V, each as H consecutive head chunks).  crackedaicode.com "ViT Encoder
+ * Block", "Multi-head attention" (the three projections); mlgrind.dev "E2E:
+ * Tiny Vision Transformer", "Details" (one product with a concatenated
+ * weight).  qkv must not overlap an input. */
+int vitblk_qkv_projection(const void* xn, const void* w_qkv_t, void* qkv, int64_t M,
+                          int64_t D, int dtype, vitblk_stream_t stream);
 
 /* Bidirectional multi-head attention over packed qkv [N*T, 3D] (as written
  * by vitblk_qkv_projection): for every sequence n and head h,
@@ -151,13 +186,14 @@ int vitblk_qkv_projection(const void* xn, const void* w_q, const void* w_k,
 int vitblk_attention(const void* qkv, void* att, int64_t N, int64_t T, int64_t D,
                      int64_t H, int dtype, vitblk_stream_t stream);
 
-/* out = epilogue(a @ w): a [M, K], w [K, Nout], out [M, Nout]; residual
- * [M, Nout] is read only for VITBLK_EPI_RESIDUAL (may be NULL otherwise).
- * Covers the output projection + first residual, MLP1 + GELU and
- * MLP2 + second residual (crackedaicode.com "ViT Encoder Block",
- * "Multi-head attention" and "Feed-forward stage").  out must not overlap
- * a, w or residual. */
-int vitblk_linear(const void* a, const void* w, const void* residual, void* out,
+/* out = epilogue(a @ W) with the weight given out-major: a [M, K],
+ * w_t [Nout, K] (row n = column n of the (in, out) weight W, as in the
+ * packed regions), out [M, Nout]; residual [M, Nout] is read only for
+ * VITBLK_EPI_RESIDUAL (may be NULL otherwise).  Covers the output projection
+ * + first residual, MLP1 + GELU and MLP2 + second residual
+ * (crackedaicode.com "ViT Encoder Block", "Multi-head attention" and
+ * "Feed-forward stage").  out must not overlap a, w_t or residual. */
+int vitblk_linear(const void* a, const void* w_t, const void* residual, void* out,
                   int64_t M, int64_t K, int64_t Nout, int epilogue, int dtype,
                   vitblk_stream_t stream);
 

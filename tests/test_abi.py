@@ -51,7 +51,9 @@ def test_workspace_bytes():
     def expect(N, T, D, F, es):
         r = lambda b: (b + 255) // 256 * 256  # noqa: E731
         M = N * T
-        return r(M * max(3 * D, F) * es) + 2 * r(M * D * es)
+        packed = r(3 * D * D * es) + r(D * D * es) + 2 * r(D * F * es)
+        assert vb.packed_weights_bytes(D, F, 1 if es == 2 else 0) == packed
+        return packed + r(M * max(3 * D, F) * es) + 2 * r(M * D * es)
     assert vb.workspace_bytes(256, 197, 1024, 4096, 16, vb.VITBLK_BF16) == expect(256, 197, 1024, 4096, 2)
     assert vb.workspace_bytes(4, 5, 16, 32, 2, vb.VITBLK_FP32) == expect(4, 5, 16, 32, 4)
     assert vb.workspace_bytes(2, 3, 8, 8, 2, vb.VITBLK_FP32) == expect(2, 3, 8, 8, 4)  # 3D > F
@@ -134,9 +136,25 @@ def test_step_entry_points_errors(lib):
     assert lib.vitblk_layernorm(a, b, 4, 8, 1e-5, 9, None) == INVALID
     assert lib.vitblk_layernorm(a, a, 4, 8, 1e-5, 1, None) == ALIAS
     # qkv
-    assert lib.vitblk_qkv_projection(a, b, c, d, None, 4, 8, 1, None) == INVALID
-    assert lib.vitblk_qkv_projection(a, b, c, d, a, 4, 8, 1, None) == ALIAS
-    assert lib.vitblk_qkv_projection(a, b, c, d, e, 4, 0, 1, None) == INVALID
+    assert lib.vitblk_qkv_projection(a, b, None, 4, 8, 1, None) == INVALID
+    assert lib.vitblk_qkv_projection(a, b, a, 4, 8, 1, None) == ALIAS
+    assert lib.vitblk_qkv_projection(a, b, e, 4, 0, 1, None) == INVALID
+    # pack
+    w = [_addr(i) for i in range(6)]
+    assert lib.vitblk_pack_weights(*w, None, 16, 32, 1, None) == INVALID
+    assert lib.vitblk_pack_weights(*w, _addr(2), 16, 32, 1, None) == ALIAS
+    assert lib.vitblk_pack_weights(*w, _addr(9), 0, 32, 1, None) == INVALID
+    assert lib.vitblk_pack_weights(*w, _addr(9), 16, 32, 5, None) == INVALID
+    assert vb.packed_weights_bytes(0, 8, 1) == 0
+    # forward_packed
+    ws_need = vb.workspace_bytes(2, 5, 16, 32, 2, 1) - vb.packed_weights_bytes(16, 32, 1)
+    fp = lambda *args: lib.vitblk_forward_packed(*args)  # noqa: E731
+    assert fp(a, b, c, 2, 5, 16, 32, 2, 1e-6, 1, _addr(9), ws_need - 1, None) == WORKSPACE
+    assert fp(a, b, a, 2, 5, 16, 32, 2, 1e-6, 1, _addr(9), ws_need, None) == ALIAS
+    assert fp(a, b, c, 2, 5, 16, 32, 3, 1e-6, 1, _addr(9), ws_need, None) == INVALID
+    assert fp(a, b, c, 2, 5, 16, 32, 2, -1.0, 1, _addr(9), ws_need, None) == INVALID
+    assert fp(a, None, c, 2, 5, 16, 32, 2, 1e-6, 1, _addr(9), ws_need, None) == INVALID
+    assert fp(a, b, c, 2, 5, 16, 32, 2, 1e-6, 1, _addr(1), ws_need, None) == ALIAS
     # attention
     assert lib.vitblk_attention(a, b, 2, 3, 8, 3, 1, None) == INVALID   # H does not divide D
     assert lib.vitblk_attention(a, a, 2, 3, 8, 2, 1, None) == ALIAS

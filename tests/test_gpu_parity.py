@@ -45,7 +45,8 @@ def test_qkv_projection(dtype, M, D):
     rng = np.random.default_rng(M + D)
     xn = _rand(rng, (M, D), dtype)
     ws = [_rand(rng, (D, D), dtype, scale=1 / math.sqrt(D)) for _ in range(3)]
-    got = to_host(vb.qkv_projection(to_dev(xn, dtype), *(to_dev(w, dtype) for w in ws)))
+    w_qkv_t = np.concatenate([w.T for w in ws], axis=0)  # out-major [3D, D]
+    got = to_host(vb.qkv_projection(to_dev(xn, dtype), to_dev(w_qkv_t, dtype)))
     ref = np.concatenate([oracle.project(xn, w) for w in ws], axis=1)
     assert_close(got, ref, dtype, f"QKV M={M} D={D}")
 
@@ -63,7 +64,7 @@ def test_linear(dtype, epi, M, K, N):
     w = _rand(rng, (K, N), dtype, scale=1 / math.sqrt(K))
     r = _rand(rng, (M, N), dtype)
     res = to_dev(r, dtype) if epi == "residual" else None
-    got = to_host(vb.linear(to_dev(a, dtype), to_dev(w, dtype), EPIS[epi], residual=res))
+    got = to_host(vb.linear(to_dev(a, dtype), to_dev(w.T, dtype), EPIS[epi], residual=res))
     ref = oracle.project(a, w)
     if epi == "residual":
         ref = r + ref
@@ -97,6 +98,31 @@ def test_attention(dtype, N, T, D, H):
     got = to_host(vb.attention(to_dev(qkv, dtype), N, T, H)).reshape(N, T, D)
     ref = _attention_ref(q, k, v, H)
     assert_close(got, ref, dtype, f"attention N={N} T={T} D={D} H={H}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("D,F", [(256, 1024), (24, 40), (768, 3072)])
+def test_pack_weights_is_an_exact_transpose(dtype, D, F):
+    import torch
+    inp = make_block_inputs(1, 1, D, F, dtype, seed=11)
+    names = ["w_q", "w_k", "w_v", "w_o", "w_mlp1", "w_mlp2"]
+    dev = [to_dev(inp[k], dtype) for k in names]
+    packed = vb.pack_weights(*dev)
+    es = 2 if dtype == "bf16" else 4
+    r = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    offs = [0, r(3 * D * D * es), r(3 * D * D * es) + r(D * D * es)]
+    offs.append(offs[2] + r(D * F * es))
+    assert packed.numel() == offs[3] + r(D * F * es)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+
+    def region(off, rows, cols):
+        return packed[off:off + rows * cols * es].view(tdt).view(rows, cols)
+
+    qkv = torch.cat([dev[0].t(), dev[1].t(), dev[2].t()], 0)
+    assert torch.equal(region(offs[0], 3 * D, D), qkv)
+    assert torch.equal(region(offs[1], D, D), dev[3].t())
+    assert torch.equal(region(offs[2], F, D), dev[4].t())
+    assert torch.equal(region(offs[3], D, F), dev[5].t())
 
 
 # ------------------------------------------------------------------ whole block
@@ -187,6 +213,17 @@ def test_token_permutation_equivariance():
     inp_p["x"] = inp["x"][:, perm]
     out_p, _ = _run_block(inp_p, 4, 1e-6, "bf16")
     assert_close(to_host(out_p), to_host(out)[:, perm], "bf16", "permuted tokens")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_forward_packed_matches_forward(dtype):
+    import torch
+    inp = make_block_inputs(2, 197, 256, 1024, dtype, seed=12)
+    out, dev = _run_block(inp, 4, 1e-6, dtype)
+    packed = vb.pack_weights(dev["w_q"], dev["w_k"], dev["w_v"], dev["w_o"], dev["w_mlp1"],
+                             dev["w_mlp2"])
+    out2 = vb.forward_packed(dev["x"], packed, 1024, 4, 1e-6)
+    assert torch.equal(out, out2)
 
 
 def test_side_stream():

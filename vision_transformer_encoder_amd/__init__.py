@@ -16,9 +16,13 @@ from ._lib import (  # noqa: F401
     VitblkError,
     attention,
     forward,
+    forward_packed,
     layernorm,
     linear,
     load,
+    pack_weights,
+    packed_views,
+    packed_weights_bytes,
     qkv_projection,
     status_string,
     workspace_bytes,

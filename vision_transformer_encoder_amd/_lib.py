@@ -23,9 +23,12 @@ _P, _I64, _I, _D, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_
 SIGNATURES = {
     "vitblk_status_string": (ctypes.c_char_p, [_I]),
     "vitblk_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64, _I]),
+    "vitblk_packed_weights_bytes": (_SZ, [_I64, _I64, _I]),
+    "vitblk_pack_weights": (_I, [_P] * 7 + [_I64, _I64, _I, _P]),
     "vitblk_forward": (_I, [_P] * 8 + [_I64] * 5 + [_D, _I, _P, _SZ, _P]),
+    "vitblk_forward_packed": (_I, [_P] * 3 + [_I64] * 5 + [_D, _I, _P, _SZ, _P]),
     "vitblk_layernorm": (_I, [_P, _P, _I64, _I64, _D, _I, _P]),
-    "vitblk_qkv_projection": (_I, [_P] * 5 + [_I64, _I64, _I, _P]),
+    "vitblk_qkv_projection": (_I, [_P] * 3 + [_I64, _I64, _I, _P]),
     "vitblk_attention": (_I, [_P, _P, _I64, _I64, _I64, _I64, _I, _P]),
     "vitblk_linear": (_I, [_P] * 4 + [_I64, _I64, _I64, _I, _I, _P]),
 }
@@ -110,6 +113,11 @@ def workspace_bytes(N, T, D, F, H, dtype) -> int:
     return int(load().vitblk_workspace_bytes(N, T, D, F, H, code))
 
 
+def packed_weights_bytes(D, F, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    return int(load().vitblk_packed_weights_bytes(D, F, code))
+
+
 def forward(x, w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, num_heads: int, eps: float,
             out=None, workspace=None, stream=None):
     """out = block(x) for x [N, T, D]; returns out (allocated if not given)."""
@@ -132,6 +140,61 @@ def forward(x, w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, num_heads: int, eps: float,
     return out
 
 
+def pack_weights(w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, packed=None, stream=None):
+    """Out-major copies of the six weights in one buffer (uint8 tensor)."""
+    torch = _torch()
+    _dev(w_q, w_k, w_v, w_o, w_mlp1, w_mlp2)
+    D, F = w_mlp1.shape
+    code = dtype_code(w_q.dtype)
+    if packed is None:
+        packed = torch.empty(max(packed_weights_bytes(D, F, code), 1), dtype=torch.uint8,
+                             device=w_q.device)
+    st = load().vitblk_pack_weights(_ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(w_o), _ptr(w_mlp1),
+                                    _ptr(w_mlp2), _ptr(packed), D, F, code,
+                                    _stream(w_q, stream))
+    _check("vitblk_pack_weights", st)
+    return packed
+
+
+def packed_views(packed, D: int, F: int, dtype):
+    """Views of the four out-major regions of a packed buffer (documented layout).
+
+    Returns (w_qkv_t [3D, D], w_o_t [D, D], w1_t [F, D], w2_t [D, F]).
+    """
+    torch = _torch()
+    es = 2 if dtype == torch.bfloat16 else 4
+
+    def up(b):
+        return (b + 255) // 256 * 256
+
+    offs = [0, up(3 * D * D * es)]
+    offs.append(offs[1] + up(D * D * es))
+    offs.append(offs[2] + up(D * F * es))
+    shapes = [(3 * D, D), (D, D), (F, D), (D, F)]
+    return tuple(packed[o:o + r * c * es].view(dtype).view(r, c)
+                 for o, (r, c) in zip(offs, shapes))
+
+
+def forward_packed(x, packed, F: int, num_heads: int, eps: float, out=None, workspace=None,
+                   stream=None):
+    """out = block(x) on weights packed by pack_weights()."""
+    torch = _torch()
+    _dev(x, out)
+    N, T, D = x.shape
+    code = dtype_code(x.dtype)
+    if out is None:
+        out = torch.empty_like(x)
+    need = workspace_bytes(N, T, D, F, num_heads, code) - packed_weights_bytes(D, F, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    st = load().vitblk_forward_packed(_ptr(x), _ptr(packed), _ptr(out), N, T, D, F, num_heads,
+                                      float(eps), code, _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(),
+                                      _stream(x, stream))
+    _check("vitblk_forward_packed", st)
+    return out
+
+
 def layernorm(x, eps: float, out=None, stream=None):
     """Row-wise LN over the last axis of a contiguous tensor."""
     torch = _torch()
@@ -146,16 +209,16 @@ def layernorm(x, eps: float, out=None, stream=None):
     return out
 
 
-def qkv_projection(xn, w_q, w_k, w_v, out=None, stream=None):
-    """Packed [M, 3D] = xn [M, D] @ [w_q | w_k | w_v]."""
+def qkv_projection(xn, w_qkv_t, out=None, stream=None):
+    """Packed [M, 3D] = xn [M, D] @ [w_q | w_k | w_v], weight given out-major [3D, D]."""
     torch = _torch()
-    _dev(xn, w_q, w_k, w_v, out)
+    _dev(xn, w_qkv_t, out)
     D = xn.shape[-1]
     M = xn.numel() // D
     if out is None:
         out = torch.empty((M, 3 * D), dtype=xn.dtype, device=xn.device)
-    st = load().vitblk_qkv_projection(_ptr(xn), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(out),
-                                      M, D, dtype_code(xn.dtype), _stream(xn, stream))
+    st = load().vitblk_qkv_projection(_ptr(xn), _ptr(w_qkv_t), _ptr(out), M, D,
+                                      dtype_code(xn.dtype), _stream(xn, stream))
     _check("vitblk_qkv_projection", st)
     return out
 
@@ -173,16 +236,16 @@ def attention(qkv, N: int, T: int, num_heads: int, out=None, stream=None):
     return out
 
 
-def linear(a, w, epilogue: int = EPI_NONE, residual=None, out=None, stream=None):
-    """out = epilogue(a [M, K] @ w [K, Nout]) (+ residual for EPI_RESIDUAL)."""
+def linear(a, w_t, epilogue: int = EPI_NONE, residual=None, out=None, stream=None):
+    """out = epilogue(a [M, K] @ W) (+ residual) with W given out-major, w_t [Nout, K]."""
     torch = _torch()
-    _dev(a, w, residual, out)
+    _dev(a, w_t, residual, out)
     K = a.shape[-1]
     M = a.numel() // K
-    Nout = w.shape[1]
+    Nout = w_t.shape[0]
     if out is None:
         out = torch.empty((M, Nout), dtype=a.dtype, device=a.device)
-    st = load().vitblk_linear(_ptr(a), _ptr(w), _ptr(residual), _ptr(out), M, K, Nout,
+    st = load().vitblk_linear(_ptr(a), _ptr(w_t), _ptr(residual), _ptr(out), M, K, Nout,
                               int(epilogue), dtype_code(a.dtype), _stream(a, stream))
     _check("vitblk_linear", st)
     return out

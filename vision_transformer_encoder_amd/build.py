@@ -21,7 +21,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libvitblk.so")
 
 ARCH = os.environ.get("VITBLK_OFFLOAD_ARCH", "gfx950")
-HIP_SOURCES = ["api.hip", "layernorm.hip", "gemm.hip", "attention.hip", "generic.hip"]
+HIP_SOURCES = ["api.hip", "layernorm.hip", "gemm.hip", "attention.hip",
+               "attention_resident.hip", "generic.hip", "pack.hip"]
 HOST_SOURCES = ["validate.cpp"]
 
 # Packed-fp32 instructions are disabled for all device code.

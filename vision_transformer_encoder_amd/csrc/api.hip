@@ -11,42 +11,81 @@ using namespace vitblk;
 namespace {
 
 // Launch-failure check after each kernel; the first failure ends the call.
-#define VITBLK_LAUNCH(expr)                            \
-  do {                                                 \
-    if ((expr) != hipSuccess) return VITBLK_ERR_HIP;   \
+#define VITBLK_LAUNCH(expr)                          \
+  do {                                               \
+    if ((expr) != hipSuccess) return VITBLK_ERR_HIP; \
   } while (0)
 
-GemmProblem make_linear(const void* a, int64_t lda, const void* w, int64_t ldw, void* c,
-                        int64_t ldc, const void* r, int64_t M, int64_t K, int64_t N, int epi,
-                        int dtype) {
+GemmProblem linear_problem(const void* a, const void* w_t, void* c, const void* r, int64_t M,
+                           int64_t K, int64_t N, int epi, int dtype) {
   GemmProblem p{};
   p.M = M;
   p.N = N;
   p.K = K;
   p.A = a;
-  p.lda = lda;
-  p.nprob = 1;
-  p.B[0] = p.B[1] = p.B[2] = w;
-  p.ldb = ldw;
+  p.lda = K;
+  p.B = w_t;
+  p.ldb = K;
   p.C = c;
-  p.ldc = ldc;
-  p.col_off[0] = p.col_off[1] = p.col_off[2] = 0;
+  p.ldc = N;
   p.R = r;
-  p.ldr = ldc;
+  p.ldr = N;
   p.epi = epi;
   p.dtype = dtype;
   return p;
 }
 
-GemmProblem make_qkv(const void* xn, const void* wq, const void* wk, const void* wv, void* qkv,
-                     int64_t M, int64_t D, int dtype) {
-  GemmProblem p = make_linear(xn, D, wq, D, qkv, 3 * D, nullptr, M, D, D, VITBLK_EPI_NONE, dtype);
-  p.nprob = 3;
-  p.B[1] = wk;
-  p.B[2] = wv;
-  p.col_off[1] = D;
-  p.col_off[2] = 2 * D;
-  return p;
+int pack_weights(const void* w_q, const void* w_k, const void* w_v, const void* w_o,
+                 const void* w_mlp1, const void* w_mlp2, void* packed, int64_t D, int64_t F,
+                 int dtype, const PackedPlan& pl, hipStream_t s) {
+  char* base = static_cast<char*>(packed);
+  const size_t es = elem_size(dtype);
+  char* qkv = base + pl.off_qkv;
+  const PackJob jobs[6] = {
+      {w_q, D, D, qkv, D},
+      {w_k, D, D, qkv + static_cast<size_t>(D) * D * es, D},
+      {w_v, D, D, qkv + 2 * static_cast<size_t>(D) * D * es, D},
+      {w_o, D, D, base + pl.off_o, D},
+      {w_mlp1, D, F, base + pl.off_1, D},
+      {w_mlp2, F, D, base + pl.off_2, F},
+  };
+  VITBLK_LAUNCH(launch_pack(jobs, 6, dtype, s));
+  return VITBLK_OK;
+}
+
+// The seven steps of the block on packed (out-major) weights.
+int run_block(const void* x, const void* packed, void* out, int64_t N, int64_t T, int64_t D,
+              int64_t F, int64_t H, double eps, int dtype, char* act, const WorkspacePlan& pl,
+              hipStream_t s) {
+  const int64_t M = N * T;
+  const size_t es = elem_size(dtype);
+  const char* pk = static_cast<const char*>(packed);
+  char* big = act + pl.off_big;  // qkv [M, 3D], later hidden [M, F]
+  char* a = act + pl.off_act;    // xn, then att, then yn: [M, D]
+  char* y = act + pl.off_y;      // [M, D]
+  const float feps = static_cast<float>(eps);
+
+  // LN1: xn = LN(x)
+  VITBLK_LAUNCH(launch_layernorm(x, a, M, D, feps, dtype, s));
+  // Q | K | V = xn @ [w_q | w_k | w_v]
+  VITBLK_LAUNCH(launch_gemm(
+      linear_problem(a, pk + pl.packed.off_qkv, big, nullptr, M, D, 3 * D, VITBLK_EPI_NONE, dtype),
+      s));
+  // att = concat_h softmax(Q_h K_h^T / sqrt(dh)) V_h   (overwrites xn)
+  VITBLK_LAUNCH(launch_attention(big, big + D * es, big + 2 * D * es, 3 * D, a, D, N, T, H,
+                                 D / H, dtype, s));
+  // y = x + att @ w_o
+  VITBLK_LAUNCH(launch_gemm(
+      linear_problem(a, pk + pl.packed.off_o, y, x, M, D, D, VITBLK_EPI_RESIDUAL, dtype), s));
+  // LN2: yn = LN(y)   (overwrites att)
+  VITBLK_LAUNCH(launch_layernorm(y, a, M, D, feps, dtype, s));
+  // hidden = GELU(yn @ w_mlp1)   (overwrites qkv)
+  VITBLK_LAUNCH(launch_gemm(
+      linear_problem(a, pk + pl.packed.off_1, big, nullptr, M, D, F, VITBLK_EPI_GELU, dtype), s));
+  // out = y + hidden @ w_mlp2
+  VITBLK_LAUNCH(launch_gemm(
+      linear_problem(big, pk + pl.packed.off_2, out, y, M, F, D, VITBLK_EPI_RESIDUAL, dtype), s));
+  return VITBLK_OK;
 }
 
 }  // namespace
@@ -72,43 +111,47 @@ size_t vitblk_workspace_bytes(int64_t N, int64_t T, int64_t D, int64_t F, int64_
   return p.total;
 }
 
+size_t vitblk_packed_weights_bytes(int64_t D, int64_t F, int dtype) {
+  PackedPlan p;
+  if (plan_packed(D, F, dtype, &p) != VITBLK_OK) return 0;
+  return p.total;
+}
+
+int vitblk_pack_weights(const void* w_q, const void* w_k, const void* w_v, const void* w_o,
+                        const void* w_mlp1, const void* w_mlp2, void* packed, int64_t D,
+                        int64_t F, int dtype, vitblk_stream_t stream) {
+  PackedPlan pl;
+  const int st = validate_pack(w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, packed, D, F, dtype, &pl);
+  if (st != VITBLK_OK) return st;
+  return pack_weights(w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, packed, D, F, dtype, pl,
+                      reinterpret_cast<hipStream_t>(stream));
+}
+
 int vitblk_forward(const void* x, const void* w_q, const void* w_k, const void* w_v,
                    const void* w_o, const void* w_mlp1, const void* w_mlp2, void* out,
                    int64_t N, int64_t T, int64_t D, int64_t F, int64_t H, double eps,
                    int dtype, void* workspace, size_t workspace_bytes, vitblk_stream_t stream) {
-  WorkspacePlan plan;
-  const int st = validate_forward(x, w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, out, N, T, D, F, H,
-                                  eps, dtype, workspace, workspace_bytes, &plan);
+  WorkspacePlan pl;
+  int st = validate_forward(x, w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, out, N, T, D, F, H, eps,
+                            dtype, workspace, workspace_bytes, &pl);
   if (st != VITBLK_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int64_t M = N * T;
-  const size_t es = elem_size(dtype);
   char* ws = static_cast<char*>(workspace);
-  void* big = ws + plan.off_big;  // qkv [M, 3D], later hidden [M, F]
-  void* act = ws + plan.off_act;  // xn, then att, then yn: [M, D]
-  void* y = ws + plan.off_y;      // [M, D]
-  const float feps = static_cast<float>(eps);
-  char* qkv = static_cast<char*>(big);
+  st = pack_weights(w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, ws, D, F, dtype, pl.packed, s);
+  if (st != VITBLK_OK) return st;
+  return run_block(x, ws, out, N, T, D, F, H, eps, dtype, ws + pl.act_base, pl, s);
+}
 
-  // LN1: xn = LN(x)
-  VITBLK_LAUNCH(launch_layernorm(x, act, M, D, feps, dtype, s));
-  // Q | K | V = xn @ [w_q | w_k | w_v]
-  VITBLK_LAUNCH(launch_gemm(make_qkv(act, w_q, w_k, w_v, big, M, D, dtype), s));
-  // att = concat_h softmax(Q_h K_h^T / sqrt(dh)) V_h   (overwrites xn)
-  VITBLK_LAUNCH(launch_attention(qkv, qkv + D * es, qkv + 2 * D * es, 3 * D, act, D, N, T, H,
-                                 D / H, dtype, s));
-  // y = x + att @ w_o
-  VITBLK_LAUNCH(launch_gemm(
-      make_linear(act, D, w_o, D, y, D, x, M, D, D, VITBLK_EPI_RESIDUAL, dtype), s));
-  // LN2: yn = LN(y)   (overwrites att)
-  VITBLK_LAUNCH(launch_layernorm(y, act, M, D, feps, dtype, s));
-  // hidden = GELU(yn @ w_mlp1)   (overwrites qkv)
-  VITBLK_LAUNCH(launch_gemm(
-      make_linear(act, D, w_mlp1, F, big, F, nullptr, M, D, F, VITBLK_EPI_GELU, dtype), s));
-  // out = y + hidden @ w_mlp2
-  VITBLK_LAUNCH(launch_gemm(
-      make_linear(big, F, w_mlp2, D, out, D, y, M, F, D, VITBLK_EPI_RESIDUAL, dtype), s));
-  return VITBLK_OK;
+int vitblk_forward_packed(const void* x, const void* packed, void* out, int64_t N, int64_t T,
+                          int64_t D, int64_t F, int64_t H, double eps, int dtype,
+                          void* workspace, size_t workspace_bytes, vitblk_stream_t stream) {
+  WorkspacePlan pl;
+  const int st = validate_forward_packed(x, packed, out, N, T, D, F, H, eps, dtype, workspace,
+                                         workspace_bytes, &pl);
+  if (st != VITBLK_OK) return st;
+  return run_block(x, packed, out, N, T, D, F, H, eps, dtype,
+                   static_cast<char*>(workspace) + pl.act_base, pl,
+                   reinterpret_cast<hipStream_t>(stream));
 }
 
 int vitblk_layernorm(const void* x, void* out, int64_t rows, int64_t D, double eps, int dtype,
@@ -120,12 +163,13 @@ int vitblk_layernorm(const void* x, void* out, int64_t rows, int64_t D, double e
   return VITBLK_OK;
 }
 
-int vitblk_qkv_projection(const void* xn, const void* w_q, const void* w_k, const void* w_v,
-                          void* qkv, int64_t M, int64_t D, int dtype, vitblk_stream_t stream) {
-  const int st = validate_qkv(xn, w_q, w_k, w_v, qkv, M, D, dtype);
+int vitblk_qkv_projection(const void* xn, const void* w_qkv_t, void* qkv, int64_t M, int64_t D,
+                          int dtype, vitblk_stream_t stream) {
+  const int st = validate_qkv(xn, w_qkv_t, qkv, M, D, dtype);
   if (st != VITBLK_OK) return st;
-  VITBLK_LAUNCH(launch_gemm(make_qkv(xn, w_q, w_k, w_v, qkv, M, D, dtype),
-                            reinterpret_cast<hipStream_t>(stream)));
+  VITBLK_LAUNCH(launch_gemm(
+      linear_problem(xn, w_qkv_t, qkv, nullptr, M, D, 3 * D, VITBLK_EPI_NONE, dtype),
+      reinterpret_cast<hipStream_t>(stream)));
   return VITBLK_OK;
 }
 
@@ -140,14 +184,14 @@ int vitblk_attention(const void* qkv, void* att, int64_t N, int64_t T, int64_t D
   return VITBLK_OK;
 }
 
-int vitblk_linear(const void* a, const void* w, const void* residual, void* out, int64_t M,
+int vitblk_linear(const void* a, const void* w_t, const void* residual, void* out, int64_t M,
                   int64_t K, int64_t Nout, int epilogue, int dtype, vitblk_stream_t stream) {
-  const int st = validate_linear(a, w, residual, out, M, K, Nout, epilogue, dtype);
+  const int st = validate_linear(a, w_t, residual, out, M, K, Nout, epilogue, dtype);
   if (st != VITBLK_OK) return st;
-  VITBLK_LAUNCH(launch_gemm(make_linear(a, K, w, Nout, out, Nout,
-                                        epilogue == VITBLK_EPI_RESIDUAL ? residual : nullptr, M,
-                                        K, Nout, epilogue, dtype),
-                            reinterpret_cast<hipStream_t>(stream)));
+  VITBLK_LAUNCH(launch_gemm(
+      linear_problem(a, w_t, out, epilogue == VITBLK_EPI_RESIDUAL ? residual : nullptr, M, K,
+                     Nout, epilogue, dtype),
+      reinterpret_cast<hipStream_t>(stream)));
   return VITBLK_OK;
 }
 

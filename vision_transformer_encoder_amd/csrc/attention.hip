@@ -282,6 +282,8 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, int64_t
   const bool fast = dtype == VITBLK_BF16 && ld % 8 == 0 && ldo % 8 == 0 && aligned16(q) &&
                     aligned16(k) && aligned16(v) && aligned16(o);
   if (fast) {
+    const hipError_t r = launch_attention_resident(q, k, v, ld, o, ldo, N, T, H, dh, s);
+    if (r != hipErrorNotSupported) return r;
     switch (dh) {
       case 32: return launch_dh<32>(q, k, v, ld, o, ldo, N, T, H, s);
       case 64: return launch_dh<64>(q, k, v, ld, o, ldo, N, T, H, s);

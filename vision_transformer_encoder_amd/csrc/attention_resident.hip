@@ -1,0 +1,271 @@
+// Bidirectional multi-head attention with the whole sequence's K and V
+// resident in LDS (sequences up to a few hundred tokens: ViT's 197 and 257).
+//
+// Computes, for every sequence n and head h, O_h = softmax(Q_h K_h^T /
+// sqrt(dh)) V_h with no mask, head h owning features [h*dh, (h+1)*dh)
+// (crackedaicode.com "ViT Encoder Block", "Multi-head attention";
+// nipunbatra.github.io vision1 transcript, Page 70).
+//
+// One workgroup per (sequence, head).  All its threads first copy K and V of
+// that head into LDS (one round of global loads, so memory latency is paid
+// once per workgroup), then each wave takes 32-query tiles and walks the keys
+// in chunks of 64 with a running maximum and sum per query (online softmax),
+// with no further barriers.
+//
+// Matrix-core mapping (v_mfma_f32_32x32x16_bf16), as in the streaming kernel:
+// scores are formed transposed, S^T = K Q^T, so each accumulator lane holds
+// 16 keys of one query and the probabilities are already the second operand
+// of O^T = V^T P^T.  V stays in its natural [key][feature] layout in LDS; its
+// transpose is read with ds_read_b64_tr_b16, which hands lane i of a 16-lane
+// group column i of the 4 x 16 block that the group's lanes point at (lane
+// m points at row m/4, columns 4*(m%4)..+3).
+//
+// LDS rows are padded so that reads are conflict-free on gfx950 (64 banks):
+// K rows (read 16 consecutive keys x 16 B) use a stride of dh*2 + 16 bytes;
+// V rows (read 4 consecutive keys x 64 B) use a stride that is 64 or 192
+// modulo 256.  Keys past T are loaded from row T-1 (finite values) and their
+// scores are set to -inf.
+#include <math.h>
+
+#include "device.h"
+#include "kernels.h"
+#include "vitblk.h"
+
+namespace vitblk {
+namespace {
+
+constexpr int kMaxWaves = 8;
+constexpr int kLdsBytes = 160 * 1024;  // gfx950 LDS per workgroup
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+template <int DH>
+struct ResCfg {
+  static_assert(DH % 16 == 0, "head width must be a multiple of 16");
+  static constexpr int DHP = (DH + 31) / 32 * 32;                     // V^T rows per MFMA block
+  static constexpr int SK = DH * 2 + 16;                              // K row stride, bytes
+  static constexpr int SV = (DHP * 2) % 128 == 0 ? DHP * 2 + 64 : DHP * 2;  // V row stride
+  static constexpr int ROW = SK + SV;
+};
+
+__device__ __forceinline__ v4i16 ds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(const_cast<char*>(p)));
+}
+
+template <int DH>
+__global__ __launch_bounds__(64 * kMaxWaves) void attn_resident_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    int64_t ld, bf16_t* __restrict__ O, int64_t ldo, int T, int H, int T_pad,
+    float scale_log2) {
+  using C = ResCfg<DH>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* const ks = smem;                 // [T_pad][SK]
+  char* const vs = smem + T_pad * C::SK;  // [T_pad][SV]
+
+  const int h = static_cast<int>(blockIdx.x % H);
+  const int64_t n = blockIdx.x / H;
+  const int64_t seq0 = n * T;
+  const int64_t hoff = static_cast<int64_t>(h) * DH;
+  const int tid = threadIdx.x, nthreads = blockDim.x;
+
+  // ---- K and V of this head into LDS (4 chunks of 16 B per operand in flight per thread).
+  constexpr int CPR = DH / 8;  // 16-byte chunks per row
+  const int chunks = T_pad * CPR;
+  for (int c0 = tid; c0 < chunks; c0 += 4 * nthreads) {
+    uint4 kv[4], vv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + u * nthreads;
+      if (c < chunks) {
+        const int key = c / CPR, dc = c % CPR;
+        const int t = key < T ? key : T - 1;
+        const int64_t g = (seq0 + t) * ld + hoff + dc * 8;
+        kv[u] = ld_global16(K + g);
+        vv[u] = ld_global16(V + g);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + u * nthreads;
+      if (c < chunks) {
+        const int key = c / CPR, dc = c % CPR;
+        *reinterpret_cast<uint4*>(ks + key * C::SK + dc * 16) = kv[u];
+        *reinterpret_cast<uint4*>(vs + key * C::SV + dc * 16) = vv[u];
+      }
+    }
+  }
+  if (C::DHP > DH) {  // features DH..DHP-1 of V feed only discarded output rows; keep them 0
+    constexpr int PC = (C::DHP - DH) / 8;
+    for (int c = tid; c < T_pad * PC; c += nthreads)
+      *reinterpret_cast<uint4*>(vs + (c / PC) * C::SV + (DH + (c % PC) * 8) * 2) =
+          make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+
+  const int lane = tid & 63, wave = tid >> 6, nw = nthreads >> 6;
+  const int lrow = lane & 31, g = lane >> 5;
+  const int i16 = lane & 15, q16 = (lane >> 4) & 1;
+  // Lane's V^T read address relative to (key0, feature block): row key0 + i16/4,
+  // columns q16*16 + 4*(i16 % 4) of the 32-feature block.
+  const int v_lane = (i16 >> 2) * C::SV + (q16 * 16 + 4 * (i16 & 3)) * 2;
+  const int nqt = T_pad / 32;
+
+  for (int qt = wave; qt < nqt; qt += nw) {
+    const int q = qt * 32 + lrow;
+    const int qc = q < T ? q : T - 1;
+    bf16x8 qf[DH / 16];
+    {
+      const bf16_t* qrow = Q + (seq0 + qc) * ld + hoff + g * 8;
+#pragma unroll
+      for (int s = 0; s < DH / 16; ++s)
+        qf[s] = __builtin_bit_cast(bf16x8, ld_global16(qrow + s * 16));
+    }
+    f32x16 o[C::DHP / 32];
+#pragma unroll
+    for (int d = 0; d < C::DHP / 32; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+
+    for (int k0 = 0; k0 < T; k0 += 64) {
+      const int nkb = (T - k0) > 32 ? 2 : 1;  // 32-key blocks holding a valid key
+      f32x16 s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+        if (kb < nkb) {
+          const char* krow = ks + (k0 + kb * 32 + lrow) * C::SK + g * 16;
+#pragma unroll
+          for (int ks_ = 0; ks_ < DH / 16; ++ks_) {
+            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + ks_ * 32);
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks_], s[kb], 0, 0, 0);
+          }
+        }
+      }
+      // Scale into the base-2 domain, mask keys past T, running maximum.
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+          float v = s[kb][r] * scale_log2;
+          v = (kb < nkb && key < T) ? v : -INFINITY;
+          s[kb][r] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      float psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pv = __builtin_amdgcn_exp2f(s[kb][r] - m_new);
+          s[kb][r] = pv;
+          psum += pv;
+        }
+      l_run = l_run * alpha + psum;
+#pragma unroll
+      for (int d = 0; d < C::DHP / 32; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+
+      // O^T += V^T P^T, 16 keys per MFMA: MFMA k-slot j of lane half g is key
+      // (j/4)*8 + g*4 + j%4 of the 16-key step, for both operands.
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if (kb >= nkb) continue;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const bf16x8 pf = __builtin_bit_cast(
+              bf16x8, make_uint4(pack_bf16x2(s[kb][s2 * 8 + 0], s[kb][s2 * 8 + 1]),
+                                 pack_bf16x2(s[kb][s2 * 8 + 2], s[kb][s2 * 8 + 3]),
+                                 pack_bf16x2(s[kb][s2 * 8 + 4], s[kb][s2 * 8 + 5]),
+                                 pack_bf16x2(s[kb][s2 * 8 + 6], s[kb][s2 * 8 + 7])));
+          const char* vb = vs + (k0 + kb * 32 + s2 * 16 + g * 4) * C::SV + v_lane;
+#pragma unroll
+          for (int d = 0; d < C::DHP / 32; ++d) {
+            const v4i16 lo = ds_read_tr16(vb + d * 64);
+            const v4i16 hi = ds_read_tr16(vb + 8 * C::SV + d * 64);
+            const bf16x8 vf = __builtin_bit_cast(
+                bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[d], 0, 0, 0);
+          }
+        }
+      }
+    }
+
+    const float inv = 1.0f / (l_run + __shfl_xor(l_run, 32));
+    if (q < T) {
+      bf16_t* orow = O + (seq0 + q) * ldo + hoff;
+#pragma unroll
+      for (int d = 0; d < C::DHP / 32; ++d)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int f = d * 32 + rr * 8 + g * 4;
+          if (f < DH)
+            *reinterpret_cast<uint2*>(orow + f) =
+                make_uint2(pack_bf16x2(o[d][rr * 4 + 0] * inv, o[d][rr * 4 + 1] * inv),
+                           pack_bf16x2(o[d][rr * 4 + 2] * inv, o[d][rr * 4 + 3] * inv));
+        }
+    }
+  }
+}
+
+template <int DH>
+hipError_t launch_res(const void* q, const void* k, const void* v, int64_t ld, void* o,
+                      int64_t ldo, int64_t N, int64_t T, int64_t H, hipStream_t s) {
+  using C = ResCfg<DH>;
+  const int64_t T_pad = (T + 31) / 32 * 32;
+  const int64_t bytes = T_pad * C::ROW;
+  if (bytes > kLdsBytes) return hipErrorNotSupported;
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&attn_resident_kernel<DH>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();  // clear it: the caller falls back to the streaming kernel
+      return hipErrorNotSupported;
+    }
+    attr_set = true;
+  }
+  const int64_t nqt = T_pad / 32;
+  const int per_wave = static_cast<int>((nqt + kMaxWaves - 1) / kMaxWaves);
+  const int nw = static_cast<int>((nqt + per_wave - 1) / per_wave);
+  const int64_t blocks = N * H;
+  if (blocks > 2147483647LL) return hipErrorInvalidValue;
+  const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(DH));
+  hipLaunchKernelGGL(attn_resident_kernel<DH>, dim3(static_cast<unsigned>(blocks)),
+                     dim3(64 * nw), static_cast<size_t>(bytes), s,
+                     static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+                     static_cast<const bf16_t*>(v), ld, static_cast<bf16_t*>(o), ldo,
+                     static_cast<int>(T), static_cast<int>(H), static_cast<int>(T_pad),
+                     scale_log2);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Returns hipErrorNotSupported (launching nothing) when the sequence does not
+// fit in LDS or the head width has no instantiation; the caller then uses the
+// streaming kernel.
+hipError_t launch_attention_resident(const void* q, const void* k, const void* v, int64_t ld,
+                                     void* o, int64_t ldo, int64_t N, int64_t T, int64_t H,
+                                     int64_t dh, hipStream_t s) {
+  switch (dh) {
+    case 32: return launch_res<32>(q, k, v, ld, o, ldo, N, T, H, s);
+    case 64: return launch_res<64>(q, k, v, ld, o, ldo, N, T, H, s);
+    case 80: return launch_res<80>(q, k, v, ld, o, ldo, N, T, H, s);
+    case 96: return launch_res<96>(q, k, v, ld, o, ldo, N, T, H, s);
+    case 128: return launch_res<128>(q, k, v, ld, o, ldo, N, T, H, s);
+    default: return hipErrorNotSupported;
+  }
+}
+
+}  // namespace vitblk

@@ -49,19 +49,15 @@ __global__ __launch_bounds__(kGenThreads) void ln_generic_kernel(const T* __rest
 }
 
 // 64x64 output tile per workgroup, 16-deep k slices staged in LDS, 4x4
-// outputs per thread.  Problems (Q, K, V) and tiles are flattened into
-// blockIdx.x.
+// outputs per thread; tiles flattened into blockIdx.x.
 template <typename T, int EPI>
-__global__ __launch_bounds__(kGenThreads) void gemm_generic_kernel(GemmProblem p, int64_t mt,
-                                                                   int64_t nt) {
+__global__ __launch_bounds__(kGenThreads) void gemm_generic_kernel(GemmProblem p, int64_t nt) {
   __shared__ float As[16][64 + 4];
   __shared__ float Bs[16][64 + 4];
-  int64_t b = blockIdx.x;
-  const int prob = static_cast<int>(b / (mt * nt));
-  b -= static_cast<int64_t>(prob) * mt * nt;
+  const int64_t b = blockIdx.x;
   const int64_t m0 = (b / nt) * 64, n0 = (b % nt) * 64;
   const T* A = static_cast<const T*>(p.A);
-  const T* B = static_cast<const T*>(p.B[prob]);
+  const T* B = static_cast<const T*>(p.B);
   T* C = static_cast<T*>(p.C);
   const T* R = static_cast<const T*>(p.R);
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
@@ -73,13 +69,8 @@ __global__ __launch_bounds__(kGenThreads) void gemm_generic_kernel(GemmProblem p
       const int r = e >> 4, kk = e & 15;
       const int64_t gm = m0 + r, gk = k0 + kk;
       As[kk][r] = (gm < p.M && gk < p.K) ? load_f32(A + gm * p.lda + gk) : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = tid + i * kGenThreads;
-      const int kk = e >> 6, c = e & 63;
-      const int64_t gk = k0 + kk, gn = n0 + c;
-      Bs[kk][c] = (gk < p.K && gn < p.N) ? load_f32(B + gk * p.ldb + gn) : 0.f;
+      const int64_t gn = n0 + r;
+      Bs[kk][r] = (gn < p.N && gk < p.K) ? load_f32(B + gn * p.ldb + gk) : 0.f;
     }
     __syncthreads();
 #pragma unroll
@@ -96,7 +87,6 @@ __global__ __launch_bounds__(kGenThreads) void gemm_generic_kernel(GemmProblem p
     }
     __syncthreads();
   }
-  const int64_t coff = p.col_off[prob];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t m = m0 + ty * 4 + i;
@@ -106,9 +96,9 @@ __global__ __launch_bounds__(kGenThreads) void gemm_generic_kernel(GemmProblem p
       const int64_t n = n0 + tx * 4 + j;
       if (n >= p.N) continue;
       float v = acc[i][j];
-      if (EPI == VITBLK_EPI_RESIDUAL) v += load_f32(R + m * p.ldr + coff + n);
+      if (EPI == VITBLK_EPI_RESIDUAL) v += load_f32(R + m * p.ldr + n);
       if (EPI == VITBLK_EPI_GELU) v = gelu_tanh_precise(v);
-      store_f32(C + m * p.ldc + coff + n, v);
+      store_f32(C + m * p.ldc + n, v);
     }
   }
 }
@@ -184,21 +174,21 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(const T* __restrict__ 
 template <typename T>
 hipError_t gemm_generic_typed(const GemmProblem& p, hipStream_t s) {
   const int64_t mt = (p.M + 63) / 64, nt = (p.N + 63) / 64;
-  const int64_t blocks = mt * nt * p.nprob;
+  const int64_t blocks = mt * nt;
   if (blocks > 2147483647LL) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(blocks));
   switch (p.epi) {
     case VITBLK_EPI_RESIDUAL:
       hipLaunchKernelGGL((gemm_generic_kernel<T, VITBLK_EPI_RESIDUAL>), grid, dim3(kGenThreads),
-                         0, s, p, mt, nt);
+                         0, s, p, nt);
       break;
     case VITBLK_EPI_GELU:
       hipLaunchKernelGGL((gemm_generic_kernel<T, VITBLK_EPI_GELU>), grid, dim3(kGenThreads), 0,
-                         s, p, mt, nt);
+                         s, p, nt);
       break;
     default:
       hipLaunchKernelGGL((gemm_generic_kernel<T, VITBLK_EPI_NONE>), grid, dim3(kGenThreads), 0,
-                         s, p, mt, nt);
+                         s, p, nt);
       break;
   }
   return hipGetLastError();

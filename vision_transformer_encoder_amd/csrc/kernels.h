@@ -6,24 +6,30 @@
 
 namespace vitblk {
 
-// C[m, col_off[p] + n] = epi(sum_k A[m, k] * B[p][k, n]) (+ R[m, col_off[p] + n])
-// for problem p < nprob, m < M, n < N.  A [M, K] with row stride lda,
-// B[p] [K, N] with row stride ldb, C and R with row strides ldc, ldr.
-// One launch covers all problems (the three Q/K/V projections share A).
+// C[m, n] = epi(sum_k A[m, k] * Wt[n, k]) (+ R[m, n]) for m < M, n < N.
+// A [M, K] with row stride lda; the weight is given out-major, Wt [N, K] with
+// row stride ldb (row n = column n of the (in, out) weight); C and R have row
+// strides ldc and ldr.  All strides in elements.
 struct GemmProblem {
   int64_t M, N, K;
   const void* A;
   int64_t lda;
-  int nprob;
-  const void* B[3];
+  const void* B;
   int64_t ldb;
   void* C;
   int64_t ldc;
-  int64_t col_off[3];
   const void* R;
   int64_t ldr;
   int epi;    // vitblk_epilogue
   int dtype;  // vitblk_dtype
+};
+
+// One (in, out) weight to write out-major: dst[c * ldd + r] = src[r * cols + c].
+struct PackJob {
+  const void* src;
+  int64_t rows, cols;
+  void* dst;
+  int64_t ldd;
 };
 
 hipError_t launch_layernorm(const void* x, void* y, int64_t rows, int64_t D, float eps,
@@ -31,11 +37,20 @@ hipError_t launch_layernorm(const void* x, void* y, int64_t rows, int64_t D, flo
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
 
+// Transpose up to 6 weights in one launch.
+hipError_t launch_pack(const PackJob* jobs, int njobs, int dtype, hipStream_t stream);
+
 // O[n*T + t, h*dh + c] = sum_j softmax_j(Q_h K_h^T / sqrt(dh))[t, j] V[n*T + j, h*dh + c]
 // with Q, K, V row strides ld (elements) and O row stride ldo.
 hipError_t launch_attention(const void* q, const void* k, const void* v, int64_t ld,
                             void* o, int64_t ldo, int64_t N, int64_t T, int64_t H,
                             int64_t dh, int dtype, hipStream_t stream);
+
+// Whole-sequence-in-LDS variant (bf16); hipErrorNotSupported when it does not
+// apply (sequence too long for LDS, head width without an instantiation).
+hipError_t launch_attention_resident(const void* q, const void* k, const void* v, int64_t ld,
+                                     void* o, int64_t ldo, int64_t N, int64_t T, int64_t H,
+                                     int64_t dh, hipStream_t stream);
 
 // Generic (any-shape, VALU, fp32 arithmetic) kernels; the fast kernels fall
 // back to these for shapes they do not tile and for fp32 tensors.

@@ -14,12 +14,26 @@ constexpr int64_t kMaxHeadDim = 1024;
 
 size_t elem_size(int dtype);  // 0 for an unknown dtype
 
-struct WorkspacePlan {
-  size_t off_big;    // [M, max(3D, F)]: packed qkv, later the MLP hidden
-  size_t off_act;    // [M, D]: LN(x), then concatenated heads, then LN(y)
-  size_t off_y;      // [M, D]: first residual output
+// Out-major weight copies written by vitblk_pack_weights (element offsets
+// rounded to kRegionAlign bytes): Wqkv^T [3D, D], Wo^T [D, D], W1^T [F, D],
+// W2^T [D, F].
+struct PackedPlan {
+  size_t off_qkv, off_o, off_1, off_2;
   size_t total;
 };
+
+// Activation regions of the forward pass, relative to `base`.
+struct WorkspacePlan {
+  PackedPlan packed;   // at the start of the vitblk_forward workspace
+  size_t act_base;     // first activation byte (0 for vitblk_forward_packed)
+  size_t off_big;      // [M, max(3D, F)]: packed qkv, later the MLP hidden
+  size_t off_act;      // [M, D]: LN(x), then concatenated heads, then LN(y)
+  size_t off_y;        // [M, D]: first residual output
+  size_t act_total;    // bytes of the three activation regions
+  size_t total;        // vitblk_forward workspace: packed.total + act_total
+};
+
+int plan_packed(int64_t D, int64_t F, int dtype, PackedPlan* plan);
 
 // Returns VITBLK_OK and fills *plan, or an error status.
 int plan_workspace(int64_t N, int64_t T, int64_t D, int64_t F, int64_t H, int dtype,
@@ -31,11 +45,20 @@ int validate_forward(const void* x, const void* w_q, const void* w_k, const void
                      int64_t H, double eps, int dtype, const void* workspace,
                      size_t workspace_bytes, WorkspacePlan* plan);
 
+int validate_forward_packed(const void* x, const void* packed, const void* out, int64_t N,
+                            int64_t T, int64_t D, int64_t F, int64_t H, double eps, int dtype,
+                            const void* workspace, size_t workspace_bytes,
+                            WorkspacePlan* plan);
+
+int validate_pack(const void* w_q, const void* w_k, const void* w_v, const void* w_o,
+                  const void* w_mlp1, const void* w_mlp2, const void* packed, int64_t D,
+                  int64_t F, int dtype, PackedPlan* plan);
+
 int validate_layernorm(const void* x, const void* out, int64_t rows, int64_t D,
                        double eps, int dtype);
 
-int validate_qkv(const void* xn, const void* w_q, const void* w_k, const void* w_v,
-                 const void* qkv, int64_t M, int64_t D, int dtype);
+int validate_qkv(const void* xn, const void* w_qkv_t, const void* qkv, int64_t M, int64_t D,
+                 int dtype);
 
 int validate_attention(const void* qkv, const void* att, int64_t N, int64_t T, int64_t D,
                        int64_t H, int dtype);

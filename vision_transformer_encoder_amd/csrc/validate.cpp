@@ -36,6 +36,28 @@ int check_eps(double eps) {
   return (std::isfinite(eps) && eps >= 0.0) ? VITBLK_OK : VITBLK_ERR_INVALID_ARG;
 }
 
+// Shape checks shared by the block-level entry points.
+int check_block_dims(int64_t N, int64_t T, int64_t D, int64_t F, int64_t H, int dtype) {
+  if (!dim_ok(N) || !dim_ok(T) || !dim_ok(D) || !dim_ok(F) || !dim_ok(H))
+    return VITBLK_ERR_INVALID_ARG;
+  if (D % H != 0) return VITBLK_ERR_INVALID_ARG;
+  if (elem_size(dtype) == 0) return VITBLK_ERR_INVALID_ARG;
+  if (N > kMaxDim || T > kMaxDim || D > kMaxDim / 3 || F > kMaxDim || N * T > kMaxDim)
+    return VITBLK_ERR_UNSUPPORTED;
+  if (D / H > kMaxHeadDim) return VITBLK_ERR_UNSUPPORTED;
+  return VITBLK_OK;
+}
+
+// out and workspace against each other and against the read-only inputs.
+int check_aliases(const void* const* ins, const size_t* in_bytes, int nin, Span out, Span ws) {
+  if (overlap(out, ws)) return VITBLK_ERR_ALIAS;
+  for (int i = 0; i < nin; ++i) {
+    const Span s = span(ins[i], in_bytes[i]);
+    if (overlap(out, s) || overlap(ws, s)) return VITBLK_ERR_ALIAS;
+  }
+  return VITBLK_OK;
+}
+
 }  // namespace
 
 size_t elem_size(int dtype) {
@@ -46,28 +68,47 @@ size_t elem_size(int dtype) {
   }
 }
 
-int plan_workspace(int64_t N, int64_t T, int64_t D, int64_t F, int64_t H, int dtype,
-                   WorkspacePlan* plan) {
-  if (!dim_ok(N) || !dim_ok(T) || !dim_ok(D) || !dim_ok(F) || !dim_ok(H))
-    return VITBLK_ERR_INVALID_ARG;
-  if (D % H != 0) return VITBLK_ERR_INVALID_ARG;
+int plan_packed(int64_t D, int64_t F, int dtype, PackedPlan* plan) {
+  if (!dim_ok(D) || !dim_ok(F)) return VITBLK_ERR_INVALID_ARG;
   const size_t es = elem_size(dtype);
   if (es == 0) return VITBLK_ERR_INVALID_ARG;
-  if (N > kMaxDim || T > kMaxDim || D > kMaxDim / 3 || F > kMaxDim || N * T > kMaxDim)
-    return VITBLK_ERR_UNSUPPORTED;
-  if (D / H > kMaxHeadDim) return VITBLK_ERR_UNSUPPORTED;
+  if (D > kMaxDim / 3 || F > kMaxDim) return VITBLK_ERR_UNSUPPORTED;
+  const size_t d = static_cast<size_t>(D), f = static_cast<size_t>(F);
+  size_t dd, df;
+  if (!mul_ok(d, d, &dd) || !mul_ok(dd, 3 * es, &dd)) return VITBLK_ERR_UNSUPPORTED;
+  if (!mul_ok(d, f, &df) || !mul_ok(df, es, &df)) return VITBLK_ERR_UNSUPPORTED;
+  PackedPlan p;
+  p.off_qkv = 0;
+  p.off_o = round_up(dd, kRegionAlign);             // 3 D^2 elements before
+  p.off_1 = p.off_o + round_up(dd / 3, kRegionAlign);
+  p.off_2 = p.off_1 + round_up(df, kRegionAlign);
+  p.total = p.off_2 + round_up(df, kRegionAlign);
+  *plan = p;
+  return VITBLK_OK;
+}
+
+int plan_workspace(int64_t N, int64_t T, int64_t D, int64_t F, int64_t H, int dtype,
+                   WorkspacePlan* plan) {
+  int st = check_block_dims(N, T, D, F, H, dtype);
+  if (st != VITBLK_OK) return st;
+  WorkspacePlan p;
+  st = plan_packed(D, F, dtype, &p.packed);
+  if (st != VITBLK_OK) return st;
+  const size_t es = elem_size(dtype);
   const size_t M = static_cast<size_t>(N) * static_cast<size_t>(T);
   const size_t wide = static_cast<size_t>(F > 3 * D ? F : 3 * D);
   size_t big, act;
   if (!mul_ok(M, wide, &big) || !mul_ok(big, es, &big)) return VITBLK_ERR_UNSUPPORTED;
   if (!mul_ok(M, static_cast<size_t>(D), &act) || !mul_ok(act, es, &act))
     return VITBLK_ERR_UNSUPPORTED;
-  WorkspacePlan p;
+  p.act_base = 0;
   p.off_big = 0;
   p.off_act = round_up(big, kRegionAlign);
   p.off_y = p.off_act + round_up(act, kRegionAlign);
-  p.total = p.off_y + round_up(act, kRegionAlign);
-  if (p.total < big) return VITBLK_ERR_UNSUPPORTED;
+  p.act_total = p.off_y + round_up(act, kRegionAlign);
+  if (p.act_total < big) return VITBLK_ERR_UNSUPPORTED;
+  p.total = p.packed.total + p.act_total;
+  if (p.total < p.act_total) return VITBLK_ERR_UNSUPPORTED;
   *plan = p;
   return VITBLK_OK;
 }
@@ -88,19 +129,60 @@ int validate_forward(const void* x, const void* w_q, const void* w_k, const void
   if (st != VITBLK_OK) return st;
   if (workspace == nullptr || !aligned16(workspace)) return VITBLK_ERR_WORKSPACE;
   if (workspace_bytes < p.total) return VITBLK_ERR_WORKSPACE;
-
   const size_t es = elem_size(dtype);
   const size_t M = static_cast<size_t>(N) * static_cast<size_t>(T);
   const size_t d = static_cast<size_t>(D), f = static_cast<size_t>(F);
   const size_t bytes[7] = {M * d * es, d * d * es, d * d * es, d * d * es,
                            d * d * es, d * f * es, f * d * es};
-  const Span o = span(out, M * d * es);
-  const Span ws = span(workspace, p.total);
-  if (overlap(o, ws)) return VITBLK_ERR_ALIAS;
-  for (int i = 0; i < 7; ++i) {
-    const Span s = span(ins[i], bytes[i]);
-    if (overlap(o, s) || overlap(ws, s)) return VITBLK_ERR_ALIAS;
-  }
+  st = check_aliases(ins, bytes, 7, span(out, M * d * es), span(workspace, p.total));
+  if (st != VITBLK_OK) return st;
+  p.act_base = p.packed.total;
+  if (plan) *plan = p;
+  return VITBLK_OK;
+}
+
+int validate_forward_packed(const void* x, const void* packed, const void* out, int64_t N,
+                            int64_t T, int64_t D, int64_t F, int64_t H, double eps, int dtype,
+                            const void* workspace, size_t workspace_bytes,
+                            WorkspacePlan* plan) {
+  if (x == nullptr || packed == nullptr || out == nullptr) return VITBLK_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(packed) || !aligned16(out)) return VITBLK_ERR_INVALID_ARG;
+  int st = check_eps(eps);
+  if (st != VITBLK_OK) return st;
+  WorkspacePlan p;
+  st = plan_workspace(N, T, D, F, H, dtype, &p);
+  if (st != VITBLK_OK) return st;
+  if (workspace == nullptr || !aligned16(workspace)) return VITBLK_ERR_WORKSPACE;
+  if (workspace_bytes < p.act_total) return VITBLK_ERR_WORKSPACE;
+  const size_t es = elem_size(dtype);
+  const size_t M = static_cast<size_t>(N) * static_cast<size_t>(T);
+  const void* ins[2] = {x, packed};
+  const size_t bytes[2] = {M * static_cast<size_t>(D) * es, p.packed.total};
+  st = check_aliases(ins, bytes, 2, span(out, M * static_cast<size_t>(D) * es),
+                     span(workspace, p.act_total));
+  if (st != VITBLK_OK) return st;
+  p.act_base = 0;
+  if (plan) *plan = p;
+  return VITBLK_OK;
+}
+
+int validate_pack(const void* w_q, const void* w_k, const void* w_v, const void* w_o,
+                  const void* w_mlp1, const void* w_mlp2, const void* packed, int64_t D,
+                  int64_t F, int dtype, PackedPlan* plan) {
+  const void* ins[6] = {w_q, w_k, w_v, w_o, w_mlp1, w_mlp2};
+  for (const void* p : ins)
+    if (p == nullptr || !aligned16(p)) return VITBLK_ERR_INVALID_ARG;
+  if (packed == nullptr || !aligned16(packed)) return VITBLK_ERR_INVALID_ARG;
+  PackedPlan p;
+  int st = plan_packed(D, F, dtype, &p);
+  if (st != VITBLK_OK) return st;
+  const size_t es = elem_size(dtype);
+  const size_t d = static_cast<size_t>(D), f = static_cast<size_t>(F);
+  const size_t bytes[6] = {d * d * es, d * d * es, d * d * es, d * d * es, d * f * es,
+                           f * d * es};
+  const Span o = span(packed, p.total);
+  for (int i = 0; i < 6; ++i)
+    if (overlap(o, span(ins[i], bytes[i]))) return VITBLK_ERR_ALIAS;
   if (plan) *plan = p;
   return VITBLK_OK;
 }
@@ -120,21 +202,18 @@ int validate_layernorm(const void* x, const void* out, int64_t rows, int64_t D, 
   return VITBLK_OK;
 }
 
-int validate_qkv(const void* xn, const void* w_q, const void* w_k, const void* w_v,
-                 const void* qkv, int64_t M, int64_t D, int dtype) {
-  const void* ins[4] = {xn, w_q, w_k, w_v};
-  for (const void* p : ins)
-    if (p == nullptr || !aligned16(p)) return VITBLK_ERR_INVALID_ARG;
-  if (qkv == nullptr || !aligned16(qkv)) return VITBLK_ERR_INVALID_ARG;
+int validate_qkv(const void* xn, const void* w_qkv_t, const void* qkv, int64_t M, int64_t D,
+                 int dtype) {
+  if (xn == nullptr || w_qkv_t == nullptr || qkv == nullptr) return VITBLK_ERR_INVALID_ARG;
+  if (!aligned16(xn) || !aligned16(w_qkv_t) || !aligned16(qkv)) return VITBLK_ERR_INVALID_ARG;
   if (!dim_ok(M) || !dim_ok(D)) return VITBLK_ERR_INVALID_ARG;
   const size_t es = elem_size(dtype);
   if (es == 0) return VITBLK_ERR_INVALID_ARG;
   if (M > kMaxDim || D > kMaxDim / 3) return VITBLK_ERR_UNSUPPORTED;
   const size_t m = static_cast<size_t>(M), d = static_cast<size_t>(D);
   const Span o = span(qkv, m * 3 * d * es);
-  const size_t bytes[4] = {m * d * es, d * d * es, d * d * es, d * d * es};
-  for (int i = 0; i < 4; ++i)
-    if (overlap(o, span(ins[i], bytes[i]))) return VITBLK_ERR_ALIAS;
+  if (overlap(o, span(xn, m * d * es)) || overlap(o, span(w_qkv_t, 3 * d * d * es)))
+    return VITBLK_ERR_ALIAS;
   return VITBLK_OK;
 }
 
