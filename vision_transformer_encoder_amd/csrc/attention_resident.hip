@@ -54,7 +54,7 @@ __device__ __forceinline__ v4i16 ds_read_tr16(const char* p) {
 }
 
 template <int DH>
-__global__ __launch_bounds__(64 * kMaxWaves) void attn_resident_kernel(
+__global__ __launch_bounds__(64 * kMaxWaves, (DH <= 64 ? 4 : 2)) void attn_resident_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     int64_t ld, bf16_t* __restrict__ O, int64_t ldo, int T, int H, int T_pad,
     float scale_log2) {
@@ -144,20 +144,20 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_resident_kernel(
           }
         }
       }
-      // Scale into the base-2 domain, mask keys past T, running maximum.
+      // Running maximum of the raw scores (keys past T masked to -inf: key
+      // kb*32 + (r/4)*8 + g*4 + r%4 of the chunk is valid iff it is < lim),
+      // then p = 2^(s * scale * log2(e) - m) with one FMA per score.
+      const int lim = T - k0 - g * 4;
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-          float v = s[kb][r] * scale_log2;
-          v = (kb < nkb && key < T) ? v : -INFINITY;
-          s[kb][r] = v;
-          mx = fmaxf(mx, v);
+          if (kb * 32 + (r >> 2) * 8 + (r & 3) >= lim) s[kb][r] = -INFINITY;
+          mx = fmaxf(mx, s[kb][r]);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
+      const float m_new = fmaxf(m_run, mx * scale_log2);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       float psum = 0.f;
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_resident_kernel(
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(s[kb][r] - m_new);
+          const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale_log2, -m_new));
           s[kb][r] = pv;
           psum += pv;
         }

@@ -11,29 +11,31 @@
 // * v_mfma_f32_32x32x16_bf16.  Each wave owns a (32*TN) x (32*TM) block of
 //   C^T: the weight tile is the MFMA's first operand and the activation tile
 //   its second, so every accumulator lane holds 4 consecutive output columns
-//   of one row (8-byte stores).
+//   of one row; lanes l and l+32 swap halves so each lane stores 16 bytes.
 // * Both tiles go straight from global memory into LDS with
 //   buffer_load_dwordx4 ... lds (no staging registers): each load instruction
 //   fills 1 KB of LDS, 16 bytes per lane at consecutive addresses.  The
 //   buffer resource (SGPRs) points at the tile's first row, each lane keeps
-//   one loop-invariant 32-bit offset per load, and the k offset is scalar.  LDS rows
-//   are 64 k (128 B, 8 chunks of 16 B); the chunk index is XOR-swizzled by
-//   (row >> 1) & 7, which each lane realises by choosing which global chunk
-//   it fetches.  Eight consecutive lanes still read one contiguous 128-B row
-//   segment of global memory, and each 16-lane phase of an MFMA operand read
-//   covers all 64 banks once.
-// * LDS stages: [A0 | A1 | B0 | B1].  A lane's fragment address differs
+//   one 32-bit offset per load, and the k offset is scalar.  LDS rows are
+//   BK k-values; the 16-byte chunk index is XOR-swizzled per row (see
+//   swz_key), which each lane realises by choosing which global chunk it
+//   fetches, so global reads stay row-contiguous and each 16-lane phase of
+//   an MFMA operand read covers all 64 banks once.
+// * LDS stages: [A stages | B stages].  A lane's fragment address differs
 //   between k-steps only through its swizzled chunk, and between fragments
 //   and stages by constants, so a wave keeps one address register per k-step
 //   and per operand.
-// * Loop: barrier (which also drains this thread's pending LDS loads), then
-//   issue the loads of the next k-slice into the other stage, then 4 k-steps
-//   of MFMAs on the current one: one barrier per 64-deep k-slice, and the
-//   next slice's loads are in flight during the MFMAs.
-// * Tile order: workgroups are dispatched round-robin over the 8 XCDs, so the
-//   linear workgroup id is remapped to give each XCD a contiguous run of
-//   tiles, walked in groups of 8 M-tiles so that the tiles resident at once
-//   on an XCD share A and W panels in its L2.
+// * k pipeline: NS - 1 k-slices in flight; one s_waitcnt + s_barrier per
+//   slice, the next slices' loads issued right after the barrier.
+// * Persistent: the grid is the number of workgroups the device holds at
+//   once and each workgroup walks tiles b, b + G, ...  The next tile's first
+//   k-slices are issued before the current tile's epilogue, so the load
+//   latency at a tile start overlaps the stores of the previous tile, and the
+//   epilogue issues all residual loads before its first store.
+// * Tile order: workgroups are dispatched round-robin over the 8 XCDs; each
+//   XCD is given a contiguous run of tiles per round, walked in groups of 8
+//   M-tiles so that the tiles resident at once on an XCD share A and W
+//   panels in its L2.
 #include "device.h"
 #include "kernels.h"
 #include "vitblk.h"
@@ -41,34 +43,49 @@
 namespace vitblk {
 namespace {
 
-constexpr int kBK = 64;     // k per LDS stage (8 chunks of 8 bf16)
 constexpr int kGroupM = 8;  // M-tiles per raster group
 constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies
 // Buffer resource word 3 for raw (untyped, stride 0) buffer access on CDNA.
 constexpr int kBufferFlags = 0x00020000;
 
-template <int BM_, int BN_, int WM_, int WN_, bool SCHED_ = true>
+template <int BM_, int BN_, int WM_, int WN_, int BK_ = 64, int NS_ = 2, bool SCHED_ = true>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int BK = BK_;    // k per LDS stage
+  static constexpr int NS = NS_;    // LDS stages (k-slices in flight: NS - 1)
   static constexpr bool SCHED = SCHED_;
   static constexpr int NT = WM * WN * 64;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int TM = WTM / 32, TN = WTN / 32;
-  static constexpr int A_LOADS = BM * 8 / NT;  // 16-B chunks per thread per k-slice
-  static constexpr int B_LOADS = BN * 8 / NT;
-  static constexpr int A_STAGE = BM * 128;     // bytes
-  static constexpr int B_STAGE = BN * 128;
-  static constexpr int LDS_BYTES = 2 * (A_STAGE + B_STAGE);
-  static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "loads must divide evenly");
+  static constexpr int CPR = BK / 8;                // 16-byte chunks per LDS row
+  static constexpr int KSTEPS = BK / 16;            // MFMA k-steps per stage
+  static constexpr int A_LOADS = BM * CPR / NT;     // 16-B chunks per thread per k-slice
+  static constexpr int B_LOADS = BN * CPR / NT;
+  static constexpr int A_STAGE = BM * BK * 2;       // bytes
+  static constexpr int B_STAGE = BN * BK * 2;
+  static constexpr int LDS_BYTES = NS * (A_STAGE + B_STAGE);
+  static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
+  static_assert(NS >= 2 && NS <= 4, "2 to 4 stages");
+  static_assert(BM * CPR % NT == 0 && BN * CPR % NT == 0, "loads must divide evenly");
   static_assert(TM >= 1 && TN >= 1, "wave tile must hold at least one 32x32 block");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
-// Linear workgroup id -> (m-tile, n-tile).
 // LDS bank swizzle.  gfx950 serves a 16-byte-per-lane LDS read 16 lanes at a
-// time over 64 four-byte banks (256 B).  Rows are 128 B, so rows r and r+1
-// already fall in different bank halves; XOR-ing the chunk index with
-// (row >> 1) & 7 spreads any 16 consecutive rows over all 16 bank groups.
-__device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
+// time over 64 four-byte banks (256 B).  A row holds CPR chunks of 16 B, so
+// 16/CPR consecutive rows fill one 256-B bank row; XOR-ing the chunk index
+// with (row / (16/CPR)) % CPR spreads any 16 consecutive rows (one MFMA
+// operand read phase) over all 16 bank groups.
+template <int CPR>
+__device__ __forceinline__ int swz_key(int row) { return (row / (16 / CPR)) % CPR; }
+
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
 
 // 16 bytes per lane from a raw buffer straight into LDS at dst + 16 * lane
 // (dst must be wave-uniform).
@@ -78,14 +95,26 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, char* dst,
                                            16, voff, soff, 0, 0);
 }
 
-__device__ __forceinline__ void tile_of(int bid, int total, int mt, int nt, int* tm, int* tn) {
-  const int q = total / kNumXcd, r = total % kNumXcd;
-  const int x = bid % kNumXcd, local = bid / kNumXcd;
-  const int t = x * q + (x < r ? x : r) + local;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff,
+                                           kBufferFlags);
+}
+
+// Persistent tile order.  Workgroup b processes tiles b, b + G, b + 2G, ...
+// The hardware places workgroup b on XCD b % 8, so within each full round of
+// G tiles (G a multiple of 8) the XCD-x workgroups get the contiguous logical
+// run [rG + x*G/8, rG + (x+1)*G/8); a partial last round keeps t.  Logical
+// tiles are walked in groups of kGroupM M-tiles, n fastest within a group.
+__device__ __forceinline__ void tile_of(int t, int grid, int total, int mt, int nt, int* tm,
+                                        int* tn) {
+  const int r = t / grid, b = t - r * grid;
+  int logical = t;
+  if ((grid % kNumXcd) == 0 && (r + 1) * grid <= total)
+    logical = r * grid + (b % kNumXcd) * (grid / kNumXcd) + b / kNumXcd;
   const int gsz = kGroupM * nt;
-  const int first_m = (t / gsz) * kGroupM;
+  const int first_m = (logical / gsz) * kGroupM;
   const int gm = (mt - first_m) < kGroupM ? (mt - first_m) : kGroupM;
-  const int w = t % gsz;
+  const int w = logical % gsz;
   *tm = first_m + w % gm;
   *tn = w / gm;
 }
@@ -93,41 +122,47 @@ __device__ __forceinline__ void tile_of(int bid, int total, int mt, int nt, int*
 template <class C, int EPI>
 __global__ __launch_bounds__(C::NT, 1) void gemm_bf16_kernel(GemmProblem p, int mt, int nt) {
   __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
-  char* const a_lds = lds;                    // [stage][BM rows][128 B]
-  char* const b_lds = lds + 2 * C::A_STAGE;   // [stage][BN rows][128 B]
+  char* const a_lds = lds;                       // [stage][BM rows][BK * 2 B]
+  char* const b_lds = lds + C::NS * C::A_STAGE;  // [stage][BN rows][BK * 2 B]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
-  int tm, tn;
-  tile_of(blockIdx.x, gridDim.x, mt, nt, &tm, &tn);
-  const int64_t m0 = static_cast<int64_t>(tm) * C::BM, n0 = static_cast<int64_t>(tn) * C::BN;
+  const int lrow = lane & 31, lhalf = lane >> 5;
   const int64_t M = p.M, N = p.N;
+  const int KT = static_cast<int>(p.K / C::BK);
+  const int total = mt * nt, grid = gridDim.x;
 
-  // Buffer resources at the tiles' first rows, and per-lane byte offsets of
-  // the chunks this thread loads (rows past M or N are clamped: their
-  // products only reach outputs that are never stored).
-  const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char*>(static_cast<const char*>(p.A) + m0 * p.lda * 2), 0, 0x7fffffff,
-      kBufferFlags);
-  const __amdgpu_buffer_rsrc_t b_rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char*>(static_cast<const char*>(p.B) + n0 * p.ldb * 2), 0, 0x7fffffff,
-      kBufferFlags);
+  // Tile-dependent load state: buffer resources at the tiles' first rows and
+  // per-lane byte offsets of the chunks this thread loads (rows past M or N
+  // are clamped: their products only reach outputs that are never stored).
+  int64_t m0 = 0, n0 = 0;
+  __amdgpu_buffer_rsrc_t a_rs, b_rs;
   uint32_t a_off[C::A_LOADS], b_off[C::B_LOADS];
+  auto prepare = [&](int t) {
+    int tm, tn;
+    tile_of(t, grid, total, mt, nt, &tm, &tn);
+    m0 = static_cast<int64_t>(tm) * C::BM;
+    n0 = static_cast<int64_t>(tn) * C::BN;
+    a_rs = make_rsrc(static_cast<const char*>(p.A) + m0 * p.lda * 2);
+    b_rs = make_rsrc(static_cast<const char*>(p.B) + n0 * p.ldb * 2);
 #pragma unroll
-  for (int i = 0; i < C::A_LOADS; ++i) {
-    const int e = i * C::NT + tid, row = e >> 3, c = (e & 7) ^ swz_key(row);
-    const int64_t r = (m0 + row < M) ? row : (M - 1 - m0);
-    a_off[i] = static_cast<uint32_t>(r * p.lda * 2 + c * 16);
-  }
+    for (int i = 0; i < C::A_LOADS; ++i) {
+      const int e = i * C::NT + tid, row = e / C::CPR;
+      const int c = (e % C::CPR) ^ swz_key<C::CPR>(row);
+      const int64_t r = (m0 + row < M) ? row : (M - 1 - m0);
+      a_off[i] = static_cast<uint32_t>(r * p.lda * 2 + c * 16);
+    }
 #pragma unroll
-  for (int i = 0; i < C::B_LOADS; ++i) {
-    const int e = i * C::NT + tid, row = e >> 3, c = (e & 7) ^ swz_key(row);
-    const int64_t r = (n0 + row < N) ? row : (N - 1 - n0);
-    b_off[i] = static_cast<uint32_t>(r * p.ldb * 2 + c * 16);
-  }
+    for (int i = 0; i < C::B_LOADS; ++i) {
+      const int e = i * C::NT + tid, row = e / C::CPR;
+      const int c = (e % C::CPR) ^ swz_key<C::CPR>(row);
+      const int64_t r = (n0 + row < N) ? row : (N - 1 - n0);
+      b_off[i] = static_cast<uint32_t>(r * p.ldb * 2 + c * 16);
+    }
+  };
   auto issue = [&](int kt, int st) {
-    const int kb = kt * kBK * 2;  // byte offset of the k-slice
+    const int kb = kt * C::BK * 2;  // byte offset of the k-slice
 #pragma unroll
     for (int i = 0; i < C::A_LOADS; ++i)
       load_lds16(a_rs, a_lds + st * C::A_STAGE + (i * C::NT + wave * 64) * 16, a_off[i], kb);
@@ -138,22 +173,15 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16_kernel(GemmProblem p, int 
 
   // Fragment addresses: row (lane & 31) of the wave's first 32-row block,
   // logical chunk 2s + (lane >> 5), swizzled.
-  const int lrow = lane & 31, lhalf = lane >> 5;
-  int a_rd[4], b_rd[4];
+  int a_rd[C::KSTEPS], b_rd[C::KSTEPS];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int ch = ((2 * s + lhalf) ^ swz_key(lrow)) * 16;
-    a_rd[s] = (wm * C::WTM + lrow) * 128 + ch;
-    b_rd[s] = (wn * C::WTN + lrow) * 128 + ch;
+  for (int s = 0; s < C::KSTEPS; ++s) {
+    const int ch = ((2 * s + lhalf) ^ swz_key<C::CPR>(lrow)) * 16;
+    a_rd[s] = (wm * C::WTM + lrow) * C::BK * 2 + ch;
+    b_rd[s] = (wn * C::WTN + lrow) * C::BK * 2 + ch;
   }
 
   f32x16 acc[C::TN][C::TM];
-#pragma unroll
-  for (int j = 0; j < C::TN; ++j)
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.f;
 
   // Fragments of k-step s+1 are read from LDS while the MFMAs of k-step s
   // run; sched_group_barrier pins that interleaving (one LDS read after each
@@ -161,10 +189,10 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16_kernel(GemmProblem p, int 
   auto read_frags = [&](const char* as, const char* bs, int s, bf16x8* af, bf16x8* bf) {
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
-      af[i] = *reinterpret_cast<const bf16x8*>(as + a_rd[s] + i * 32 * 128);
+      af[i] = *reinterpret_cast<const bf16x8*>(as + a_rd[s] + i * 32 * C::BK * 2);
 #pragma unroll
     for (int j = 0; j < C::TN; ++j)
-      bf[j] = *reinterpret_cast<const bf16x8*>(bs + b_rd[s] + j * 32 * 128);
+      bf[j] = *reinterpret_cast<const bf16x8*>(bs + b_rd[s] + j * 32 * C::BK * 2);
   };
   auto compute = [&](int st) {
     const char* as = a_lds + st * C::A_STAGE;
@@ -172,15 +200,15 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16_kernel(GemmProblem p, int 
     bf16x8 af[2][C::TM], bf[2][C::TN];
     read_frags(as, bs, 0, af[0], bf[0]);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (s + 1 < 4) read_frags(as, bs, s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
+    for (int s = 0; s < C::KSTEPS; ++s) {
+      if (s + 1 < C::KSTEPS) read_frags(as, bs, s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
 #pragma unroll
       for (int j = 0; j < C::TN; ++j)
 #pragma unroll
         for (int i = 0; i < C::TM; ++i)
           acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[s & 1][j], af[s & 1][i],
                                                               acc[j][i], 0, 0, 0);
-      if (C::SCHED && s + 1 < 4) {
+      if (C::SCHED && s + 1 < C::KSTEPS) {
 #pragma unroll
         for (int r = 0; r < C::TM + C::TN; ++r) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
@@ -191,73 +219,179 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16_kernel(GemmProblem p, int 
     }
   };
 
-  const int KT = static_cast<int>(p.K / kBK);
-  issue(0, 0);
-  for (int kt = 0; kt < KT; ++kt) {
-    __syncthreads();
-    if (kt + 1 < KT) issue(kt + 1, (kt + 1) & 1);
-    compute(kt & 1);
-  }
+  int t = blockIdx.x;
+  if (t >= total) return;  // whole workgroup
+  prepare(t);
+#pragma unroll
+  for (int s = 0; s < C::NS - 1; ++s)
+    if (s < KT) issue(s, s);
 
-  // Epilogue: accumulator element r of lane l in block (j, i) is
-  // C[m0 + wm*WTM + i*32 + (l & 31)][n0 + wn*WTN + j*32 + (r/4)*8 + (l/32)*4 + r%4].
-  bf16_t* Cp = static_cast<bf16_t*>(p.C);
-  const bf16_t* Rp = static_cast<const bf16_t*>(p.R);
+  while (true) {
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i) {
-    const int64_t m = m0 + wm * C::WTM + i * 32 + lrow;
-    if (m >= M) continue;
+    for (int j = 0; j < C::TN; ++j)
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j) {
+      for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int64_t n = n0 + wn * C::WTN + j * 32 + rr * 8 + lhalf * 4;
-        if (n >= N) continue;
-        float v[4];
+        for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.f;
+
+    // Before computing slice kt a wave waits until its own loads of slice kt
+    // have landed (newer slices may stay outstanding; vmcnt retires in issue
+    // order), then the barrier makes every wave's part visible and
+    // guarantees that the stage refilled next (read in the previous
+    // iteration) is no longer being read.
+    for (int kt = 0; kt < KT; ++kt) {
+      if (kt + C::NS - 2 < KT)
+        wait_vmcnt<(C::NS - 2) * (C::A_LOADS + C::B_LOADS)>();
+      else
+        wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      if (kt + C::NS - 1 < KT) issue(kt + C::NS - 1, (kt + C::NS - 1) % C::NS);
+      compute(kt % C::NS);
+    }
+
+    // Start the next tile's first k-slices before this tile's epilogue (all
+    // waves are done reading LDS once past this barrier).
+    const int64_t cm0 = m0, cn0 = n0;
+    const int t_next = t + grid;
+    const bool more = t_next < total;
+    __builtin_amdgcn_s_barrier();
+    if (more) {
+      prepare(t_next);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[j][i][rr * 4 + e];
-        if (EPI == VITBLK_EPI_RESIDUAL) {
-          const uint2 rv = *reinterpret_cast<const uint2*>(Rp + m * p.ldr + n);
-          v[0] += __uint_as_float(rv.x << 16);
-          v[1] += __uint_as_float(rv.x & 0xffff0000u);
-          v[2] += __uint_as_float(rv.y << 16);
-          v[3] += __uint_as_float(rv.y & 0xffff0000u);
-        }
-        if (EPI == VITBLK_EPI_GELU) {
+      for (int s = 0; s < C::NS - 1; ++s)
+        if (s < KT) issue(s, s);
+    }
+
+    // Epilogue.  Accumulator element r of lane l in block (j, i) is
+    // C[m0 + wm*WTM + i*32 + (l & 31)][n0 + wn*WTN + j*32 + (r/4)*8 + (l/32)*4 + r%4].
+    // Lanes l and l+32 hold the two halves of 8 consecutive columns; one
+    // v_permlane32_swap per dword hands lane l the columns 16q + 0..7 and lane
+    // l+32 the columns 16q + 8..15 (q = 0, 1), so every lane writes 16
+    // contiguous bytes.  Residuals are read in that layout, all before the
+    // first store (addresses clamped into range), and added in fp32 before
+    // the single rounding to bf16.
+    bf16_t* Cp = static_cast<bf16_t*>(p.C);
+    const bf16_t* Rp = static_cast<const bf16_t*>(p.R);
+    uint4 res[C::TM][C::TN][2];
+    if (EPI == VITBLK_EPI_RESIDUAL) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = gelu_tanh_fast(v[e]);
-        }
-        *reinterpret_cast<uint2*>(Cp + m * p.ldc + n) =
-            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      for (int i = 0; i < C::TM; ++i) {
+        int64_t m = cm0 + wm * C::WTM + i * 32 + lrow;
+        m = m < M ? m : M - 1;
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            int64_t n = cn0 + wn * C::WTN + j * 32 + q * 16 + lhalf * 8;
+            n = n < N ? n : N - 8;
+            res[i][j][q] = ld_global16(Rp + m * p.ldr + n);
+          }
       }
     }
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) {
+      const int64_t m = cm0 + wm * C::WTM + i * 32 + lrow;
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int64_t n = cn0 + wn * C::WTN + j * 32 + q * 16 + lhalf * 8;
+          uint4 out;
+          if (EPI == VITBLK_EPI_RESIDUAL) {
+            // fp32 exchange: lane's 8 columns are x[0..3] then y[0..3].
+            float x[4], y[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const auto r = __builtin_amdgcn_permlane32_swap(
+                  __float_as_uint(acc[j][i][(2 * q) * 4 + e]),
+                  __float_as_uint(acc[j][i][(2 * q + 1) * 4 + e]), false, false);
+              x[e] = __uint_as_float(r[0]);
+              y[e] = __uint_as_float(r[1]);
+            }
+            const uint4 rv = res[i][j][q];
+            const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              v[e] = x[e];
+              v[4 + e] = y[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              v[2 * e] += __uint_as_float(rw[e] << 16);
+              v[2 * e + 1] += __uint_as_float(rw[e] & 0xffff0000u);
+            }
+            out = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                             pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+          } else {
+            // round first, then exchange bf16 pairs (4 dwords per lane).
+            uint32_t w[2][2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              float v[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                v[e] = acc[j][i][(2 * q + h) * 4 + e];
+                if (EPI == VITBLK_EPI_GELU) v[e] = gelu_tanh_fast(v[e]);
+              }
+              w[h][0] = pack_bf16x2(v[0], v[1]);
+              w[h][1] = pack_bf16x2(v[2], v[3]);
+            }
+            const auto s0 = __builtin_amdgcn_permlane32_swap(w[0][0], w[1][0], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(w[0][1], w[1][1], false, false);
+            out = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+          }
+          if (m < M && n < N) st_global16(Cp + m * p.ldc + n, out);
+        }
+      }
+    }
+    if (!more) break;
+    t = t_next;
   }
 }
 
 using BigTile = Cfg<256, 256, 2, 4>;  // 8 waves (2 per SIMD), 128x64 per wave
 
+// Workgroups of this kernel the device holds at once (cached per kernel).
+template <class C, int EPI>
+int resident_workgroups() {
+  static int cached = 0;
+  if (cached == 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(&gemm_bf16_kernel<C, EPI>), C::NT, 0) !=
+            hipSuccess) {
+      (void)hipGetLastError();
+      return 0;
+    }
+    cached = cus * (per_cu > 0 ? per_cu : 1);
+  }
+  return cached;
+}
+
+template <class C, int EPI>
+hipError_t launch_epi(const GemmProblem& p, hipStream_t s) {
+  const int64_t mt = (p.M + C::BM - 1) / C::BM, nt = (p.N + C::BN - 1) / C::BN;
+  const int64_t tiles = mt * nt;
+  if (tiles > 2147483647LL) return hipErrorInvalidValue;
+  int64_t grid = resident_workgroups<C, EPI>();
+  if (grid <= 0) return hipErrorInvalidValue;
+  grid = grid / kNumXcd * kNumXcd;  // keeps the XCD-contiguous mapping exact
+  if (grid <= 0 || grid > tiles) grid = tiles;
+  hipLaunchKernelGGL((gemm_bf16_kernel<C, EPI>), dim3(static_cast<unsigned>(grid)), dim3(C::NT),
+                     0, s, p, static_cast<int>(mt), static_cast<int>(nt));
+  return hipGetLastError();
+}
+
 template <class C>
 hipError_t launch_cfg(const GemmProblem& p, hipStream_t s) {
-  const int64_t mt = (p.M + C::BM - 1) / C::BM, nt = (p.N + C::BN - 1) / C::BN;
-  const int64_t blocks = mt * nt;
-  if (blocks > 2147483647LL) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<unsigned>(blocks)), block(C::NT);
-  const int imt = static_cast<int>(mt), int_nt = static_cast<int>(nt);
   switch (p.epi) {
-    case VITBLK_EPI_RESIDUAL:
-      hipLaunchKernelGGL((gemm_bf16_kernel<C, VITBLK_EPI_RESIDUAL>), grid, block, 0, s, p, imt,
-                         int_nt);
-      break;
-    case VITBLK_EPI_GELU:
-      hipLaunchKernelGGL((gemm_bf16_kernel<C, VITBLK_EPI_GELU>), grid, block, 0, s, p, imt,
-                         int_nt);
-      break;
-    default:
-      hipLaunchKernelGGL((gemm_bf16_kernel<C, VITBLK_EPI_NONE>), grid, block, 0, s, p, imt,
-                         int_nt);
-      break;
+    case VITBLK_EPI_RESIDUAL: return launch_epi<C, VITBLK_EPI_RESIDUAL>(p, s);
+    case VITBLK_EPI_GELU: return launch_epi<C, VITBLK_EPI_GELU>(p, s);
+    default: return launch_epi<C, VITBLK_EPI_NONE>(p, s);
   }
-  return hipGetLastError();
 }
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
@@ -268,7 +402,7 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u
 // aligned rows, and a 256-row panel of either operand to span < 2 GiB (its
 // buffer offsets are 32-bit).  Everything else takes the generic kernel.
 bool gemm_fast_ok(const GemmProblem& p) {
-  bool ok = p.dtype == VITBLK_BF16 && p.K % kBK == 0 && p.N % 8 == 0 && p.N >= 8 &&
+  bool ok = p.dtype == VITBLK_BF16 && p.K % 64 == 0 && p.N % 8 == 0 && p.N >= 8 &&
             p.lda % 8 == 0 && p.ldb % 8 == 0 && p.ldc % 8 == 0 && aligned16(p.A) &&
             aligned16(p.B) && aligned16(p.C) && p.lda * 2 * 256 < (1LL << 31) &&
             p.ldb * 2 * 256 < (1LL << 31) && p.K * 2 < (1LL << 31);
