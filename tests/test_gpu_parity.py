@@ -73,6 +73,21 @@ def test_linear(dtype, epi, M, K, N):
     assert_close(got, ref, dtype, f"linear {epi} M={M} K={K} N={N}")
 
 
+@pytest.mark.parametrize("epi", ["none", "residual"])
+def test_linear_with_ragged_tail_rows(epi):
+    # 71 M-tiles of 256 rows (ragged): the big tile takes a whole number of
+    # rounds and the remaining rows go to the smaller tail tile.
+    M, K, N = 70 * 256 + 77, 256, 1024
+    rng = np.random.default_rng(31)
+    a = _rand(rng, (M, K), "bf16")
+    w = _rand(rng, (K, N), "bf16", scale=1 / math.sqrt(K))
+    r = _rand(rng, (M, N), "bf16")
+    res = to_dev(r, "bf16") if epi == "residual" else None
+    got = to_host(vb.linear(to_dev(a, "bf16"), to_dev(w.T, "bf16"), EPIS[epi], residual=res))
+    ref = oracle.project(a, w) + (r if epi == "residual" else 0.0)
+    assert_close(got, ref, "bf16", f"linear {epi} M={M}")
+
+
 def _attention_ref(q, k, v, H):
     a = oracle.softmax_rows(oracle.attention_scores(oracle.split_heads(q, H),
                                                     oracle.split_heads(k, H)))

@@ -350,7 +350,8 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16_kernel(GemmProblem p, int 
   }
 }
 
-using BigTile = Cfg<256, 256, 2, 4>;  // 8 waves (2 per SIMD), 128x64 per wave
+using BigTile = Cfg<256, 256, 2, 4>;   // 8 waves (2 per SIMD), 128x64 per wave
+using TailTile = Cfg<128, 128, 2, 2>;  // 4 waves, 64x64 per wave (2 workgroups per CU)
 
 // Workgroups of this kernel the device holds at once (cached per kernel).
 template <class C, int EPI>
@@ -410,9 +411,47 @@ bool gemm_fast_ok(const GemmProblem& p) {
   return ok;
 }
 
+// Rows [r0, r0 + rows) of p as a problem of its own.
+GemmProblem row_slice(const GemmProblem& p, int64_t r0, int64_t rows) {
+  GemmProblem q = p;
+  q.M = rows;
+  q.A = static_cast<const char*>(p.A) + r0 * p.lda * 2;
+  q.C = static_cast<char*>(p.C) + r0 * p.ldc * 2;
+  if (p.R) q.R = static_cast<const char*>(p.R) + r0 * p.ldr * 2;
+  return q;
+}
+
+// Wave quantisation: with G resident big-tile workgroups, the last partial
+// round of tiles would run a handful of tiles for a full round's time.  The
+// big tile therefore covers the largest block of M-tiles that makes a whole
+// number of rounds, and the remaining rows run as a second launch with a
+// quarter-size tile, which finishes in a fraction of a round.
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t s) {
   if (!gemm_fast_ok(p)) return launch_gemm_generic(p, s);
-  return launch_cfg<BigTile>(p, s);
+  using Big = BigTile;
+  using Small = TailTile;
+  const int64_t mt = (p.M + Big::BM - 1) / Big::BM, nt = (p.N + Big::BN - 1) / Big::BN;
+  int64_t grid = 0;
+  switch (p.epi) {
+    case VITBLK_EPI_RESIDUAL: grid = resident_workgroups<Big, VITBLK_EPI_RESIDUAL>(); break;
+    case VITBLK_EPI_GELU: grid = resident_workgroups<Big, VITBLK_EPI_GELU>(); break;
+    default: grid = resident_workgroups<Big, VITBLK_EPI_NONE>(); break;
+  }
+  grid = grid / kNumXcd * kNumXcd;
+  if (grid <= 0 || mt * nt <= grid) return launch_cfg<Big>(p, s);
+  int64_t g = grid, b = nt;  // gcd(grid, nt)
+  while (b) {
+    const int64_t r = g % b;
+    g = b;
+    b = r;
+  }
+  const int64_t step = grid / g;           // M-tiles per whole number of rounds
+  const int64_t m_main = mt / step * step;  // M-tiles done with the big tile
+  if (m_main == 0 || m_main == mt || (mt * nt) % grid == 0) return launch_cfg<Big>(p, s);
+  const int64_t rows_main = m_main * Big::BM;
+  const hipError_t e = launch_cfg<Big>(row_slice(p, 0, rows_main), s);
+  if (e != hipSuccess) return e;
+  return launch_cfg<Small>(row_slice(p, rows_main, p.M - rows_main), s);
 }
 
 }  // namespace vitblk
