@@ -26,7 +26,10 @@
 //   and stages by constants, so a wave keeps one address register per k-step
 //   and per operand.
 // * k pipeline: NS - 1 k-slices in flight; one s_waitcnt + s_barrier per
-//   slice, the next slices' loads issued right after the barrier.
+//   slice, the next slices' loads issued right after the slice's first
+//   fragment reads.  With
+//   NSA = 3 A stages (and NS = 2 W stages) the activation slice, the operand
+//   that misses L2 most, is issued two slices ahead and the weight slice one.
 // * Persistent: the grid is the number of workgroups the device holds at
 //   once and each workgroup walks tiles b, b + G, ...  The next tile's first
 //   k-slices are issued before the current tile's epilogue, so the load
@@ -48,11 +51,15 @@ constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies
 // Buffer resource word 3 for raw (untyped, stride 0) buffer access on CDNA.
 constexpr int kBufferFlags = 0x00020000;
 
-template <int BM_, int BN_, int WM_, int WN_, int BK_ = 64, int NS_ = 2, bool SCHED_ = true>
+template <int BM_, int BN_, int WM_, int WN_, int BK_ = 64, int NS_ = 2, int NSA_ = NS_,
+          bool SCHED_ = true>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   static constexpr int BK = BK_;    // k per LDS stage
-  static constexpr int NS = NS_;    // LDS stages (k-slices in flight: NS - 1)
+  static constexpr int NS = NS_;    // LDS stages of W (k-slices in flight: NS - 1)
+  // LDS stages of A.  NSA = NS + 1 gives the activation operand, whose panels
+  // miss L2 far more often than the weights', one more k-slice of lead.
+  static constexpr int NSA = NSA_;
   static constexpr bool SCHED = SCHED_;
   static constexpr int NT = WM * WN * 64;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -63,7 +70,8 @@ struct Cfg {
   static constexpr int B_LOADS = BN * CPR / NT;
   static constexpr int A_STAGE = BM * BK * 2;       // bytes
   static constexpr int B_STAGE = BN * BK * 2;
-  static constexpr int LDS_BYTES = NS * (A_STAGE + B_STAGE);
+  static constexpr int LDS_BYTES = NSA * A_STAGE + NS * B_STAGE;
+  static_assert(NSA == NS || (NSA == 3 && NS == 2), "A stages: NS, or 3 with NS = 2");
   static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
   static_assert(NS >= 2 && NS <= 4, "2 to 4 stages");
   static_assert(BM * CPR % NT == 0 && BN * CPR % NT == 0, "loads must divide evenly");
@@ -123,7 +131,7 @@ template <class C, int EPI>
 __global__ __launch_bounds__(C::NT, 1) void gemm_bf16_kernel(GemmProblem p, int mt, int nt) {
   __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
   char* const a_lds = lds;                       // [stage][BM rows][BK * 2 B]
-  char* const b_lds = lds + C::NS * C::A_STAGE;  // [stage][BN rows][BK * 2 B]
+  char* const b_lds = lds + C::NSA * C::A_STAGE;  // [stage][BN rows][BK * 2 B]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -161,14 +169,33 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16_kernel(GemmProblem p, int 
       b_off[i] = static_cast<uint32_t>(r * p.ldb * 2 + c * 16);
     }
   };
-  auto issue = [&](int kt, int st) {
+  auto issue_a = [&](int kt, int st) {
     const int kb = kt * C::BK * 2;  // byte offset of the k-slice
 #pragma unroll
     for (int i = 0; i < C::A_LOADS; ++i)
       load_lds16(a_rs, a_lds + st * C::A_STAGE + (i * C::NT + wave * 64) * 16, a_off[i], kb);
+  };
+  auto issue_b = [&](int kt, int st) {
+    const int kb = kt * C::BK * 2;
 #pragma unroll
     for (int i = 0; i < C::B_LOADS; ++i)
       load_lds16(b_rs, b_lds + st * C::B_STAGE + (i * C::NT + wave * 64) * 16, b_off[i], kb);
+  };
+  auto issue = [&](int kt, int st) {
+    issue_a(kt, st);
+    issue_b(kt, st);
+  };
+  // Start of a tile: the first k-slices in flight (A(0), W(0) [, A(1)]).
+  auto start_tile = [&]() {
+    if (C::NSA > C::NS) {
+      issue_a(0, 0);
+      issue_b(0, 0);
+      if (1 < KT) issue_a(1, 1);
+    } else {
+#pragma unroll
+      for (int s = 0; s < C::NS - 1; ++s)
+        if (s < KT) issue(s, s);
+    }
   };
 
   // Fragment addresses: row (lane & 31) of the wave's first 32-row block,
@@ -194,11 +221,14 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16_kernel(GemmProblem p, int 
     for (int j = 0; j < C::TN; ++j)
       bf[j] = *reinterpret_cast<const bf16x8*>(bs + b_rd[s] + j * 32 * C::BK * 2);
   };
-  auto compute = [&](int st) {
-    const char* as = a_lds + st * C::A_STAGE;
-    const char* bs = b_lds + st * C::B_STAGE;
+  auto compute = [&](int sa, int sb, auto&& loads) {
+    const char* as = a_lds + sa * C::A_STAGE;
+    const char* bs = b_lds + sb * C::B_STAGE;
     bf16x8 af[2][C::TM], bf[2][C::TN];
+    // The first fragment reads go out before the next slices' loads, so the
+    // matrix cores restart as soon as possible after the barrier.
     read_frags(as, bs, 0, af[0], bf[0]);
+    loads();
 #pragma unroll
     for (int s = 0; s < C::KSTEPS; ++s) {
       if (s + 1 < C::KSTEPS) read_frags(as, bs, s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
@@ -222,9 +252,7 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16_kernel(GemmProblem p, int 
   int t = blockIdx.x;
   if (t >= total) return;  // whole workgroup
   prepare(t);
-#pragma unroll
-  for (int s = 0; s < C::NS - 1; ++s)
-    if (s < KT) issue(s, s);
+  start_tile();
 
   while (true) {
 #pragma unroll
@@ -240,13 +268,32 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16_kernel(GemmProblem p, int 
     // guarantees that the stage refilled next (read in the previous
     // iteration) is no longer being read.
     for (int kt = 0; kt < KT; ++kt) {
-      if (kt + C::NS - 2 < KT)
+      if (C::NSA > C::NS) {
+        // Iteration j issues W(j+1) then A(j+2); at the top of iteration kt
+        // only A(kt+1) is newer than W(kt) (and A(kt) is older).  Loads
+        // retire in issue order; at kt = 0 the previous tile's stores are
+        // pending too, so wait for everything.
+        if (kt > 0 && kt + 1 < KT)
+          wait_vmcnt<C::A_LOADS>();
+        else
+          wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        compute(kt % C::NSA, kt % C::NS, [&]() {
+          if (kt + 1 < KT) issue_b(kt + 1, (kt + 1) % C::NS);
+          if (kt + 2 < KT) issue_a(kt + 2, (kt + 2) % C::NSA);
+        });
+        continue;
+      }
+      // Loads issued after slice kt's: those of the newer slices (at kt = 0
+      // the previous tile's stores are pending too).
+      if (kt > 0 && kt + C::NS - 2 < KT)
         wait_vmcnt<(C::NS - 2) * (C::A_LOADS + C::B_LOADS)>();
       else
         wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
-      if (kt + C::NS - 1 < KT) issue(kt + C::NS - 1, (kt + C::NS - 1) % C::NS);
-      compute(kt % C::NS);
+      compute(kt % C::NS, kt % C::NS, [&]() {
+        if (kt + C::NS - 1 < KT) issue(kt + C::NS - 1, (kt + C::NS - 1) % C::NS);
+      });
     }
 
     // Start the next tile's first k-slices before this tile's epilogue (all
@@ -257,9 +304,7 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16_kernel(GemmProblem p, int 
     __builtin_amdgcn_s_barrier();
     if (more) {
       prepare(t_next);
-#pragma unroll
-      for (int s = 0; s < C::NS - 1; ++s)
-        if (s < KT) issue(s, s);
+      start_tile();
     }
 
     // Epilogue.  Accumulator element r of lane l in block (j, i) is
@@ -350,8 +395,10 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16_kernel(GemmProblem p, int 
   }
 }
 
-using BigTile = Cfg<256, 256, 2, 4>;   // 8 waves (2 per SIMD), 128x64 per wave
-using TailTile = Cfg<128, 128, 2, 2>;  // 4 waves, 64x64 per wave (2 workgroups per CU)
+// 8 waves (2 per SIMD), 128x64 per wave, 3 A stages + 2 W stages: 160 KB LDS.
+using BigTile = Cfg<256, 256, 2, 4, 64, 2, 3>;
+// 4 waves, 64x64 per wave, 80 KB LDS: 2 workgroups per CU.
+using SmallTile = Cfg<128, 128, 2, 2, 64, 2, 3>;
 
 // Workgroups of this kernel the device holds at once (cached per kernel).
 template <class C, int EPI>
@@ -421,15 +468,22 @@ GemmProblem row_slice(const GemmProblem& p, int64_t r0, int64_t rows) {
   return q;
 }
 
+// Tile choice.  With one big-tile workgroup per CU, a tile's epilogue runs
+// with the matrix cores idle; when it also reads a residual and K is short
+// (the output projection: K = D) that share is large, and the small tile,
+// two workgroups per CU, lets one workgroup's epilogue overlap the other's
+// main loop.  Otherwise the big tile (half the operand traffic per flop).
+//
 // Wave quantisation: with G resident big-tile workgroups, the last partial
 // round of tiles would run a handful of tiles for a full round's time.  The
 // big tile therefore covers the largest block of M-tiles that makes a whole
-// number of rounds, and the remaining rows run as a second launch with a
+// number of rounds, and the remaining rows run as a second launch with the
 // quarter-size tile, which finishes in a fraction of a round.
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t s) {
   if (!gemm_fast_ok(p)) return launch_gemm_generic(p, s);
   using Big = BigTile;
-  using Small = TailTile;
+  using Small = SmallTile;
+  if (p.epi == VITBLK_EPI_RESIDUAL && p.K <= 1024) return launch_cfg<Small>(p, s);
   const int64_t mt = (p.M + Big::BM - 1) / Big::BM, nt = (p.N + Big::BN - 1) / Big::BN;
   int64_t grid = 0;
   switch (p.epi) {
