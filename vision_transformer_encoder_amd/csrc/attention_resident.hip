@@ -27,6 +27,8 @@
 // scores are set to -inf.
 #include <math.h>
 
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 #include "vitblk.h"
@@ -39,6 +41,11 @@ constexpr int kLdsBytes = 160 * 1024;  // gfx950 LDS per workgroup
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
+// Slack of the reference maximum, in log2 units (probabilities < 2^8).
+constexpr float kSlack = 8.0f;
+// bf16 pair (1, 1): a dot product with it sums a packed pair.
+constexpr bf16x2_t kOnes = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+
 template <int DH>
 struct ResCfg {
   static_assert(DH % 16 == 0, "head width must be a multiple of 16");
@@ -47,6 +54,23 @@ struct ResCfg {
   static constexpr int SV = (DHP * 2) % 128 == 0 ? DHP * 2 + 64 : DHP * 2;  // V row stride
   static constexpr int ROW = SK + SV;
 };
+
+// (x of lane l, x of lane l ^ 32) for every lane, by one v_permlane32_swap:
+// its first result holds lanes 0-31 of x in both halves, its second lanes
+// 32-63 in both halves.
+__device__ __forceinline__ uint2 with_other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return make_uint2(r[0], r[1]);
+}
+__device__ __forceinline__ float max_halves(float x) {
+  const uint2 r = with_other_half(x);
+  return fmaxf(__uint_as_float(r.x), __uint_as_float(r.y));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const uint2 r = with_other_half(x);
+  return __uint_as_float(r.x) + __uint_as_float(r.y);
+}
 
 __device__ __forceinline__ v4i16 ds_read_tr16(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -68,6 +92,24 @@ __global__ __launch_bounds__(64 * kMaxWaves, (DH <= 64 ? 4 : 2)) void attn_resid
   const int64_t seq0 = n * T;
   const int64_t hoff = static_cast<int64_t>(h) * DH;
   const int tid = threadIdx.x, nthreads = blockDim.x;
+
+  const int lane = tid & 63, wave = tid >> 6, nw = nthreads >> 6;
+  const int lrow = lane & 31, g = lane >> 5;
+  const int nqt = T_pad / 32;
+
+  // Q fragments of a 32-query tile: lane (lrow, g) holds features
+  // 16s + 8g .. +7 of query qt*32 + lrow (clamped to T-1), s = 0 .. DH/16-1.
+  bf16x8 qf[DH / 16];
+  auto load_q = [&](int qt) {
+    const int q = qt * 32 + lrow;
+    const bf16_t* qrow = Q + (seq0 + (q < T ? q : T - 1)) * ld + hoff + g * 8;
+#pragma unroll
+    for (int s = 0; s < DH / 16; ++s)
+      qf[s] = __builtin_bit_cast(bf16x8, ld_global16(qrow + s * 16));
+  };
+  // The wave's first Q tile is requested together with K and V, so the
+  // workgroup waits for one round of memory latency, not two.
+  if (wave < nqt) load_q(wave);
 
   // ---- K and V of this head into LDS (4 chunks of 16 B per operand in flight per thread).
   constexpr int CPR = DH / 8;  // 16-byte chunks per row
@@ -103,78 +145,91 @@ __global__ __launch_bounds__(64 * kMaxWaves, (DH <= 64 ? 4 : 2)) void attn_resid
   }
   __syncthreads();
 
-  const int lane = tid & 63, wave = tid >> 6, nw = nthreads >> 6;
-  const int lrow = lane & 31, g = lane >> 5;
   const int i16 = lane & 15, q16 = (lane >> 4) & 1;
   // Lane's V^T read address relative to (key0, feature block): row key0 + i16/4,
   // columns q16*16 + 4*(i16 % 4) of the 32-feature block.
   const int v_lane = (i16 >> 2) * C::SV + (q16 * 16 + 4 * (i16 & 3)) * 2;
-  const int nqt = T_pad / 32;
 
   for (int qt = wave; qt < nqt; qt += nw) {
     const int q = qt * 32 + lrow;
-    const int qc = q < T ? q : T - 1;
-    bf16x8 qf[DH / 16];
-    {
-      const bf16_t* qrow = Q + (seq0 + qc) * ld + hoff + g * 8;
-#pragma unroll
-      for (int s = 0; s < DH / 16; ++s)
-        qf[s] = __builtin_bit_cast(bf16x8, ld_global16(qrow + s * 16));
-    }
+    if (qt != wave) load_q(qt);
     f32x16 o[C::DHP / 32];
 #pragma unroll
     for (int d = 0; d < C::DHP / 32; ++d)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
+    // m_run: the reference maximum (log2 units) the probabilities are taken
+    // against; l_run: this lane's share of their sum (the other lane half
+    // holds the rest of the query's keys).
     float m_run = -INFINITY, l_run = 0.f;
 
-    for (int k0 = 0; k0 < T; k0 += 64) {
-      const int nkb = (T - k0) > 32 ? 2 : 1;  // 32-key blocks holding a valid key
-      f32x16 s[2];
+    // One chunk of 64 keys starting at k0.  TAIL: the chunk runs past T
+    // (its keys >= T get score -inf, and a second 32-key block with no
+    // valid key is skipped).
+    auto chunk = [&](const int k0, auto tail) {
+      constexpr bool TAIL = decltype(tail)::value;
+      const int nkb = (!TAIL || T - k0 > 32) ? 2 : 1;  // 32-key blocks holding a valid key
+      f32x16 sc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
         if (kb < nkb) {
           const char* krow = ks + (k0 + kb * 32 + lrow) * C::SK + g * 16;
+          sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              *reinterpret_cast<const bf16x8*>(krow), qf[0], f32x16{}, 0, 0, 0);
 #pragma unroll
-          for (int ks_ = 0; ks_ < DH / 16; ++ks_) {
+          for (int ks_ = 1; ks_ < DH / 16; ++ks_) {
             const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + ks_ * 32);
-            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks_], s[kb], 0, 0, 0);
+            sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks_], sc[kb], 0, 0, 0);
           }
         }
       }
-      // Running maximum of the raw scores (keys past T masked to -inf: key
-      // kb*32 + (r/4)*8 + g*4 + r%4 of the chunk is valid iff it is < lim),
-      // then p = 2^(s * scale * log2(e) - m) with one FMA per score.
-      const int lim = T - k0 - g * 4;
+      // Maximum of the raw scores.  Key kb*32 + (r/4)*8 + g*4 + r%4 of the
+      // chunk is valid iff it is < T - k0.
       float mx = -INFINITY;
+      if (TAIL) {
+        const int lim = T - k0 - g * 4;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (kb * 32 + (r >> 2) * 8 + (r & 3) >= lim) s[kb][r] = -INFINITY;
-          mx = fmaxf(mx, s[kb][r]);
+          for (int r = 0; r < 16; ++r) {
+            if (kb >= nkb || kb * 32 + (r >> 2) * 8 + (r & 3) >= lim) sc[kb][r] = -INFINITY;
+            mx = fmaxf(mx, sc[kb][r]);
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+      }
+      mx = max_halves(mx) * scale_log2;
+      // The reference maximum moves only when some query's maximum exceeds
+      // it by more than kSlack (so probabilities stay below 2^kSlack); the
+      // accumulators are rescaled only then, for the whole wave at once.
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(mx > m_run + kSlack) != 0, 0)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < C::DHP / 32; ++d)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+      }
+      // p = 2^(s * scale * log2(e) - m), rounded once to bf16: that is the
+      // MFMA operand, and its row sum is taken from the same rounded values.
+      uint32_t pk[2][8];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if (kb >= nkb) continue;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pk[kb][e] = pack_bf16x2(
+              __builtin_amdgcn_exp2f(fmaf(sc[kb][2 * e], scale_log2, -m_run)),
+              __builtin_amdgcn_exp2f(fmaf(sc[kb][2 * e + 1], scale_log2, -m_run)));
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[kb][e]),
+                                                  kOnes, l_run, false);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * scale_log2);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      float psum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale_log2, -m_new));
-          s[kb][r] = pv;
-          psum += pv;
-        }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int d = 0; d < C::DHP / 32; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
-
+      }
       // O^T += V^T P^T, 16 keys per MFMA: MFMA k-slot j of lane half g is key
       // (j/4)*8 + g*4 + j%4 of the 16-key step, for both operands.
 #pragma unroll
@@ -183,10 +238,8 @@ __global__ __launch_bounds__(64 * kMaxWaves, (DH <= 64 ? 4 : 2)) void attn_resid
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           const bf16x8 pf = __builtin_bit_cast(
-              bf16x8, make_uint4(pack_bf16x2(s[kb][s2 * 8 + 0], s[kb][s2 * 8 + 1]),
-                                 pack_bf16x2(s[kb][s2 * 8 + 2], s[kb][s2 * 8 + 3]),
-                                 pack_bf16x2(s[kb][s2 * 8 + 4], s[kb][s2 * 8 + 5]),
-                                 pack_bf16x2(s[kb][s2 * 8 + 6], s[kb][s2 * 8 + 7])));
+              bf16x8, make_uint4(pk[kb][s2 * 4 + 0], pk[kb][s2 * 4 + 1], pk[kb][s2 * 4 + 2],
+                                 pk[kb][s2 * 4 + 3]));
           const char* vb = vs + (k0 + kb * 32 + s2 * 16 + g * 4) * C::SV + v_lane;
 #pragma unroll
           for (int d = 0; d < C::DHP / 32; ++d) {
@@ -198,9 +251,12 @@ __global__ __launch_bounds__(64 * kMaxWaves, (DH <= 64 ? 4 : 2)) void attn_resid
           }
         }
       }
-    }
+    };
+    int k0 = 0;
+    for (; k0 + 64 <= T; k0 += 64) chunk(k0, std::false_type{});
+    if (k0 < T) chunk(k0, std::true_type{});
 
-    const float inv = 1.0f / (l_run + __shfl_xor(l_run, 32));
+    const float inv = 1.0f / sum_halves(l_run);
     if (q < T) {
       bf16_t* orow = O + (seq0 + q) * ldo + hoff;
 #pragma unroll
