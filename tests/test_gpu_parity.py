@@ -97,6 +97,8 @@ def _attention_ref(q, k, v, H):
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("N,T,D,H", [
     (2, 197, 128, 2),    # d_h 64, ViT token count
+    (20, 197, 1024, 16),  # 320 (sequence, head) items: some workgroups take two
+    (80, 100, 512, 8),   # 640 items over several workgroups each; ragged last chunk
     (2, 257, 160, 2),    # d_h 80
     (1, 1025, 64, 1),    # long sequence
     (3, 1, 128, 2),      # single token: output = V
