@@ -5,6 +5,9 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 """
 
 from .block import (  # noqa: F401
+    AFFINE_KEYS,
+    add_bias,
+    affine,
     attention_scores,
     attention_weights,
     gelu_tanh,

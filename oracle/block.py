@@ -21,11 +21,21 @@ Sources (the pages this follows; each function names the section it restates):
          "Key Equations" steps 1-6, "Numerical Example".
   [MLG]  mlgrind.dev, "E2E: Tiny Vision Transformer" -- "Details" (MHA, GELU).
   [NB]   nipunbatra.github.io, vision1 lecture transcript -- Page 70
-         (head h owns features h*d_h .. (h+1)*d_h-1), Pages 106-110 (code).
+         (head h owns features h*d_h .. (h+1)*d_h-1), Pages 106-110 (code),
+         Pages 24-26 and 36 (a linear layer is a weighted sum plus a bias).
 
 Readings taken where the pages differ (all fixed by the block definition in
 [CAC]): no LayerNorm scale/shift, no projection biases, tanh-GELU, and a
 caller-supplied eps (1e-5 in [CAC], 1e-6 in [TT]).
+
+The affine variant (``params`` of ``vit_block``) is the block of [AEE]
+"Key Equations": each LayerNorm with its own per-feature gain gamma and
+shift beta (steps 1 and 4; [MLG] "Details": learnable gain and bias), the MLP
+with biases b_1, b_2 (step 5), and -- reading the projections as the linear
+layers of [NB] Pages 24-26 -- optional biases on Q, K, V and the output
+projection too.  Every parameter is optional; an absent one is gamma = 1,
+beta = 0 or bias = 0, which is the plain block above ([MLG] "Details" has no
+MHA bias and initialises gains to 1 and biases to 0).
 
 Every function here has pins in ``tests/test_oracle.py`` that do not reuse
 this code: the printed worked examples of [TT] "Examples" and the hand trace
@@ -52,7 +62,14 @@ __all__ = [
     "mlp",
     "vit_block",
     "vit_block_stages",
+    "affine",
+    "add_bias",
+    "AFFINE_KEYS",
 ]
+
+# Optional parameters of the affine variant, in the order of the block.
+AFFINE_KEYS = ("ln1_gamma", "ln1_beta", "b_q", "b_k", "b_v", "b_o",
+               "ln2_gamma", "ln2_beta", "b_mlp1", "b_mlp2")
 
 
 def _f64(a) -> np.ndarray:
@@ -72,6 +89,31 @@ def layer_norm(x, eps: float) -> np.ndarray:
     dev = x - mean
     var = (dev * dev).mean(axis=-1, keepdims=True)
     return dev / np.sqrt(var + eps)
+
+
+def affine(t, gamma=None, beta=None) -> np.ndarray:
+    """Per-feature gain and shift of a normalised tensor: gamma_j * t_ij + beta_j.
+
+    [AEE] "Key Equations" step 1 (x_hat_ij = gamma_j (x_ij - mu_i) /
+    sqrt(sigma_i^2 + eps) + beta_j) and step 4 (the second LayerNorm has its own
+    gamma and beta).  Absent gamma is 1, absent beta is 0.
+    """
+    t = _f64(t)
+    if gamma is not None:
+        t = t * _f64(gamma)
+    if beta is not None:
+        t = t + _f64(beta)
+    return t
+
+
+def add_bias(t, b=None) -> np.ndarray:
+    """A projection's bias, one value per output feature: t_ij + b_j.
+
+    [AEE] "Key Equations" step 5 (x_hat' W_1 + b_1, then W_2 + b_2);
+    [NB] Pages 24-26 (each output of a linear layer adds its bias).
+    """
+    t = _f64(t)
+    return t if b is None else t + _f64(b)
 
 
 def project(a, w) -> np.ndarray:
@@ -163,8 +205,16 @@ def mlp(yn, w_mlp1, w_mlp2) -> np.ndarray:
     return project(gelu_tanh(project(yn, w_mlp1)), w_mlp2)
 
 
+def _params(params) -> dict:
+    p = dict(params or {})
+    unknown = set(p) - set(AFFINE_KEYS)
+    if unknown:
+        raise ValueError(f"unknown block parameters: {sorted(unknown)}")
+    return {k: p.get(k) for k in AFFINE_KEYS}
+
+
 def vit_block_stages(x, w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, num_heads: int,
-                     eps: float) -> dict:
+                     eps: float, params=None) -> dict:
     """Every intermediate of the block for a batch of sequences, float64.
 
     Keys: xn = LN(x); q, k, v = xn @ w_{q,k,v}; att = concatenated heads;
@@ -174,6 +224,11 @@ def vit_block_stages(x, w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, num_heads: int,
     [CAC] "Multi-head attention" and "Feed-forward stage": the first residual
     adds the un-normalised x, the second LayerNorm normalises y (not x).
     [AEE] "Key Equations" steps 1-6 give the same order.
+
+    ``params`` (optional; keys in ``AFFINE_KEYS``) adds the affine variant:
+    xn = gamma_1 LN(x) + beta_1, q = xn @ w_q + b_q (and k, v), y = x + att @ w_o
+    + b_o, yn = gamma_2 LN(y) + beta_2, z = yn @ w_mlp1 + b_mlp1,
+    out = y + GELU(z) @ w_mlp2 + b_mlp2 ([AEE] "Key Equations" steps 1-6).
     """
     x = _f64(x)
     if x.ndim != 3:
@@ -181,32 +236,34 @@ def vit_block_stages(x, w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, num_heads: int,
     d = x.shape[-1]
     if num_heads <= 0 or d % num_heads:
         raise ValueError("num_heads must be positive and divide D")
-    xn = layer_norm(x, eps)
-    q = project(xn, w_q)
-    k = project(xn, w_k)
-    v = project(xn, w_v)
+    p = _params(params)
+    xn = affine(layer_norm(x, eps), p["ln1_gamma"], p["ln1_beta"])
+    q = add_bias(project(xn, w_q), p["b_q"])
+    k = add_bias(project(xn, w_k), p["b_k"])
+    v = add_bias(project(xn, w_v), p["b_v"])
     a = softmax_rows(attention_scores(split_heads(q, num_heads), split_heads(k, num_heads)))
     att = merge_heads(np.matmul(a, split_heads(v, num_heads)))
-    y = x + project(att, w_o)
-    yn = layer_norm(y, eps)
-    z = project(yn, w_mlp1)
+    y = x + add_bias(project(att, w_o), p["b_o"])
+    yn = affine(layer_norm(y, eps), p["ln2_gamma"], p["ln2_beta"])
+    z = add_bias(project(yn, w_mlp1), p["b_mlp1"])
     h = gelu_tanh(z)
-    out = y + project(h, w_mlp2)
+    out = y + add_bias(project(h, w_mlp2), p["b_mlp2"])
     return dict(xn=xn, q=q, k=k, v=v, weights=a, att=att, y=y, yn=yn, z=z, h=h, out=out)
 
 
 def vit_block(x, w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, num_heads: int, eps: float,
-              chunk: int = 8) -> np.ndarray:
+              chunk: int = 8, params=None) -> np.ndarray:
     """Output of one pre-LN encoder block, (N, T, D) float64.
 
     Sequences never interact ([CAC] "Inputs and output": N independent
     sequences), so they are processed ``chunk`` at a time to bound memory;
-    this changes no arithmetic.
+    this changes no arithmetic.  ``params``: the affine variant's optional
+    gains, shifts and biases (see ``vit_block_stages``).
     """
     x = _f64(x)
     out = np.empty_like(x)
     for s in range(0, x.shape[0], max(1, int(chunk))):
         st = vit_block_stages(x[s:s + chunk], w_q, w_k, w_v, w_o, w_mlp1, w_mlp2,
-                              num_heads, eps)
+                              num_heads, eps, params=params)
         out[s:s + chunk] = st["out"]
     return out

@@ -16,6 +16,14 @@ The oracle is trusted only through checks that do not reuse its code:
 * float64 library cross-checks (torch's layer_norm, tanh-GELU and
   scaled-dot-product attention), used here only, never by the oracle.
 
+The affine variant (LayerNorm gains and shifts, projection biases, from
+ai-engineer-exhaustive.pages.dev "ViT Encoder Block", "Key Equations" steps
+1, 4 and 5) is pinned the same way: the scalar loop takes the parameters
+too, and closed forms fix each parameter's place (the value path with
+w_v = 0, the MLP with w_mlp1 = 0, the second LayerNorm through torch's
+layer_norm with weight and bias), plus the invariance of the output to the
+key bias (it shifts every score of a query by the same amount).
+
 The last group plants plausible mistakes into one oracle step at a time and
 asserts that the pins above catch every one of them.
 """
@@ -71,22 +79,36 @@ def _brute_gelu(z):
     return 0.5 * z * (1.0 + math.tanh(math.sqrt(2.0 / math.pi) * (z + 0.044715 * z * z * z)))
 
 
-def brute_force_block(x, wq, wk, wv, wo, w1, w2, H, eps):
-    """Scalar loops over (sequence, token, head, key, feature); tiny inputs only."""
+def brute_force_block(x, wq, wk, wv, wo, w1, w2, H, eps, params=None):
+    """Scalar loops over (sequence, token, head, key, feature); tiny inputs only.
+
+    ``params``: the affine variant's gains, shifts and biases by name (absent:
+    gain 1, shift 0, bias 0), applied where the "Key Equations" put them.
+    """
     x = np.asarray(x).tolist()
     wq, wk, wv, wo, w1, w2 = (np.asarray(w).tolist() for w in (wq, wk, wv, wo, w1, w2))
     N, T, D = len(x), len(x[0]), len(x[0][0])
     F = len(w1[0])
     dh = D // H
+    prm = {k: np.asarray(v).tolist() for k, v in (params or {}).items()}
+
+    def vec(name, n, fill):
+        return prm.get(name, [fill] * n)
+
+    g1, be1, g2, be2 = vec("ln1_gamma", D, 1.0), vec("ln1_beta", D, 0.0), \
+        vec("ln2_gamma", D, 1.0), vec("ln2_beta", D, 0.0)
+    bq, bk, bv, bo = (vec(k, D, 0.0) for k in ("b_q", "b_k", "b_v", "b_o"))
+    b1, b2 = vec("b_mlp1", F, 0.0), vec("b_mlp2", D, 0.0)
     out = [[[0.0] * D for _ in range(T)] for _ in range(N)]
     for n in range(N):
-        xn = [_brute_ln(x[n][t], eps) for t in range(T)]
+        xn = [[g1[j] * val + be1[j] for j, val in enumerate(_brute_ln(x[n][t], eps))]
+              for t in range(T)]
 
-        def mat(a, w, cols):
-            return [[sum(a[t][i] * w[i][j] for i in range(len(w))) for j in range(cols)]
+        def mat(a, w, cols, b):
+            return [[sum(a[t][i] * w[i][j] for i in range(len(w))) + b[j] for j in range(cols)]
                     for t in range(len(a))]
 
-        q, k, v = mat(xn, wq, D), mat(xn, wk, D), mat(xn, wv, D)
+        q, k, v = mat(xn, wq, D, bq), mat(xn, wk, D, bk), mat(xn, wv, D, bv)
         att = [[0.0] * D for _ in range(T)]
         for h in range(H):
             c0 = h * dh
@@ -98,11 +120,12 @@ def brute_force_block(x, wq, wk, wv, wo, w1, w2, H, eps):
                 z = sum(e)
                 for c in range(dh):
                     att[i][c0 + c] = sum(e[j] / z * v[j][c0 + c] for j in range(T))
-        proj = mat(att, wo, D)
+        proj = mat(att, wo, D, bo)
         y = [[x[n][t][j] + proj[t][j] for j in range(D)] for t in range(T)]
-        yn = [_brute_ln(y[t], eps) for t in range(T)]
-        hid = [[_brute_gelu(val) for val in row] for row in mat(yn, w1, F)]
-        upd = mat(hid, w2, D)
+        yn = [[g2[j] * val + be2[j] for j, val in enumerate(_brute_ln(y[t], eps))]
+              for t in range(T)]
+        hid = [[_brute_gelu(val) for val in row] for row in mat(yn, w1, F, b1)]
+        upd = mat(hid, w2, D, b2)
         for t in range(T):
             for j in range(D):
                 out[n][t][j] = y[t][j] + upd[t][j]
@@ -126,6 +149,28 @@ def _brute_max_err():
         args = _rand_block(rng, N, T, D, F)
         ref = brute_force_block(*args, H, 1e-5)
         got = oracle.vit_block(*args, H, 1e-5)
+        worst = max(worst, float(np.abs(ref - got).max()))
+    return worst
+
+
+def _rand_params(rng, D, F):
+    """Gains near 1, shifts and biases of a few tenths: every term visible."""
+    p = {}
+    for k in oracle.AFFINE_KEYS:
+        n = F if k == "b_mlp1" else D
+        p[k] = (1.0 + 0.3 * rng.standard_normal(n)) if k.endswith("gamma") \
+            else 0.3 * rng.standard_normal(n)
+    return p
+
+
+def _brute_affine_max_err():
+    rng = np.random.default_rng(4321)
+    worst = 0.0
+    for (N, T, D, H, F) in BRUTE_SHAPES:
+        args = _rand_block(rng, N, T, D, F)
+        prm = _rand_params(rng, D, F)
+        ref = brute_force_block(*args, H, 1e-5, params=prm)
+        got = oracle.vit_block(*args, H, 1e-5, params=prm)
         worst = max(worst, float(np.abs(ref - got).max()))
     return worst
 
@@ -310,6 +355,88 @@ def test_shape_checks():
 
 # ------------------------------------------------------- planted mistakes
 
+# ------------------------------------------------------- the affine variant
+
+def test_affine_brute_force_agrees():
+    assert _brute_affine_max_err() < 1e-12
+
+
+def test_affine_with_identity_parameters_is_the_plain_block():
+    rng = np.random.default_rng(7)
+    N, T, D, H, F = 2, 5, 8, 2, 12
+    args = _rand_block(rng, N, T, D, F)
+    ident = {k: (np.ones(D) if k.endswith("gamma") else
+                 np.zeros(F if k == "b_mlp1" else D)) for k in oracle.AFFINE_KEYS}
+    plain = oracle.vit_block(*args, H, 1e-6)
+    assert np.array_equal(oracle.vit_block(*args, H, 1e-6, params=ident), plain)
+    assert np.array_equal(oracle.vit_block(*args, H, 1e-6, params={}), plain)
+
+
+def test_value_path_biases_closed_form():
+    # w_v = 0: every value row is b_v, so whatever the weights, each head
+    # outputs its part of b_v and y = x + b_v @ w_o + b_o, token by token.
+    rng = np.random.default_rng(8)
+    N, T, D, H, F = 2, 4, 6, 3, 5
+    x, wq, wk, _, wo, w1, w2 = _rand_block(rng, N, T, D, F)
+    prm = _rand_params(rng, D, F)
+    st = oracle.vit_block_stages(x, wq, wk, np.zeros((D, D)), wo, w1, w2, H, 1e-6, params=prm)
+    want = x + (prm["b_v"] @ wo + prm["b_o"])[None, None, :]
+    assert np.abs(st["y"] - want).max() < 1e-12
+
+
+def test_key_bias_does_not_change_the_output():
+    # b_k adds q_i . b_k to every score of query i: softmax is unchanged.
+    rng = np.random.default_rng(9)
+    N, T, D, H, F = 2, 6, 8, 2, 10
+    args = _rand_block(rng, N, T, D, F)
+    prm = _rand_params(rng, D, F)
+    a = oracle.vit_block(*args, H, 1e-6, params=prm)
+    prm2 = dict(prm, b_k=prm["b_k"] + 3.0 * rng.standard_normal(D))
+    b = oracle.vit_block(*args, H, 1e-6, params=prm2)
+    assert np.abs(a - b).max() < 1e-11
+    # ... while the same shift on the query bias does change it.
+    prm3 = dict(prm, b_q=prm["b_q"] + 3.0 * rng.standard_normal(D))
+    assert np.abs(oracle.vit_block(*args, H, 1e-6, params=prm3) - a).max() > 1e-3
+
+
+def test_mlp_biases_closed_form():
+    # w_mlp1 = 0: every hidden row is GELU(b_1), so out = y + GELU(b_1) @ w_mlp2 + b_2.
+    rng = np.random.default_rng(10)
+    N, T, D, H, F = 1, 3, 4, 2, 6
+    x, wq, wk, wv, wo, _, w2 = _rand_block(rng, N, T, D, F)
+    prm = _rand_params(rng, D, F)
+    st = oracle.vit_block_stages(x, wq, wk, wv, wo, np.zeros((D, F)), w2, H, 1e-6, params=prm)
+    g = np.array([_brute_gelu(float(b)) for b in prm["b_mlp1"]])
+    want = st["y"] + (g @ w2 + prm["b_mlp2"])[None, None, :]
+    assert np.abs(st["out"] - want).max() < 1e-12
+
+
+def test_second_layer_norm_affine_matches_torch():
+    # w_o = 0 (so y = x + b_o), w_mlp1 = w_mlp2 = I, no MLP biases:
+    # out = y + GELU(gamma_2 LN(y) + beta_2), LN from torch.
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(11)
+    N, T, D, H = 2, 3, 8, 2
+    x, wq, wk, wv, _, _, _ = _rand_block(rng, N, T, D, D)
+    prm = _rand_params(rng, D, D)
+    prm["b_mlp1"] = np.zeros(D)
+    prm["b_mlp2"] = np.zeros(D)
+    eye = np.eye(D)
+    out = oracle.vit_block(x, wq, wk, wv, np.zeros((D, D)), eye, eye, H, 1e-6, params=prm)
+    y = torch.from_numpy(x + prm["b_o"])
+    ln = torch.nn.functional.layer_norm(y, (D,), torch.from_numpy(prm["ln2_gamma"]),
+                                        torch.from_numpy(prm["ln2_beta"]), eps=1e-6)
+    want = y + torch.nn.functional.gelu(ln, approximate="tanh")
+    assert np.abs(out - want.numpy()).max() < 1e-12
+
+
+def test_affine_rejects_unknown_parameter():
+    rng = np.random.default_rng(12)
+    args = _rand_block(rng, 1, 2, 4, 4)
+    with pytest.raises(ValueError):
+        oracle.vit_block(*args, 2, 1e-6, params={"b_qkv": np.zeros(12)})
+
+
 def _ln_unbiased(x, eps):
     x = np.asarray(x, dtype=np.float64)
     return (x - x.mean(-1, keepdims=True)) / np.sqrt(x.var(-1, ddof=1, keepdims=True) + eps)
@@ -365,6 +492,41 @@ _MERGE = ob.merge_heads
 
 def _merge_reversed(o):
     return _MERGE(np.asarray(o)[:, ::-1])
+
+
+def _affine_shift_then_gain(t, gamma=None, beta=None):
+    t = np.asarray(t, dtype=np.float64)
+    if beta is not None:
+        t = t + beta
+    return t if gamma is None else t * gamma
+
+
+def _affine_ignored(t, gamma=None, beta=None):
+    return np.asarray(t, dtype=np.float64)
+
+
+def _bias_ignored(t, b=None):
+    return np.asarray(t, dtype=np.float64)
+
+
+def _bias_subtracted(t, b=None):
+    t = np.asarray(t, dtype=np.float64)
+    return t if b is None else t - b
+
+
+AFFINE_MUTANTS = {
+    "shift before gain": ("affine", _affine_shift_then_gain),
+    "gain and shift ignored": ("affine", _affine_ignored),
+    "biases ignored": ("add_bias", _bias_ignored),
+    "biases subtracted": ("add_bias", _bias_subtracted),
+}
+
+
+@pytest.mark.parametrize("name", sorted(AFFINE_MUTANTS))
+def test_affine_pins_catch_planted_mistake(name, monkeypatch):
+    attr, fn = AFFINE_MUTANTS[name]
+    monkeypatch.setattr(ob, attr, fn)
+    assert _brute_affine_max_err() > 1e-9, f"pins did not catch: {name}"
 
 
 MUTANTS = {

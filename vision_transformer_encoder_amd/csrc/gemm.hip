@@ -52,7 +52,7 @@ constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies
 constexpr int kBufferFlags = 0x00020000;
 
 template <int BM_, int BN_, int WM_, int WN_, int BK_ = 64, int NS_ = 2, int NSA_ = NS_,
-          bool SCHED_ = true>
+          bool SCHED_ = true, int WPE_ = 1>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   static constexpr int BK = BK_;    // k per LDS stage
@@ -61,6 +61,7 @@ struct Cfg {
   // miss L2 far more often than the weights', one more k-slice of lead.
   static constexpr int NSA = NSA_;
   static constexpr bool SCHED = SCHED_;
+  static constexpr int WPE = WPE_;  // launch bound: waves per SIMD the registers must allow
   static constexpr int NT = WM * WN * 64;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int TM = WTM / 32, TN = WTN / 32;
@@ -128,7 +129,7 @@ __device__ __forceinline__ void tile_of(int t, int grid, int total, int mt, int 
 }
 
 template <class C, int EPI>
-__global__ __launch_bounds__(C::NT, 1) void gemm_bf16_kernel(GemmProblem p, int mt, int nt) {
+__global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p, int mt, int nt) {
   __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
   char* const a_lds = lds;                       // [stage][BM rows][BK * 2 B]
   char* const b_lds = lds + C::NSA * C::A_STAGE;  // [stage][BN rows][BK * 2 B]
