@@ -19,7 +19,8 @@
  *   GELU_tanh(z) = 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3)))
  *
  * There are no biases.  Weights are stored (in_features, out_features) and
- * applied as x @ W.
+ * applied as x @ W.  vitblk_forward_affine() adds the optional LayerNorm
+ * gains and shifts and projection biases of the affine variant (see there).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -147,6 +148,51 @@ int vitblk_forward(const void* x, const void* w_q, const void* w_k, const void* 
                    vitblk_stream_t stream);
 
 /*
+ * Optional parameters of the affine block variant
+ * (ai-engineer-exhaustive.pages.dev "ViT Encoder Block", "Key Equations":
+ * step 1 and step 4, a LayerNorm with a per-feature gain gamma and shift beta,
+ * each LayerNorm with its own; step 5, the MLP's biases b_1 and b_2; the
+ * nn.Linear projections of the nipunbatra.github.io vision1 transcript,
+ * Pages 24-26, give Q, K, V and the output projection a bias too):
+ *
+ *   xn  = LN(x) * ln1_gamma + ln1_beta
+ *   Q, K, V = xn @ w_q + b_q, xn @ w_k + b_k, xn @ w_v + b_v
+ *   y   = x + att @ w_o + b_o
+ *   yn  = LN(y) * ln2_gamma + ln2_beta
+ *   out = y + GELU_tanh(yn @ w_mlp1 + b_mlp1) @ w_mlp2 + b_mlp2
+ *
+ * Every member is a device pointer to a vector in the block's dtype, 16-byte
+ * aligned, or NULL for "absent" (gain 1, shift 0, bias 0).  Lengths: D for
+ * all of them except b_mlp1, which has F.  A NULL parameter set is the plain
+ * block.  The parameters are read directly by the kernels (no copy); they
+ * must not overlap out or the workspace (VITBLK_ERR_ALIAS).
+ */
+typedef struct {
+  const void* ln1_gamma;
+  const void* ln1_beta;
+  const void* b_q;
+  const void* b_k;
+  const void* b_v;
+  const void* b_o;
+  const void* ln2_gamma;
+  const void* ln2_beta;
+  const void* b_mlp1;
+  const void* b_mlp2;
+} vitblk_affine_params;
+
+/*
+ * vitblk_forward() with the affine variant's parameters (may be NULL).  The
+ * same eight kernels: the gains and shifts are applied by the LayerNorm
+ * kernel, the biases in the GEMM epilogues (before GELU and before the
+ * residual add, in fp32).  Same workspace and errors as vitblk_forward().
+ */
+int vitblk_forward_affine(const void* x, const void* w_q, const void* w_k, const void* w_v,
+                          const void* w_o, const void* w_mlp1, const void* w_mlp2,
+                          const vitblk_affine_params* params, void* out, int64_t N, int64_t T,
+                          int64_t D, int64_t F, int64_t H, double eps, int dtype,
+                          void* workspace, size_t workspace_bytes, vitblk_stream_t stream);
+
+/*
  * The same block on weights already packed by vitblk_pack_weights() (the
  * seven kernels after packing).  workspace must hold at least
  * vitblk_workspace_bytes() - vitblk_packed_weights_bytes() bytes and must not
@@ -155,6 +201,13 @@ int vitblk_forward(const void* x, const void* w_q, const void* w_k, const void* 
 int vitblk_forward_packed(const void* x, const void* packed, void* out, int64_t N, int64_t T,
                           int64_t D, int64_t F, int64_t H, double eps, int dtype,
                           void* workspace, size_t workspace_bytes, vitblk_stream_t stream);
+
+/* vitblk_forward_packed() with the affine variant's parameters (may be NULL). */
+int vitblk_forward_packed_affine(const void* x, const void* packed,
+                                 const vitblk_affine_params* params, void* out, int64_t N,
+                                 int64_t T, int64_t D, int64_t F, int64_t H, double eps,
+                                 int dtype, void* workspace, size_t workspace_bytes,
+                                 vitblk_stream_t stream);
 
 /*
  * The steps of the block, one call each, on the same kernels vitblk_forward
@@ -167,6 +220,14 @@ int vitblk_forward_packed(const void* x, const void* packed, void* out, int64_t 
  * out must not overlap x. */
 int vitblk_layernorm(const void* x, void* out, int64_t rows, int64_t D, double eps,
                      int dtype, vitblk_stream_t stream);
+
+/* out[r, :] = LN(x[r, :]) * gamma + beta: the affine LayerNorm of
+ * ai-engineer-exhaustive.pages.dev "ViT Encoder Block", "Key Equations"
+ * step 1.  gamma and beta ([D], 16-byte aligned) may each be NULL (1, 0);
+ * out must not overlap x, gamma or beta. */
+int vitblk_layernorm_affine(const void* x, const void* gamma, const void* beta, void* out,
+                            int64_t rows, int64_t D, double eps, int dtype,
+                            vitblk_stream_t stream);
 
 /* qkv = xn @ [w_q | w_k | w_v]: xn [M, D], w_qkv_t [3D, D] (the first
  * region of the packed weights), qkv [M, 3D] (one row holds a token's Q, K
@@ -196,6 +257,15 @@ int vitblk_attention(const void* qkv, void* att, int64_t N, int64_t T, int64_t D
 int vitblk_linear(const void* a, const void* w_t, const void* residual, void* out,
                   int64_t M, int64_t K, int64_t Nout, int epilogue, int dtype,
                   vitblk_stream_t stream);
+
+/* vitblk_linear() with a bias ([Nout], 16-byte aligned, or NULL) added to
+ * a @ W in fp32 before the epilogue: out = epilogue(a @ W + bias), i.e.
+ * GELU_tanh(a @ W + bias) or residual + a @ W + bias
+ * (ai-engineer-exhaustive.pages.dev "ViT Encoder Block", "Key Equations"
+ * step 5).  out must not overlap the bias either. */
+int vitblk_linear_bias(const void* a, const void* w_t, const void* bias, const void* residual,
+                       void* out, int64_t M, int64_t K, int64_t Nout, int epilogue, int dtype,
+                       vitblk_stream_t stream);
 
 #ifdef __cplusplus
 }

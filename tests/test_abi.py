@@ -167,6 +167,57 @@ def test_step_entry_points_errors(lib):
     assert lib.vitblk_linear(a, b, None, c, 4, -8, 8, vb.EPI_GELU, 1, None) == INVALID
 
 
+def test_affine_entry_points_errors(lib):
+    AP = vb._lib.AffineParams
+    need = vb.workspace_bytes(2, 5, 16, 32, 2, 1)
+    w = [_addr(i) for i in range(7)]   # x, w_q .. w_mlp2
+    out, ws = _addr(8), _addr(20)
+
+    def fa(prm, out=out, ws_bytes=need):
+        ref = None if prm is None else ctypes.byref(prm)
+        return lib.vitblk_forward_affine(*w, ref, out, 2, 5, 16, 32, 2, 1e-6, 1, ws, ws_bytes,
+                                         None)
+
+    assert fa(None, ws_bytes=need - 1) == WORKSPACE          # plain checks still apply
+    assert fa(AP(), out=ctypes.c_void_p(w[0].value)) == ALIAS
+    prm = AP(**{k: (30 + i) * GAP for i, k in enumerate(vb.AFFINE_KEYS)})
+    assert fa(AP(ln1_gamma=31 * GAP + 8)) == INVALID         # misaligned parameter
+    assert fa(AP(b_mlp1=out.value + 64)) == ALIAS            # parameter inside out
+    assert fa(AP(b_o=ws.value + 256)) == ALIAS               # parameter inside the workspace
+    assert fa(AP(b_q=ws.value + need - 16)) == ALIAS         # ... at its last bytes
+    prm_bad = AP(**{k: getattr(prm, k) for k in vb.AFFINE_KEYS})
+    prm_bad.b_mlp2 = out.value
+    assert fa(prm_bad) == ALIAS
+    # packed variant: same parameter checks against the activation workspace
+    ws_need = need - vb.packed_weights_bytes(16, 32, 1)
+    fpa = lambda prm, n=ws_need: lib.vitblk_forward_packed_affine(  # noqa: E731
+        w[0], w[1], ctypes.byref(prm), out, 2, 5, 16, 32, 2, 1e-6, 1, ws, n, None)
+    assert fpa(AP(), n=ws_need - 1) == WORKSPACE
+    assert fpa(AP(ln2_beta=ws.value)) == ALIAS
+    assert fpa(AP(ln2_beta=ws.value + 8)) == INVALID
+    # layernorm with gain/shift
+    a, b, c = _addr(0), _addr(1), _addr(2)
+    assert lib.vitblk_layernorm_affine(a, ctypes.c_void_p(c.value + 4), None, b, 4, 8, 1e-5, 1,
+                                       None) == INVALID
+    assert lib.vitblk_layernorm_affine(a, None, ctypes.c_void_p(b.value), b, 4, 8, 1e-5, 1,
+                                       None) == ALIAS
+    assert lib.vitblk_layernorm_affine(a, c, c, a, 4, 8, 1e-5, 1, None) == ALIAS
+    # linear with bias
+    d = _addr(3)
+    assert lib.vitblk_linear_bias(a, b, ctypes.c_void_p(d.value + 2), None, c, 4, 8, 8,
+                                  vb.EPI_NONE, 1, None) == INVALID
+    assert lib.vitblk_linear_bias(a, b, c, None, c, 4, 8, 8, vb.EPI_GELU, 1, None) == ALIAS
+    assert lib.vitblk_linear_bias(a, b, d, None, c, 4, 8, 8, 9, 1, None) == INVALID
+
+
+def test_python_binding_rejects_unknown_affine_parameter():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 2, 8)
+    w = torch.zeros(8, 8)
+    with pytest.raises(ValueError):
+        vb.forward_affine(x, w, w, w, w, w, w, 2, 1e-6, params={"b_qkv": w})
+
+
 def test_python_binding_rejects_cpu_tensors():
     torch = pytest.importorskip("torch")
     x = torch.zeros(1, 2, 8)

@@ -8,6 +8,7 @@ first call does, and it raises if the library has not been built.
 """
 
 from ._lib import (  # noqa: F401
+    AFFINE_KEYS,
     EPI_GELU,
     EPI_NONE,
     EPI_RESIDUAL,
@@ -16,7 +17,9 @@ from ._lib import (  # noqa: F401
     VitblkError,
     attention,
     forward,
+    forward_affine,
     forward_packed,
+    forward_packed_affine,
     layernorm,
     linear,
     load,

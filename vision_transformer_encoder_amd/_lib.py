@@ -18,8 +18,19 @@ EPI_NONE, EPI_RESIDUAL, EPI_GELU = 0, 1, 2
 STATUS = {0: "VITBLK_OK", -1: "VITBLK_ERR_INVALID_ARG", -2: "VITBLK_ERR_UNSUPPORTED",
           -3: "VITBLK_ERR_WORKSPACE", -4: "VITBLK_ERR_ALIAS", -5: "VITBLK_ERR_HIP"}
 
+# Names of the affine variant's optional parameters, in vitblk_affine_params order.
+AFFINE_KEYS = ("ln1_gamma", "ln1_beta", "b_q", "b_k", "b_v", "b_o",
+               "ln2_gamma", "ln2_beta", "b_mlp1", "b_mlp2")
+
+
+class AffineParams(ctypes.Structure):
+    """vitblk_affine_params: ten nullable device pointers."""
+    _fields_ = [(k, ctypes.c_void_p) for k in AFFINE_KEYS]
+
+
 # Every symbol include/vitblk.h declares, with its ctypes signature.
 _P, _I64, _I, _D, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_size_t
+_AP = ctypes.POINTER(AffineParams)
 SIGNATURES = {
     "vitblk_status_string": (ctypes.c_char_p, [_I]),
     "vitblk_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64, _I]),
@@ -31,6 +42,10 @@ SIGNATURES = {
     "vitblk_qkv_projection": (_I, [_P] * 3 + [_I64, _I64, _I, _P]),
     "vitblk_attention": (_I, [_P, _P, _I64, _I64, _I64, _I64, _I, _P]),
     "vitblk_linear": (_I, [_P] * 4 + [_I64, _I64, _I64, _I, _I, _P]),
+    "vitblk_forward_affine": (_I, [_P] * 7 + [_AP, _P] + [_I64] * 5 + [_D, _I, _P, _SZ, _P]),
+    "vitblk_forward_packed_affine": (_I, [_P, _P, _AP, _P] + [_I64] * 5 + [_D, _I, _P, _SZ, _P]),
+    "vitblk_layernorm_affine": (_I, [_P] * 4 + [_I64, _I64, _D, _I, _P]),
+    "vitblk_linear_bias": (_I, [_P] * 5 + [_I64, _I64, _I64, _I, _I, _P]),
 }
 
 _lib = None
@@ -140,6 +155,42 @@ def forward(x, w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, num_heads: int, eps: float,
     return out
 
 
+def _affine(params, ref):
+    """AffineParams from a {name: tensor or None} dict (None: no parameters)."""
+    if params is None:
+        return None
+    unknown = set(params) - set(AFFINE_KEYS)
+    if unknown:
+        raise ValueError(f"unknown block parameters: {sorted(unknown)}")
+    ts = [params.get(k) for k in AFFINE_KEYS]
+    _dev(ref, *ts)
+    return AffineParams(*[0 if t is None else t.data_ptr() for t in ts])
+
+
+def forward_affine(x, w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, num_heads: int, eps: float,
+                   params=None, out=None, workspace=None, stream=None):
+    """The affine block: params maps AFFINE_KEYS names to [D] (b_mlp1: [F]) tensors."""
+    torch = _torch()
+    _dev(x, w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, out)
+    N, T, D = x.shape
+    F = w_mlp1.shape[1]
+    code = dtype_code(x.dtype)
+    ap = _affine(params, x)
+    if out is None:
+        out = torch.empty_like(x)
+    need = workspace_bytes(N, T, D, F, num_heads, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    st = load().vitblk_forward_affine(_ptr(x), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(w_o),
+                                      _ptr(w_mlp1), _ptr(w_mlp2),
+                                      None if ap is None else ctypes.byref(ap), _ptr(out), N, T,
+                                      D, F, num_heads, float(eps), code, _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(),
+                                      _stream(x, stream))
+    _check("vitblk_forward_affine", st)
+    return out
+
+
 def pack_weights(w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, packed=None, stream=None):
     """Out-major copies of the six weights in one buffer (uint8 tensor)."""
     torch = _torch()
@@ -195,17 +246,45 @@ def forward_packed(x, packed, F: int, num_heads: int, eps: float, out=None, work
     return out
 
 
-def layernorm(x, eps: float, out=None, stream=None):
-    """Row-wise LN over the last axis of a contiguous tensor."""
+def forward_packed_affine(x, packed, F: int, num_heads: int, eps: float, params=None,
+                          out=None, workspace=None, stream=None):
+    """The affine block on weights packed by pack_weights()."""
     torch = _torch()
     _dev(x, out)
+    N, T, D = x.shape
+    code = dtype_code(x.dtype)
+    ap = _affine(params, x)
+    if out is None:
+        out = torch.empty_like(x)
+    need = workspace_bytes(N, T, D, F, num_heads, code) - packed_weights_bytes(D, F, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    st = load().vitblk_forward_packed_affine(_ptr(x), _ptr(packed),
+                                             None if ap is None else ctypes.byref(ap), _ptr(out),
+                                             N, T, D, F, num_heads, float(eps), code,
+                                             _ptr(workspace),
+                                             workspace.numel() * workspace.element_size(),
+                                             _stream(x, stream))
+    _check("vitblk_forward_packed_affine", st)
+    return out
+
+
+def layernorm(x, eps: float, gamma=None, beta=None, out=None, stream=None):
+    """Row-wise LN over the last axis of a contiguous tensor, optionally * gamma + beta."""
+    torch = _torch()
+    _dev(x, gamma, beta, out)
     D = x.shape[-1]
     rows = x.numel() // D
     if out is None:
         out = torch.empty_like(x)
-    st = load().vitblk_layernorm(_ptr(x), _ptr(out), rows, D, float(eps),
-                                 dtype_code(x.dtype), _stream(x, stream))
-    _check("vitblk_layernorm", st)
+    if gamma is None and beta is None:
+        st = load().vitblk_layernorm(_ptr(x), _ptr(out), rows, D, float(eps),
+                                     dtype_code(x.dtype), _stream(x, stream))
+        _check("vitblk_layernorm", st)
+    else:
+        st = load().vitblk_layernorm_affine(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(out), rows, D,
+                                            float(eps), dtype_code(x.dtype), _stream(x, stream))
+        _check("vitblk_layernorm_affine", st)
     return out
 
 
@@ -236,16 +315,23 @@ def attention(qkv, N: int, T: int, num_heads: int, out=None, stream=None):
     return out
 
 
-def linear(a, w_t, epilogue: int = EPI_NONE, residual=None, out=None, stream=None):
-    """out = epilogue(a [M, K] @ W) (+ residual) with W given out-major, w_t [Nout, K]."""
+def linear(a, w_t, epilogue: int = EPI_NONE, residual=None, out=None, stream=None,
+           bias=None):
+    """out = epilogue(a [M, K] @ W + bias) (+ residual), W given out-major, w_t [Nout, K]."""
     torch = _torch()
-    _dev(a, w_t, residual, out)
+    _dev(a, w_t, residual, bias, out)
     K = a.shape[-1]
     M = a.numel() // K
     Nout = w_t.shape[0]
     if out is None:
         out = torch.empty((M, Nout), dtype=a.dtype, device=a.device)
-    st = load().vitblk_linear(_ptr(a), _ptr(w_t), _ptr(residual), _ptr(out), M, K, Nout,
-                              int(epilogue), dtype_code(a.dtype), _stream(a, stream))
-    _check("vitblk_linear", st)
+    if bias is None:
+        st = load().vitblk_linear(_ptr(a), _ptr(w_t), _ptr(residual), _ptr(out), M, K, Nout,
+                                  int(epilogue), dtype_code(a.dtype), _stream(a, stream))
+        _check("vitblk_linear", st)
+    else:
+        st = load().vitblk_linear_bias(_ptr(a), _ptr(w_t), _ptr(bias), _ptr(residual), _ptr(out),
+                                       M, K, Nout, int(epilogue), dtype_code(a.dtype),
+                                       _stream(a, stream))
+        _check("vitblk_linear_bias", st)
     return out

@@ -17,7 +17,9 @@ namespace {
   } while (0)
 
 GemmProblem linear_problem(const void* a, const void* w_t, void* c, const void* r, int64_t M,
-                           int64_t K, int64_t N, int epi, int dtype) {
+                           int64_t K, int64_t N, int epi, int dtype, const void* b0 = nullptr,
+                           const void* b1 = nullptr, const void* b2 = nullptr,
+                           int64_t bias_seg = 0) {
   GemmProblem p{};
   p.M = M;
   p.N = N;
@@ -32,6 +34,10 @@ GemmProblem linear_problem(const void* a, const void* w_t, void* c, const void* 
   p.ldr = N;
   p.epi = epi;
   p.dtype = dtype;
+  p.bias[0] = b0;
+  p.bias[1] = b1;
+  p.bias[2] = b2;
+  p.bias_seg = bias_seg > 0 ? bias_seg : N;
   return p;
 }
 
@@ -53,10 +59,13 @@ int pack_weights(const void* w_q, const void* w_k, const void* w_v, const void* 
   return VITBLK_OK;
 }
 
-// The seven steps of the block on packed (out-major) weights.
-int run_block(const void* x, const void* packed, void* out, int64_t N, int64_t T, int64_t D,
-              int64_t F, int64_t H, double eps, int dtype, char* act, const WorkspacePlan& pl,
-              hipStream_t s) {
+// The seven steps of the block on packed (out-major) weights.  prm: the
+// affine variant's optional gains, shifts and biases (null: none).
+int run_block(const void* x, const void* packed, const vitblk_affine_params* prm, void* out,
+              int64_t N, int64_t T, int64_t D, int64_t F, int64_t H, double eps, int dtype,
+              char* act, const WorkspacePlan& pl, hipStream_t s) {
+  const vitblk_affine_params none{};
+  const vitblk_affine_params& q = prm != nullptr ? *prm : none;
   const int64_t M = N * T;
   const size_t es = elem_size(dtype);
   const char* pk = static_cast<const char*>(packed);
@@ -65,26 +74,29 @@ int run_block(const void* x, const void* packed, void* out, int64_t N, int64_t T
   char* y = act + pl.off_y;      // [M, D]
   const float feps = static_cast<float>(eps);
 
-  // LN1: xn = LN(x)
-  VITBLK_LAUNCH(launch_layernorm(x, a, M, D, feps, dtype, s));
-  // Q | K | V = xn @ [w_q | w_k | w_v]
-  VITBLK_LAUNCH(launch_gemm(
-      linear_problem(a, pk + pl.packed.off_qkv, big, nullptr, M, D, 3 * D, VITBLK_EPI_NONE, dtype),
-      s));
+  // LN1: xn = gamma_1 LN(x) + beta_1
+  VITBLK_LAUNCH(launch_layernorm(x, q.ln1_gamma, q.ln1_beta, a, M, D, feps, dtype, s));
+  // Q | K | V = xn @ [w_q | w_k | w_v] + [b_q | b_k | b_v]
+  VITBLK_LAUNCH(launch_gemm(linear_problem(a, pk + pl.packed.off_qkv, big, nullptr, M, D, 3 * D,
+                                           VITBLK_EPI_NONE, dtype, q.b_q, q.b_k, q.b_v, D),
+                            s));
   // att = concat_h softmax(Q_h K_h^T / sqrt(dh)) V_h   (overwrites xn)
   VITBLK_LAUNCH(launch_attention(big, big + D * es, big + 2 * D * es, 3 * D, a, D, N, T, H,
                                  D / H, dtype, s));
-  // y = x + att @ w_o
-  VITBLK_LAUNCH(launch_gemm(
-      linear_problem(a, pk + pl.packed.off_o, y, x, M, D, D, VITBLK_EPI_RESIDUAL, dtype), s));
-  // LN2: yn = LN(y)   (overwrites att)
-  VITBLK_LAUNCH(launch_layernorm(y, a, M, D, feps, dtype, s));
-  // hidden = GELU(yn @ w_mlp1)   (overwrites qkv)
-  VITBLK_LAUNCH(launch_gemm(
-      linear_problem(a, pk + pl.packed.off_1, big, nullptr, M, D, F, VITBLK_EPI_GELU, dtype), s));
-  // out = y + hidden @ w_mlp2
-  VITBLK_LAUNCH(launch_gemm(
-      linear_problem(big, pk + pl.packed.off_2, out, y, M, F, D, VITBLK_EPI_RESIDUAL, dtype), s));
+  // y = x + att @ w_o + b_o
+  VITBLK_LAUNCH(launch_gemm(linear_problem(a, pk + pl.packed.off_o, y, x, M, D, D,
+                                           VITBLK_EPI_RESIDUAL, dtype, q.b_o),
+                            s));
+  // LN2: yn = gamma_2 LN(y) + beta_2   (overwrites att)
+  VITBLK_LAUNCH(launch_layernorm(y, q.ln2_gamma, q.ln2_beta, a, M, D, feps, dtype, s));
+  // hidden = GELU(yn @ w_mlp1 + b_mlp1)   (overwrites qkv)
+  VITBLK_LAUNCH(launch_gemm(linear_problem(a, pk + pl.packed.off_1, big, nullptr, M, D, F,
+                                           VITBLK_EPI_GELU, dtype, q.b_mlp1),
+                            s));
+  // out = y + hidden @ w_mlp2 + b_mlp2
+  VITBLK_LAUNCH(launch_gemm(linear_problem(big, pk + pl.packed.off_2, out, y, M, F, D,
+                                           VITBLK_EPI_RESIDUAL, dtype, q.b_mlp2),
+                            s));
   return VITBLK_OK;
 }
 
@@ -139,7 +151,25 @@ int vitblk_forward(const void* x, const void* w_q, const void* w_k, const void* 
   char* ws = static_cast<char*>(workspace);
   st = pack_weights(w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, ws, D, F, dtype, pl.packed, s);
   if (st != VITBLK_OK) return st;
-  return run_block(x, ws, out, N, T, D, F, H, eps, dtype, ws + pl.act_base, pl, s);
+  return run_block(x, ws, nullptr, out, N, T, D, F, H, eps, dtype, ws + pl.act_base, pl, s);
+}
+
+int vitblk_forward_affine(const void* x, const void* w_q, const void* w_k, const void* w_v,
+                          const void* w_o, const void* w_mlp1, const void* w_mlp2,
+                          const vitblk_affine_params* params, void* out, int64_t N, int64_t T,
+                          int64_t D, int64_t F, int64_t H, double eps, int dtype,
+                          void* workspace, size_t workspace_bytes, vitblk_stream_t stream) {
+  WorkspacePlan pl;
+  int st = validate_forward(x, w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, out, N, T, D, F, H, eps,
+                            dtype, workspace, workspace_bytes, &pl);
+  if (st != VITBLK_OK) return st;
+  st = validate_affine_params(params, out, N * T, D, F, dtype, workspace, pl.total);
+  if (st != VITBLK_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  st = pack_weights(w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, ws, D, F, dtype, pl.packed, s);
+  if (st != VITBLK_OK) return st;
+  return run_block(x, ws, params, out, N, T, D, F, H, eps, dtype, ws + pl.act_base, pl, s);
 }
 
 int vitblk_forward_packed(const void* x, const void* packed, void* out, int64_t N, int64_t T,
@@ -149,16 +179,38 @@ int vitblk_forward_packed(const void* x, const void* packed, void* out, int64_t 
   const int st = validate_forward_packed(x, packed, out, N, T, D, F, H, eps, dtype, workspace,
                                          workspace_bytes, &pl);
   if (st != VITBLK_OK) return st;
-  return run_block(x, packed, out, N, T, D, F, H, eps, dtype,
+  return run_block(x, packed, nullptr, out, N, T, D, F, H, eps, dtype,
+                   static_cast<char*>(workspace) + pl.act_base, pl,
+                   reinterpret_cast<hipStream_t>(stream));
+}
+
+int vitblk_forward_packed_affine(const void* x, const void* packed,
+                                 const vitblk_affine_params* params, void* out, int64_t N,
+                                 int64_t T, int64_t D, int64_t F, int64_t H, double eps,
+                                 int dtype, void* workspace, size_t workspace_bytes,
+                                 vitblk_stream_t stream) {
+  WorkspacePlan pl;
+  int st = validate_forward_packed(x, packed, out, N, T, D, F, H, eps, dtype, workspace,
+                                   workspace_bytes, &pl);
+  if (st != VITBLK_OK) return st;
+  st = validate_affine_params(params, out, N * T, D, F, dtype, workspace, pl.act_total);
+  if (st != VITBLK_OK) return st;
+  return run_block(x, packed, params, out, N, T, D, F, H, eps, dtype,
                    static_cast<char*>(workspace) + pl.act_base, pl,
                    reinterpret_cast<hipStream_t>(stream));
 }
 
 int vitblk_layernorm(const void* x, void* out, int64_t rows, int64_t D, double eps, int dtype,
                      vitblk_stream_t stream) {
-  const int st = validate_layernorm(x, out, rows, D, eps, dtype);
+  return vitblk_layernorm_affine(x, nullptr, nullptr, out, rows, D, eps, dtype, stream);
+}
+
+int vitblk_layernorm_affine(const void* x, const void* gamma, const void* beta, void* out,
+                            int64_t rows, int64_t D, double eps, int dtype,
+                            vitblk_stream_t stream) {
+  const int st = validate_layernorm(x, gamma, beta, out, rows, D, eps, dtype);
   if (st != VITBLK_OK) return st;
-  VITBLK_LAUNCH(launch_layernorm(x, out, rows, D, static_cast<float>(eps), dtype,
+  VITBLK_LAUNCH(launch_layernorm(x, gamma, beta, out, rows, D, static_cast<float>(eps), dtype,
                                  reinterpret_cast<hipStream_t>(stream)));
   return VITBLK_OK;
 }
@@ -186,11 +238,17 @@ int vitblk_attention(const void* qkv, void* att, int64_t N, int64_t T, int64_t D
 
 int vitblk_linear(const void* a, const void* w_t, const void* residual, void* out, int64_t M,
                   int64_t K, int64_t Nout, int epilogue, int dtype, vitblk_stream_t stream) {
-  const int st = validate_linear(a, w_t, residual, out, M, K, Nout, epilogue, dtype);
+  return vitblk_linear_bias(a, w_t, nullptr, residual, out, M, K, Nout, epilogue, dtype, stream);
+}
+
+int vitblk_linear_bias(const void* a, const void* w_t, const void* bias, const void* residual,
+                       void* out, int64_t M, int64_t K, int64_t Nout, int epilogue, int dtype,
+                       vitblk_stream_t stream) {
+  const int st = validate_linear(a, w_t, bias, residual, out, M, K, Nout, epilogue, dtype);
   if (st != VITBLK_OK) return st;
   VITBLK_LAUNCH(launch_gemm(
       linear_problem(a, w_t, out, epilogue == VITBLK_EPI_RESIDUAL ? residual : nullptr, M, K,
-                     Nout, epilogue, dtype),
+                     Nout, epilogue, dtype, bias),
       reinterpret_cast<hipStream_t>(stream)));
   return VITBLK_OK;
 }

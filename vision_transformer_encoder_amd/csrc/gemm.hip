@@ -128,7 +128,7 @@ __device__ __forceinline__ void tile_of(int t, int grid, int total, int mt, int 
   *tn = w / gm;
 }
 
-template <class C, int EPI>
+template <class C, int EPI, bool BIAS>
 __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p, int mt, int nt) {
   __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
   char* const a_lds = lds;                       // [stage][BM rows][BK * 2 B]
@@ -318,6 +318,35 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
     // the single rounding to bf16.
     bf16_t* Cp = static_cast<bf16_t*>(p.C);
     const bf16_t* Rp = static_cast<const bf16_t*>(p.R);
+    // Bias, added in fp32 to the accumulators first (before GELU or the
+    // residual).  Accumulator element r of block (j, i) is column
+    // (r/4)*8 + (l/32)*4 + r%4 of the block: 4 runs of 4 columns per lane, the
+    // same for every i.  Columns past N are clamped (never stored).
+    if (BIAS) {
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        float bv[16];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          int64_t n = cn0 + wn * C::WTN + j * 32 + g4 * 8 + lhalf * 4;
+          n = n < N ? n : N - 4;
+          const int seg = static_cast<int>(n / p.bias_seg);
+          const void* bs = seg == 0 ? p.bias[0] : (seg == 1 ? p.bias[1] : p.bias[2]);
+          uint2 u = make_uint2(0u, 0u);
+          if (bs != nullptr)
+            u = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(bs) +
+                                                (n - static_cast<int64_t>(seg) * p.bias_seg));
+          bv[g4 * 4 + 0] = __uint_as_float(u.x << 16);
+          bv[g4 * 4 + 1] = __uint_as_float(u.x & 0xffff0000u);
+          bv[g4 * 4 + 2] = __uint_as_float(u.y << 16);
+          bv[g4 * 4 + 3] = __uint_as_float(u.y & 0xffff0000u);
+        }
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[j][i][r] += bv[r];
+      }
+    }
     uint4 res[C::TM][C::TN][2];
     if (EPI == VITBLK_EPI_RESIDUAL) {
 #pragma unroll
@@ -402,7 +431,7 @@ using BigTile = Cfg<256, 256, 2, 4, 64, 2, 3>;
 using SmallTile = Cfg<128, 128, 2, 2, 64, 2, 3>;
 
 // Workgroups of this kernel the device holds at once (cached per kernel).
-template <class C, int EPI>
+template <class C, int EPI, bool BIAS = false>
 int resident_workgroups() {
   static int cached = 0;
   if (cached == 0) {
@@ -410,7 +439,7 @@ int resident_workgroups() {
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&gemm_bf16_kernel<C, EPI>), C::NT, 0) !=
+            &per_cu, reinterpret_cast<const void*>(&gemm_bf16_kernel<C, EPI, BIAS>), C::NT, 0) !=
             hipSuccess) {
       (void)hipGetLastError();
       return 0;
@@ -420,27 +449,34 @@ int resident_workgroups() {
   return cached;
 }
 
-template <class C, int EPI>
+template <class C, int EPI, bool BIAS>
 hipError_t launch_epi(const GemmProblem& p, hipStream_t s) {
   const int64_t mt = (p.M + C::BM - 1) / C::BM, nt = (p.N + C::BN - 1) / C::BN;
   const int64_t tiles = mt * nt;
   if (tiles > 2147483647LL) return hipErrorInvalidValue;
-  int64_t grid = resident_workgroups<C, EPI>();
+  int64_t grid = resident_workgroups<C, EPI, BIAS>();
   if (grid <= 0) return hipErrorInvalidValue;
   grid = grid / kNumXcd * kNumXcd;  // keeps the XCD-contiguous mapping exact
   if (grid <= 0 || grid > tiles) grid = tiles;
-  hipLaunchKernelGGL((gemm_bf16_kernel<C, EPI>), dim3(static_cast<unsigned>(grid)), dim3(C::NT),
-                     0, s, p, static_cast<int>(mt), static_cast<int>(nt));
+  hipLaunchKernelGGL((gemm_bf16_kernel<C, EPI, BIAS>), dim3(static_cast<unsigned>(grid)),
+                     dim3(C::NT), 0, s, p, static_cast<int>(mt), static_cast<int>(nt));
   return hipGetLastError();
+}
+
+// Epilogue and bias as template arguments: the kernels without a bias carry
+// no bias state at all.
+template <class C, bool BIAS>
+hipError_t launch_bias(const GemmProblem& p, hipStream_t s) {
+  switch (p.epi) {
+    case VITBLK_EPI_RESIDUAL: return launch_epi<C, VITBLK_EPI_RESIDUAL, BIAS>(p, s);
+    case VITBLK_EPI_GELU: return launch_epi<C, VITBLK_EPI_GELU, BIAS>(p, s);
+    default: return launch_epi<C, VITBLK_EPI_NONE, BIAS>(p, s);
+  }
 }
 
 template <class C>
 hipError_t launch_cfg(const GemmProblem& p, hipStream_t s) {
-  switch (p.epi) {
-    case VITBLK_EPI_RESIDUAL: return launch_epi<C, VITBLK_EPI_RESIDUAL>(p, s);
-    case VITBLK_EPI_GELU: return launch_epi<C, VITBLK_EPI_GELU>(p, s);
-    default: return launch_epi<C, VITBLK_EPI_NONE>(p, s);
-  }
+  return has_bias(p) ? launch_bias<C, true>(p, s) : launch_bias<C, false>(p, s);
 }
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
@@ -449,13 +485,20 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u
 
 // The MFMA kernel needs bf16, K a multiple of 64, N a multiple of 8, 16-byte
 // aligned rows, and a 256-row panel of either operand to span < 2 GiB (its
-// buffer offsets are 32-bit).  Everything else takes the generic kernel.
+// buffer offsets are 32-bit); a bias in segments of a multiple of 8 columns
+// (so no lane's run of columns straddles two segments), 8-byte aligned.
+// Everything else takes the generic kernel.
 bool gemm_fast_ok(const GemmProblem& p) {
   bool ok = p.dtype == VITBLK_BF16 && p.K % 64 == 0 && p.N % 8 == 0 && p.N >= 8 &&
             p.lda % 8 == 0 && p.ldb % 8 == 0 && p.ldc % 8 == 0 && aligned16(p.A) &&
             aligned16(p.B) && aligned16(p.C) && p.lda * 2 * 256 < (1LL << 31) &&
             p.ldb * 2 * 256 < (1LL << 31) && p.K * 2 < (1LL << 31);
   if (p.epi == VITBLK_EPI_RESIDUAL) ok = ok && p.ldr % 8 == 0 && aligned16(p.R);
+  if (has_bias(p)) {
+    ok = ok && p.bias_seg > 0 && p.bias_seg % 8 == 0 && p.N <= 3 * p.bias_seg;
+    for (const void* b : p.bias)
+      ok = ok && (reinterpret_cast<uintptr_t>(b) & 7u) == 0;
+  }
   return ok;
 }
 

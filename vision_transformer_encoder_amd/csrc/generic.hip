@@ -27,9 +27,9 @@ __device__ float block_sum_256(float v, float* red) {
 // LayerNorm of one row per workgroup: mean, then population variance of the
 // deviations (two passes over the row), then (x - mean) / sqrt(var + eps).
 template <typename T>
-__global__ __launch_bounds__(kGenThreads) void ln_generic_kernel(const T* __restrict__ x,
-                                                                 T* __restrict__ y, int64_t D,
-                                                                 float eps) {
+__global__ __launch_bounds__(kGenThreads) void ln_generic_kernel(
+    const T* __restrict__ x, const T* __restrict__ gamma, const T* __restrict__ beta,
+    T* __restrict__ y, int64_t D, float eps) {
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
   const T* xr = x + row * D;
@@ -44,8 +44,12 @@ __global__ __launch_bounds__(kGenThreads) void ln_generic_kernel(const T* __rest
   }
   const float var = block_sum_256(q, red) / static_cast<float>(D);
   const float rstd = 1.0f / sqrtf(var + eps);
-  for (int64_t i = threadIdx.x; i < D; i += kGenThreads)
-    store_f32(yr + i, (load_f32(xr + i) - mean) * rstd);
+  for (int64_t i = threadIdx.x; i < D; i += kGenThreads) {
+    float o = (load_f32(xr + i) - mean) * rstd;
+    if (gamma != nullptr) o *= load_f32(gamma + i);
+    if (beta != nullptr) o += load_f32(beta + i);
+    store_f32(yr + i, o);
+  }
 }
 
 // 64x64 output tile per workgroup, 16-deep k slices staged in LDS, 4x4
@@ -96,6 +100,11 @@ __global__ __launch_bounds__(kGenThreads) void gemm_generic_kernel(GemmProblem p
       const int64_t n = n0 + tx * 4 + j;
       if (n >= p.N) continue;
       float v = acc[i][j];
+      if (has_bias(p)) {
+        const int64_t seg = n / p.bias_seg;
+        const void* bs = seg == 0 ? p.bias[0] : (seg == 1 ? p.bias[1] : p.bias[2]);
+        if (bs != nullptr) v += load_f32(static_cast<const T*>(bs) + (n - seg * p.bias_seg));
+      }
       if (EPI == VITBLK_EPI_RESIDUAL) v += load_f32(R + m * p.ldr + n);
       if (EPI == VITBLK_EPI_GELU) v = gelu_tanh_precise(v);
       store_f32(C + m * p.ldc + n, v);
@@ -196,15 +205,18 @@ hipError_t gemm_generic_typed(const GemmProblem& p, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_layernorm_generic(const void* x, void* y, int64_t rows, int64_t D, float eps,
-                                    int dtype, hipStream_t s) {
+hipError_t launch_layernorm_generic(const void* x, const void* gamma, const void* beta, void* y,
+                                    int64_t rows, int64_t D, float eps, int dtype,
+                                    hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(rows));
   if (dtype == VITBLK_BF16)
     hipLaunchKernelGGL(ln_generic_kernel<bf16_t>, grid, dim3(kGenThreads), 0, s,
-                       static_cast<const bf16_t*>(x), static_cast<bf16_t*>(y), D, eps);
+                       static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(gamma),
+                       static_cast<const bf16_t*>(beta), static_cast<bf16_t*>(y), D, eps);
   else
     hipLaunchKernelGGL(ln_generic_kernel<float>, grid, dim3(kGenThreads), 0, s,
-                       static_cast<const float*>(x), static_cast<float*>(y), D, eps);
+                       static_cast<const float*>(x), static_cast<const float*>(gamma),
+                       static_cast<const float*>(beta), static_cast<float*>(y), D, eps);
   return hipGetLastError();
 }
 

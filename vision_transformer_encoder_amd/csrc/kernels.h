@@ -6,10 +6,13 @@
 
 namespace vitblk {
 
-// C[m, n] = epi(sum_k A[m, k] * Wt[n, k]) (+ R[m, n]) for m < M, n < N.
+// C[m, n] = epi(sum_k A[m, k] * Wt[n, k] + b[n]) (+ R[m, n]) for m < M, n < N.
 // A [M, K] with row stride lda; the weight is given out-major, Wt [N, K] with
 // row stride ldb (row n = column n of the (in, out) weight); C and R have row
-// strides ldc and ldr.  All strides in elements.
+// strides ldc and ldr.  All strides in elements.  The bias is optional and
+// given in segments of bias_seg columns: b[n] = bias[n / bias_seg][n %
+// bias_seg] (one segment per Q, K, V in the fused projection); a null
+// segment is zero, and all three null means no bias.
 struct GemmProblem {
   int64_t M, N, K;
   const void* A;
@@ -22,7 +25,13 @@ struct GemmProblem {
   int64_t ldr;
   int epi;    // vitblk_epilogue
   int dtype;  // vitblk_dtype
+  const void* bias[3];
+  int64_t bias_seg;
 };
+
+__host__ __device__ inline bool has_bias(const GemmProblem& p) {
+  return p.bias[0] != nullptr || p.bias[1] != nullptr || p.bias[2] != nullptr;
+}
 
 // One (in, out) weight to write out-major: dst[c * ldd + r] = src[r * cols + c].
 struct PackJob {
@@ -32,8 +41,9 @@ struct PackJob {
   int64_t ldd;
 };
 
-hipError_t launch_layernorm(const void* x, void* y, int64_t rows, int64_t D, float eps,
-                            int dtype, hipStream_t stream);
+// y = LN(x) * gamma + beta per row; gamma and beta ([D]) may be null (1, 0).
+hipError_t launch_layernorm(const void* x, const void* gamma, const void* beta, void* y,
+                            int64_t rows, int64_t D, float eps, int dtype, hipStream_t stream);
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
 
@@ -54,8 +64,9 @@ hipError_t launch_attention_resident(const void* q, const void* k, const void* v
 
 // Generic (any-shape, VALU, fp32 arithmetic) kernels; the fast kernels fall
 // back to these for shapes they do not tile and for fp32 tensors.
-hipError_t launch_layernorm_generic(const void* x, void* y, int64_t rows, int64_t D,
-                                    float eps, int dtype, hipStream_t stream);
+hipError_t launch_layernorm_generic(const void* x, const void* gamma, const void* beta, void* y,
+                                    int64_t rows, int64_t D, float eps, int dtype,
+                                    hipStream_t stream);
 hipError_t launch_gemm_generic(const GemmProblem& p, hipStream_t stream);
 hipError_t launch_attention_generic(const void* q, const void* k, const void* v, int64_t ld,
                                     void* o, int64_t ldo, int64_t N, int64_t T, int64_t H,

@@ -6,6 +6,8 @@
 #include <cstddef>
 #include <cstdint>
 
+#include "vitblk.h"
+
 namespace vitblk {
 
 constexpr size_t kRegionAlign = 256;
@@ -54,8 +56,9 @@ int validate_pack(const void* w_q, const void* w_k, const void* w_v, const void*
                   const void* w_mlp1, const void* w_mlp2, const void* packed, int64_t D,
                   int64_t F, int dtype, PackedPlan* plan);
 
-int validate_layernorm(const void* x, const void* out, int64_t rows, int64_t D,
-                       double eps, int dtype);
+// gamma and beta may be null.
+int validate_layernorm(const void* x, const void* gamma, const void* beta, const void* out,
+                       int64_t rows, int64_t D, double eps, int dtype);
 
 int validate_qkv(const void* xn, const void* w_qkv_t, const void* qkv, int64_t M, int64_t D,
                  int dtype);
@@ -63,7 +66,16 @@ int validate_qkv(const void* xn, const void* w_qkv_t, const void* qkv, int64_t M
 int validate_attention(const void* qkv, const void* att, int64_t N, int64_t T, int64_t D,
                        int64_t H, int dtype);
 
-int validate_linear(const void* a, const void* w, const void* residual, const void* out,
-                    int64_t M, int64_t K, int64_t Nout, int epilogue, int dtype);
+// bias may be null.
+int validate_linear(const void* a, const void* w, const void* bias, const void* residual,
+                    const void* out, int64_t M, int64_t K, int64_t Nout, int epilogue,
+                    int dtype);
+
+// The affine variant's parameters (params may be null; so may every member):
+// each present one 16-byte aligned and clear of out ([rows, D]) and of the
+// workspace's first workspace_bytes bytes.
+int validate_affine_params(const vitblk_affine_params* params, const void* out, int64_t rows,
+                           int64_t D, int64_t F, int dtype, const void* workspace,
+                           size_t workspace_bytes);
 
 }  // namespace vitblk

@@ -187,10 +187,11 @@ int validate_pack(const void* w_q, const void* w_k, const void* w_v, const void*
   return VITBLK_OK;
 }
 
-int validate_layernorm(const void* x, const void* out, int64_t rows, int64_t D, double eps,
-                       int dtype) {
+int validate_layernorm(const void* x, const void* gamma, const void* beta, const void* out,
+                       int64_t rows, int64_t D, double eps, int dtype) {
   if (x == nullptr || out == nullptr || !aligned16(x) || !aligned16(out))
     return VITBLK_ERR_INVALID_ARG;
+  if (!aligned16(gamma) || !aligned16(beta)) return VITBLK_ERR_INVALID_ARG;
   if (!dim_ok(rows) || !dim_ok(D)) return VITBLK_ERR_INVALID_ARG;
   const size_t es = elem_size(dtype);
   if (es == 0) return VITBLK_ERR_INVALID_ARG;
@@ -198,7 +199,12 @@ int validate_layernorm(const void* x, const void* out, int64_t rows, int64_t D, 
   if (st != VITBLK_OK) return st;
   if (rows > kMaxDim || D > kMaxDim) return VITBLK_ERR_UNSUPPORTED;
   const size_t n = static_cast<size_t>(rows) * static_cast<size_t>(D) * es;
-  if (overlap(span(x, n), span(out, n))) return VITBLK_ERR_ALIAS;
+  const Span o = span(out, n);
+  if (overlap(span(x, n), o)) return VITBLK_ERR_ALIAS;
+  const size_t v = static_cast<size_t>(D) * es;
+  if ((gamma != nullptr && overlap(span(gamma, v), o)) ||
+      (beta != nullptr && overlap(span(beta, v), o)))
+    return VITBLK_ERR_ALIAS;
   return VITBLK_OK;
 }
 
@@ -234,10 +240,12 @@ int validate_attention(const void* qkv, const void* att, int64_t N, int64_t T, i
   return VITBLK_OK;
 }
 
-int validate_linear(const void* a, const void* w, const void* residual, const void* out,
-                    int64_t M, int64_t K, int64_t Nout, int epilogue, int dtype) {
+int validate_linear(const void* a, const void* w, const void* bias, const void* residual,
+                    const void* out, int64_t M, int64_t K, int64_t Nout, int epilogue,
+                    int dtype) {
   if (a == nullptr || w == nullptr || out == nullptr) return VITBLK_ERR_INVALID_ARG;
-  if (!aligned16(a) || !aligned16(w) || !aligned16(out)) return VITBLK_ERR_INVALID_ARG;
+  if (!aligned16(a) || !aligned16(w) || !aligned16(out) || !aligned16(bias))
+    return VITBLK_ERR_INVALID_ARG;
   if (epilogue != VITBLK_EPI_NONE && epilogue != VITBLK_EPI_RESIDUAL &&
       epilogue != VITBLK_EPI_GELU)
     return VITBLK_ERR_INVALID_ARG;
@@ -254,6 +262,30 @@ int validate_linear(const void* a, const void* w, const void* residual, const vo
     return VITBLK_ERR_ALIAS;
   if (epilogue == VITBLK_EPI_RESIDUAL && overlap(o, span(residual, m * n * es)))
     return VITBLK_ERR_ALIAS;
+  if (bias != nullptr && overlap(o, span(bias, n * es))) return VITBLK_ERR_ALIAS;
+  return VITBLK_OK;
+}
+
+int validate_affine_params(const vitblk_affine_params* params, const void* out, int64_t rows,
+                           int64_t D, int64_t F, int dtype, const void* workspace,
+                           size_t workspace_bytes) {
+  if (params == nullptr) return VITBLK_OK;
+  const size_t es = elem_size(dtype);
+  if (es == 0 || !dim_ok(rows) || !dim_ok(D) || !dim_ok(F)) return VITBLK_ERR_INVALID_ARG;
+  const size_t d = static_cast<size_t>(D) * es, f = static_cast<size_t>(F) * es;
+  const void* ptrs[10] = {params->ln1_gamma, params->ln1_beta, params->b_q,
+                          params->b_k,       params->b_v,      params->b_o,
+                          params->ln2_gamma, params->ln2_beta, params->b_mlp1,
+                          params->b_mlp2};
+  const size_t bytes[10] = {d, d, d, d, d, d, d, d, f, d};
+  const Span o = span(out, static_cast<size_t>(rows) * d);
+  const Span w = span(workspace, workspace_bytes);
+  for (int i = 0; i < 10; ++i) {
+    if (ptrs[i] == nullptr) continue;
+    if (!aligned16(ptrs[i])) return VITBLK_ERR_INVALID_ARG;
+    const Span s = span(ptrs[i], bytes[i]);
+    if (overlap(s, o) || overlap(s, w)) return VITBLK_ERR_ALIAS;
+  }
   return VITBLK_OK;
 }
 

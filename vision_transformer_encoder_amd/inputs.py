@@ -18,6 +18,14 @@ Recipe
   of the float32 value after RNE; fp32: numpy's float64 -> float32 cast).
   The float64 arrays returned are those rounded values, upcast exactly.
 
+Affine variant (``make_affine_params``): a second, independent generator,
+``numpy.random.default_rng([seed, 1])``, draws in the order ln1_gamma,
+ln1_beta, b_q, b_k, b_v, b_o, ln2_gamma, ln2_beta, b_mlp1, b_mlp2 (lengths D,
+except F for b_mlp1): gains 1 + 0.1 N(0, 1), shifts and biases 0.1 N(0, 1),
+then the same rounding.  The pages initialise gains to 1 and shifts and
+biases to 0 (mlgrind.dev, "Details"); trained values differ from that, and
+these stand in for them so that every term is visible in a parity check.
+
 The workloads are the shapes of ViT-B/16, ViT-L/16 and ViT-H/14 (widths and
 MLP sizes from ai-engineer-exhaustive.pages.dev "ViT Encoder Block", section
 "Paper Context"), with T = patches + 1 class token (224/16 -> 197,
@@ -34,7 +42,11 @@ import math
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "bf16_round", "round_to", "make_block_inputs"]
+__all__ = ["Workload", "WORKLOADS", "bf16_round", "round_to", "make_block_inputs",
+           "AFFINE_PARAM_ORDER", "make_affine_params"]
+
+AFFINE_PARAM_ORDER = ("ln1_gamma", "ln1_beta", "b_q", "b_k", "b_v", "b_o",
+                      "ln2_gamma", "ln2_beta", "b_mlp1", "b_mlp2")
 
 
 @dataclasses.dataclass(frozen=True)
@@ -105,4 +117,15 @@ def make_block_inputs(N: int, T: int, D: int, F: int, dtype: str, seed: int = 0)
     out = {}
     for name, shape, std in shapes:
         out[name] = round_to(rng.standard_normal(shape) * std, dtype)
+    return out
+
+
+def make_affine_params(D: int, F: int, dtype: str, seed: int = 0) -> dict:
+    """Draw the affine variant's gains, shifts and biases (device-exact float64)."""
+    rng = np.random.default_rng([seed, 1])
+    out = {}
+    for name in AFFINE_PARAM_ORDER:
+        n = F if name == "b_mlp1" else D
+        z = rng.standard_normal(n)
+        out[name] = round_to(1.0 + 0.1 * z if name.endswith("gamma") else 0.1 * z, dtype)
     return out
