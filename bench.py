@@ -1,6 +1,7 @@
 """Throughput of one pre-LN ViT encoder block forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload vit_l16]
+                    [--variant plain|affine]
 
 A step is one full block forward (8 kernels through vitblk_forward: weight packing
 and the seven steps of the block) over one
@@ -10,7 +11,8 @@ fraction of the bf16 dense MFMA peak, per-kernel times (each step's kernel
 timed alone with HIP events on the launch stream), the roofline of the
 dominant kernel, a parity check of the timed output against the float64
 oracle on sampled sequences, and the oracle's own throughput on the host
-cores (cpu_baseline).
+cores (cpu_baseline).  ``--variant affine`` times the affine block instead
+(LayerNorm gains and shifts, projection biases: vitblk_forward_affine).
 """
 
 from __future__ import annotations
@@ -75,6 +77,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target host time for the oracle baseline sample (0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--variant", choices=["plain", "affine"], default="plain",
+                    help="plain block (default) or the affine variant")
     ap.add_argument("--profile-step", default=None,
                     help="run only a 512 MiB copy (counter calibration) and 3 launches of this "
                          "step's kernel, for rocprofv3 --pmc; prints no JSON")
@@ -106,18 +110,18 @@ def blas_threads():
     return len(os.sched_getaffinity(0)), "unknown"
 
 
-def cpu_baseline(inp, w, target_s, got_out):
+def cpu_baseline(inp, w, target_s, got_out, params=None):
     """Time the float64 oracle on a bounded sample of sequences; also check parity there."""
     import oracle
     args = (inp["w_q"], inp["w_k"], inp["w_v"], inp["w_o"], inp["w_mlp1"], inp["w_mlp2"],
             w.H, w.eps)
     t0 = time.perf_counter()
-    ref0 = oracle.vit_block(inp["x"][:1], *args)
+    ref0 = oracle.vit_block(inp["x"][:1], *args, params=params)
     t1 = time.perf_counter() - t0
     n = int(max(1, min(w.N, math.floor(target_s / max(t1, 1e-6)))))
     seqs = sorted(set(np.linspace(0, w.N - 1, n).astype(int).tolist()))
     t0 = time.perf_counter()
-    ref = oracle.vit_block(inp["x"][seqs], *args)
+    ref = oracle.vit_block(inp["x"][seqs], *args, params=params)
     dt = time.perf_counter() - t0
     got = got_out[seqs]
     err = np.abs(got - ref)
@@ -143,7 +147,8 @@ def main():
     import torch
 
     import vision_transformer_encoder_amd as vb
-    from vision_transformer_encoder_amd.inputs import WORKLOADS, make_block_inputs
+    from vision_transformer_encoder_amd.inputs import (WORKLOADS, make_affine_params,
+                                                       make_block_inputs)
 
     if a.profile_step:  # counters only: one untimed block, then the step alone
         a.warmup, a.steps, a.cpu_seconds = 0, 1, 0
@@ -156,10 +161,18 @@ def main():
     out = torch.empty_like(g["x"])
     ws = torch.empty(vb.workspace_bytes(w.N, w.T, w.D, w.F, w.H, tdt), dtype=torch.uint8,
                      device=dev)
+    affine = a.variant == "affine"
+    prm = make_affine_params(w.D, w.F, w.dtype, seed=a.seed) if affine else None
+    gp = ({k: torch.from_numpy(v.astype(np.float32)).to(dev, tdt) for k, v in prm.items()}
+          if affine else {})
 
     def step():
-        vb.forward(g["x"], g["w_q"], g["w_k"], g["w_v"], g["w_o"], g["w_mlp1"], g["w_mlp2"],
-                   w.H, w.eps, out=out, workspace=ws)
+        if affine:
+            vb.forward_affine(g["x"], g["w_q"], g["w_k"], g["w_v"], g["w_o"], g["w_mlp1"],
+                              g["w_mlp2"], w.H, w.eps, params=gp, out=out, workspace=ws)
+        else:
+            vb.forward(g["x"], g["w_q"], g["w_k"], g["w_v"], g["w_o"], g["w_mlp1"],
+                       g["w_mlp2"], w.H, w.eps, out=out, workspace=ws)
 
     for _ in range(a.warmup):
         step()
@@ -188,29 +201,34 @@ def main():
     yn = torch.empty_like(x2)
     hid = torch.empty((M, F), dtype=tdt, device=dev)
     o2 = torch.empty_like(x2)
-    vb.layernorm(x2, w.eps, out=xn)
-    vb.qkv_projection(xn, wqkv_t, out=qkv)
-    vb.attention(qkv, w.N, w.T, w.H, out=att)
-    vb.linear(att, wo_t, vb.EPI_RESIDUAL, residual=x2, out=y)
-    vb.layernorm(y, w.eps, out=yn)
-    vb.linear(yn, w1_t, vb.EPI_GELU, out=hid)
+    # The affine variant's steps: LN with gain/shift, GEMMs with bias (the
+    # fused QKV bias as one [3D] vector here, the same values).
+    gq = gp.get
+    bqkv = torch.cat([gp["b_q"], gp["b_k"], gp["b_v"]]) if affine else None
     es = 2 if w.dtype == "bf16" else 4
     wbytes = (4 * D * D + 2 * D * F) * es
     kern = {
         "pack_weights": (lambda: vb.pack_weights(g["w_q"], g["w_k"], g["w_v"], g["w_o"],
                                                  g["w_mlp1"], g["w_mlp2"], packed=packed),
                          "hbm", 2 * wbytes),
-        "ln1": (lambda: vb.layernorm(x2, w.eps, out=xn), "hbm", 2 * M * D * es),
-        "qkv_gemm": (lambda: vb.qkv_projection(xn, wqkv_t, out=qkv), "mfma", 2 * M * D * 3 * D),
+        "ln1": (lambda: vb.layernorm(x2, w.eps, gamma=gq("ln1_gamma"), beta=gq("ln1_beta"),
+                                     out=xn), "hbm", 2 * M * D * es),
+        "qkv_gemm": ((lambda: vb.linear(xn, wqkv_t, vb.EPI_NONE, bias=bqkv, out=qkv)) if affine
+                     else (lambda: vb.qkv_projection(xn, wqkv_t, out=qkv)),
+                     "mfma", 2 * M * D * 3 * D),
         "attention": (lambda: vb.attention(qkv, w.N, w.T, w.H, out=att), "mfma",
                       4 * w.N * w.T * w.T * D),
-        "oproj_residual": (lambda: vb.linear(att, wo_t, vb.EPI_RESIDUAL, residual=x2, out=y),
-                           "mfma", 2 * M * D * D),
-        "ln2": (lambda: vb.layernorm(y, w.eps, out=yn), "hbm", 2 * M * D * es),
-        "mlp1_gelu": (lambda: vb.linear(yn, w1_t, vb.EPI_GELU, out=hid), "mfma", 2 * M * D * F),
-        "mlp2_residual": (lambda: vb.linear(hid, w2_t, vb.EPI_RESIDUAL, residual=y, out=o2),
-                          "mfma", 2 * M * F * D),
+        "oproj_residual": (lambda: vb.linear(att, wo_t, vb.EPI_RESIDUAL, residual=x2,
+                                             bias=gq("b_o"), out=y), "mfma", 2 * M * D * D),
+        "ln2": (lambda: vb.layernorm(y, w.eps, gamma=gq("ln2_gamma"), beta=gq("ln2_beta"),
+                                     out=yn), "hbm", 2 * M * D * es),
+        "mlp1_gelu": (lambda: vb.linear(yn, w1_t, vb.EPI_GELU, bias=gq("b_mlp1"), out=hid),
+                      "mfma", 2 * M * D * F),
+        "mlp2_residual": (lambda: vb.linear(hid, w2_t, vb.EPI_RESIDUAL, residual=y,
+                                            bias=gq("b_mlp2"), out=o2), "mfma", 2 * M * F * D),
     }
+    for name in ["ln1", "qkv_gemm", "attention", "oproj_residual", "ln2", "mlp1_gelu"]:
+        kern[name][0]()  # realistic operands for every step
     if a.profile_step:
         x_copy = torch.empty(256 * 1024 * 1024, dtype=torch.bfloat16, device=dev).fill_(1.0)
         y_copy = torch.empty_like(x_copy)
@@ -239,13 +257,13 @@ def main():
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                "traffic": recorded_traffic(dom, w.name),
+                "traffic": None if affine else recorded_traffic(dom, w.name),
                 "work_per_launch": f"{work / 1e9:.2f} GFLOP"}
     else:
         ach = work / (dms * 1e-3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                "traffic": recorded_traffic(dom, w.name),
+                "traffic": None if affine else recorded_traffic(dom, w.name),
                 "work_per_launch": f"{work / 1e6:.1f} MB"}
 
     flops = block_flops(w.N, w.T, w.D, w.F)
@@ -264,7 +282,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) weights)",
         "config": {"workload": w.name, "N": w.N, "T": w.T, "D": w.D, "H": w.H, "F": w.F,
-                   "eps": w.eps, "global_batch": w.N, "seq_len": w.T, "parallelism": "none"},
+                   "eps": w.eps, "global_batch": w.N, "seq_len": w.T, "parallelism": "none",
+                   **({"variant": "affine"} if affine else {})},
         "block_tflops": round(tflops, 2),
         "block_frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "wall_s_timed": round(t_wall, 3),
@@ -272,7 +291,7 @@ def main():
         "roofline": roof,
     }
     if a.cpu_seconds > 0:
-        cb, par = cpu_baseline(inp, w, a.cpu_seconds, got)
+        cb, par = cpu_baseline(inp, w, a.cpu_seconds, got, params=prm)
         res["cpu_baseline"] = cb
         res["parity"] = par
     else:
