@@ -10,6 +10,7 @@ from .block import (  # noqa: F401
     affine,
     attention_scores,
     attention_weights,
+    encoder,
     gelu_tanh,
     layer_norm,
     merge_heads,

@@ -19,7 +19,8 @@ Sources (the pages this follows; each function names the section it restates):
          "Requirements" (population variance, eps 1e-6), "Examples".
   [AEE]  ai-engineer-exhaustive.pages.dev, "ViT Encoder Block" --
          "Key Equations" steps 1-6, "Numerical Example".
-  [MLG]  mlgrind.dev, "E2E: Tiny Vision Transformer" -- "Details" (MHA, GELU).
+  [MLG]  mlgrind.dev, "E2E: Tiny Vision Transformer" -- "Details" (MHA, GELU),
+         "Architecture" (final LayerNorm of the class token).
   [NB]   nipunbatra.github.io, vision1 lecture transcript -- Page 70
          (head h owns features h*d_h .. (h+1)*d_h-1), Pages 106-110 (code),
          Pages 24-26 and 36 (a linear layer is a weighted sum plus a bias).
@@ -65,6 +66,7 @@ __all__ = [
     "affine",
     "add_bias",
     "AFFINE_KEYS",
+    "encoder",
 ]
 
 # Optional parameters of the affine variant, in the order of the block.
@@ -267,3 +269,24 @@ def vit_block(x, w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, num_heads: int, eps: float,
                               num_heads, eps, params=params)
         out[s:s + chunk] = st["out"]
     return out
+
+
+def encoder(x, layers, num_heads: int, eps: float, final_gamma=None, final_beta=None,
+            chunk: int = 8):
+    """L encoder blocks in sequence, then the final LayerNorm; (tokens, cls).
+
+    [AEE] "What It Is": the encoder stacks L identical blocks, each with its
+    own weights (L = 12, 24, 32 for ViT-B/L/H, "Paper Context").  [MLG]
+    "Architecture": after the last block, cls = LN_f(t[:, 0]), a LayerNorm
+    with its own gain and shift.  ``layers`` is a sequence of dicts holding
+    w_q, w_k, w_v, w_o, w_mlp1, w_mlp2 and, optionally, ``params`` (the affine
+    variant's parameters of that block).  Returns tokens = LN_f(t) for every
+    token, (N, T, D), and cls = LN_f(t[:, 0]), (N, D).
+    """
+    t = _f64(x)
+    for layer in layers:
+        t = vit_block(t, layer["w_q"], layer["w_k"], layer["w_v"], layer["w_o"],
+                      layer["w_mlp1"], layer["w_mlp2"], num_heads, eps, chunk=chunk,
+                      params=layer.get("params"))
+    tokens = affine(layer_norm(t, eps), final_gamma, final_beta)
+    return tokens, tokens[:, 0, :]

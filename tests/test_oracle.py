@@ -437,6 +437,66 @@ def test_affine_rejects_unknown_parameter():
         oracle.vit_block(*args, 2, 1e-6, params={"b_qkv": np.zeros(12)})
 
 
+# ------------------------------------------------------- the encoder stack
+
+def _brute_final_ln(t, eps, g, b):
+    return [[g[j] * v + b[j] for j, v in enumerate(_brute_ln(row, eps))] for row in t]
+
+
+def test_encoder_brute_force_agrees():
+    # L blocks by the scalar loop, then the final LN by scalar loops too.
+    rng = np.random.default_rng(99)
+    N, T, D, H, F, L = 2, 3, 4, 2, 6, 3
+    x = rng.standard_normal((N, T, D))
+    layers = []
+    for _ in range(L):
+        ws = _rand_block(rng, N, T, D, F)[1:]
+        layers.append(dict(zip(["w_q", "w_k", "w_v", "w_o", "w_mlp1", "w_mlp2"], ws),
+                           params=_rand_params(rng, D, F)))
+    g, b = 1.0 + 0.3 * rng.standard_normal(D), 0.3 * rng.standard_normal(D)
+    t = x
+    for lay in layers:
+        t = brute_force_block(t, *(lay[k] for k in ["w_q", "w_k", "w_v", "w_o", "w_mlp1",
+                                                     "w_mlp2"]), H, 1e-5, params=lay["params"])
+    want = np.array([_brute_final_ln(t[n].tolist(), 1e-5, g.tolist(), b.tolist())
+                     for n in range(N)])
+    tokens, cls = oracle.encoder(x, layers, H, 1e-5, g, b)
+    assert np.abs(tokens - want).max() < 1e-12
+    assert np.array_equal(cls, tokens[:, 0])
+
+
+def test_encoder_of_zero_updates_is_the_final_layer_norm():
+    # Every block with w_o = w_mlp2 = 0 passes x through; the stack is then LN_f(x).
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(98)
+    N, T, D, H, F = 2, 5, 8, 2, 12
+    x = rng.standard_normal((N, T, D))
+    layers = []
+    for _ in range(4):
+        ws = _rand_block(rng, N, T, D, F)[1:]
+        lay = dict(zip(["w_q", "w_k", "w_v", "w_o", "w_mlp1", "w_mlp2"], ws))
+        lay["w_o"] = np.zeros((D, D))
+        lay["w_mlp2"] = np.zeros((F, D))
+        layers.append(lay)
+    g, b = 1.0 + 0.3 * rng.standard_normal(D), 0.3 * rng.standard_normal(D)
+    tokens, cls = oracle.encoder(x, layers, H, 1e-6, g, b)
+    want = torch.nn.functional.layer_norm(torch.from_numpy(x), (D,), torch.from_numpy(g),
+                                          torch.from_numpy(b), eps=1e-6).numpy()
+    assert np.abs(tokens - want).max() < 1e-12
+    assert np.abs(cls - want[:, 0]).max() < 1e-12
+
+
+def test_encoder_of_one_block_is_the_block_then_layer_norm():
+    rng = np.random.default_rng(97)
+    N, T, D, H, F = 2, 4, 8, 2, 10
+    args = _rand_block(rng, N, T, D, F)
+    lay = dict(zip(["w_q", "w_k", "w_v", "w_o", "w_mlp1", "w_mlp2"], args[1:]))
+    tokens, _ = oracle.encoder(args[0], [lay], H, 1e-6)
+    blk = brute_force_block(*args, H, 1e-6)
+    want = np.array([[_brute_ln(row, 1e-6) for row in blk[n].tolist()] for n in range(N)])
+    assert np.abs(tokens - want).max() < 1e-12
+
+
 def _ln_unbiased(x, eps):
     x = np.asarray(x, dtype=np.float64)
     return (x - x.mean(-1, keepdims=True)) / np.sqrt(x.var(-1, ddof=1, keepdims=True) + eps)
