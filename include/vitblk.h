@@ -210,6 +210,40 @@ int vitblk_forward_packed_affine(const void* x, const void* packed,
                                  vitblk_stream_t stream);
 
 /*
+ * The encoder stack: L blocks in sequence, each with its own packed weights
+ * (and, optionally, its own affine parameters), then a final LayerNorm with
+ * its own gain and shift (ai-engineer-exhaustive.pages.dev "ViT Encoder
+ * Block", "What It Is": L identical blocks with their own weights, L = 12,
+ * 24, 32 for ViT-B/L/H; mlgrind.dev "E2E: Tiny Vision Transformer",
+ * "Architecture": cls = LN_f(t[:, 0]) after the last block):
+ *
+ *   t_0 = x;  t_l = block_l(t_{l-1}), l = 1..L
+ *   out     = LN(t_L) * final_gamma + final_beta          [N, T, D]
+ *   cls_out = LN(t_L[:, 0, :]) * final_gamma + final_beta [N, D]
+ *
+ *   packed  HOST array of L device pointers, each a buffer written by
+ *           vitblk_pack_weights() (the block's six weights, out-major)
+ *   params  HOST array of L vitblk_affine_params, or NULL for plain blocks
+ *   final_gamma, final_beta  [D] device vectors, each may be NULL (1, 0)
+ *   out, cls_out  either may be NULL, not both; neither may overlap an
+ *           input, the other output or the workspace
+ *   workspace  at least vitblk_encoder_workspace_bytes() bytes: one block's
+ *           activations plus two [N*T, D] token buffers the blocks alternate
+ *           between (x itself is never written)
+ *
+ * 7 L + 1 or 2 kernels on `stream`.
+ */
+size_t vitblk_encoder_workspace_bytes(int64_t N, int64_t T, int64_t D, int64_t F, int64_t H,
+                                      int dtype);
+
+int vitblk_encoder_forward(const void* x, const void* const* packed,
+                           const vitblk_affine_params* params, int64_t L,
+                           const void* final_gamma, const void* final_beta, void* out,
+                           void* cls_out, int64_t N, int64_t T, int64_t D, int64_t F, int64_t H,
+                           double eps, int dtype, void* workspace, size_t workspace_bytes,
+                           vitblk_stream_t stream);
+
+/*
  * The steps of the block, one call each, on the same kernels vitblk_forward
  * uses.  They exist so that each step can be checked and timed alone and so
  * that callers can compose blocks of their own.

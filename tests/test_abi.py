@@ -210,6 +210,42 @@ def test_affine_entry_points_errors(lib):
     assert lib.vitblk_linear_bias(a, b, d, None, c, 4, 8, 8, 9, 1, None) == INVALID
 
 
+def test_encoder_errors(lib):
+    N, T, D, F, H = 2, 5, 16, 32, 2
+    need = vb.encoder_workspace_bytes(N, T, D, F, H, 1)
+    r = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    assert need == (vb.workspace_bytes(N, T, D, F, H, 1) - vb.packed_weights_bytes(D, F, 1)
+                    + 2 * r(N * T * D * 2))
+    assert vb.encoder_workspace_bytes(N, T, D, F, 3, 1) == 0
+    x, out, cls, ws = _addr(0), _addr(1), _addr(2), _addr(20)
+    pk = (ctypes.c_void_p * 3)(*[_addr(5 + i).value for i in range(3)])
+
+    def enc(L=3, packed=pk, params=None, fg=None, fb=None, out=out, cls=cls, ws_bytes=need,
+            eps=1e-6):
+        return lib.vitblk_encoder_forward(x, packed, params, L, fg, fb, out, cls, N, T, D, F, H,
+                                          eps, 1, ws, ws_bytes, None)
+
+    assert enc(L=0) == INVALID
+    assert enc(packed=None) == INVALID
+    assert enc(out=None, cls=None) == INVALID
+    assert enc(eps=-1.0) == INVALID
+    assert enc(ws_bytes=need - 1) == WORKSPACE
+    bad = (ctypes.c_void_p * 3)(pk[0], None, pk[2])
+    assert enc(packed=bad) == INVALID
+    bad = (ctypes.c_void_p * 3)(pk[0], pk[1] + 8, pk[2])
+    assert enc(packed=bad) == INVALID
+    bad = (ctypes.c_void_p * 3)(pk[0], out.value, pk[2])      # packed weights inside out
+    assert enc(packed=bad) == ALIAS
+    assert enc(cls=ctypes.c_void_p(out.value + 32)) == ALIAS  # the two outputs overlap
+    assert enc(out=ctypes.c_void_p(x.value)) == ALIAS
+    assert enc(cls=ctypes.c_void_p(ws.value + 64)) == ALIAS
+    assert enc(fg=ctypes.c_void_p(out.value)) == ALIAS
+    assert enc(fb=ctypes.c_void_p(_addr(9).value + 4)) == INVALID
+    AP = vb._lib.AffineParams
+    prm = (AP * 3)(AP(), AP(b_o=cls.value), AP())
+    assert enc(params=ctypes.cast(prm, ctypes.POINTER(AP))) == ALIAS
+
+
 def test_python_binding_rejects_unknown_affine_parameter():
     torch = pytest.importorskip("torch")
     x = torch.zeros(1, 2, 8)

@@ -16,6 +16,8 @@ from ._lib import (  # noqa: F401
     VITBLK_FP32,
     VitblkError,
     attention,
+    encoder_forward,
+    encoder_workspace_bytes,
     forward,
     forward_affine,
     forward_packed,

@@ -46,6 +46,9 @@ SIGNATURES = {
     "vitblk_forward_packed_affine": (_I, [_P, _P, _AP, _P] + [_I64] * 5 + [_D, _I, _P, _SZ, _P]),
     "vitblk_layernorm_affine": (_I, [_P] * 4 + [_I64, _I64, _D, _I, _P]),
     "vitblk_linear_bias": (_I, [_P] * 5 + [_I64, _I64, _I64, _I, _I, _P]),
+    "vitblk_encoder_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64, _I]),
+    "vitblk_encoder_forward": (_I, [_P, ctypes.POINTER(ctypes.c_void_p), _AP, _I64, _P, _P, _P,
+                                    _P] + [_I64] * 5 + [_D, _I, _P, _SZ, _P]),
 }
 
 _lib = None
@@ -189,6 +192,46 @@ def forward_affine(x, w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, num_heads: int, eps: f
                                       _stream(x, stream))
     _check("vitblk_forward_affine", st)
     return out
+
+
+def encoder_workspace_bytes(N, T, D, F, H, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    return int(load().vitblk_encoder_workspace_bytes(N, T, D, F, H, code))
+
+
+def encoder_forward(x, packed, F: int, num_heads: int, eps: float, params=None,
+                    final_gamma=None, final_beta=None, want_tokens=True, want_cls=True,
+                    out=None, cls_out=None, workspace=None, stream=None):
+    """L blocks (packed: list of pack_weights() buffers) then the final LayerNorm.
+
+    params: None or a list of L dicts (see forward_affine).  Returns
+    (tokens [N, T, D] or None, cls [N, D] or None).
+    """
+    torch = _torch()
+    _dev(x, final_gamma, final_beta, out, cls_out)
+    N, T, D = x.shape
+    L = len(packed)
+    code = dtype_code(x.dtype)
+    if want_tokens and out is None:
+        out = torch.empty_like(x)
+    if want_cls and cls_out is None:
+        cls_out = torch.empty((N, D), dtype=x.dtype, device=x.device)
+    arr = (ctypes.c_void_p * L)(*[p.data_ptr() for p in packed])
+    aps = None
+    if params is not None:
+        if len(params) != L:
+            raise ValueError("one parameter dict per block")
+        aps = (AffineParams * L)(*[_affine(p, x) or AffineParams() for p in params])
+    need = encoder_workspace_bytes(N, T, D, F, num_heads, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    st = load().vitblk_encoder_forward(
+        _ptr(x), arr, None if aps is None else ctypes.cast(aps, _AP), L, _ptr(final_gamma),
+        _ptr(final_beta), _ptr(out if want_tokens else None),
+        _ptr(cls_out if want_cls else None), N, T, D, F, num_heads, float(eps), code,
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(x, stream))
+    _check("vitblk_encoder_forward", st)
+    return (out if want_tokens else None), (cls_out if want_cls else None)
 
 
 def pack_weights(w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, packed=None, stream=None):

@@ -75,7 +75,7 @@ int run_block(const void* x, const void* packed, const vitblk_affine_params* prm
   const float feps = static_cast<float>(eps);
 
   // LN1: xn = gamma_1 LN(x) + beta_1
-  VITBLK_LAUNCH(launch_layernorm(x, q.ln1_gamma, q.ln1_beta, a, M, D, feps, dtype, s));
+  VITBLK_LAUNCH(launch_layernorm(x, D, q.ln1_gamma, q.ln1_beta, a, M, D, feps, dtype, s));
   // Q | K | V = xn @ [w_q | w_k | w_v] + [b_q | b_k | b_v]
   VITBLK_LAUNCH(launch_gemm(linear_problem(a, pk + pl.packed.off_qkv, big, nullptr, M, D, 3 * D,
                                            VITBLK_EPI_NONE, dtype, q.b_q, q.b_k, q.b_v, D),
@@ -88,7 +88,7 @@ int run_block(const void* x, const void* packed, const vitblk_affine_params* prm
                                            VITBLK_EPI_RESIDUAL, dtype, q.b_o),
                             s));
   // LN2: yn = gamma_2 LN(y) + beta_2   (overwrites att)
-  VITBLK_LAUNCH(launch_layernorm(y, q.ln2_gamma, q.ln2_beta, a, M, D, feps, dtype, s));
+  VITBLK_LAUNCH(launch_layernorm(y, D, q.ln2_gamma, q.ln2_beta, a, M, D, feps, dtype, s));
   // hidden = GELU(yn @ w_mlp1 + b_mlp1)   (overwrites qkv)
   VITBLK_LAUNCH(launch_gemm(linear_problem(a, pk + pl.packed.off_1, big, nullptr, M, D, F,
                                            VITBLK_EPI_GELU, dtype, q.b_mlp1),
@@ -100,9 +100,54 @@ int run_block(const void* x, const void* packed, const vitblk_affine_params* prm
   return VITBLK_OK;
 }
 
+// L blocks in sequence through two token buffers, then the final LayerNorm
+// of every token (out) and/or of each sequence's first token (cls).
+int run_encoder(const void* x, const void* const* packed, const vitblk_affine_params* params,
+                int64_t L, const void* fg, const void* fb, void* out, void* cls, int64_t N,
+                int64_t T, int64_t D, int64_t F, int64_t H, double eps, int dtype, char* ws,
+                const EncoderPlan& pl, hipStream_t s) {
+  char* tok[2] = {ws + pl.off_tok0, ws + pl.off_tok1};
+  const void* cur = x;
+  for (int64_t l = 0; l < L; ++l) {
+    char* dst = tok[l & 1];
+    const int st = run_block(cur, packed[l], params != nullptr ? &params[l] : nullptr, dst, N, T,
+                             D, F, H, eps, dtype, ws + pl.block.act_base, pl.block, s);
+    if (st != VITBLK_OK) return st;
+    cur = dst;
+  }
+  const float feps = static_cast<float>(eps);
+  if (out != nullptr)
+    VITBLK_LAUNCH(launch_layernorm(cur, D, fg, fb, out, N * T, D, feps, dtype, s));
+  if (cls != nullptr)  // rows n*T: stride T*D
+    VITBLK_LAUNCH(launch_layernorm(cur, T * D, fg, fb, cls, N, D, feps, dtype, s));
+  return VITBLK_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t vitblk_encoder_workspace_bytes(int64_t N, int64_t T, int64_t D, int64_t F, int64_t H,
+                                      int dtype) {
+  EncoderPlan p;
+  if (plan_encoder(N, T, D, F, H, dtype, &p) != VITBLK_OK) return 0;
+  return p.total;
+}
+
+int vitblk_encoder_forward(const void* x, const void* const* packed,
+                           const vitblk_affine_params* params, int64_t L,
+                           const void* final_gamma, const void* final_beta, void* out,
+                           void* cls_out, int64_t N, int64_t T, int64_t D, int64_t F, int64_t H,
+                           double eps, int dtype, void* workspace, size_t workspace_bytes,
+                           vitblk_stream_t stream) {
+  EncoderPlan pl;
+  const int st = validate_encoder(x, packed, params, L, final_gamma, final_beta, out, cls_out, N,
+                                  T, D, F, H, eps, dtype, workspace, workspace_bytes, &pl);
+  if (st != VITBLK_OK) return st;
+  return run_encoder(x, packed, params, L, final_gamma, final_beta, out, cls_out, N, T, D, F, H,
+                     eps, dtype, static_cast<char*>(workspace), pl,
+                     reinterpret_cast<hipStream_t>(stream));
+}
 
 const char* vitblk_status_string(int status) {
   switch (status) {
@@ -210,7 +255,7 @@ int vitblk_layernorm_affine(const void* x, const void* gamma, const void* beta, 
                             vitblk_stream_t stream) {
   const int st = validate_layernorm(x, gamma, beta, out, rows, D, eps, dtype);
   if (st != VITBLK_OK) return st;
-  VITBLK_LAUNCH(launch_layernorm(x, gamma, beta, out, rows, D, static_cast<float>(eps), dtype,
+  VITBLK_LAUNCH(launch_layernorm(x, D, gamma, beta, out, rows, D, static_cast<float>(eps), dtype,
                                  reinterpret_cast<hipStream_t>(stream)));
   return VITBLK_OK;
 }

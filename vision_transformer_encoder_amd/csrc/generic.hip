@@ -28,11 +28,11 @@ __device__ float block_sum_256(float v, float* red) {
 // deviations (two passes over the row), then (x - mean) / sqrt(var + eps).
 template <typename T>
 __global__ __launch_bounds__(kGenThreads) void ln_generic_kernel(
-    const T* __restrict__ x, const T* __restrict__ gamma, const T* __restrict__ beta,
-    T* __restrict__ y, int64_t D, float eps) {
+    const T* __restrict__ x, int64_t ld_in, const T* __restrict__ gamma,
+    const T* __restrict__ beta, T* __restrict__ y, int64_t D, float eps) {
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
-  const T* xr = x + row * D;
+  const T* xr = x + row * ld_in;
   T* yr = y + row * D;
   float s = 0.f;
   for (int64_t i = threadIdx.x; i < D; i += kGenThreads) s += load_f32(xr + i);
@@ -205,17 +205,17 @@ hipError_t gemm_generic_typed(const GemmProblem& p, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_layernorm_generic(const void* x, const void* gamma, const void* beta, void* y,
-                                    int64_t rows, int64_t D, float eps, int dtype,
-                                    hipStream_t s) {
+hipError_t launch_layernorm_generic(const void* x, int64_t ld_in, const void* gamma,
+                                    const void* beta, void* y, int64_t rows, int64_t D,
+                                    float eps, int dtype, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(rows));
   if (dtype == VITBLK_BF16)
     hipLaunchKernelGGL(ln_generic_kernel<bf16_t>, grid, dim3(kGenThreads), 0, s,
-                       static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(gamma),
+                       static_cast<const bf16_t*>(x), ld_in, static_cast<const bf16_t*>(gamma),
                        static_cast<const bf16_t*>(beta), static_cast<bf16_t*>(y), D, eps);
   else
     hipLaunchKernelGGL(ln_generic_kernel<float>, grid, dim3(kGenThreads), 0, s,
-                       static_cast<const float*>(x), static_cast<const float*>(gamma),
+                       static_cast<const float*>(x), ld_in, static_cast<const float*>(gamma),
                        static_cast<const float*>(beta), static_cast<float*>(y), D, eps);
   return hipGetLastError();
 }

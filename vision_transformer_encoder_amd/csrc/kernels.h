@@ -42,8 +42,10 @@ struct PackJob {
 };
 
 // y = LN(x) * gamma + beta per row; gamma and beta ([D]) may be null (1, 0).
-hipError_t launch_layernorm(const void* x, const void* gamma, const void* beta, void* y,
-                            int64_t rows, int64_t D, float eps, int dtype, hipStream_t stream);
+// Input row r starts at x + r * ld_in elements (ld_in >= D); y is [rows, D].
+hipError_t launch_layernorm(const void* x, int64_t ld_in, const void* gamma, const void* beta,
+                            void* y, int64_t rows, int64_t D, float eps, int dtype,
+                            hipStream_t stream);
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
 
@@ -64,9 +66,9 @@ hipError_t launch_attention_resident(const void* q, const void* k, const void* v
 
 // Generic (any-shape, VALU, fp32 arithmetic) kernels; the fast kernels fall
 // back to these for shapes they do not tile and for fp32 tensors.
-hipError_t launch_layernorm_generic(const void* x, const void* gamma, const void* beta, void* y,
-                                    int64_t rows, int64_t D, float eps, int dtype,
-                                    hipStream_t stream);
+hipError_t launch_layernorm_generic(const void* x, int64_t ld_in, const void* gamma,
+                                    const void* beta, void* y, int64_t rows, int64_t D,
+                                    float eps, int dtype, hipStream_t stream);
 hipError_t launch_gemm_generic(const GemmProblem& p, hipStream_t stream);
 hipError_t launch_attention_generic(const void* q, const void* k, const void* v, int64_t ld,
                                     void* o, int64_t ldo, int64_t N, int64_t T, int64_t H,

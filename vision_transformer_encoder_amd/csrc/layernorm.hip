@@ -49,13 +49,13 @@ __device__ __forceinline__ void store8(float* p, const float v[8]) {
 // NCH = upper bound on 8-element chunks per lane (D <= 512 * NCH).
 template <typename T, int NCH>
 __global__ __launch_bounds__(64 * kRowsPerBlock) void ln_rows_kernel(
-    const T* __restrict__ x, const T* __restrict__ gamma, const T* __restrict__ beta,
-    T* __restrict__ y, int64_t rows, int D, float eps) {
+    const T* __restrict__ x, int64_t ld_in, const T* __restrict__ gamma,
+    const T* __restrict__ beta, T* __restrict__ y, int64_t rows, int D, float eps) {
   const int lane = threadIdx.x & 63;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;  // whole wave leaves; no workgroup barrier follows
   const int nchunks = D >> 3;
-  const T* xr = x + row * D;
+  const T* xr = x + row * ld_in;
   T* yr = y + row * D;
   float v[NCH][8];
   float s = 0.f;
@@ -108,37 +108,38 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void ln_rows_kernel(
 }
 
 template <typename T>
-hipError_t ln_fast_typed(const T* x, const T* g, const T* b, T* y, int64_t rows, int D,
-                         float eps, hipStream_t s) {
+hipError_t ln_fast_typed(const T* x, int64_t ld, const T* g, const T* b, T* y, int64_t rows,
+                         int D, float eps, hipStream_t s) {
   const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
   const dim3 grid(static_cast<unsigned>(blocks)), block(64 * kRowsPerBlock);
   const int cpl = (D / 8 + 63) / 64;  // chunks per lane
   if (cpl <= 1)
-    hipLaunchKernelGGL((ln_rows_kernel<T, 1>), grid, block, 0, s, x, g, b, y, rows, D, eps);
+    hipLaunchKernelGGL((ln_rows_kernel<T, 1>), grid, block, 0, s, x, ld, g, b, y, rows, D, eps);
   else if (cpl <= 2)
-    hipLaunchKernelGGL((ln_rows_kernel<T, 2>), grid, block, 0, s, x, g, b, y, rows, D, eps);
+    hipLaunchKernelGGL((ln_rows_kernel<T, 2>), grid, block, 0, s, x, ld, g, b, y, rows, D, eps);
   else if (cpl <= 3)
-    hipLaunchKernelGGL((ln_rows_kernel<T, 3>), grid, block, 0, s, x, g, b, y, rows, D, eps);
+    hipLaunchKernelGGL((ln_rows_kernel<T, 3>), grid, block, 0, s, x, ld, g, b, y, rows, D, eps);
   else if (cpl <= 4)
-    hipLaunchKernelGGL((ln_rows_kernel<T, 4>), grid, block, 0, s, x, g, b, y, rows, D, eps);
+    hipLaunchKernelGGL((ln_rows_kernel<T, 4>), grid, block, 0, s, x, ld, g, b, y, rows, D, eps);
   else
-    hipLaunchKernelGGL((ln_rows_kernel<T, 8>), grid, block, 0, s, x, g, b, y, rows, D, eps);
+    hipLaunchKernelGGL((ln_rows_kernel<T, 8>), grid, block, 0, s, x, ld, g, b, y, rows, D, eps);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_layernorm(const void* x, const void* gamma, const void* beta, void* y,
-                            int64_t rows, int64_t D, float eps, int dtype, hipStream_t s) {
-  // Register-resident rows: D a multiple of 8 (16-byte bf16 vectors), at most
-  // 8 chunks of 8 per lane.
-  const bool fast = (D % 8 == 0) && (D <= 64 * 8 * 8);
-  if (!fast) return launch_layernorm_generic(x, gamma, beta, y, rows, D, eps, dtype, s);
+hipError_t launch_layernorm(const void* x, int64_t ld_in, const void* gamma, const void* beta,
+                            void* y, int64_t rows, int64_t D, float eps, int dtype,
+                            hipStream_t s) {
+  // Register-resident rows: D and the row stride multiples of 8 (16-byte
+  // vectors), at most 8 chunks of 8 per lane.
+  const bool fast = (D % 8 == 0) && (ld_in % 8 == 0) && (D <= 64 * 8 * 8);
+  if (!fast) return launch_layernorm_generic(x, ld_in, gamma, beta, y, rows, D, eps, dtype, s);
   if (dtype == VITBLK_BF16)
-    return ln_fast_typed(static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(gamma),
+    return ln_fast_typed(static_cast<const bf16_t*>(x), ld_in, static_cast<const bf16_t*>(gamma),
                          static_cast<const bf16_t*>(beta), static_cast<bf16_t*>(y), rows,
                          static_cast<int>(D), eps, s);
-  return ln_fast_typed(static_cast<const float*>(x), static_cast<const float*>(gamma),
+  return ln_fast_typed(static_cast<const float*>(x), ld_in, static_cast<const float*>(gamma),
                        static_cast<const float*>(beta), static_cast<float*>(y), rows,
                        static_cast<int>(D), eps, s);
 }

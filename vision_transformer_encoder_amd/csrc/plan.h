@@ -35,7 +35,18 @@ struct WorkspacePlan {
   size_t total;        // vitblk_forward workspace: packed.total + act_total
 };
 
+// Encoder stack workspace: one block's activations, then two [M, D] token
+// buffers that the blocks alternate between.
+struct EncoderPlan {
+  WorkspacePlan block;  // activations at block.act_base (packed weights are the caller's)
+  size_t off_tok0, off_tok1;
+  size_t total;
+};
+
 int plan_packed(int64_t D, int64_t F, int dtype, PackedPlan* plan);
+
+int plan_encoder(int64_t N, int64_t T, int64_t D, int64_t F, int64_t H, int dtype,
+                 EncoderPlan* plan);
 
 // Returns VITBLK_OK and fills *plan, or an error status.
 int plan_workspace(int64_t N, int64_t T, int64_t D, int64_t F, int64_t H, int dtype,
@@ -70,6 +81,15 @@ int validate_attention(const void* qkv, const void* att, int64_t N, int64_t T, i
 int validate_linear(const void* a, const void* w, const void* bias, const void* residual,
                     const void* out, int64_t M, int64_t K, int64_t Nout, int epilogue,
                     int dtype);
+
+// The encoder stack: L >= 1 packed weight buffers (host array of device
+// pointers), optional per-block parameters (host array of L) and final
+// gain/shift; at least one of out and cls_out.
+int validate_encoder(const void* x, const void* const* packed, const vitblk_affine_params* params,
+                     int64_t L, const void* final_gamma, const void* final_beta,
+                     const void* out, const void* cls_out, int64_t N, int64_t T, int64_t D,
+                     int64_t F, int64_t H, double eps, int dtype, const void* workspace,
+                     size_t workspace_bytes, EncoderPlan* plan);
 
 // The affine variant's parameters (params may be null; so may every member):
 // each present one 16-byte aligned and clear of out ([rows, D]) and of the

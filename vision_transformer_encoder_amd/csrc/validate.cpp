@@ -113,6 +113,26 @@ int plan_workspace(int64_t N, int64_t T, int64_t D, int64_t F, int64_t H, int dt
   return VITBLK_OK;
 }
 
+int plan_encoder(int64_t N, int64_t T, int64_t D, int64_t F, int64_t H, int dtype,
+                 EncoderPlan* plan) {
+  EncoderPlan p;
+  const int st = plan_workspace(N, T, D, F, H, dtype, &p.block);
+  if (st != VITBLK_OK) return st;
+  const size_t es = elem_size(dtype);
+  size_t tok;
+  if (!mul_ok(static_cast<size_t>(N) * static_cast<size_t>(T), static_cast<size_t>(D), &tok) ||
+      !mul_ok(tok, es, &tok))
+    return VITBLK_ERR_UNSUPPORTED;
+  tok = round_up(tok, kRegionAlign);
+  p.block.act_base = 0;
+  p.off_tok0 = p.block.act_total;
+  p.off_tok1 = p.off_tok0 + tok;
+  p.total = p.off_tok1 + tok;
+  if (p.total < p.off_tok1) return VITBLK_ERR_UNSUPPORTED;
+  *plan = p;
+  return VITBLK_OK;
+}
+
 int validate_forward(const void* x, const void* w_q, const void* w_k, const void* w_v,
                      const void* w_o, const void* w_mlp1, const void* w_mlp2,
                      const void* out, int64_t N, int64_t T, int64_t D, int64_t F,
@@ -266,6 +286,54 @@ int validate_linear(const void* a, const void* w, const void* bias, const void* 
   return VITBLK_OK;
 }
 
+int validate_encoder(const void* x, const void* const* packed, const vitblk_affine_params* params,
+                     int64_t L, const void* final_gamma, const void* final_beta,
+                     const void* out, const void* cls_out, int64_t N, int64_t T, int64_t D,
+                     int64_t F, int64_t H, double eps, int dtype, const void* workspace,
+                     size_t workspace_bytes, EncoderPlan* plan) {
+  if (x == nullptr || packed == nullptr || L <= 0) return VITBLK_ERR_INVALID_ARG;
+  if (out == nullptr && cls_out == nullptr) return VITBLK_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(out) || !aligned16(cls_out) || !aligned16(final_gamma) ||
+      !aligned16(final_beta))
+    return VITBLK_ERR_INVALID_ARG;
+  int st = check_eps(eps);
+  if (st != VITBLK_OK) return st;
+  EncoderPlan p;
+  st = plan_encoder(N, T, D, F, H, dtype, &p);
+  if (st != VITBLK_OK) return st;
+  if (workspace == nullptr || !aligned16(workspace)) return VITBLK_ERR_WORKSPACE;
+  if (workspace_bytes < p.total) return VITBLK_ERR_WORKSPACE;
+  const size_t es = elem_size(dtype);
+  const size_t m = static_cast<size_t>(N) * static_cast<size_t>(T);
+  const size_t d = static_cast<size_t>(D) * es;
+  const Span ws = span(workspace, p.total);
+  const Span o = span(out, out != nullptr ? m * d : 0);
+  const Span c = span(cls_out, cls_out != nullptr ? static_cast<size_t>(N) * d : 0);
+  if (overlap(o, c) || overlap(o, ws) || overlap(c, ws)) return VITBLK_ERR_ALIAS;
+  // Read-only inputs against every output and the workspace.
+  auto clear = [&](const void* ptr, size_t bytes) {
+    const Span s = span(ptr, bytes);
+    return !(overlap(s, o) || overlap(s, c) || overlap(s, ws));
+  };
+  if (!clear(x, m * d)) return VITBLK_ERR_ALIAS;
+  if ((final_gamma != nullptr && !clear(final_gamma, d)) ||
+      (final_beta != nullptr && !clear(final_beta, d)))
+    return VITBLK_ERR_ALIAS;
+  for (int64_t l = 0; l < L; ++l) {
+    if (packed[l] == nullptr || !aligned16(packed[l])) return VITBLK_ERR_INVALID_ARG;
+    if (!clear(packed[l], p.block.packed.total)) return VITBLK_ERR_ALIAS;
+    if (params != nullptr) {
+      // The block-level checks against out and the workspace, then cls_out.
+      st = validate_affine_params(&params[l], out, N * T, D, F, dtype, workspace, p.total);
+      if (st != VITBLK_OK) return st;
+      st = validate_affine_params(&params[l], cls_out, N, D, F, dtype, workspace, p.total);
+      if (st != VITBLK_OK) return st;
+    }
+  }
+  if (plan) *plan = p;
+  return VITBLK_OK;
+}
+
 int validate_affine_params(const vitblk_affine_params* params, const void* out, int64_t rows,
                            int64_t D, int64_t F, int dtype, const void* workspace,
                            size_t workspace_bytes) {
@@ -278,7 +346,7 @@ int validate_affine_params(const vitblk_affine_params* params, const void* out, 
                           params->ln2_gamma, params->ln2_beta, params->b_mlp1,
                           params->b_mlp2};
   const size_t bytes[10] = {d, d, d, d, d, d, d, d, f, d};
-  const Span o = span(out, static_cast<size_t>(rows) * d);
+  const Span o = span(out, out != nullptr ? static_cast<size_t>(rows) * d : 0);
   const Span w = span(workspace, workspace_bytes);
   for (int i = 0; i < 10; ++i) {
     if (ptrs[i] == nullptr) continue;
