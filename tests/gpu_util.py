@@ -34,9 +34,18 @@ def violation(gpu, ref):
     return float((err / (1.0 + np.abs(ref))).max()), float(err.mean())
 
 
-def assert_close(gpu, ref, dtype, what=""):
+def assert_close(gpu, ref, dtype, what="", scale=1.0):
+    """Bar: TOL[dtype] * scale (scale > 1 only for stacks of blocks, see stack_scale)."""
     v, mae = violation(gpu, ref)
-    print(f"  {what}: violation {v:.3e} (bar {TOL[dtype]:.0e}), mean abs err {mae:.3e}",
-          flush=True)
-    assert v <= TOL[dtype], f"{what}: violation {v:.3e} > {TOL[dtype]}"
+    bar = TOL[dtype] * scale
+    print(f"  {what}: violation {v:.3e} (bar {bar:.2e}), mean abs err {mae:.3e}", flush=True)
+    assert v <= bar, f"{what}: violation {v:.3e} > {bar}"
     return v, mae
+
+
+def stack_scale(L):
+    """Bar multiplier for L blocks in sequence: each block's rounding error is
+    independent of the others', so in the residual stream they add in
+    quadrature and the one-block bar grows as sqrt(L)."""
+    import math
+    return math.sqrt(L)
