@@ -22,3 +22,4 @@ from .block import (  # noqa: F401
     vit_block,
     vit_block_stages,
 )
+from .embed import patch_embed, patchify  # noqa: F401
