@@ -210,6 +210,35 @@ int vitblk_forward_packed_affine(const void* x, const void* packed,
                                  vitblk_stream_t stream);
 
 /*
+ * The front end: images to the tokens the encoder takes (mlgrind.dev "E2E:
+ * Tiny Vision Transformer", "Architecture": patchify, @ W_patch + b_patch,
+ * prepend the class token, add position embeddings; "Details": patches in
+ * row-major order over the (H/P, W/P) grid, each flattened as (p1, p2, c),
+ * the same map as a stride-P convolution):
+ *
+ *   patches[b, i*(W/P) + j, (p1*P + p2)*C + c] = images[b, c, i*P + p1, j*P + p2]
+ *   tokens[b] = [cls_token ; patches[b] @ w_patch + b_patch] + pos_emb
+ *
+ *   images     [B, C, H, W]; H and W multiples of P
+ *   w_patch    [P*P*C, D] (x @ W orientation)
+ *   b_patch    [D] or NULL; cls_token [D] or NULL (no class token: T = N);
+ *   pos_emb    [T, D] or NULL, T = N + (cls_token != NULL), N = (H/P)(W/P)
+ *   tokens     [B, T, D]; must not overlap an input or the workspace
+ *   workspace  at least vitblk_patch_embed_workspace_bytes() bytes
+ *
+ * Five kernels: W_patch transposed into the workspace (and its padding
+ * zeroed: the patch width is padded to a multiple of 64), the patch matrix,
+ * the embedding GEMM with its bias, the token rows.
+ */
+size_t vitblk_patch_embed_workspace_bytes(int64_t B, int64_t C, int64_t H, int64_t W,
+                                          int64_t P, int64_t D, int dtype);
+
+int vitblk_patch_embed(const void* images, const void* w_patch, const void* b_patch,
+                       const void* cls_token, const void* pos_emb, void* tokens, int64_t B,
+                       int64_t C, int64_t H, int64_t W, int64_t P, int64_t D, int dtype,
+                       void* workspace, size_t workspace_bytes, vitblk_stream_t stream);
+
+/*
  * The encoder stack: L blocks in sequence, each with its own packed weights
  * (and, optionally, its own affine parameters), then a final LayerNorm with
  * its own gain and shift (ai-engineer-exhaustive.pages.dev "ViT Encoder

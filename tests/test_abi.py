@@ -246,6 +246,34 @@ def test_encoder_errors(lib):
     assert enc(params=ctypes.cast(prm, ctypes.POINTER(AP))) == ALIAS
 
 
+def test_patch_embed_errors(lib):
+    B, C, H, W, P, D = 2, 3, 32, 32, 8, 64
+    need = vb.patch_embed_workspace_bytes(B, C, H, W, P, D, 1)
+    r = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    Kp = 192  # 8*8*3 = 192, already a multiple of 64
+    assert need == r(D * Kp * 2) + r(B * 16 * Kp * 2) + r(B * 16 * D * 2)
+    assert vb.patch_embed_workspace_bytes(B, C, 30, W, P, D, 1) == 0   # 30 % 8 != 0
+    # P = 14, C = 3: patch width 588 padded to 640
+    assert vb.patch_embed_workspace_bytes(1, 3, 28, 28, 14, 64, 1) == \
+        r(64 * 640 * 2) + r(4 * 640 * 2) + r(4 * 64 * 2)
+    img, w, out, ws = _addr(0), _addr(1), _addr(2), _addr(20)
+
+    def pe(b=None, cls=None, pos=None, out=out, H=H, ws_bytes=need, dtype=1):
+        return lib.vitblk_patch_embed(img, w, b, cls, pos, out, B, C, H, W, P, D, dtype, ws,
+                                      ws_bytes, None)
+
+    assert pe(H=30) == INVALID
+    assert pe(dtype=4) == INVALID
+    assert pe(ws_bytes=need - 1) == WORKSPACE
+    assert pe(out=None) == INVALID
+    assert pe(b=ctypes.c_void_p(_addr(5).value + 2)) == INVALID
+    assert pe(out=ctypes.c_void_p(img.value + 64)) == ALIAS
+    assert pe(pos=ctypes.c_void_p(out.value)) == ALIAS
+    assert pe(cls=ctypes.c_void_p(ws.value + 512)) == ALIAS
+    assert lib.vitblk_patch_embed(img, None, None, None, None, out, B, C, H, W, P, D, 1, ws,
+                                  need, None) == INVALID
+
+
 def test_python_binding_rejects_unknown_affine_parameter():
     torch = pytest.importorskip("torch")
     x = torch.zeros(1, 2, 8)

@@ -28,6 +28,8 @@ from ._lib import (  # noqa: F401
     pack_weights,
     packed_views,
     packed_weights_bytes,
+    patch_embed,
+    patch_embed_workspace_bytes,
     qkv_projection,
     status_string,
     workspace_bytes,

@@ -47,6 +47,8 @@ SIGNATURES = {
     "vitblk_layernorm_affine": (_I, [_P] * 4 + [_I64, _I64, _D, _I, _P]),
     "vitblk_linear_bias": (_I, [_P] * 5 + [_I64, _I64, _I64, _I, _I, _P]),
     "vitblk_encoder_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64, _I]),
+    "vitblk_patch_embed_workspace_bytes": (_SZ, [_I64] * 6 + [_I]),
+    "vitblk_patch_embed": (_I, [_P] * 6 + [_I64] * 6 + [_I, _P, _SZ, _P]),
     "vitblk_encoder_forward": (_I, [_P, ctypes.POINTER(ctypes.c_void_p), _AP, _I64, _P, _P, _P,
                                     _P] + [_I64] * 5 + [_D, _I, _P, _SZ, _P]),
 }
@@ -191,6 +193,33 @@ def forward_affine(x, w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, num_heads: int, eps: f
                                       workspace.numel() * workspace.element_size(),
                                       _stream(x, stream))
     _check("vitblk_forward_affine", st)
+    return out
+
+
+def patch_embed_workspace_bytes(B, C, H, W, P, D, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    return int(load().vitblk_patch_embed_workspace_bytes(B, C, H, W, P, D, code))
+
+
+def patch_embed(images, w_patch, patch: int, b_patch=None, cls_token=None, pos_emb=None,
+                out=None, workspace=None, stream=None):
+    """Tokens [B, N (+1), D] from images [B, C, H, W] (see vitblk_patch_embed)."""
+    torch = _torch()
+    _dev(images, w_patch, b_patch, cls_token, pos_emb, out)
+    B, C, H, W = images.shape
+    D = w_patch.shape[1]
+    code = dtype_code(images.dtype)
+    T = (H // patch) * (W // patch) + (1 if cls_token is not None else 0)
+    if out is None:
+        out = torch.empty((B, T, D), dtype=images.dtype, device=images.device)
+    need = patch_embed_workspace_bytes(B, C, H, W, patch, D, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=images.device)
+    st = load().vitblk_patch_embed(_ptr(images), _ptr(w_patch), _ptr(b_patch), _ptr(cls_token),
+                                   _ptr(pos_emb), _ptr(out), B, C, H, W, patch, D, code,
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(images, stream))
+    _check("vitblk_patch_embed", st)
     return out
 
 

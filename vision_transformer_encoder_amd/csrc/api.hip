@@ -127,6 +127,44 @@ int run_encoder(const void* x, const void* const* packed, const vitblk_affine_pa
 
 extern "C" {
 
+size_t vitblk_patch_embed_workspace_bytes(int64_t B, int64_t C, int64_t H, int64_t W,
+                                          int64_t P, int64_t D, int dtype) {
+  EmbedPlan p;
+  if (plan_embed(B, C, H, W, P, D, dtype, &p) != VITBLK_OK) return 0;
+  return p.total;
+}
+
+int vitblk_patch_embed(const void* images, const void* w_patch, const void* b_patch,
+                       const void* cls_token, const void* pos_emb, void* tokens, int64_t B,
+                       int64_t C, int64_t H, int64_t W, int64_t P, int64_t D, int dtype,
+                       void* workspace, size_t workspace_bytes, vitblk_stream_t stream) {
+  EmbedPlan pl;
+  const int st = validate_patch_embed(images, w_patch, b_patch, cls_token, pos_emb, tokens, B, C,
+                                      H, W, P, D, dtype, workspace, workspace_bytes, &pl);
+  if (st != VITBLK_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  PatchEmbedArgs a{};
+  a.images = images;
+  a.w_patch = w_patch;
+  a.b_patch = b_patch;
+  a.cls = cls_token;
+  a.pos = pos_emb;
+  a.tokens = tokens;
+  a.w_t = ws + pl.off_wt;
+  a.patches = ws + pl.off_patches;
+  a.embedded = ws + pl.off_embedded;
+  a.B = B;
+  a.C = C;
+  a.H = H;
+  a.W = W;
+  a.P = P;
+  a.D = D;
+  a.Kp = pl.Kp;
+  a.dtype = dtype;
+  VITBLK_LAUNCH(launch_patch_embed(a, reinterpret_cast<hipStream_t>(stream)));
+  return VITBLK_OK;
+}
+
 size_t vitblk_encoder_workspace_bytes(int64_t N, int64_t T, int64_t D, int64_t F, int64_t H,
                                       int dtype) {
   EncoderPlan p;

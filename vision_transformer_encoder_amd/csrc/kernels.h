@@ -49,6 +49,24 @@ hipError_t launch_layernorm(const void* x, int64_t ld_in, const void* gamma, con
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
 
+// The front end: images [B, C, H, W] -> tokens [B, N (+1), D] (patch matrix,
+// embedding GEMM, token assembly); w_t, patches and embedded are workspace.
+struct PatchEmbedArgs {
+  const void* images;
+  const void* w_patch;  // [P*P*C, D]
+  const void* b_patch;  // [D] or null
+  const void* cls;      // [D] or null
+  const void* pos;      // [N (+1), D] or null
+  void* tokens;         // [B, N (+1), D]
+  void* w_t;            // [D, Kp]
+  void* patches;        // [B*N, Kp]
+  void* embedded;       // [B*N, D]
+  int64_t B, C, H, W, P, D, Kp;
+  int dtype;
+};
+
+hipError_t launch_patch_embed(const PatchEmbedArgs& p, hipStream_t stream);
+
 // Transpose up to 6 weights in one launch.
 hipError_t launch_pack(const PackJob* jobs, int njobs, int dtype, hipStream_t stream);
 

@@ -1,0 +1,143 @@
+// The ViT front end: patch extraction and token assembly around one GEMM
+// (mlgrind.dev "E2E: Tiny Vision Transformer", "Architecture": patchify,
+// @ W_patch + b_patch, prepend the class token, add position embeddings;
+// "Details": patches row-major over the (H/P, W/P) grid, each flattened as
+// (p1, p2, c)).
+//
+// patchify_kernel writes the patches as GEMM rows [B*N, Kp] (Kp = P*P*C
+// rounded up to 64 with zero columns, so the MFMA GEMM's k-slices tile it);
+// the GEMM (bias epilogue) then embeds them into [B*N, D]; tokens_kernel
+// writes the sequences [B, N (+1), D]: the class token (if any) as token 0,
+// then the embedded patches, each plus its position embedding (if any).
+// All three are HBM-bound except the GEMM (MFMA).
+#include "device.h"
+#include "kernels.h"
+#include "vitblk.h"
+
+namespace vitblk {
+namespace {
+
+// One thread per element of the patch matrix: a[row][k], row = b * N + cell,
+// k = (p1 * P + p2) * C + c (< K) or a zero pad column (K <= k < Kp).
+// Consecutive threads write consecutive k; their reads fall in C image rows
+// of P consecutive pixels each.
+template <typename T>
+__global__ __launch_bounds__(256) void patchify_kernel(const T* __restrict__ x,
+                                                       T* __restrict__ a, int64_t total,
+                                                       int C, int H, int W, int P, int K,
+                                                       int Kp) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= total) return;
+  const int64_t row = e / Kp;
+  const int k = static_cast<int>(e - row * Kp);
+  T v = T(0);
+  if (k < K) {
+    const int gw = W / P, cells = (H / P) * gw;
+    const int64_t b = row / cells;
+    const int cell = static_cast<int>(row - b * cells);
+    const int gi = cell / gw, gj = cell - gi * gw;
+    const int c = k % C, pix = k / C;
+    const int p1 = pix / P, p2 = pix - p1 * P;
+    v = x[((b * C + c) * H + gi * P + p1) * static_cast<int64_t>(W) + gj * P + p2];
+  }
+  a[e] = v;
+}
+
+// Zero columns [K, Kp) of every row of w_t [rows, Kp] (the packed weight's
+// padding; the pack kernel writes columns [0, K)).
+template <typename T>
+__global__ __launch_bounds__(256) void zero_pad_kernel(T* __restrict__ w, int64_t rows, int K,
+                                                       int Kp) {
+  const int pad = Kp - K;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= rows * pad) return;
+  const int64_t r = e / pad;
+  w[r * Kp + K + (e - r * pad)] = T(0);
+}
+
+// Token rows: out[b, t, :] = (t < HC ? cls : emb[b * N + t - HC]) + pos[t], for
+// VEC consecutive features per thread (VEC = 8 needs D % 8 == 0).
+template <typename T, int VEC>
+__global__ __launch_bounds__(256) void tokens_kernel(const T* __restrict__ emb,
+                                                     const T* __restrict__ cls,
+                                                     const T* __restrict__ pos,
+                                                     T* __restrict__ out, int64_t B, int N,
+                                                     int HC, int D) {
+  const int Tn = N + HC;
+  const int per_row = D / VEC;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= B * Tn * per_row) return;
+  const int64_t row = e / per_row;
+  const int d0 = static_cast<int>(e - row * per_row) * VEC;
+  const int64_t b = row / Tn;
+  const int t = static_cast<int>(row - b * Tn);
+  const T* src = t < HC ? cls + d0 : emb + (b * N + t - HC) * D + d0;
+  float v[VEC];
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) v[i] = load_f32(src + i);
+  if (pos != nullptr) {
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) v[i] += load_f32(pos + static_cast<int64_t>(t) * D + d0 + i);
+  }
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) store_f32(out + row * D + d0 + i, v[i]);
+}
+
+unsigned blocks_for(int64_t n) { return static_cast<unsigned>((n + 255) / 256); }
+
+template <typename T>
+hipError_t launch_typed(const PatchEmbedArgs& p, hipStream_t s) {
+  const int K = static_cast<int>(p.P * p.P * p.C), Kp = static_cast<int>(p.Kp);
+  const int N = static_cast<int>((p.H / p.P) * (p.W / p.P));
+  const int64_t rows = p.B * N;
+  // W_patch [K, D] -> out-major [D, Kp], pad columns zero.
+  const PackJob job{p.w_patch, K, p.D, p.w_t, Kp};
+  hipError_t e = launch_pack(&job, 1, p.dtype, s);
+  if (e != hipSuccess) return e;
+  if (Kp > K) {
+    hipLaunchKernelGGL(zero_pad_kernel<T>, dim3(blocks_for(p.D * (Kp - K))), dim3(256), 0, s,
+                       static_cast<T*>(p.w_t), p.D, K, Kp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(patchify_kernel<T>, dim3(blocks_for(rows * Kp)), dim3(256), 0, s,
+                     static_cast<const T*>(p.images), static_cast<T*>(p.patches), rows * Kp,
+                     static_cast<int>(p.C), static_cast<int>(p.H), static_cast<int>(p.W),
+                     static_cast<int>(p.P), K, Kp);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  GemmProblem g{};
+  g.M = rows;
+  g.N = p.D;
+  g.K = Kp;
+  g.A = p.patches;
+  g.lda = Kp;
+  g.B = p.w_t;
+  g.ldb = Kp;
+  g.C = p.embedded;
+  g.ldc = p.D;
+  g.epi = VITBLK_EPI_NONE;
+  g.dtype = p.dtype;
+  g.bias[0] = p.b_patch;
+  g.bias_seg = p.D;
+  if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+  const int HC = p.cls != nullptr ? 1 : 0;
+  const int64_t toks = p.B * (N + HC);
+  if (p.D % 8 == 0)
+    hipLaunchKernelGGL((tokens_kernel<T, 8>), dim3(blocks_for(toks * (p.D / 8))), dim3(256), 0,
+                       s, static_cast<const T*>(p.embedded), static_cast<const T*>(p.cls),
+                       static_cast<const T*>(p.pos), static_cast<T*>(p.tokens), p.B, N, HC,
+                       static_cast<int>(p.D));
+  else
+    hipLaunchKernelGGL((tokens_kernel<T, 1>), dim3(blocks_for(toks * p.D)), dim3(256), 0, s,
+                       static_cast<const T*>(p.embedded), static_cast<const T*>(p.cls),
+                       static_cast<const T*>(p.pos), static_cast<T*>(p.tokens), p.B, N, HC,
+                       static_cast<int>(p.D));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_patch_embed(const PatchEmbedArgs& p, hipStream_t s) {
+  return p.dtype == VITBLK_BF16 ? launch_typed<bf16_t>(p, s) : launch_typed<float>(p, s);
+}
+
+}  // namespace vitblk

@@ -43,6 +43,23 @@ struct EncoderPlan {
   size_t total;
 };
 
+// Front-end workspace: packed W_patch^T [D, Kp], the patch matrix [B*N, Kp]
+// and the embedded patches [B*N, D] (Kp = P*P*C rounded up to 64).
+struct EmbedPlan {
+  int64_t N, Kp;  // patches per image, padded patch width
+  size_t off_wt, off_patches, off_embedded;
+  size_t total;
+};
+
+int plan_embed(int64_t B, int64_t C, int64_t H, int64_t W, int64_t P, int64_t D, int dtype,
+               EmbedPlan* plan);
+
+int validate_patch_embed(const void* images, const void* w_patch, const void* b_patch,
+                         const void* cls_token, const void* pos_emb, const void* tokens,
+                         int64_t B, int64_t C, int64_t H, int64_t W, int64_t P, int64_t D,
+                         int dtype, const void* workspace, size_t workspace_bytes,
+                         EmbedPlan* plan);
+
 int plan_packed(int64_t D, int64_t F, int dtype, PackedPlan* plan);
 
 int plan_encoder(int64_t N, int64_t T, int64_t D, int64_t F, int64_t H, int dtype,

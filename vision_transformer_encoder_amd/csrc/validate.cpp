@@ -113,6 +113,69 @@ int plan_workspace(int64_t N, int64_t T, int64_t D, int64_t F, int64_t H, int dt
   return VITBLK_OK;
 }
 
+int plan_embed(int64_t B, int64_t C, int64_t H, int64_t W, int64_t P, int64_t D, int dtype,
+               EmbedPlan* plan) {
+  if (!dim_ok(B) || !dim_ok(C) || !dim_ok(H) || !dim_ok(W) || !dim_ok(P) || !dim_ok(D))
+    return VITBLK_ERR_INVALID_ARG;
+  if (H % P != 0 || W % P != 0) return VITBLK_ERR_INVALID_ARG;
+  const size_t es = elem_size(dtype);
+  if (es == 0) return VITBLK_ERR_INVALID_ARG;
+  if (B > kMaxDim || C > kMaxDim || H > kMaxDim || W > kMaxDim || D > kMaxDim)
+    return VITBLK_ERR_UNSUPPORTED;
+  EmbedPlan p;
+  p.N = (H / P) * (W / P);
+  const int64_t K = P * P * C;  // P <= H, C, H < 2^31: may overflow only via P * P * C
+  if (P > 65536 || K > kMaxDim / 2) return VITBLK_ERR_UNSUPPORTED;
+  p.Kp = (K + 63) / 64 * 64;
+  if (B * C > kMaxDim || B * (p.N + 1) > kMaxDim || (p.N + 1) > kMaxDim) return VITBLK_ERR_UNSUPPORTED;
+  const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(p.N);
+  size_t wt, pa, em;
+  if (!mul_ok(static_cast<size_t>(D), static_cast<size_t>(p.Kp) * es, &wt) ||
+      !mul_ok(rows, static_cast<size_t>(p.Kp) * es, &pa) ||
+      !mul_ok(rows, static_cast<size_t>(D) * es, &em))
+    return VITBLK_ERR_UNSUPPORTED;
+  if (rows * static_cast<size_t>(p.Kp) > static_cast<size_t>(kMaxDim) * 64)
+    return VITBLK_ERR_UNSUPPORTED;
+  p.off_wt = 0;
+  p.off_patches = round_up(wt, kRegionAlign);
+  p.off_embedded = p.off_patches + round_up(pa, kRegionAlign);
+  p.total = p.off_embedded + round_up(em, kRegionAlign);
+  *plan = p;
+  return VITBLK_OK;
+}
+
+int validate_patch_embed(const void* images, const void* w_patch, const void* b_patch,
+                         const void* cls_token, const void* pos_emb, const void* tokens,
+                         int64_t B, int64_t C, int64_t H, int64_t W, int64_t P, int64_t D,
+                         int dtype, const void* workspace, size_t workspace_bytes,
+                         EmbedPlan* plan) {
+  if (images == nullptr || w_patch == nullptr || tokens == nullptr) return VITBLK_ERR_INVALID_ARG;
+  if (!aligned16(images) || !aligned16(w_patch) || !aligned16(tokens) || !aligned16(b_patch) ||
+      !aligned16(cls_token) || !aligned16(pos_emb))
+    return VITBLK_ERR_INVALID_ARG;
+  EmbedPlan p;
+  int st = plan_embed(B, C, H, W, P, D, dtype, &p);
+  if (st != VITBLK_OK) return st;
+  if (workspace == nullptr || !aligned16(workspace)) return VITBLK_ERR_WORKSPACE;
+  if (workspace_bytes < p.total) return VITBLK_ERR_WORKSPACE;
+  const size_t es = elem_size(dtype);
+  const size_t d = static_cast<size_t>(D) * es;
+  const size_t t = static_cast<size_t>(p.N + (cls_token != nullptr ? 1 : 0));
+  const Span o = span(tokens, static_cast<size_t>(B) * t * d);
+  const Span ws = span(workspace, p.total);
+  if (overlap(o, ws)) return VITBLK_ERR_ALIAS;
+  const void* ins[5] = {images, w_patch, b_patch, cls_token, pos_emb};
+  const size_t bytes[5] = {static_cast<size_t>(B) * C * H * W * es,
+                           static_cast<size_t>(P) * P * C * d, d, d, t * d};
+  for (int i = 0; i < 5; ++i) {
+    if (ins[i] == nullptr) continue;
+    const Span s = span(ins[i], bytes[i]);
+    if (overlap(s, o) || overlap(s, ws)) return VITBLK_ERR_ALIAS;
+  }
+  if (plan) *plan = p;
+  return VITBLK_OK;
+}
+
 int plan_encoder(int64_t N, int64_t T, int64_t D, int64_t F, int64_t H, int dtype,
                  EncoderPlan* plan) {
   EncoderPlan p;
