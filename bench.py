@@ -1,7 +1,7 @@
 """Throughput of one pre-LN ViT encoder block forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload vit_l16]
-                    [--variant plain|affine|encoder] [--layers L]
+                    [--variant plain|affine|encoder|embed] [--layers L]
 
 A step is one full block forward (8 kernels through vitblk_forward: weight packing
 and the seven steps of the block) over one
@@ -15,7 +15,10 @@ cores (cpu_baseline).  ``--variant affine`` times the affine block instead
 (LayerNorm gains and shifts, projection biases: vitblk_forward_affine);
 ``--variant encoder`` times the encoder stack (L affine blocks on pre-packed
 weights, the final LayerNorm of every token and of the class tokens:
-vitblk_encoder_forward), L = the model's depth unless --layers is given.
+vitblk_encoder_forward), L = the model's depth unless --layers is given;
+``--variant embed`` times the front end (vitblk_patch_embed: N images of
+(sqrt(T-1) * P)^2 pixels, 3 channels, P = 16 for ViT-B/L and 14 for ViT-H,
+with class token and position embeddings) and reports tokens/s out of it.
 """
 
 from __future__ import annotations
@@ -80,8 +83,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target host time for the oracle baseline sample (0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--variant", choices=["plain", "affine", "encoder"], default="plain",
-                    help="plain block (default), the affine variant, or the encoder stack")
+    ap.add_argument("--variant", choices=["plain", "affine", "encoder", "embed"],
+                    default="plain",
+                    help="plain block (default), the affine variant, the encoder stack, or "
+                         "the front end")
     ap.add_argument("--layers", type=int, default=0,
                     help="encoder depth (default: 12 / 24 / 32 for ViT-B / L / H)")
     ap.add_argument("--profile-step", default=None,
@@ -140,6 +145,84 @@ def cpu_baseline(ref_fn, w, target_s, got_out, layers=1):
              "mean_abs_err": float(err.mean()), "sequences": len(seqs)})
 
 
+def bench_embed(a, w, torch, vb):
+    """The front end alone: images -> tokens (vitblk_patch_embed)."""
+    from vision_transformer_encoder_amd.inputs import round_to
+    import oracle
+    P = 14 if w.name == "vit_h14" else 16
+    side = int(round(math.sqrt(w.T - 1))) * P
+    B, C, D = w.N, 3, w.D
+    K = P * P * C
+    rng = np.random.default_rng([a.seed, 3])
+    img = round_to(rng.standard_normal((B, C, side, side)), w.dtype)
+    wp = round_to(rng.standard_normal((K, D)) / math.sqrt(K), w.dtype)
+    bp = round_to(0.1 * rng.standard_normal(D), w.dtype)
+    cls = round_to(0.02 * rng.standard_normal(D), w.dtype)
+    pos = round_to(0.02 * rng.standard_normal((w.T, D)), w.dtype)
+    tdt = {"fp32": torch.float32, "bf16": torch.bfloat16}[w.dtype]
+    dev = torch.device("cuda:0")
+    to_g = lambda v: torch.from_numpy(v.astype(np.float32)).to(dev, tdt)  # noqa: E731
+    gi, gw, gb, gc, gpos = map(to_g, (img, wp, bp, cls, pos))
+    out = torch.empty((B, w.T, D), dtype=tdt, device=dev)
+    ws = torch.empty(vb.patch_embed_workspace_bytes(B, C, side, side, P, D, tdt),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        vb.patch_embed(gi, gw, P, gb, gc, gpos, out=out, workspace=ws)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(s)
+    for _ in range(a.steps):
+        step()
+    e1.record(s)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / a.steps
+    got = out.to("cpu", torch.float64).numpy()
+    # The embedding GEMM alone, on the same shapes: the dominant kernel.
+    Kp = (K + 63) // 64 * 64
+    pm = torch.zeros((B * (w.T - 1), Kp), dtype=tdt, device=dev)
+    wt = torch.zeros((D, Kp), dtype=tdt, device=dev)
+    emb = torch.empty((B * (w.T - 1), D), dtype=tdt, device=dev)
+    gemm = lambda: vb.linear(pm, wt, vb.EPI_NONE, bias=gb, out=emb)  # noqa: E731
+    gms = time_launches(gemm, a.kernel_reps, torch)
+    gflop = 2 * B * (w.T - 1) * Kp * D
+    es = 2 if w.dtype == "bf16" else 4
+    io_bytes = (B * C * side * side + K * D + B * w.T * D) * es
+    ach = gflop / (gms * 1e-3) / 1e12
+    res = {
+        "metric": f"front-end (patch embedding) tokens/sec, {w.name} shape N={w.N}",
+        "value": round(B * w.T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) pixels, N(0,1/fan_in) W_patch)",
+        "config": {"workload": w.name, "images": B, "image_side": side, "channels": C,
+                   "patch": P, "D": D, "tokens_per_image": w.T, "variant": "embed"},
+        "wall_s_timed": round(t_wall, 3),
+        "io_gbs": round(io_bytes / (ms * 1e-3) / 1e9, 1),
+        "kernels": {"embed_gemm": {"ms": round(gms, 5), "bound": "mfma",
+                                   "tflops": round(ach, 2)}},
+        "roofline": {"kernel": "embed_gemm", "bound": "mfma", "achieved": round(ach, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "work_per_launch": f"{gflop / 1e9:.2f} GFLOP"},
+    }
+    if a.cpu_seconds > 0:
+        def ref_fn(seqs):
+            return oracle.patch_embed(img[seqs], wp, P, bp, cls, pos)
+        cb, par = cpu_baseline(ref_fn, w, a.cpu_seconds, got)
+        res["cpu_baseline"] = cb
+        res["parity"] = par
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -156,6 +239,9 @@ def main():
     if a.profile_step:  # counters only: one untimed block, then the step alone
         a.warmup, a.steps, a.cpu_seconds = 0, 1, 0
     w = WORKLOADS[a.workload]
+    if a.variant == "embed":
+        torch.cuda.set_device(torch.device("cuda:0"))
+        return bench_embed(a, w, torch, vb)
     tdt = {"fp32": torch.float32, "bf16": torch.bfloat16}[w.dtype]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

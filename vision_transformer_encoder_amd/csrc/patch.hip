@@ -17,30 +17,45 @@
 namespace vitblk {
 namespace {
 
-// One thread per element of the patch matrix: a[row][k], row = b * N + cell,
-// k = (p1 * P + p2) * C + c (< K) or a zero pad column (K <= k < Kp).
-// Consecutive threads write consecutive k; their reads fall in C image rows
-// of P consecutive pixels each.
+// Patch matrix a[row][k], row = b * N + cell, k = (p1 * P + p2) * C + c
+// (< K) or a zero pad column (K <= k < Kp).  Each thread writes VEC = 16 /
+// sizeof(T) consecutive k as one 16-byte store (Kp is a multiple of 64);
+// it decodes (p1, p2, c) of its first k once and steps through the rest.
+// Its reads fall in at most two image rows per channel, which the
+// neighbouring threads of the same patch row also read (cache hits).
 template <typename T>
 __global__ __launch_bounds__(256) void patchify_kernel(const T* __restrict__ x,
-                                                       T* __restrict__ a, int64_t total,
+                                                       T* __restrict__ a, int64_t total_vec,
                                                        int C, int H, int W, int P, int K,
                                                        int Kp) {
+  constexpr int VEC = 16 / sizeof(T);
   const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (e >= total) return;
-  const int64_t row = e / Kp;
-  const int k = static_cast<int>(e - row * Kp);
-  T v = T(0);
-  if (k < K) {
-    const int gw = W / P, cells = (H / P) * gw;
-    const int64_t b = row / cells;
-    const int cell = static_cast<int>(row - b * cells);
-    const int gi = cell / gw, gj = cell - gi * gw;
-    const int c = k % C, pix = k / C;
-    const int p1 = pix / P, p2 = pix - p1 * P;
-    v = x[((b * C + c) * H + gi * P + p1) * static_cast<int64_t>(W) + gj * P + p2];
+  if (e >= total_vec) return;
+  const int vpr = Kp / VEC;  // vectors per row
+  const int64_t row = e / vpr;
+  const int k0 = static_cast<int>(e - row * vpr) * VEC;
+  const int gw = W / P, cells = (H / P) * gw;
+  const int64_t b = row / cells;
+  const int cell = static_cast<int>(row - b * cells);
+  const int gi = cell / gw, gj = cell - gi * gw;
+  // pixel (p1, p2) of channel c of this patch: x + ((b*C + c)*H + gi*P + p1)*W + gj*P + p2
+  const T* base = x + (b * C * H + static_cast<int64_t>(gi) * P) * W + static_cast<int64_t>(gj) * P;
+  const int64_t plane = static_cast<int64_t>(H) * W;
+  int c = k0 % C, pix = k0 / C;
+  int p1 = pix / P, p2 = pix - p1 * P;
+  T v[VEC];
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) {
+    v[i] = (k0 + i < K) ? base[c * plane + static_cast<int64_t>(p1) * W + p2] : T(0);
+    if (++c == C) {
+      c = 0;
+      if (++p2 == P) {
+        p2 = 0;
+        ++p1;
+      }
+    }
   }
-  a[e] = v;
+  *reinterpret_cast<uint4*>(a + row * Kp + k0) = *reinterpret_cast<const uint4*>(v);
 }
 
 // Zero columns [K, Kp) of every row of w_t [rows, Kp] (the packed weight's
@@ -99,8 +114,10 @@ hipError_t launch_typed(const PatchEmbedArgs& p, hipStream_t s) {
                        static_cast<T*>(p.w_t), p.D, K, Kp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(patchify_kernel<T>, dim3(blocks_for(rows * Kp)), dim3(256), 0, s,
-                     static_cast<const T*>(p.images), static_cast<T*>(p.patches), rows * Kp,
+  constexpr int VEC = 16 / sizeof(T);
+  hipLaunchKernelGGL(patchify_kernel<T>, dim3(blocks_for(rows * Kp / VEC)), dim3(256), 0, s,
+                     static_cast<const T*>(p.images), static_cast<T*>(p.patches),
+                     rows * Kp / VEC,
                      static_cast<int>(p.C), static_cast<int>(p.H), static_cast<int>(p.W),
                      static_cast<int>(p.P), K, Kp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
