@@ -23,3 +23,12 @@ from .block import (  # noqa: F401
     vit_block_stages,
 )
 from .embed import patch_embed, patchify  # noqa: F401
+from .backward import (  # noqa: F401
+    GRAD_KEYS,
+    attention_backward,
+    gelu_tanh_grad,
+    layer_norm_backward,
+    softmax_backward,
+    vit_block_backward,
+    vit_block_backward_stages,
+)
