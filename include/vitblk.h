@@ -77,7 +77,9 @@ typedef enum {
 typedef enum {
   VITBLK_EPI_NONE = 0,     /* out = a @ w                      */
   VITBLK_EPI_RESIDUAL = 1, /* out = residual + a @ w           */
-  VITBLK_EPI_GELU = 2      /* out = GELU_tanh(a @ w)           */
+  VITBLK_EPI_GELU = 2,     /* out = GELU_tanh(a @ w)           */
+  VITBLK_EPI_GELU_GRAD = 3 /* out = (a @ w) * GELU_tanh'(residual): the
+                              MLP's backward through the activation */
 } vitblk_epilogue;
 
 /* Human-readable name of a vitblk_status value (static storage; never NULL). */
@@ -313,7 +315,8 @@ int vitblk_attention(const void* qkv, void* att, int64_t N, int64_t T, int64_t D
 /* out = epilogue(a @ W) with the weight given out-major: a [M, K],
  * w_t [Nout, K] (row n = column n of the (in, out) weight W, as in the
  * packed regions), out [M, Nout]; residual [M, Nout] is read only for
- * VITBLK_EPI_RESIDUAL (may be NULL otherwise).  Covers the output projection
+ * VITBLK_EPI_RESIDUAL and VITBLK_EPI_GELU_GRAD (there it holds the GELU's
+ * input z; may be NULL otherwise).  Covers the output projection
  * + first residual, MLP1 + GELU and MLP2 + second residual
  * (crackedaicode.com "ViT Encoder Block", "Multi-head attention" and
  * "Feed-forward stage").  out must not overlap a, w_t or residual. */
@@ -329,6 +332,89 @@ int vitblk_linear(const void* a, const void* w_t, const void* residual, void* ou
 int vitblk_linear_bias(const void* a, const void* w_t, const void* bias, const void* residual,
                        void* out, int64_t M, int64_t K, int64_t Nout, int epilogue, int dtype,
                        vitblk_stream_t stream);
+
+/*
+ * ------------------------------------------------------------------------
+ * Backward pass of the plain block (training; the gradients autograd would
+ * produce: nipunbatra.github.io vision1 transcript, Page 88 -- backward()
+ * fills dL/dtheta for every block -- and Page 113, one training step;
+ * mlgrind.dev "E2E: Tiny Vision Transformer", "Method contract": every
+ * parameter is trained).
+ *
+ * Given dout = dL/d(out) for out = block(x) (the plain block above), write
+ *   dx      = dL/dx                                  [N, T, D]
+ *   dw_q, dw_k, dw_v, dw_o = dL/dw_*                 [D, D]
+ *   dw_mlp1 = dL/dw_mlp1 [D, F],  dw_mlp2 = dL/dw_mlp2 [F, D]
+ * i.e. the exact derivative of the forward definition (the vector-Jacobian
+ * product with dout).  The weight gradients are written, not accumulated:
+ * each is the sum over all N*T tokens of the call.
+ *
+ * The forward activations are recomputed inside the call (x and the weights
+ * are all it needs), then the steps are walked in reverse:
+ *   dW2 = h^T dout;  dz = (dout W2^T) * GELU'(z);  dW1 = yn^T dz;
+ *   dy  = dout + LN'(y)^T (dz W1^T);  dWo = att^T dy;  datt = dy Wo^T;
+ *   dq, dk, dv = attention backward (softmax gradient per head);
+ *   dWq|dWk|dWv = xn^T [dq|dk|dv];  dx = dy + LN'(x)^T ([dq|dk|dv] [Wq|Wk|Wv]^T)
+ * with h = GELU(z), z = yn W1, yn = LN(y), att the concatenated heads.
+ *
+ * Precision: as in the forward (bf16 operands and stored intermediates, fp32
+ * accumulation and statistics); the weight gradients are reduced in fp32 and
+ * rounded once.  Arguments: as vitblk_forward, plus dout [N, T, D] (input)
+ * and the seven outputs, which must not overlap each other, an input or the
+ * workspace.  workspace: at least vitblk_backward_workspace_bytes() bytes
+ * (the forward's packed weights and activations, the concatenated
+ * [w_q | w_k | w_v], the gradient buffers and the fp32 partial sums of the
+ * weight gradients; about 1.8 GB for ViT-L/16 with N = 256 in bf16).
+ */
+size_t vitblk_backward_workspace_bytes(int64_t N, int64_t T, int64_t D, int64_t F, int64_t H,
+                                       int dtype);
+
+int vitblk_backward(const void* x, const void* w_q, const void* w_k, const void* w_v,
+                    const void* w_o, const void* w_mlp1, const void* w_mlp2, const void* dout,
+                    void* dx, void* dw_q, void* dw_k, void* dw_v, void* dw_o, void* dw_mlp1,
+                    void* dw_mlp2, int64_t N, int64_t T, int64_t D, int64_t F, int64_t H,
+                    double eps, int dtype, void* workspace, size_t workspace_bytes,
+                    vitblk_stream_t stream);
+
+/* The backward's steps, one call each (same kernels as vitblk_backward). */
+
+/* Weight gradient of a projection: out[i, j] = sum_m a[m, i] * b[m, j] over
+ * the M token rows, i.e. out = a^T b with a [M, I] (the projection's input)
+ * and b [M, J] (the gradient of its output); out [I, J].  Reduced in fp32
+ * (split over the token rows into fp32 partial sums held in the workspace,
+ * then summed in a fixed order: deterministic) and rounded once.  workspace:
+ * at least vitblk_weight_grad_workspace_bytes(M, I, J) bytes.  out must not
+ * overlap a, b or the workspace. */
+size_t vitblk_weight_grad_workspace_bytes(int64_t M, int64_t I, int64_t J);
+
+int vitblk_weight_grad(const void* a, const void* b, void* out, int64_t M, int64_t I, int64_t J,
+                       int dtype, void* workspace, size_t workspace_bytes,
+                       vitblk_stream_t stream);
+
+/* Backward of LN (as in vitblk_layernorm: no gain or shift) plus a residual
+ * gradient: dx[r, :] = residual[r, :] + J_r^T g[r, :], where J_r is the
+ * Jacobian of LN at x[r, :], i.e.
+ *   dx = residual + rstd * (g - mean(g) - xhat * mean(g * xhat)),
+ *   xhat = (x - mean(x)) * rstd, rstd = 1 / sqrt(var(x) + eps).
+ * x, g, dx [rows, D]; residual [rows, D] or NULL (zero).  dx must not
+ * overlap x, g or residual. */
+int vitblk_layernorm_backward(const void* x, const void* g, const void* residual, void* dx,
+                              int64_t rows, int64_t D, double eps, int dtype,
+                              vitblk_stream_t stream);
+
+/* Backward of vitblk_attention: given qkv [N*T, 3D] (the forward's input)
+ * and datt = dL/d(att) [N*T, D], write dqkv [N*T, 3D] = [dQ | dK | dV] with,
+ * per sequence and head, P = softmax(Q_h K_h^T / sqrt(dh)),
+ *   dV_h = P^T dO_h,  dS = P * (dO_h V_h^T - rowsum(P * dO_h V_h^T)),
+ *   dQ_h = dS K_h / sqrt(dh),  dK_h = dS^T Q_h / sqrt(dh).
+ * workspace: at least vitblk_attention_backward_workspace_bytes() bytes
+ * (per-query softmax statistics).  dqkv must not overlap qkv, datt or the
+ * workspace. */
+size_t vitblk_attention_backward_workspace_bytes(int64_t N, int64_t T, int64_t D, int64_t H);
+
+int vitblk_attention_backward(const void* qkv, const void* datt, void* dqkv, int64_t N, int64_t T,
+                              int64_t D, int64_t H, int dtype, void* workspace,
+                              size_t workspace_bytes, vitblk_stream_t stream);
 
 #ifdef __cplusplus
 }

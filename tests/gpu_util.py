@@ -49,3 +49,30 @@ def stack_scale(L):
     quadrature and the one-block bar grows as sqrt(L)."""
     import math
     return math.sqrt(L)
+
+
+def grad_violation(gpu, ref):
+    """max |g - o| / (rms(o) + |o|), and the mean absolute error."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    if not np.all(np.isfinite(gpu)):
+        return float("inf"), float("inf")
+    rms = float(np.sqrt(np.mean(ref * ref))) or 1.0
+    err = np.abs(gpu - ref)
+    return float((err / (rms + np.abs(ref))).max()), float(err.mean())
+
+
+def assert_close_grad(gpu, ref, dtype, what=""):
+    """Gradient bar: TOL[dtype] * (rms(o) + |o|).
+
+    A gradient has no unit scale of its own (a weight gradient is a sum over
+    every token of the batch), so the forward bar's "1 +" -- the block
+    output's unit scale -- becomes the RMS of the oracle's tensor: the bar is
+    the forward's relative bar measured in the tensor's own units.
+    """
+    v, mae = grad_violation(gpu, ref)
+    bar = TOL[dtype]
+    print(f"  {what}: violation {v:.3e} (bar {bar:.2e}), mean abs err {mae:.3e}", flush=True)
+    assert v <= bar, f"{what}: violation {v:.3e} > {bar}"
+    return v, mae

@@ -288,3 +288,113 @@ def test_python_binding_rejects_cpu_tensors():
     w = torch.zeros(8, 8)
     with pytest.raises(ValueError):
         vb.forward(x, w, w, w, w, w, w, 2, 1e-6)
+
+
+# ------------------------------------------------------------------ backward
+
+def _bwd(lib, N=2, T=5, D=16, F=32, H=2, eps=1e-6, dtype=1, ptrs=None, ws=None, ws_bytes=None):
+    """vitblk_backward with fake pointers: 8 inputs (x, six weights, dout), then 7 gradients."""
+    p = [_addr(i) for i in range(15)] if ptrs is None else ptrs
+    if ws is None:
+        ws = _addr(40)
+    if ws_bytes is None:
+        ws_bytes = max(vb.backward_workspace_bytes(max(N, 1), max(T, 1), max(D, 1), max(F, 1),
+                                                   max(H, 1), 1), 1 << 20)
+    return lib.vitblk_backward(*p, N, T, D, F, H, eps, dtype, ws, ws_bytes, None)
+
+
+def _split(M, I, J):
+    tiles = -(-I // 256) * -(-J // 256)
+    return max(1, min(256 // tiles if tiles < 256 else 1, max(1, M // 512)))
+
+
+def test_backward_workspace_bytes():
+    r = lambda b: (b + 255) // 256 * 256  # noqa: E731
+
+    def expect(N, T, D, F, H, es):
+        M = N * T
+        packed = r(3 * D * D * es) + r(D * D * es) + 2 * r(D * F * es)
+        wcat = r(3 * D * D * es)
+        # xn, att, y, yn, dy [M, D]; qkv [M, 3D]; z [M, max(F, 3D)]; h [M, F]
+        acts = 5 * r(M * D * es) + r(M * 3 * D * es) + r(M * max(F, 3 * D) * es) + r(M * F * es)
+        stats = r(M * H * 3 * 4)  # score max, exp sum and rowsum(P * dP) per query and head
+        part = max(r(_split(M, i, j) * i * j * 4) for i, j in
+                   [(F, D), (D, F), (D, D), (D, 3 * D)])
+        return packed + wcat + acts + stats + part
+
+    for (N, T, D, F, H, es) in [(256, 197, 1024, 4096, 16, 2), (4, 5, 16, 32, 2, 4),
+                                (2, 3, 8, 8, 2, 4), (64, 197, 768, 3072, 12, 2)]:
+        code = 1 if es == 2 else 0
+        assert vb.backward_workspace_bytes(N, T, D, F, H, code) == \
+            expect(N, T, D, F, H, es), (N, T, D, F, H)
+    assert vb.backward_workspace_bytes(1, 1, 6, 4, 4, 1) == 0   # H does not divide D
+    assert vb.backward_workspace_bytes(0, 1, 8, 8, 1, 1) == 0   # empty batch
+    assert vb.backward_workspace_bytes(1, 1, 8, 8, 1, 5) == 0   # unknown dtype
+    # weight gradient: split over token rows into fp32 partials
+    assert vb.weight_grad_workspace_bytes(50432, 1024, 1024) == 16 * 1024 * 1024 * 4
+    assert vb.weight_grad_workspace_bytes(50432, 1024, 4096) == 4 * 1024 * 4096 * 4
+    assert vb.weight_grad_workspace_bytes(50432, 1024, 3072) == 5 * 1024 * 3072 * 4
+    assert vb.weight_grad_workspace_bytes(20, 16, 32) == r(16 * 32 * 4)  # few rows: no split
+    assert vb.weight_grad_workspace_bytes(0, 16, 32) == 0
+    assert vb.attention_backward_workspace_bytes(256, 197, 1024, 16) == r(256 * 197 * 16 * 12)
+    assert vb.attention_backward_workspace_bytes(2, 5, 16, 3) == 0
+
+
+def test_backward_errors(lib):
+    assert _bwd(lib, N=0) == INVALID
+    assert _bwd(lib, D=16, H=3) == INVALID
+    assert _bwd(lib, eps=-1.0) == INVALID
+    assert _bwd(lib, eps=math.nan) == INVALID
+    assert _bwd(lib, dtype=3) == INVALID
+    for i in range(15):
+        p = [_addr(j) for j in range(15)]
+        p[i] = None
+        assert _bwd(lib, ptrs=p) == INVALID, i
+        p[i] = ctypes.c_void_p((i + 1) * GAP + 4)  # misaligned
+        assert _bwd(lib, ptrs=p) == INVALID, i
+    assert _bwd(lib, D=4096, H=2, F=8) == UNSUPPORTED
+    need = vb.backward_workspace_bytes(2, 5, 16, 32, 2, 1)
+    assert _bwd(lib, ws_bytes=need - 1) == WORKSPACE
+    assert _bwd(lib, ws=ctypes.c_void_p(0)) == WORKSPACE
+    # a gradient overlapping an input, another gradient, or the workspace
+    for gi, other in [(8, 0), (9, 1), (14, 7), (10, 11), (13, 8)]:
+        p = [_addr(j) for j in range(15)]
+        p[gi] = ctypes.c_void_p(p[other].value)
+        assert _bwd(lib, ptrs=p) == ALIAS, (gi, other)
+    assert _bwd(lib, ws=ctypes.c_void_p(_addr(12).value)) == ALIAS
+    assert _bwd(lib, ws=ctypes.c_void_p(_addr(7).value)) == ALIAS   # dout inside the workspace
+
+
+def test_backward_step_entry_points_errors(lib):
+    a, b, c, d = (_addr(i) for i in range(4))
+    big = 1 << 30
+    # weight gradient
+    assert lib.vitblk_weight_grad(None, b, c, 64, 16, 16, 1, d, big, None) == INVALID
+    assert lib.vitblk_weight_grad(a, b, c, 0, 16, 16, 1, d, big, None) == INVALID
+    assert lib.vitblk_weight_grad(a, b, c, 64, 16, 16, 9, d, big, None) == INVALID
+    assert lib.vitblk_weight_grad(a, b, c, 64, 16, 16, 1, None, big, None) == WORKSPACE
+    assert lib.vitblk_weight_grad(a, b, c, 64, 16, 16, 1, d, 16 * 16 * 4 - 1, None) == WORKSPACE
+    assert lib.vitblk_weight_grad(a, b, a, 64, 16, 16, 1, d, big, None) == ALIAS
+    assert lib.vitblk_weight_grad(a, b, c, 64, 16, 16, 1, ctypes.c_void_p(c.value + 32), big,
+                                  None) == ALIAS
+    # LayerNorm backward (residual may be NULL: that is not an error by itself)
+    assert lib.vitblk_layernorm_backward(None, b, c, d, 4, 8, 1e-5, 1, None) == INVALID
+    assert lib.vitblk_layernorm_backward(a, b, c, d, 4, 0, 1e-5, 1, None) == INVALID
+    assert lib.vitblk_layernorm_backward(a, b, c, d, 4, 8, -1.0, 1, None) == INVALID
+    assert lib.vitblk_layernorm_backward(a, b, None, a, 4, 8, 1e-5, 1, None) == ALIAS
+    assert lib.vitblk_layernorm_backward(a, b, c, c, 4, 8, 1e-5, 1, None) == ALIAS
+    assert lib.vitblk_layernorm_backward(a, b, c, ctypes.c_void_p(b.value + 16), 4, 8, 1e-5, 1,
+                                         None) == ALIAS
+    # attention backward
+    assert lib.vitblk_attention_backward(a, b, None, 2, 5, 16, 2, 1, d, big, None) == INVALID
+    assert lib.vitblk_attention_backward(a, b, c, 2, 5, 16, 3, 1, d, big, None) == INVALID
+    assert lib.vitblk_attention_backward(a, b, c, 2, 5, 16, 2, 1, None, big, None) == WORKSPACE
+    assert lib.vitblk_attention_backward(a, b, c, 2, 5, 16, 2, 1, d, 2 * 5 * 2 * 12 - 1,
+                                         None) == WORKSPACE
+    assert lib.vitblk_attention_backward(a, b, a, 2, 5, 16, 2, 1, d, big, None) == ALIAS
+    assert lib.vitblk_attention_backward(a, b, c, 2, 5, 16, 2, 1, ctypes.c_void_p(c.value),
+                                         big, None) == ALIAS
+    # the GELU-derivative epilogue reads z through `residual`, so it must be given
+    assert lib.vitblk_linear(a, b, None, c, 64, 64, 64, vb.EPI_GELU_GRAD, 1, None) == INVALID
+    assert lib.vitblk_linear(a, b, c, c, 64, 64, 64, vb.EPI_GELU_GRAD, 1, None) == ALIAS
+    assert lib.vitblk_linear(a, b, c, d, 64, 64, 64, 4, 1, None) == INVALID

@@ -10,12 +10,18 @@ first call does, and it raises if the library has not been built.
 from ._lib import (  # noqa: F401
     AFFINE_KEYS,
     EPI_GELU,
+    EPI_GELU_GRAD,
+    GRAD_KEYS,
     EPI_NONE,
     EPI_RESIDUAL,
     VITBLK_BF16,
     VITBLK_FP32,
     VitblkError,
     attention,
+    attention_backward,
+    attention_backward_workspace_bytes,
+    backward,
+    backward_workspace_bytes,
     encoder_forward,
     encoder_workspace_bytes,
     forward,
@@ -23,6 +29,7 @@ from ._lib import (  # noqa: F401
     forward_packed,
     forward_packed_affine,
     layernorm,
+    layernorm_backward,
     linear,
     load,
     pack_weights,
@@ -32,5 +39,7 @@ from ._lib import (  # noqa: F401
     patch_embed_workspace_bytes,
     qkv_projection,
     status_string,
+    weight_grad,
+    weight_grad_workspace_bytes,
     workspace_bytes,
 )

@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libvitblk.so")
 
 VITBLK_FP32, VITBLK_BF16 = 0, 1
-EPI_NONE, EPI_RESIDUAL, EPI_GELU = 0, 1, 2
+EPI_NONE, EPI_RESIDUAL, EPI_GELU, EPI_GELU_GRAD = 0, 1, 2, 3
 STATUS = {0: "VITBLK_OK", -1: "VITBLK_ERR_INVALID_ARG", -2: "VITBLK_ERR_UNSUPPORTED",
           -3: "VITBLK_ERR_WORKSPACE", -4: "VITBLK_ERR_ALIAS", -5: "VITBLK_ERR_HIP"}
 
@@ -51,7 +51,17 @@ SIGNATURES = {
     "vitblk_patch_embed": (_I, [_P] * 6 + [_I64] * 6 + [_I, _P, _SZ, _P]),
     "vitblk_encoder_forward": (_I, [_P, ctypes.POINTER(ctypes.c_void_p), _AP, _I64, _P, _P, _P,
                                     _P] + [_I64] * 5 + [_D, _I, _P, _SZ, _P]),
+    "vitblk_backward_workspace_bytes": (_SZ, [_I64] * 5 + [_I]),
+    "vitblk_backward": (_I, [_P] * 15 + [_I64] * 5 + [_D, _I, _P, _SZ, _P]),
+    "vitblk_weight_grad_workspace_bytes": (_SZ, [_I64] * 3),
+    "vitblk_weight_grad": (_I, [_P] * 3 + [_I64] * 3 + [_I, _P, _SZ, _P]),
+    "vitblk_layernorm_backward": (_I, [_P] * 4 + [_I64, _I64, _D, _I, _P]),
+    "vitblk_attention_backward_workspace_bytes": (_SZ, [_I64] * 4),
+    "vitblk_attention_backward": (_I, [_P] * 3 + [_I64] * 4 + [_I, _P, _SZ, _P]),
 }
+
+# Gradients written by vitblk_backward, in argument order.
+GRAD_KEYS = ("dx", "dw_q", "dw_k", "dw_v", "dw_o", "dw_mlp1", "dw_mlp2")
 
 _lib = None
 
@@ -406,4 +416,97 @@ def linear(a, w_t, epilogue: int = EPI_NONE, residual=None, out=None, stream=Non
                                        M, K, Nout, int(epilogue), dtype_code(a.dtype),
                                        _stream(a, stream))
         _check("vitblk_linear_bias", st)
+    return out
+
+
+# ------------------------------------------------------------------ backward
+
+def backward_workspace_bytes(N, T, D, F, H, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    return int(load().vitblk_backward_workspace_bytes(N, T, D, F, H, code))
+
+
+def backward(x, w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, dout, num_heads: int, eps: float,
+             grads=None, workspace=None, stream=None):
+    """Gradients of sum(dout * block(x)): dict keyed by GRAD_KEYS (allocated if not given)."""
+    torch = _torch()
+    ws_ = (w_q, w_k, w_v, w_o, w_mlp1, w_mlp2)
+    _dev(x, dout, *ws_)
+    N, T, D = x.shape
+    F = w_mlp1.shape[1]
+    code = dtype_code(x.dtype)
+    if grads is None:
+        grads = {"dx": torch.empty_like(x)}
+        for k, w in zip(GRAD_KEYS[1:], ws_):
+            grads[k] = torch.empty_like(w)
+    _dev(*grads.values())
+    need = backward_workspace_bytes(N, T, D, F, num_heads, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    st = load().vitblk_backward(_ptr(x), *[_ptr(w) for w in ws_], _ptr(dout),
+                                *[_ptr(grads[k]) for k in GRAD_KEYS], N, T, D, F, num_heads,
+                                float(eps), code, _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(x, stream))
+    _check("vitblk_backward", st)
+    return grads
+
+
+def weight_grad_workspace_bytes(M, I, J) -> int:
+    return int(load().vitblk_weight_grad_workspace_bytes(M, I, J))
+
+
+def weight_grad(a, b, out=None, workspace=None, stream=None):
+    """out [I, J] = a^T b for a [M, I], b [M, J] (sum over the M token rows)."""
+    torch = _torch()
+    _dev(a, b, out)
+    I, J = a.shape[-1], b.shape[-1]
+    M = a.numel() // I
+    if b.numel() // J != M:
+        raise ValueError("a and b must have the same number of rows")
+    if out is None:
+        out = torch.empty((I, J), dtype=a.dtype, device=a.device)
+    if workspace is None:
+        workspace = torch.empty(max(weight_grad_workspace_bytes(M, I, J), 1), dtype=torch.uint8,
+                                device=a.device)
+    st = load().vitblk_weight_grad(_ptr(a), _ptr(b), _ptr(out), M, I, J, dtype_code(a.dtype),
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(a, stream))
+    _check("vitblk_weight_grad", st)
+    return out
+
+
+def layernorm_backward(x, g, eps: float, residual=None, out=None, stream=None):
+    """dx = residual + LN'(x)^T g, row by row over the last axis."""
+    torch = _torch()
+    _dev(x, g, residual, out)
+    D = x.shape[-1]
+    rows = x.numel() // D
+    if out is None:
+        out = torch.empty_like(x)
+    st = load().vitblk_layernorm_backward(_ptr(x), _ptr(g), _ptr(residual), _ptr(out), rows, D,
+                                          float(eps), dtype_code(x.dtype), _stream(x, stream))
+    _check("vitblk_layernorm_backward", st)
+    return out
+
+
+def attention_backward_workspace_bytes(N, T, D, H) -> int:
+    return int(load().vitblk_attention_backward_workspace_bytes(N, T, D, H))
+
+
+def attention_backward(qkv, datt, N: int, T: int, num_heads: int, out=None, workspace=None,
+                       stream=None):
+    """dqkv [N*T, 3D] from the forward's qkv [N*T, 3D] and datt [N*T, D]."""
+    torch = _torch()
+    _dev(qkv, datt, out)
+    D = datt.shape[-1]
+    if out is None:
+        out = torch.empty((N * T, 3 * D), dtype=qkv.dtype, device=qkv.device)
+    if workspace is None:
+        workspace = torch.empty(max(attention_backward_workspace_bytes(N, T, D, num_heads), 1),
+                                dtype=torch.uint8, device=qkv.device)
+    st = load().vitblk_attention_backward(_ptr(qkv), _ptr(datt), _ptr(out), N, T, D, num_heads,
+                                          dtype_code(qkv.dtype), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(),
+                                          _stream(qkv, stream))
+    _check("vitblk_attention_backward", st)
     return out

@@ -123,9 +123,176 @@ int run_encoder(const void* x, const void* const* packed, const vitblk_affine_pa
   return VITBLK_OK;
 }
 
+WgradProblem wgrad_problem(const void* a, int64_t lda, const void* b, int64_t ldb, void* c,
+                           int64_t M, int64_t I, int64_t J, int dtype) {
+  WgradProblem p{};
+  p.M = M;
+  p.I = I;
+  p.J = J;
+  p.A = a;
+  p.lda = lda;
+  p.B = b;
+  p.ldb = ldb;
+  p.C[0] = c;
+  p.ldc = J;
+  p.seg = J;
+  p.dtype = dtype;
+  return p;
+}
+
+// The backward of the plain block: recompute the forward's activations, then
+// walk its steps in reverse (each gradient step names the forward step it
+// differentiates).  w: w_q, w_k, w_v, w_o, w_mlp1, w_mlp2; g: dx, dw_q, dw_k,
+// dw_v, dw_o, dw_mlp1, dw_mlp2.
+int run_backward(const void* x, const void* const* w, const void* dout, void* const* g,
+                 int64_t N, int64_t T, int64_t D, int64_t F, int64_t H, double eps, int dtype,
+                 char* ws, const BackwardPlan& pl, hipStream_t s) {
+  const int64_t M = N * T;
+  const size_t es = elem_size(dtype);
+  const float feps = static_cast<float>(eps);
+  char* pk = ws;  // forward packed weights at offset 0
+  char* wcat = ws + pl.off_wcat;
+  char* xn = ws + pl.off_xn;
+  char* qkv = ws + pl.off_qkv;
+  char* att = ws + pl.off_att;
+  char* y = ws + pl.off_y;
+  char* yn = ws + pl.off_yn;
+  char* z = ws + pl.off_z;
+  char* h = ws + pl.off_h;
+  char* dy = ws + pl.off_dy;
+  float* stats = reinterpret_cast<float*>(ws + pl.off_stats);
+  float* partial = reinterpret_cast<float*>(ws + pl.off_partial);
+
+  // Weights: the forward's out-major copies, and [w_q | w_k | w_v] row by row.
+  int st = pack_weights(w[0], w[1], w[2], w[3], w[4], w[5], pk, D, F, dtype, pl.packed, s);
+  if (st != VITBLK_OK) return st;
+  for (int i = 0; i < 3; ++i)
+    VITBLK_LAUNCH(hipMemcpy2DAsync(wcat + i * D * es, 3 * D * es, w[i], D * es, D * es, D,
+                                   hipMemcpyDeviceToDevice, s));
+
+  // ---- forward, keeping every activation the gradients need
+  VITBLK_LAUNCH(launch_layernorm(x, D, nullptr, nullptr, xn, M, D, feps, dtype, s));
+  VITBLK_LAUNCH(launch_gemm(linear_problem(xn, pk + pl.packed.off_qkv, qkv, nullptr, M, D, 3 * D,
+                                           VITBLK_EPI_NONE, dtype),
+                            s));
+  VITBLK_LAUNCH(launch_attention(qkv, qkv + D * es, qkv + 2 * D * es, 3 * D, att, D, N, T, H,
+                                 D / H, dtype, s));
+  VITBLK_LAUNCH(launch_gemm(
+      linear_problem(att, pk + pl.packed.off_o, y, x, M, D, D, VITBLK_EPI_RESIDUAL, dtype), s));
+  VITBLK_LAUNCH(launch_layernorm(y, D, nullptr, nullptr, yn, M, D, feps, dtype, s));
+  VITBLK_LAUNCH(launch_gemm(
+      linear_problem(yn, pk + pl.packed.off_1, z, nullptr, M, D, F, VITBLK_EPI_NONE, dtype), s));
+  VITBLK_LAUNCH(launch_gelu(z, h, M * F, dtype, s));
+
+  // ---- out = y + h @ w_mlp2
+  VITBLK_LAUNCH(launch_wgrad(wgrad_problem(h, F, dout, D, g[6], M, F, D, dtype), partial,
+                             wgrad_split(M, F, D), s));
+  // h = GELU(z):  dz = (dout @ w_mlp2^T) * GELU'(z)   (into h's region)
+  VITBLK_LAUNCH(launch_gemm(
+      linear_problem(dout, w[5], h, z, M, D, F, VITBLK_EPI_GELU_GRAD, dtype), s));
+  // z = yn @ w_mlp1
+  VITBLK_LAUNCH(launch_wgrad(wgrad_problem(yn, D, h, F, g[5], M, D, F, dtype), partial,
+                             wgrad_split(M, D, F), s));
+  VITBLK_LAUNCH(launch_gemm(
+      linear_problem(h, w[4], yn, nullptr, M, F, D, VITBLK_EPI_NONE, dtype), s));  // dyn
+  // yn = LN(y); y also feeds out directly:  dy = dout + LN'(y)^T dyn
+  VITBLK_LAUNCH(launch_layernorm_backward(y, yn, dout, dy, M, D, feps, dtype, s));
+  // y = x + att @ w_o
+  VITBLK_LAUNCH(launch_wgrad(wgrad_problem(att, D, dy, D, g[4], M, D, D, dtype), partial,
+                             wgrad_split(M, D, D), s));
+  VITBLK_LAUNCH(launch_gemm(
+      linear_problem(dy, w[3], y, nullptr, M, D, D, VITBLK_EPI_NONE, dtype), s));  // datt
+  // att = heads of softmax(q k^T / sqrt(dh)) v:  dqkv into z's region
+  VITBLK_LAUNCH(launch_attention_backward(qkv, qkv + D * es, qkv + 2 * D * es, 3 * D, y, D, z,
+                                          z + D * es, z + 2 * D * es, 3 * D, N, T, H, D / H,
+                                          dtype, stats, s));
+  // q | k | v = xn @ [w_q | w_k | w_v]
+  WgradProblem pq = wgrad_problem(xn, D, z, 3 * D, g[1], M, D, 3 * D, dtype);
+  pq.C[1] = g[2];
+  pq.C[2] = g[3];
+  pq.ldc = D;
+  pq.seg = D;
+  VITBLK_LAUNCH(launch_wgrad(pq, partial, wgrad_split(M, D, 3 * D), s));
+  // dxn = dqkv @ [w_q | w_k | w_v]^T   (into att's region)
+  GemmProblem px = linear_problem(z, wcat, att, nullptr, M, 3 * D, D, VITBLK_EPI_NONE, dtype);
+  VITBLK_LAUNCH(launch_gemm(px, s));
+  // xn = LN(x); x also feeds y directly:  dx = dy + LN'(x)^T dxn
+  VITBLK_LAUNCH(launch_layernorm_backward(x, att, dy, g[0], M, D, feps, dtype, s));
+  return VITBLK_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t vitblk_backward_workspace_bytes(int64_t N, int64_t T, int64_t D, int64_t F, int64_t H,
+                                       int dtype) {
+  BackwardPlan p;
+  if (plan_backward(N, T, D, F, H, dtype, &p) != VITBLK_OK) return 0;
+  return p.total;
+}
+
+int vitblk_backward(const void* x, const void* w_q, const void* w_k, const void* w_v,
+                    const void* w_o, const void* w_mlp1, const void* w_mlp2, const void* dout,
+                    void* dx, void* dw_q, void* dw_k, void* dw_v, void* dw_o, void* dw_mlp1,
+                    void* dw_mlp2, int64_t N, int64_t T, int64_t D, int64_t F, int64_t H,
+                    double eps, int dtype, void* workspace, size_t workspace_bytes,
+                    vitblk_stream_t stream) {
+  const void* w[6] = {w_q, w_k, w_v, w_o, w_mlp1, w_mlp2};
+  void* g[7] = {dx, dw_q, dw_k, dw_v, dw_o, dw_mlp1, dw_mlp2};
+  BackwardPlan pl;
+  const int st = validate_backward(x, w, dout, g, N, T, D, F, H, eps, dtype, workspace,
+                                   workspace_bytes, &pl);
+  if (st != VITBLK_OK) return st;
+  return run_backward(x, w, dout, g, N, T, D, F, H, eps, dtype, static_cast<char*>(workspace),
+                      pl, reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t vitblk_weight_grad_workspace_bytes(int64_t M, int64_t I, int64_t J) {
+  return wgrad_partial_bytes(M, I, J);
+}
+
+int vitblk_weight_grad(const void* a, const void* b, void* out, int64_t M, int64_t I, int64_t J,
+                       int dtype, void* workspace, size_t workspace_bytes,
+                       vitblk_stream_t stream) {
+  const int st = validate_weight_grad(a, b, out, M, I, J, dtype, workspace, workspace_bytes);
+  if (st != VITBLK_OK) return st;
+  VITBLK_LAUNCH(launch_wgrad(wgrad_problem(a, I, b, J, out, M, I, J, dtype),
+                             static_cast<float*>(workspace), wgrad_split(M, I, J),
+                             reinterpret_cast<hipStream_t>(stream)));
+  return VITBLK_OK;
+}
+
+int vitblk_layernorm_backward(const void* x, const void* g, const void* residual, void* dx,
+                              int64_t rows, int64_t D, double eps, int dtype,
+                              vitblk_stream_t stream) {
+  const int st = validate_layernorm_backward(x, g, residual, dx, rows, D, eps, dtype);
+  if (st != VITBLK_OK) return st;
+  VITBLK_LAUNCH(launch_layernorm_backward(x, g, residual, dx, rows, D, static_cast<float>(eps),
+                                          dtype, reinterpret_cast<hipStream_t>(stream)));
+  return VITBLK_OK;
+}
+
+size_t vitblk_attention_backward_workspace_bytes(int64_t N, int64_t T, int64_t D, int64_t H) {
+  if (D <= 0 || H <= 0 || D % H != 0) return 0;
+  return attention_stats_bytes(N, T, H);
+}
+
+int vitblk_attention_backward(const void* qkv, const void* datt, void* dqkv, int64_t N, int64_t T,
+                              int64_t D, int64_t H, int dtype, void* workspace,
+                              size_t workspace_bytes, vitblk_stream_t stream) {
+  const int st = validate_attention_backward(qkv, datt, dqkv, N, T, D, H, dtype, workspace,
+                                             workspace_bytes);
+  if (st != VITBLK_OK) return st;
+  const size_t es = elem_size(dtype);
+  const char* q = static_cast<const char*>(qkv);
+  char* d = static_cast<char*>(dqkv);
+  VITBLK_LAUNCH(launch_attention_backward(q, q + D * es, q + 2 * D * es, 3 * D, datt, D, d,
+                                          d + D * es, d + 2 * D * es, 3 * D, N, T, H, D / H,
+                                          dtype, static_cast<float*>(workspace),
+                                          reinterpret_cast<hipStream_t>(stream)));
+  return VITBLK_OK;
+}
 
 size_t vitblk_patch_embed_workspace_bytes(int64_t B, int64_t C, int64_t H, int64_t W,
                                           int64_t P, int64_t D, int dtype) {
@@ -330,8 +497,11 @@ int vitblk_linear_bias(const void* a, const void* w_t, const void* bias, const v
   const int st = validate_linear(a, w_t, bias, residual, out, M, K, Nout, epilogue, dtype);
   if (st != VITBLK_OK) return st;
   VITBLK_LAUNCH(launch_gemm(
-      linear_problem(a, w_t, out, epilogue == VITBLK_EPI_RESIDUAL ? residual : nullptr, M, K,
-                     Nout, epilogue, dtype, bias),
+      linear_problem(a, w_t, out,
+                     (epilogue == VITBLK_EPI_RESIDUAL || epilogue == VITBLK_EPI_GELU_GRAD)
+                         ? residual
+                         : nullptr,
+                     M, K, Nout, epilogue, dtype, bias),
       reinterpret_cast<hipStream_t>(stream)));
   return VITBLK_OK;
 }

@@ -66,6 +66,32 @@ __device__ __forceinline__ float gelu_tanh_precise(float z) {
   return 0.5f * z * (1.0f + tanhf(k0 * (z + 0.044715f * z * z * z)));
 }
 
+// Derivative of the tanh-form GELU: with s = 0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u))
+// and 1 - tanh(u)^2 = 4 s (1 - s),  d/dz GELU = s + 2 z s (1 - s) u'(z),
+// u'(z) = sqrt(2/pi) (1 + 3 * 0.044715 z^2).  z is clamped inside u'(z) only,
+// where s (1 - s) is already exactly 0 (|z| > 100), so that z^2 cannot overflow.
+__device__ __forceinline__ float gelu_tanh_grad_fast(float z) {
+  const float k0 = 0.7978845608028654f;
+  const float k1 = 0.044715f;
+  const float m2log2e = -2.8853900817779268f;
+  const float zc = fminf(fmaxf(z, -100.0f), 100.0f);
+  const float u = k0 * (zc + k1 * zc * zc * zc);
+  const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(m2log2e * u));
+  const float du = k0 * (1.0f + 3.0f * k1 * zc * zc);
+  return s + 2.0f * zc * s * (1.0f - s) * du;
+}
+
+// Same derivative through the library tanh, for the fp32 path:
+// 0.5 (1 + t) + 0.5 z (1 - t^2) u'(z), t = tanh(u).
+__device__ __forceinline__ float gelu_tanh_grad_precise(float z) {
+  const float k0 = 0.7978845608028654f;
+  const float k1 = 0.044715f;
+  const float zc = fminf(fmaxf(z, -100.0f), 100.0f);
+  const float t = tanhf(k0 * (zc + k1 * zc * zc * zc));
+  const float du = k0 * (1.0f + 3.0f * k1 * zc * zc);
+  return 0.5f * (1.0f + t) + 0.5f * zc * (1.0f - t * t) * du;
+}
+
 // ------------------------------------------------------------- wave reductions
 
 template <int CTRL>

@@ -347,8 +347,10 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
           for (int r = 0; r < 16; ++r) acc[j][i][r] += bv[r];
       }
     }
+    // R: the residual, or GELU's input z for the GELU-derivative epilogue.
+    constexpr bool kReadsR = EPI == VITBLK_EPI_RESIDUAL || EPI == VITBLK_EPI_GELU_GRAD;
     uint4 res[C::TM][C::TN][2];
-    if (EPI == VITBLK_EPI_RESIDUAL) {
+    if (kReadsR) {
 #pragma unroll
       for (int i = 0; i < C::TM; ++i) {
         int64_t m = cm0 + wm * C::WTM + i * 32 + lrow;
@@ -372,7 +374,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
         for (int q = 0; q < 2; ++q) {
           const int64_t n = cn0 + wn * C::WTN + j * 32 + q * 16 + lhalf * 8;
           uint4 out;
-          if (EPI == VITBLK_EPI_RESIDUAL) {
+          if (kReadsR) {
             // fp32 exchange: lane's 8 columns are x[0..3] then y[0..3].
             float x[4], y[4];
 #pragma unroll
@@ -393,8 +395,15 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              v[2 * e] += __uint_as_float(rw[e] << 16);
-              v[2 * e + 1] += __uint_as_float(rw[e] & 0xffff0000u);
+              const float r0 = __uint_as_float(rw[e] << 16);
+              const float r1 = __uint_as_float(rw[e] & 0xffff0000u);
+              if (EPI == VITBLK_EPI_GELU_GRAD) {
+                v[2 * e] *= gelu_tanh_grad_fast(r0);
+                v[2 * e + 1] *= gelu_tanh_grad_fast(r1);
+              } else {
+                v[2 * e] += r0;
+                v[2 * e + 1] += r1;
+              }
             }
             out = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
                              pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
@@ -470,6 +479,7 @@ hipError_t launch_bias(const GemmProblem& p, hipStream_t s) {
   switch (p.epi) {
     case VITBLK_EPI_RESIDUAL: return launch_epi<C, VITBLK_EPI_RESIDUAL, BIAS>(p, s);
     case VITBLK_EPI_GELU: return launch_epi<C, VITBLK_EPI_GELU, BIAS>(p, s);
+    case VITBLK_EPI_GELU_GRAD: return launch_epi<C, VITBLK_EPI_GELU_GRAD, BIAS>(p, s);
     default: return launch_epi<C, VITBLK_EPI_NONE, BIAS>(p, s);
   }
 }
@@ -493,7 +503,8 @@ bool gemm_fast_ok(const GemmProblem& p) {
             p.lda % 8 == 0 && p.ldb % 8 == 0 && p.ldc % 8 == 0 && aligned16(p.A) &&
             aligned16(p.B) && aligned16(p.C) && p.lda * 2 * 256 < (1LL << 31) &&
             p.ldb * 2 * 256 < (1LL << 31) && p.K * 2 < (1LL << 31);
-  if (p.epi == VITBLK_EPI_RESIDUAL) ok = ok && p.ldr % 8 == 0 && aligned16(p.R);
+  if (p.epi == VITBLK_EPI_RESIDUAL || p.epi == VITBLK_EPI_GELU_GRAD)
+    ok = ok && p.ldr % 8 == 0 && aligned16(p.R);
   if (has_bias(p)) {
     ok = ok && p.bias_seg > 0 && p.bias_seg % 8 == 0 && p.N <= 3 * p.bias_seg;
     for (const void* b : p.bias)
@@ -524,6 +535,7 @@ GemmProblem row_slice(const GemmProblem& p, int64_t r0, int64_t rows) {
 // number of rounds, and the remaining rows run as a second launch with the
 // quarter-size tile, which finishes in a fraction of a round.
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t s) {
+  if (reads_r(p) && p.R == nullptr) return hipErrorInvalidValue;  // never launch on a null R
   if (!gemm_fast_ok(p)) return launch_gemm_generic(p, s);
   using Big = BigTile;
   using Small = SmallTile;
@@ -533,6 +545,7 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t s) {
   switch (p.epi) {
     case VITBLK_EPI_RESIDUAL: grid = resident_workgroups<Big, VITBLK_EPI_RESIDUAL>(); break;
     case VITBLK_EPI_GELU: grid = resident_workgroups<Big, VITBLK_EPI_GELU>(); break;
+    case VITBLK_EPI_GELU_GRAD: grid = resident_workgroups<Big, VITBLK_EPI_GELU_GRAD>(); break;
     default: grid = resident_workgroups<Big, VITBLK_EPI_NONE>(); break;
   }
   grid = grid / kNumXcd * kNumXcd;

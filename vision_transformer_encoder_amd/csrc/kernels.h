@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "vitblk.h"
+
 namespace vitblk {
 
 // C[m, n] = epi(sum_k A[m, k] * Wt[n, k] + b[n]) (+ R[m, n]) for m < M, n < N.
@@ -31,6 +33,11 @@ struct GemmProblem {
 
 __host__ __device__ inline bool has_bias(const GemmProblem& p) {
   return p.bias[0] != nullptr || p.bias[1] != nullptr || p.bias[2] != nullptr;
+}
+
+// Epilogues that read R (the residual, or GELU's input for its derivative).
+__host__ __device__ inline bool reads_r(const GemmProblem& p) {
+  return p.epi == VITBLK_EPI_RESIDUAL || p.epi == VITBLK_EPI_GELU_GRAD;
 }
 
 // One (in, out) weight to write out-major: dst[c * ldd + r] = src[r * cols + c].
@@ -91,5 +98,50 @@ hipError_t launch_gemm_generic(const GemmProblem& p, hipStream_t stream);
 hipError_t launch_attention_generic(const void* q, const void* k, const void* v, int64_t ld,
                                     void* o, int64_t ldo, int64_t N, int64_t T, int64_t H,
                                     int64_t dh, int dtype, hipStream_t stream);
+
+// ------------------------------------------------------------------ backward
+
+// Weight gradient: C[i, j] = sum_m A[m, i] * B[m, j] over the M token rows.
+// A [M, I] (row stride lda), B [M, J] (row stride ldb); output column j goes
+// to C[j / seg] at column j % seg (row stride ldc), so the fused Q|K|V
+// gradient lands in three separate [D, D] outputs.  The token rows are split
+// into `split` ranges, each reduced into partial[s] ([I, J] fp32), and a
+// second kernel sums the partials in order and rounds to the dtype.
+struct WgradProblem {
+  int64_t M, I, J;
+  const void* A;
+  int64_t lda;
+  const void* B;
+  int64_t ldb;
+  void* C[3];
+  int64_t ldc, seg;
+  int dtype;
+};
+
+hipError_t launch_wgrad(const WgradProblem& p, float* partial, int split, hipStream_t stream);
+
+// The matrix-core weight gradient over the first wgrad_mfma_rows() token rows
+// (0: the problem does not qualify), in at most `split` ranges; *used gets
+// the number of partials written.  hipErrorNotSupported: nothing launched.
+int64_t wgrad_mfma_rows(const WgradProblem& p, int split);
+hipError_t launch_wgrad_mfma(const WgradProblem& p, float* partial, int split, int* used,
+                             hipStream_t stream);
+
+// dx[r, :] = res[r, :] + J^T g[r, :] for the Jacobian J of LN (no gain or
+// shift) at x[r, :]; res may be null.  All [rows, D].
+hipError_t launch_layernorm_backward(const void* x, const void* g, const void* res, void* dx,
+                                     int64_t rows, int64_t D, float eps, int dtype,
+                                     hipStream_t stream);
+
+// h[i] = GELU_tanh(z[i]) for i < n.
+hipError_t launch_gelu(const void* z, void* h, int64_t n, int dtype, hipStream_t stream);
+
+// Attention backward: dQ, dK, dV (row stride ldd) from Q, K, V (row stride
+// ld) and dO (row stride ldo).  stats: 3 * N * H * T floats of workspace
+// (each query's score maximum, exponential sum and rowsum(P * dP)).
+hipError_t launch_attention_backward(const void* q, const void* k, const void* v, int64_t ld,
+                                     const void* d_o, int64_t ldo, void* dq, void* dk, void* dv,
+                                     int64_t ldd, int64_t N, int64_t T, int64_t H, int64_t dh,
+                                     int dtype, float* stats, hipStream_t stream);
 
 }  // namespace vitblk

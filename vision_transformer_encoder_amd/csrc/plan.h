@@ -115,4 +115,52 @@ int validate_affine_params(const vitblk_affine_params* params, const void* out, 
                            int64_t D, int64_t F, int dtype, const void* workspace,
                            size_t workspace_bytes);
 
+// Weight gradients (out = a^T b over M token rows, out [I, J]): the token
+// rows are split into `wgrad_split` ranges, each reduced into an fp32
+// partial [I, J]; a second kernel sums the partials in order and rounds.
+// The split fills about one round of 256x256 output tiles on 256 compute
+// units and keeps at least 512 token rows per range.
+int wgrad_split(int64_t M, int64_t I, int64_t J);
+size_t wgrad_partial_bytes(int64_t M, int64_t I, int64_t J);  // 0: invalid or overflow
+
+// Per-query softmax statistics of the attention backward: the score maximum,
+// the sum of exponentials and rowsum(P * dP) for every (sequence, head,
+// query), fp32.
+size_t attention_stats_bytes(int64_t N, int64_t T, int64_t H);
+
+// vitblk_backward workspace: the forward's packed weights, the concatenated
+// [w_q | w_k | w_v] ([D, 3D], the B operand of the input gradient of the
+// fused projection), the recomputed forward activations, the gradient
+// buffers, the softmax statistics and the weight-gradient partials.  The
+// gradient steps reuse activation regions once these are dead: dz -> h,
+// dyn -> yn, datt -> y, dqkv -> z, dxn -> att.
+struct BackwardPlan {
+  PackedPlan packed;  // at offset 0
+  size_t off_wcat;
+  size_t off_xn, off_qkv, off_att, off_y, off_yn, off_z, off_h, off_dy;
+  size_t off_stats, off_partial;
+  size_t partial_bytes;
+  size_t total;
+};
+
+int plan_backward(int64_t N, int64_t T, int64_t D, int64_t F, int64_t H, int dtype,
+                  BackwardPlan* plan);
+
+// grads: dx, dw_q, dw_k, dw_v, dw_o, dw_mlp1, dw_mlp2 (all non-null).
+int validate_backward(const void* x, const void* const* w, const void* dout,
+                      void* const* grads, int64_t N, int64_t T, int64_t D, int64_t F,
+                      int64_t H, double eps, int dtype, const void* workspace,
+                      size_t workspace_bytes, BackwardPlan* plan);
+
+int validate_weight_grad(const void* a, const void* b, const void* out, int64_t M, int64_t I,
+                         int64_t J, int dtype, const void* workspace, size_t workspace_bytes);
+
+// residual may be null.
+int validate_layernorm_backward(const void* x, const void* g, const void* residual,
+                                const void* dx, int64_t rows, int64_t D, double eps, int dtype);
+
+int validate_attention_backward(const void* qkv, const void* datt, const void* dqkv, int64_t N,
+                                int64_t T, int64_t D, int64_t H, int dtype,
+                                const void* workspace, size_t workspace_bytes);
+
 }  // namespace vitblk

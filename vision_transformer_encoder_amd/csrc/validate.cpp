@@ -330,10 +330,10 @@ int validate_linear(const void* a, const void* w, const void* bias, const void* 
   if (!aligned16(a) || !aligned16(w) || !aligned16(out) || !aligned16(bias))
     return VITBLK_ERR_INVALID_ARG;
   if (epilogue != VITBLK_EPI_NONE && epilogue != VITBLK_EPI_RESIDUAL &&
-      epilogue != VITBLK_EPI_GELU)
+      epilogue != VITBLK_EPI_GELU && epilogue != VITBLK_EPI_GELU_GRAD)
     return VITBLK_ERR_INVALID_ARG;
-  if (epilogue == VITBLK_EPI_RESIDUAL && (residual == nullptr || !aligned16(residual)))
-    return VITBLK_ERR_INVALID_ARG;
+  const bool reads_r = epilogue == VITBLK_EPI_RESIDUAL || epilogue == VITBLK_EPI_GELU_GRAD;
+  if (reads_r && (residual == nullptr || !aligned16(residual))) return VITBLK_ERR_INVALID_ARG;
   if (!dim_ok(M) || !dim_ok(K) || !dim_ok(Nout)) return VITBLK_ERR_INVALID_ARG;
   const size_t es = elem_size(dtype);
   if (es == 0) return VITBLK_ERR_INVALID_ARG;
@@ -343,8 +343,7 @@ int validate_linear(const void* a, const void* w, const void* bias, const void* 
   const Span o = span(out, m * n * es);
   if (overlap(o, span(a, m * k * es)) || overlap(o, span(w, k * n * es)))
     return VITBLK_ERR_ALIAS;
-  if (epilogue == VITBLK_EPI_RESIDUAL && overlap(o, span(residual, m * n * es)))
-    return VITBLK_ERR_ALIAS;
+  if (reads_r && overlap(o, span(residual, m * n * es))) return VITBLK_ERR_ALIAS;
   if (bias != nullptr && overlap(o, span(bias, n * es))) return VITBLK_ERR_ALIAS;
   return VITBLK_OK;
 }
@@ -417,6 +416,189 @@ int validate_affine_params(const vitblk_affine_params* params, const void* out, 
     const Span s = span(ptrs[i], bytes[i]);
     if (overlap(s, o) || overlap(s, w)) return VITBLK_ERR_ALIAS;
   }
+  return VITBLK_OK;
+}
+
+int wgrad_split(int64_t M, int64_t I, int64_t J) {
+  if (!dim_ok(M) || !dim_ok(I) || !dim_ok(J)) return 1;
+  const int64_t tiles = ((I + 255) / 256) * ((J + 255) / 256);
+  int64_t split = tiles >= 256 ? 1 : 256 / tiles;
+  const int64_t by_rows = M / 512 > 1 ? M / 512 : 1;
+  if (split > by_rows) split = by_rows;
+  return static_cast<int>(split);
+}
+
+size_t wgrad_partial_bytes(int64_t M, int64_t I, int64_t J) {
+  if (!dim_ok(M) || !dim_ok(I) || !dim_ok(J) || I > kMaxDim || J > kMaxDim) return 0;
+  size_t n;
+  if (!mul_ok(static_cast<size_t>(I), static_cast<size_t>(J), &n) ||
+      !mul_ok(n, static_cast<size_t>(wgrad_split(M, I, J)) * 4, &n))
+    return 0;
+  return round_up(n, kRegionAlign);
+}
+
+size_t attention_stats_bytes(int64_t N, int64_t T, int64_t H) {
+  if (!dim_ok(N) || !dim_ok(T) || !dim_ok(H)) return 0;
+  size_t n;
+  if (!mul_ok(static_cast<size_t>(N) * static_cast<size_t>(T), static_cast<size_t>(H), &n) ||
+      !mul_ok(n, 3 * sizeof(float), &n))
+    return 0;
+  return round_up(n, kRegionAlign);
+}
+
+int plan_backward(int64_t N, int64_t T, int64_t D, int64_t F, int64_t H, int dtype,
+                  BackwardPlan* plan) {
+  int st = check_block_dims(N, T, D, F, H, dtype);
+  if (st != VITBLK_OK) return st;
+  BackwardPlan p;
+  st = plan_packed(D, F, dtype, &p.packed);
+  if (st != VITBLK_OK) return st;
+  const size_t es = elem_size(dtype);
+  const size_t M = static_cast<size_t>(N) * static_cast<size_t>(T);
+  const size_t d = static_cast<size_t>(D), f = static_cast<size_t>(F);
+  const size_t wide = f > 3 * d ? f : 3 * d;
+  size_t act, qkv, zb, hb, wcat;
+  if (!mul_ok(M, d * es, &act) || !mul_ok(M, 3 * d * es, &qkv) || !mul_ok(M, wide * es, &zb) ||
+      !mul_ok(M, f * es, &hb) || !mul_ok(d, 3 * d * es, &wcat))
+    return VITBLK_ERR_UNSUPPORTED;
+  act = round_up(act, kRegionAlign);
+  // The largest of the four weight gradients' partials.
+  size_t part = 0;
+  const int64_t shapes[4][2] = {{F, D}, {D, F}, {D, D}, {D, 3 * D}};
+  for (const auto& sh : shapes) {
+    const size_t b = wgrad_partial_bytes(static_cast<int64_t>(M), sh[0], sh[1]);
+    if (b == 0) return VITBLK_ERR_UNSUPPORTED;
+    if (b > part) part = b;
+  }
+  const size_t stats = attention_stats_bytes(N, T, H);
+  if (stats == 0) return VITBLK_ERR_UNSUPPORTED;
+  size_t o = p.packed.total;
+  p.off_wcat = o;
+  o += round_up(wcat, kRegionAlign);
+  p.off_xn = o;
+  o += act;
+  p.off_qkv = o;
+  o += round_up(qkv, kRegionAlign);
+  p.off_att = o;
+  o += act;
+  p.off_y = o;
+  o += act;
+  p.off_yn = o;
+  o += act;
+  p.off_z = o;
+  o += round_up(zb, kRegionAlign);
+  p.off_h = o;
+  o += round_up(hb, kRegionAlign);
+  p.off_dy = o;
+  o += act;
+  p.off_stats = o;
+  o += stats;
+  p.off_partial = o;
+  p.partial_bytes = part;
+  o += part;
+  if (o < part) return VITBLK_ERR_UNSUPPORTED;
+  p.total = o;
+  *plan = p;
+  return VITBLK_OK;
+}
+
+int validate_backward(const void* x, const void* const* w, const void* dout,
+                      void* const* grads, int64_t N, int64_t T, int64_t D, int64_t F,
+                      int64_t H, double eps, int dtype, const void* workspace,
+                      size_t workspace_bytes, BackwardPlan* plan) {
+  if (w == nullptr || grads == nullptr) return VITBLK_ERR_INVALID_ARG;
+  const void* ins[8] = {x, w[0], w[1], w[2], w[3], w[4], w[5], dout};
+  for (const void* q : ins)
+    if (q == nullptr || !aligned16(q)) return VITBLK_ERR_INVALID_ARG;
+  for (int i = 0; i < 7; ++i)
+    if (grads[i] == nullptr || !aligned16(grads[i])) return VITBLK_ERR_INVALID_ARG;
+  int st = check_eps(eps);
+  if (st != VITBLK_OK) return st;
+  BackwardPlan p;
+  st = plan_backward(N, T, D, F, H, dtype, &p);
+  if (st != VITBLK_OK) return st;
+  if (workspace == nullptr || !aligned16(workspace)) return VITBLK_ERR_WORKSPACE;
+  if (workspace_bytes < p.total) return VITBLK_ERR_WORKSPACE;
+  const size_t es = elem_size(dtype);
+  const size_t M = static_cast<size_t>(N) * static_cast<size_t>(T);
+  const size_t d = static_cast<size_t>(D), f = static_cast<size_t>(F);
+  const size_t in_bytes[8] = {M * d * es, d * d * es, d * d * es, d * d * es,
+                              d * d * es, d * f * es, f * d * es, M * d * es};
+  const size_t out_bytes[7] = {M * d * es, d * d * es, d * d * es, d * d * es,
+                               d * d * es, d * f * es, f * d * es};
+  const Span ws = span(workspace, p.total);
+  for (int i = 0; i < 7; ++i) {
+    const Span o = span(grads[i], out_bytes[i]);
+    if (overlap(o, ws)) return VITBLK_ERR_ALIAS;
+    for (int j = 0; j < 8; ++j)
+      if (overlap(o, span(ins[j], in_bytes[j]))) return VITBLK_ERR_ALIAS;
+    for (int j = i + 1; j < 7; ++j)
+      if (overlap(o, span(grads[j], out_bytes[j]))) return VITBLK_ERR_ALIAS;
+  }
+  for (int j = 0; j < 8; ++j)
+    if (overlap(ws, span(ins[j], in_bytes[j]))) return VITBLK_ERR_ALIAS;
+  if (plan) *plan = p;
+  return VITBLK_OK;
+}
+
+int validate_weight_grad(const void* a, const void* b, const void* out, int64_t M, int64_t I,
+                         int64_t J, int dtype, const void* workspace, size_t workspace_bytes) {
+  if (a == nullptr || b == nullptr || out == nullptr) return VITBLK_ERR_INVALID_ARG;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(out)) return VITBLK_ERR_INVALID_ARG;
+  if (!dim_ok(M) || !dim_ok(I) || !dim_ok(J)) return VITBLK_ERR_INVALID_ARG;
+  const size_t es = elem_size(dtype);
+  if (es == 0) return VITBLK_ERR_INVALID_ARG;
+  if (M > kMaxDim || I > kMaxDim || J > kMaxDim) return VITBLK_ERR_UNSUPPORTED;
+  const size_t need = wgrad_partial_bytes(M, I, J);
+  if (need == 0) return VITBLK_ERR_UNSUPPORTED;
+  if (workspace == nullptr || !aligned16(workspace)) return VITBLK_ERR_WORKSPACE;
+  if (workspace_bytes < need) return VITBLK_ERR_WORKSPACE;
+  const size_t m = static_cast<size_t>(M), i = static_cast<size_t>(I), j = static_cast<size_t>(J);
+  const Span o = span(out, i * j * es);
+  const Span ws = span(workspace, need);
+  const Span sa = span(a, m * i * es), sb = span(b, m * j * es);
+  if (overlap(o, ws) || overlap(o, sa) || overlap(o, sb) || overlap(ws, sa) || overlap(ws, sb))
+    return VITBLK_ERR_ALIAS;
+  return VITBLK_OK;
+}
+
+int validate_layernorm_backward(const void* x, const void* g, const void* residual,
+                                const void* dx, int64_t rows, int64_t D, double eps, int dtype) {
+  if (x == nullptr || g == nullptr || dx == nullptr) return VITBLK_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(g) || !aligned16(dx) || !aligned16(residual))
+    return VITBLK_ERR_INVALID_ARG;
+  if (!dim_ok(rows) || !dim_ok(D)) return VITBLK_ERR_INVALID_ARG;
+  const size_t es = elem_size(dtype);
+  if (es == 0) return VITBLK_ERR_INVALID_ARG;
+  int st = check_eps(eps);
+  if (st != VITBLK_OK) return st;
+  if (rows > kMaxDim || D > kMaxDim) return VITBLK_ERR_UNSUPPORTED;
+  const size_t n = static_cast<size_t>(rows) * static_cast<size_t>(D) * es;
+  const Span o = span(dx, n);
+  if (overlap(o, span(x, n)) || overlap(o, span(g, n))) return VITBLK_ERR_ALIAS;
+  if (residual != nullptr && overlap(o, span(residual, n))) return VITBLK_ERR_ALIAS;
+  return VITBLK_OK;
+}
+
+int validate_attention_backward(const void* qkv, const void* datt, const void* dqkv, int64_t N,
+                                int64_t T, int64_t D, int64_t H, int dtype,
+                                const void* workspace, size_t workspace_bytes) {
+  if (datt == nullptr || dqkv == nullptr || !aligned16(datt) || !aligned16(dqkv))
+    return VITBLK_ERR_INVALID_ARG;
+  int st = validate_attention(qkv, datt, N, T, D, H, dtype);
+  if (st != VITBLK_OK) return st;
+  const size_t need = attention_stats_bytes(N, T, H);
+  if (need == 0) return VITBLK_ERR_UNSUPPORTED;
+  if (workspace == nullptr || !aligned16(workspace)) return VITBLK_ERR_WORKSPACE;
+  if (workspace_bytes < need) return VITBLK_ERR_WORKSPACE;
+  const size_t es = elem_size(dtype);
+  const size_t m = static_cast<size_t>(N) * static_cast<size_t>(T);
+  const size_t d = static_cast<size_t>(D);
+  const Span o = span(dqkv, m * 3 * d * es);
+  const Span ws = span(workspace, need);
+  const Span sq = span(qkv, m * 3 * d * es), sd = span(datt, m * d * es);
+  if (overlap(o, sq) || overlap(o, sd) || overlap(o, ws) || overlap(ws, sq) || overlap(ws, sd))
+    return VITBLK_ERR_ALIAS;
   return VITBLK_OK;
 }
 

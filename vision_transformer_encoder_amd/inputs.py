@@ -18,6 +18,13 @@ Recipe
   of the float32 value after RNE; fp32: numpy's float64 -> float32 cast).
   The float64 arrays returned are those rounded values, upcast exactly.
 
+Backward (``make_dout``): the gradient arriving at the block's output is
+drawn by a third generator, ``numpy.random.default_rng([seed, 4])``, as
+standard_normal (N, T, D) then rounded: unit scale, like the output itself.
+The pages train with a cross-entropy loss on class labels (nipunbatra.github.io
+vision1 transcript, Page 113); its gradient at one block depends on the
+layers above and the labels, and a seeded N(0, 1) tensor stands in for it.
+
 Affine variant (``make_affine_params``): a second, independent generator,
 ``numpy.random.default_rng([seed, 1])``, draws in the order ln1_gamma,
 ln1_beta, b_q, b_k, b_v, b_o, ln2_gamma, ln2_beta, b_mlp1, b_mlp2 (lengths D,
@@ -43,7 +50,7 @@ import math
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "bf16_round", "round_to", "make_block_inputs",
-           "AFFINE_PARAM_ORDER", "make_affine_params"]
+           "AFFINE_PARAM_ORDER", "make_affine_params", "make_dout"]
 
 AFFINE_PARAM_ORDER = ("ln1_gamma", "ln1_beta", "b_q", "b_k", "b_v", "b_o",
                       "ln2_gamma", "ln2_beta", "b_mlp1", "b_mlp2")
@@ -129,3 +136,9 @@ def make_affine_params(D: int, F: int, dtype: str, seed: int = 0) -> dict:
         z = rng.standard_normal(n)
         out[name] = round_to(1.0 + 0.1 * z if name.endswith("gamma") else 0.1 * z, dtype)
     return out
+
+
+def make_dout(N: int, T: int, D: int, dtype: str, seed: int = 0) -> np.ndarray:
+    """dL/d(out) for the backward: N(0, 1), device-exact float64."""
+    rng = np.random.default_rng([seed, 4])
+    return round_to(rng.standard_normal((N, T, D)), dtype)
