@@ -51,28 +51,43 @@ def stack_scale(L):
     return math.sqrt(L)
 
 
+# Gradient bars (see assert_close_grad): normwise and elementwise, per dtype.
+GRAD_NORM_TOL = {"fp32": 1e-5, "bf16": 1e-2}
+GRAD_ELEM_TOL = {"fp32": 2e-4, "bf16": 5e-2}
+
+
 def grad_violation(gpu, ref):
-    """max |g - o| / (rms(o) + |o|), and the mean absolute error."""
+    """(max |g - o| / (rms(o) + |o|), ||g - o|| / ||o||, mean abs err)."""
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
     if not np.all(np.isfinite(gpu)):
-        return float("inf"), float("inf")
+        return float("inf"), float("inf"), float("inf")
     rms = float(np.sqrt(np.mean(ref * ref))) or 1.0
     err = np.abs(gpu - ref)
-    return float((err / (rms + np.abs(ref))).max()), float(err.mean())
+    norm = float(np.sqrt(np.sum(err * err)) / (np.sqrt(np.sum(ref * ref)) or 1.0))
+    return float((err / (rms + np.abs(ref))).max()), norm, float(err.mean())
 
 
 def assert_close_grad(gpu, ref, dtype, what=""):
-    """Gradient bar: TOL[dtype] * (rms(o) + |o|).
+    """Gradient bars: ||g - o|| / ||o|| <= GRAD_NORM_TOL and
+    max |g - o| / (rms(o) + |o|) <= GRAD_ELEM_TOL.
 
     A gradient has no unit scale of its own (a weight gradient is a sum over
-    every token of the batch), so the forward bar's "1 +" -- the block
-    output's unit scale -- becomes the RMS of the oracle's tensor: the bar is
-    the forward's relative bar measured in the tensor's own units.
+    every token of the batch), so the elementwise bar is taken against the
+    tensor's RMS instead of the forward bar's unit "1 +".  In bf16 every
+    gradient has passed through about ten roundings to bf16 (relative error
+    up to 2^-9 each) on its way from the output gradient, and the measured
+    relative RMS error of the weight gradients is 0.5-0.6 %; the largest of
+    n such errors is about sqrt(2 ln n) = 5.5 standard deviations for the 4M
+    elements of an MLP weight, i.e. about 3 %.  Hence 5e-2 elementwise, and
+    1e-2 normwise (twice the measured RMS error; a dropped or wrong term
+    shows up at order 1 in both).  fp32: 2e-4 and 1e-5.
     """
-    v, mae = grad_violation(gpu, ref)
-    bar = TOL[dtype]
-    print(f"  {what}: violation {v:.3e} (bar {bar:.2e}), mean abs err {mae:.3e}", flush=True)
-    assert v <= bar, f"{what}: violation {v:.3e} > {bar}"
+    v, norm, mae = grad_violation(gpu, ref)
+    bar, nbar = GRAD_ELEM_TOL[dtype], GRAD_NORM_TOL[dtype]
+    print(f"  {what}: elementwise {v:.3e} (bar {bar:.0e}), normwise {norm:.3e} (bar {nbar:.0e}), "
+          f"mean abs err {mae:.3e}", flush=True)
+    assert norm <= nbar, f"{what}: normwise error {norm:.3e} > {nbar}"
+    assert v <= bar, f"{what}: elementwise violation {v:.3e} > {bar}"
     return v, mae

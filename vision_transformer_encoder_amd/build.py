@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(PKG, "libvitblk.so")
 ARCH = os.environ.get("VITBLK_OFFLOAD_ARCH", "gfx950")
 HIP_SOURCES = ["api.hip", "layernorm.hip", "gemm.hip", "attention.hip",
                "attention_resident.hip", "patch.hip", "generic.hip", "pack.hip",
-               "backward.hip", "wgrad.hip"]
+               "backward.hip", "wgrad.hip", "attention_bwd.hip"]
 HOST_SOURCES = ["validate.cpp"]
 
 # Packed-fp32 instructions are disabled for all device code.

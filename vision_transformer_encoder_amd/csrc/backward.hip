@@ -490,6 +490,11 @@ hipError_t launch_attention_backward(const void* q, const void* k, const void* v
                                      const void* d_o, int64_t ldo, void* dq, void* dk, void* dv,
                                      int64_t ldd, int64_t N, int64_t T, int64_t H, int64_t dh,
                                      int dtype, float* stats, hipStream_t s) {
+  if (dtype == VITBLK_BF16) {
+    const hipError_t e = launch_attention_backward_mfma(q, k, v, ld, d_o, ldo, dq, dk, dv, ldd,
+                                                        N, T, H, dh, stats, s);
+    if (e != hipErrorNotSupported) return e;
+  }
   return dtype == VITBLK_BF16
              ? attention_backward_typed<bf16_t>(q, k, v, ld, d_o, ldo, dq, dk, dv, ldd, N, T, H,
                                                 dh, stats, s)

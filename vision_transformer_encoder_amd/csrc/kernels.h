@@ -139,6 +139,14 @@ hipError_t launch_gelu(const void* z, void* h, int64_t n, int dtype, hipStream_t
 // Attention backward: dQ, dK, dV (row stride ldd) from Q, K, V (row stride
 // ld) and dO (row stride ldo).  stats: 3 * N * H * T floats of workspace
 // (each query's score maximum, exponential sum and rowsum(P * dP)).
+// Matrix-core attention backward (bf16, the head resident in LDS);
+// hipErrorNotSupported when the shape does not qualify (nothing launched).
+hipError_t launch_attention_backward_mfma(const void* q, const void* k, const void* v,
+                                          int64_t ld, const void* d_o, int64_t ldo, void* dq,
+                                          void* dk, void* dv, int64_t ldd, int64_t N, int64_t T,
+                                          int64_t H, int64_t dh, float* stats,
+                                          hipStream_t stream);
+
 hipError_t launch_attention_backward(const void* q, const void* k, const void* v, int64_t ld,
                                      const void* d_o, int64_t ldo, void* dq, void* dk, void* dv,
                                      int64_t ldd, int64_t N, int64_t T, int64_t H, int64_t dh,
