@@ -1,7 +1,7 @@
 """Throughput of one pre-LN ViT encoder block forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload vit_l16]
-                    [--variant plain|affine|encoder|embed] [--layers L]
+                    [--variant plain|affine|encoder|embed|backward] [--layers L]
 
 A step is one full block forward (8 kernels through vitblk_forward: weight packing
 and the seven steps of the block) over one
@@ -18,7 +18,12 @@ weights, the final LayerNorm of every token and of the class tokens:
 vitblk_encoder_forward), L = the model's depth unless --layers is given;
 ``--variant embed`` times the front end (vitblk_patch_embed: N images of
 (sqrt(T-1) * P)^2 pixels, 3 channels, P = 16 for ViT-B/L and 14 for ViT-H,
-with class token and position embeddings) and reports tokens/s out of it.
+with class token and position embeddings) and reports tokens/s out of it;
+``--variant backward`` times the block backward (vitblk_backward: the forward
+recomputed, then dx and the six weight gradients for a seeded N(0, 1) output
+gradient) and checks dx on sampled sequences against the float64 backward
+oracle (the weight gradients, sums over the whole batch, are checked by the
+GPU tests).
 """
 
 from __future__ import annotations
@@ -83,10 +88,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target host time for the oracle baseline sample (0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--variant", choices=["plain", "affine", "encoder", "embed"],
+    ap.add_argument("--variant", choices=["plain", "affine", "encoder", "embed", "backward"],
                     default="plain",
-                    help="plain block (default), the affine variant, the encoder stack, or "
-                         "the front end")
+                    help="plain block (default), the affine variant, the encoder stack, "
+                         "the front end, or the block backward")
     ap.add_argument("--layers", type=int, default=0,
                     help="encoder depth (default: 12 / 24 / 32 for ViT-B / L / H)")
     ap.add_argument("--profile-step", default=None,
@@ -223,6 +228,156 @@ def bench_embed(a, w, torch, vb):
     print(json.dumps(res), flush=True)
 
 
+def backward_flops(N, T, D, F):
+    """Matmul FLOPs of one block backward with the forward recomputed:
+    the forward's N*T*(8 D^2 + 4 D F + 4 T D), then twice the projections'
+    (input and weight gradients) and four attention products (dV, dP, dQ, dK)."""
+    return N * T * (24 * D * D + 12 * D * F + 12 * T * D)
+
+
+def bench_backward(a, w, torch, vb):
+    """The block backward: x, weights and dL/d(out) -> dx and the six weight gradients."""
+    import oracle
+    from vision_transformer_encoder_amd.inputs import make_block_inputs, make_dout
+    tdt = {"fp32": torch.float32, "bf16": torch.bfloat16}[w.dtype]
+    dev = torch.device("cuda:0")
+    WN = ["w_q", "w_k", "w_v", "w_o", "w_mlp1", "w_mlp2"]
+    inp = make_block_inputs(w.N, w.T, w.D, w.F, w.dtype, seed=a.seed)
+    dout = make_dout(w.N, w.T, w.D, w.dtype, seed=a.seed)
+    to_g = lambda v: torch.from_numpy(v.astype(np.float32)).to(dev, tdt)  # noqa: E731
+    g = {k: to_g(v) for k, v in inp.items()}
+    gd = to_g(dout)
+    ws = torch.empty(vb.backward_workspace_bytes(w.N, w.T, w.D, w.F, w.H, tdt),
+                     dtype=torch.uint8, device=dev)
+    grads = vb.backward(g["x"], *(g[k] for k in WN), gd, w.H, w.eps, workspace=ws)
+
+    def step():
+        vb.backward(g["x"], *(g[k] for k in WN), gd, w.H, w.eps, grads=grads, workspace=ws)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(s)
+    for _ in range(a.steps):
+        step()
+    e1.record(s)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / a.steps
+    got_dx = grads["dx"].to("cpu", torch.float64).numpy()
+
+    # The backward's steps alone, on the same shapes and realistic operands.
+    M, D, F = w.M, w.D, w.F
+    es = 2 if w.dtype == "bf16" else 4
+    x2, dout2 = g["x"].view(M, D), gd.view(M, D)
+    packed = vb.pack_weights(*(g[k] for k in WN))
+    wqkv_t, wo_t, w1_t, w2_t = vb.packed_views(packed, D, F, tdt)
+    xn = vb.layernorm(x2, w.eps)
+    qkv = vb.qkv_projection(xn, wqkv_t)
+    att = vb.attention(qkv, w.N, w.T, w.H)
+    y = vb.linear(att, wo_t, vb.EPI_RESIDUAL, residual=x2)
+    yn = vb.layernorm(y, w.eps)
+    z = vb.linear(yn, w1_t, vb.EPI_NONE)
+    hid = vb.linear(yn, w1_t, vb.EPI_GELU)
+    dz = vb.linear(dout2, g["w_mlp2"], vb.EPI_GELU_GRAD, residual=z)
+    dyn = vb.linear(dz, g["w_mlp1"], vb.EPI_NONE)
+    dy = vb.layernorm_backward(y, dyn, w.eps, residual=dout2)
+    datt = vb.linear(dy, g["w_o"], vb.EPI_NONE)
+    dqkv = vb.attention_backward(qkv, datt, w.N, w.T, w.H)
+    wcat = torch.cat([g["w_q"], g["w_k"], g["w_v"]], dim=1).contiguous()
+    dxn = vb.linear(dqkv, wcat, vb.EPI_NONE)
+    outs = {k: torch.empty_like(v) for k, v in (("dz", dz), ("dyn", dyn), ("dy", dy),
+                                                ("datt", datt), ("dqkv", dqkv), ("dxn", dxn))}
+    wouts = {"dw_mlp2": torch.empty((F, D), dtype=tdt, device=dev),
+             "dw_mlp1": torch.empty((D, F), dtype=tdt, device=dev),
+             "dw_o": torch.empty((D, D), dtype=tdt, device=dev),
+             "dw_qkv": torch.empty((D, 3 * D), dtype=tdt, device=dev)}
+    wws = torch.empty(max(vb.weight_grad_workspace_bytes(M, i, j) for i, j in
+                          ((F, D), (D, F), (D, D), (D, 3 * D))), dtype=torch.uint8, device=dev)
+    aws = torch.empty(vb.attention_backward_workspace_bytes(w.N, w.T, D, w.H), dtype=torch.uint8,
+                      device=dev)
+    T_ = w.T
+    kern = {
+        "dw_mlp2": (lambda: vb.weight_grad(hid, dout2, out=wouts["dw_mlp2"], workspace=wws),
+                    "mfma", 2 * M * F * D),
+        "dz_gemm_gelu_grad": (lambda: vb.linear(dout2, g["w_mlp2"], vb.EPI_GELU_GRAD,
+                                                residual=z, out=outs["dz"]), "mfma",
+                              2 * M * D * F),
+        "dw_mlp1": (lambda: vb.weight_grad(yn, dz, out=wouts["dw_mlp1"], workspace=wws), "mfma",
+                    2 * M * D * F),
+        "dyn_gemm": (lambda: vb.linear(dz, g["w_mlp1"], vb.EPI_NONE, out=outs["dyn"]), "mfma",
+                     2 * M * F * D),
+        "ln2_backward": (lambda: vb.layernorm_backward(y, dyn, w.eps, residual=dout2,
+                                                       out=outs["dy"]), "hbm", 4 * M * D * es),
+        "dw_o": (lambda: vb.weight_grad(att, dy, out=wouts["dw_o"], workspace=wws), "mfma",
+                 2 * M * D * D),
+        "datt_gemm": (lambda: vb.linear(dy, g["w_o"], vb.EPI_NONE, out=outs["datt"]), "mfma",
+                      2 * M * D * D),
+        "attention_backward": (lambda: vb.attention_backward(qkv, datt, w.N, T_, w.H,
+                                                             out=outs["dqkv"], workspace=aws),
+                               "mfma", 8 * w.N * T_ * T_ * D),
+        "dw_qkv": (lambda: vb.weight_grad(xn, dqkv, out=wouts["dw_qkv"], workspace=wws), "mfma",
+                   2 * M * D * 3 * D),
+        "dxn_gemm": (lambda: vb.linear(dqkv, wcat, vb.EPI_NONE, out=outs["dxn"]), "mfma",
+                     2 * M * 3 * D * D),
+        "ln1_backward": (lambda: vb.layernorm_backward(x2, dxn, w.eps, residual=dy,
+                                                       out=outs["dy"]), "hbm", 4 * M * D * es),
+    }
+    per = {}
+    for name, (fn, bound, work) in kern.items():
+        kms = time_launches(fn, a.kernel_reps, torch)
+        rate = work / (kms * 1e-3)
+        per[name] = {"ms": round(kms, 5), "bound": bound,
+                     ("tflops" if bound == "mfma" else "gbs"):
+                     round(rate / (1e12 if bound == "mfma" else 1e9), 2)}
+    dom = max(per, key=lambda k: per[k]["ms"])
+    fn, bound, work = kern[dom]
+    dms = per[dom]["ms"]
+    if bound == "mfma":
+        ach = work / (dms * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "work_per_launch": f"{work / 1e9:.2f} GFLOP"}
+    else:
+        ach = work / (dms * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                "work_per_launch": f"{work / 1e6:.1f} MB"}
+    flops = backward_flops(w.N, w.T, w.D, w.F)
+    tflops = flops / (ms * 1e-3) / 1e12
+    res = {
+        "metric": f"encoder-block backward tokens/sec (forward recomputed; dx and the six "
+                  f"weight gradients), {w.name} shape N={w.N}",
+        "value": round(M / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) tokens and output gradient, N(0,1/fan_in) weights)",
+        "config": {"workload": w.name, "N": w.N, "T": w.T, "D": w.D, "H": w.H, "F": w.F,
+                   "eps": w.eps, "global_batch": w.N, "seq_len": w.T, "parallelism": "none",
+                   "variant": "backward"},
+        "block_tflops": round(tflops, 2),
+        "block_frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "wall_s_timed": round(t_wall, 3),
+        "kernels": per,
+        "roofline": roof,
+    }
+    if a.cpu_seconds > 0:
+        def ref_fn(seqs):
+            return oracle.vit_block_backward(inp["x"][seqs], *(inp[k] for k in WN), dout[seqs],
+                                             w.H, w.eps, chunk=1)["dx"]
+        cb, par = cpu_baseline(ref_fn, w, a.cpu_seconds, got_dx)
+        par["checked"] = "dx"
+        res["cpu_baseline"] = cb
+        res["parity"] = par
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -242,6 +397,9 @@ def main():
     if a.variant == "embed":
         torch.cuda.set_device(torch.device("cuda:0"))
         return bench_embed(a, w, torch, vb)
+    if a.variant == "backward":
+        torch.cuda.set_device(torch.device("cuda:0"))
+        return bench_backward(a, w, torch, vb)
     tdt = {"fp32": torch.float32, "bf16": torch.bfloat16}[w.dtype]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
