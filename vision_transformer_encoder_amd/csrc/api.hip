@@ -180,16 +180,17 @@ int run_backward(const void* x, const void* const* w, const void* dout, void* co
   VITBLK_LAUNCH(launch_gemm(
       linear_problem(att, pk + pl.packed.off_o, y, x, M, D, D, VITBLK_EPI_RESIDUAL, dtype), s));
   VITBLK_LAUNCH(launch_layernorm(y, D, nullptr, nullptr, yn, M, D, feps, dtype, s));
-  VITBLK_LAUNCH(launch_gemm(
-      linear_problem(yn, pk + pl.packed.off_1, z, nullptr, M, D, F, VITBLK_EPI_NONE, dtype), s));
-  VITBLK_LAUNCH(launch_gelu(z, h, M * F, dtype, s));
+  // h = GELU(yn @ w_mlp1) and, from the same product, GELU'(yn @ w_mlp1) (into z's region)
+  GemmProblem p1 = linear_problem(yn, pk + pl.packed.off_1, h, nullptr, M, D, F, kEpiGeluDual,
+                                  dtype);
+  p1.C2 = z;
+  VITBLK_LAUNCH(launch_gemm(p1, s));
 
   // ---- out = y + h @ w_mlp2
   VITBLK_LAUNCH(launch_wgrad(wgrad_problem(h, F, dout, D, g[6], M, F, D, dtype), partial,
                              wgrad_split(M, F, D), s));
   // h = GELU(z):  dz = (dout @ w_mlp2^T) * GELU'(z)   (into h's region)
-  VITBLK_LAUNCH(launch_gemm(
-      linear_problem(dout, w[5], h, z, M, D, F, VITBLK_EPI_GELU_GRAD, dtype), s));
+  VITBLK_LAUNCH(launch_gemm(linear_problem(dout, w[5], h, z, M, D, F, kEpiMul, dtype), s));
   // z = yn @ w_mlp1
   VITBLK_LAUNCH(launch_wgrad(wgrad_problem(yn, D, h, F, g[5], M, D, F, dtype), partial,
                              wgrad_split(M, D, F), s));

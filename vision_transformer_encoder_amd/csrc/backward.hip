@@ -1,7 +1,8 @@
-// Backward-pass kernels of the block that have no matrix-core version: the
-// LayerNorm backward, the element-wise GELU of the recomputed forward, the
-// any-shape weight gradient and its partial-sum reduction, and the any-shape
-// attention backward.  fp32 arithmetic on the VALU.
+// Backward-pass kernels of the block on the VALU (fp32 arithmetic): the
+// any-shape LayerNorm backward, the any-shape weight gradient and the
+// partial-sum reduction of every weight gradient, and the any-shape
+// attention backward.  The matrix-core paths fall back to these for shapes
+// they do not take and for fp32 tensors.
 //
 // The gradients are those of the block's forward definition
 // (crackedaicode.com "ViT Encoder Block"), as training needs them
@@ -66,17 +67,6 @@ __global__ __launch_bounds__(kThreads) void ln_backward_kernel(const T* __restri
     float o = rstd * (load_f32(gr + i) - mg - xhat * mgx);
     if (res != nullptr) o += load_f32(res + row * D + i);
     store_f32(dx + row * D + i, o);
-  }
-}
-
-// ------------------------------------------------------------------- GELU
-template <typename T>
-__global__ __launch_bounds__(kThreads) void gelu_kernel(const T* __restrict__ z, T* __restrict__ h,
-                                                        int64_t n) {
-  for (int64_t i = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; i < n;
-       i += static_cast<int64_t>(gridDim.x) * kThreads) {
-    const float v = load_f32(z + i);
-    store_f32(h + i, sizeof(T) == 2 ? gelu_tanh_fast(v) : gelu_tanh_precise(v));
   }
 }
 
@@ -452,9 +442,9 @@ hipError_t wgrad_typed(const WgradProblem& p, float* partial, int split, hipStre
 
 }  // namespace
 
-hipError_t launch_layernorm_backward(const void* x, const void* g, const void* res, void* dx,
-                                     int64_t rows, int64_t D, float eps, int dtype,
-                                     hipStream_t s) {
+hipError_t launch_layernorm_backward_generic(const void* x, const void* g, const void* res,
+                                             void* dx, int64_t rows, int64_t D, float eps,
+                                             int dtype, hipStream_t s) {
   if (rows > 2147483647LL) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(rows));
   if (dtype == VITBLK_BF16)
@@ -465,18 +455,6 @@ hipError_t launch_layernorm_backward(const void* x, const void* g, const void* r
     hipLaunchKernelGGL(ln_backward_kernel<float>, grid, dim3(kThreads), 0, s,
                        static_cast<const float*>(x), static_cast<const float*>(g),
                        static_cast<const float*>(res), static_cast<float*>(dx), D, eps);
-  return hipGetLastError();
-}
-
-hipError_t launch_gelu(const void* z, void* h, int64_t n, int dtype, hipStream_t s) {
-  const int64_t blocks = (n + kThreads - 1) / kThreads < 65536 ? (n + kThreads - 1) / kThreads
-                                                              : 65536;
-  if (dtype == VITBLK_BF16)
-    hipLaunchKernelGGL(gelu_kernel<bf16_t>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
-                       0, s, static_cast<const bf16_t*>(z), static_cast<bf16_t*>(h), n);
-  else
-    hipLaunchKernelGGL(gelu_kernel<float>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
-                       0, s, static_cast<const float*>(z), static_cast<float*>(h), n);
   return hipGetLastError();
 }
 

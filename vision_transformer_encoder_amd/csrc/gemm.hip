@@ -348,7 +348,8 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
       }
     }
     // R: the residual, or GELU's input z for the GELU-derivative epilogue.
-    constexpr bool kReadsR = EPI == VITBLK_EPI_RESIDUAL || EPI == VITBLK_EPI_GELU_GRAD;
+    constexpr bool kReadsR =
+        EPI == VITBLK_EPI_RESIDUAL || EPI == VITBLK_EPI_GELU_GRAD || EPI == kEpiMul;
     uint4 res[C::TM][C::TN][2];
     if (kReadsR) {
 #pragma unroll
@@ -400,6 +401,9 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
               if (EPI == VITBLK_EPI_GELU_GRAD) {
                 v[2 * e] *= gelu_tanh_grad_fast(r0);
                 v[2 * e + 1] *= gelu_tanh_grad_fast(r1);
+              } else if (EPI == kEpiMul) {
+                v[2 * e] *= r0;
+                v[2 * e + 1] *= r1;
               } else {
                 v[2 * e] += r0;
                 v[2 * e + 1] += r1;
@@ -409,21 +413,33 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
                              pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
           } else {
             // round first, then exchange bf16 pairs (4 dwords per lane).
-            uint32_t w[2][2];
+            uint32_t w[2][2], w2[2][2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-              float v[4];
+              float v[4], d[4];
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 v[e] = acc[j][i][(2 * q + h) * 4 + e];
-                if (EPI == VITBLK_EPI_GELU) v[e] = gelu_tanh_fast(v[e]);
+                if (EPI == kEpiGeluDual) d[e] = gelu_tanh_grad_fast(v[e]);
+                if (EPI == VITBLK_EPI_GELU || EPI == kEpiGeluDual) v[e] = gelu_tanh_fast(v[e]);
               }
               w[h][0] = pack_bf16x2(v[0], v[1]);
               w[h][1] = pack_bf16x2(v[2], v[3]);
+              if (EPI == kEpiGeluDual) {
+                w2[h][0] = pack_bf16x2(d[0], d[1]);
+                w2[h][1] = pack_bf16x2(d[2], d[3]);
+              }
             }
             const auto s0 = __builtin_amdgcn_permlane32_swap(w[0][0], w[1][0], false, false);
             const auto s1 = __builtin_amdgcn_permlane32_swap(w[0][1], w[1][1], false, false);
             out = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+            if (EPI == kEpiGeluDual) {
+              const auto t0 = __builtin_amdgcn_permlane32_swap(w2[0][0], w2[1][0], false, false);
+              const auto t1 = __builtin_amdgcn_permlane32_swap(w2[0][1], w2[1][1], false, false);
+              if (m < M && n < N)
+                st_global16(static_cast<bf16_t*>(p.C2) + m * p.ldc + n,
+                            make_uint4(t0[0], t1[0], t0[1], t1[1]));
+            }
           }
           if (m < M && n < N) st_global16(Cp + m * p.ldc + n, out);
         }
@@ -480,6 +496,8 @@ hipError_t launch_bias(const GemmProblem& p, hipStream_t s) {
     case VITBLK_EPI_RESIDUAL: return launch_epi<C, VITBLK_EPI_RESIDUAL, BIAS>(p, s);
     case VITBLK_EPI_GELU: return launch_epi<C, VITBLK_EPI_GELU, BIAS>(p, s);
     case VITBLK_EPI_GELU_GRAD: return launch_epi<C, VITBLK_EPI_GELU_GRAD, BIAS>(p, s);
+    case kEpiGeluDual: return launch_epi<C, kEpiGeluDual, BIAS>(p, s);
+    case kEpiMul: return launch_epi<C, kEpiMul, BIAS>(p, s);
     default: return launch_epi<C, VITBLK_EPI_NONE, BIAS>(p, s);
   }
 }
@@ -503,8 +521,8 @@ bool gemm_fast_ok(const GemmProblem& p) {
             p.lda % 8 == 0 && p.ldb % 8 == 0 && p.ldc % 8 == 0 && aligned16(p.A) &&
             aligned16(p.B) && aligned16(p.C) && p.lda * 2 * 256 < (1LL << 31) &&
             p.ldb * 2 * 256 < (1LL << 31) && p.K * 2 < (1LL << 31);
-  if (p.epi == VITBLK_EPI_RESIDUAL || p.epi == VITBLK_EPI_GELU_GRAD)
-    ok = ok && p.ldr % 8 == 0 && aligned16(p.R);
+  if (reads_r(p)) ok = ok && p.ldr % 8 == 0 && aligned16(p.R);
+  if (p.epi == kEpiGeluDual) ok = ok && aligned16(p.C2);
   if (has_bias(p)) {
     ok = ok && p.bias_seg > 0 && p.bias_seg % 8 == 0 && p.N <= 3 * p.bias_seg;
     for (const void* b : p.bias)
@@ -520,6 +538,7 @@ GemmProblem row_slice(const GemmProblem& p, int64_t r0, int64_t rows) {
   q.A = static_cast<const char*>(p.A) + r0 * p.lda * 2;
   q.C = static_cast<char*>(p.C) + r0 * p.ldc * 2;
   if (p.R) q.R = static_cast<const char*>(p.R) + r0 * p.ldr * 2;
+  if (p.C2) q.C2 = static_cast<char*>(p.C2) + r0 * p.ldc * 2;
   return q;
 }
 
@@ -536,6 +555,7 @@ GemmProblem row_slice(const GemmProblem& p, int64_t r0, int64_t rows) {
 // quarter-size tile, which finishes in a fraction of a round.
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t s) {
   if (reads_r(p) && p.R == nullptr) return hipErrorInvalidValue;  // never launch on a null R
+  if (p.epi == kEpiGeluDual && p.C2 == nullptr) return hipErrorInvalidValue;
   if (!gemm_fast_ok(p)) return launch_gemm_generic(p, s);
   using Big = BigTile;
   using Small = SmallTile;
@@ -546,6 +566,8 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t s) {
     case VITBLK_EPI_RESIDUAL: grid = resident_workgroups<Big, VITBLK_EPI_RESIDUAL>(); break;
     case VITBLK_EPI_GELU: grid = resident_workgroups<Big, VITBLK_EPI_GELU>(); break;
     case VITBLK_EPI_GELU_GRAD: grid = resident_workgroups<Big, VITBLK_EPI_GELU_GRAD>(); break;
+    case kEpiGeluDual: grid = resident_workgroups<Big, kEpiGeluDual>(); break;
+    case kEpiMul: grid = resident_workgroups<Big, kEpiMul>(); break;
     default: grid = resident_workgroups<Big, VITBLK_EPI_NONE>(); break;
   }
   grid = grid / kNumXcd * kNumXcd;

@@ -107,6 +107,11 @@ __global__ __launch_bounds__(kGenThreads) void gemm_generic_kernel(GemmProblem p
       }
       if (EPI == VITBLK_EPI_RESIDUAL) v += load_f32(R + m * p.ldr + n);
       if (EPI == VITBLK_EPI_GELU_GRAD) v *= gelu_tanh_grad_precise(load_f32(R + m * p.ldr + n));
+      if (EPI == kEpiMul) v *= load_f32(R + m * p.ldr + n);
+      if (EPI == kEpiGeluDual) {
+        store_f32(static_cast<T*>(p.C2) + m * p.ldc + n, gelu_tanh_grad_precise(v));
+        v = gelu_tanh_precise(v);
+      }
       if (EPI == VITBLK_EPI_GELU) v = gelu_tanh_precise(v);
       store_f32(C + m * p.ldc + n, v);
     }
@@ -200,6 +205,14 @@ hipError_t gemm_generic_typed(const GemmProblem& p, hipStream_t s) {
       hipLaunchKernelGGL((gemm_generic_kernel<T, VITBLK_EPI_GELU_GRAD>), grid, dim3(kGenThreads),
                          0, s, p, nt);
       break;
+    case kEpiGeluDual:
+      hipLaunchKernelGGL((gemm_generic_kernel<T, kEpiGeluDual>), grid, dim3(kGenThreads), 0, s,
+                         p, nt);
+      break;
+    case kEpiMul:
+      hipLaunchKernelGGL((gemm_generic_kernel<T, kEpiMul>), grid, dim3(kGenThreads), 0, s, p,
+                         nt);
+      break;
     default:
       hipLaunchKernelGGL((gemm_generic_kernel<T, VITBLK_EPI_NONE>), grid, dim3(kGenThreads), 0,
                          s, p, nt);
@@ -227,6 +240,7 @@ hipError_t launch_layernorm_generic(const void* x, int64_t ld_in, const void* ga
 
 hipError_t launch_gemm_generic(const GemmProblem& p, hipStream_t s) {
   if (reads_r(p) && p.R == nullptr) return hipErrorInvalidValue;
+  if (p.epi == kEpiGeluDual && p.C2 == nullptr) return hipErrorInvalidValue;
   return p.dtype == VITBLK_BF16 ? gemm_generic_typed<bf16_t>(p, s)
                                 : gemm_generic_typed<float>(p, s);
 }

@@ -29,7 +29,14 @@ struct GemmProblem {
   int dtype;  // vitblk_dtype
   const void* bias[3];
   int64_t bias_seg;
+  void* C2;  // second output of kEpiGeluDual (same layout as C), else unused
 };
+
+// Internal epilogues of the backward (not part of the C interface):
+// kEpiGeluDual: C = GELU_tanh(acc), C2 = GELU_tanh'(acc) (the recomputed MLP
+// hidden layer and its derivative, from one product); kEpiMul: C = acc * R.
+constexpr int kEpiGeluDual = 16;
+constexpr int kEpiMul = 17;
 
 __host__ __device__ inline bool has_bias(const GemmProblem& p) {
   return p.bias[0] != nullptr || p.bias[1] != nullptr || p.bias[2] != nullptr;
@@ -37,7 +44,7 @@ __host__ __device__ inline bool has_bias(const GemmProblem& p) {
 
 // Epilogues that read R (the residual, or GELU's input for its derivative).
 __host__ __device__ inline bool reads_r(const GemmProblem& p) {
-  return p.epi == VITBLK_EPI_RESIDUAL || p.epi == VITBLK_EPI_GELU_GRAD;
+  return p.epi == VITBLK_EPI_RESIDUAL || p.epi == VITBLK_EPI_GELU_GRAD || p.epi == kEpiMul;
 }
 
 // One (in, out) weight to write out-major: dst[c * ldd + r] = src[r * cols + c].
@@ -133,8 +140,10 @@ hipError_t launch_layernorm_backward(const void* x, const void* g, const void* r
                                      int64_t rows, int64_t D, float eps, int dtype,
                                      hipStream_t stream);
 
-// h[i] = GELU_tanh(z[i]) for i < n.
-hipError_t launch_gelu(const void* z, void* h, int64_t n, int dtype, hipStream_t stream);
+// Any-D version (one workgroup per row); the fast kernel falls back to it.
+hipError_t launch_layernorm_backward_generic(const void* x, const void* g, const void* res,
+                                             void* dx, int64_t rows, int64_t D, float eps,
+                                             int dtype, hipStream_t stream);
 
 // Attention backward: dQ, dK, dV (row stride ldd) from Q, K, V (row stride
 // ld) and dO (row stride ldo).  stats: 3 * N * H * T floats of workspace

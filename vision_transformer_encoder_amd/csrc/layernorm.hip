@@ -126,7 +126,101 @@ hipError_t ln_fast_typed(const T* x, int64_t ld, const T* g, const T* b, T* y, i
   return hipGetLastError();
 }
 
+// Backward of the plain LayerNorm plus a residual gradient, one wave per
+// row with the row of x and of g held in registers:
+// dx = res + rstd * (g - mean(g) - xhat * mean(g * xhat)).  Reads x, g and
+// res once and writes dx once (4 * D * element size bytes per row).
+template <typename T, int NCH>
+__global__ __launch_bounds__(64 * kRowsPerBlock) void ln_bwd_rows_kernel(
+    const T* __restrict__ x, const T* __restrict__ g, const T* __restrict__ res,
+    T* __restrict__ dx, int64_t rows, int D, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;  // whole wave leaves; no workgroup barrier follows
+  const int nchunks = D >> 3;
+  const T* xr = x + row * D;
+  const T* gr = g + row * D;
+  float v[NCH][8], gv[NCH][8];
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int idx = lane + 64 * c;
+    if (idx < nchunks) {
+      load8(xr + idx * 8, v[c]);
+      load8(gr + idx * 8, gv[c]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += v[c][e];
+    }
+  }
+  const float inv_d = 1.0f / static_cast<float>(D);
+  const float mean = wave_sum(s) * inv_d;
+  float q = 0.f, sg = 0.f, sgd = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    if (lane + 64 * c < nchunks) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float d = v[c][e] - mean;
+        q += d * d;
+        sg += gv[c][e];
+        sgd += gv[c][e] * d;
+      }
+    }
+  }
+  const float rstd = 1.0f / sqrtf(wave_sum(q) * inv_d + eps);
+  const float mg = wave_sum(sg) * inv_d;
+  const float mgx = wave_sum(sgd) * rstd * inv_d;  // mean(g * xhat)
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int idx = lane + 64 * c;
+    if (idx < nchunks) {
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = rstd * (gv[c][e] - mg - (v[c][e] - mean) * rstd * mgx);
+      if (res != nullptr) {
+        float r[8];
+        load8(res + row * D + idx * 8, r);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] += r[e];
+      }
+      store8(dx + row * D + idx * 8, o);
+    }
+  }
+}
+
+template <typename T>
+hipError_t ln_bwd_fast_typed(const T* x, const T* g, const T* r, T* dx, int64_t rows, int D,
+                             float eps, hipStream_t s) {
+  const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  const dim3 grid(static_cast<unsigned>(blocks)), block(64 * kRowsPerBlock);
+  const int cpl = (D / 8 + 63) / 64;
+  if (cpl <= 1)
+    hipLaunchKernelGGL((ln_bwd_rows_kernel<T, 1>), grid, block, 0, s, x, g, r, dx, rows, D, eps);
+  else if (cpl <= 2)
+    hipLaunchKernelGGL((ln_bwd_rows_kernel<T, 2>), grid, block, 0, s, x, g, r, dx, rows, D, eps);
+  else if (cpl <= 4)
+    hipLaunchKernelGGL((ln_bwd_rows_kernel<T, 4>), grid, block, 0, s, x, g, r, dx, rows, D, eps);
+  else
+    hipLaunchKernelGGL((ln_bwd_rows_kernel<T, 8>), grid, block, 0, s, x, g, r, dx, rows, D, eps);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_layernorm_backward(const void* x, const void* g, const void* res, void* dx,
+                                     int64_t rows, int64_t D, float eps, int dtype,
+                                     hipStream_t s) {
+  const bool fast = (D % 8 == 0) && (D <= 64 * 8 * 8) &&
+                    (rows + kRowsPerBlock - 1) / kRowsPerBlock <= 2147483647LL;
+  if (!fast) return launch_layernorm_backward_generic(x, g, res, dx, rows, D, eps, dtype, s);
+  if (dtype == VITBLK_BF16)
+    return ln_bwd_fast_typed(static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(g),
+                             static_cast<const bf16_t*>(res), static_cast<bf16_t*>(dx), rows,
+                             static_cast<int>(D), eps, s);
+  return ln_bwd_fast_typed(static_cast<const float*>(x), static_cast<const float*>(g),
+                           static_cast<const float*>(res), static_cast<float*>(dx), rows,
+                           static_cast<int>(D), eps, s);
+}
 
 hipError_t launch_layernorm(const void* x, int64_t ld_in, const void* gamma, const void* beta,
                             void* y, int64_t rows, int64_t D, float eps, int dtype,
