@@ -109,6 +109,54 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
                                            kBufferFlags);
 }
 
+// Output rows as whole 128-byte lines.  A 32-row x 64-column bf16 block
+// arrives as v[2j + q]: lane l holds row l & 31, columns j*32 + q*16 +
+// (l >> 5)*8 .. +7 (16 bytes), so one store instruction would write 32 rows x
+// 32 bytes, a quarter of each row's cache line.  Afterwards v[t] holds rows
+// 8t .. 8t+7, lane L row 8t + (L >> 3) and columns (L & 7)*8 .. +7: each
+// group of 8 lanes covers one row's 64 columns, one full line.
+// The register index bits (j, q) trade places with the lane bits 4 and 3
+// (v_permlane16_swap swaps 16-lane rows; a row_ror:8 DPP read plus a select
+// swaps lanes l and l ^ 8), then one ds_bpermute per dword moves lane
+// (h, j, q, r2 r1 r0) to lane (r2 r1 r0, j, q, h).
+__device__ __forceinline__ void rows_to_lines(uint4 v[4], int lane) {
+  uint32_t w[4][4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    w[s][0] = v[s].x;
+    w[s][1] = v[s].y;
+    w[s][2] = v[s].z;
+    w[s][3] = v[s].w;
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const auto r = __builtin_amdgcn_permlane16_swap(w[q][d], w[2 + q][d], false, false);
+      w[q][d] = r[0];
+      w[2 + q][d] = r[1];
+    }
+  const bool hi8 = (lane >> 3) & 1;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t x = w[2 * a][d], y = w[2 * a + 1][d];
+      const uint32_t xr = __builtin_amdgcn_update_dpp(0u, x, 0x128, 0xf, 0xf, false);
+      const uint32_t yr = __builtin_amdgcn_update_dpp(0u, y, 0x128, 0xf, 0xf, false);
+      w[2 * a][d] = hi8 ? yr : x;
+      w[2 * a + 1][d] = hi8 ? y : xr;
+    }
+  const int src = ((((lane & 1) << 5) | (((lane >> 2) & 1) << 4) | (((lane >> 1) & 1) << 3) |
+                    (lane >> 3)) << 2);
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    v[t] = make_uint4(__builtin_amdgcn_ds_bpermute(src, w[t][0]),
+                      __builtin_amdgcn_ds_bpermute(src, w[t][1]),
+                      __builtin_amdgcn_ds_bpermute(src, w[t][2]),
+                      __builtin_amdgcn_ds_bpermute(src, w[t][3]));
+}
+
 // Persistent tile order.  Workgroup b processes tiles b, b + G, b + 2G, ...
 // The hardware places workgroup b on XCD b % 8, so within each full round of
 // G tiles (G a multiple of 8) the XCD-x workgroups get the contiguous logical
@@ -347,6 +395,43 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
           for (int r = 0; r < 16; ++r) acc[j][i][r] += bv[r];
       }
     }
+    // The plain epilogue rounds and stores each 32-row block as whole row
+    // lines (rows_to_lines): 8% faster on the fused Q|K|V projection.  The GELU
+    // epilogue keeps the direct stores: its exponentials already pace the
+    // stores, and the extra exchange work made it 2% slower.
+    constexpr bool kLines = EPI == VITBLK_EPI_NONE && C::TN == 2;
+    if (kLines) {
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) {
+        uint4 v[4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            uint32_t w[2][2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              float f[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                f[e] = acc[j][i][(2 * q + h) * 4 + e];
+              }
+              w[h][0] = pack_bf16x2(f[0], f[1]);
+              w[h][1] = pack_bf16x2(f[2], f[3]);
+            }
+            const auto s0 = __builtin_amdgcn_permlane32_swap(w[0][0], w[1][0], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(w[0][1], w[1][1], false, false);
+            v[2 * j + q] = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+          }
+        rows_to_lines(v, lane);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int64_t m = cm0 + wm * C::WTM + i * 32 + t * 8 + (lane >> 3);
+          const int64_t n = cn0 + wn * C::WTN + (lane & 7) * 8;
+          if (m < M && n < N) st_global16(Cp + m * p.ldc + n, v[t]);
+        }
+      }
+    }
     // R: the residual, or GELU's input z for the GELU-derivative epilogue.
     constexpr bool kReadsR =
         EPI == VITBLK_EPI_RESIDUAL || EPI == VITBLK_EPI_GELU_GRAD || EPI == kEpiMul;
@@ -367,7 +452,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
       }
     }
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i) {
+    for (int i = 0; i < (kLines ? 0 : C::TM); ++i) {
       const int64_t m = cm0 + wm * C::WTM + i * 32 + lrow;
 #pragma unroll
       for (int j = 0; j < C::TN; ++j) {
