@@ -395,43 +395,6 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
           for (int r = 0; r < 16; ++r) acc[j][i][r] += bv[r];
       }
     }
-    // The plain epilogue rounds and stores each 32-row block as whole row
-    // lines (rows_to_lines): 8% faster on the fused Q|K|V projection.  The GELU
-    // epilogue keeps the direct stores: its exponentials already pace the
-    // stores, and the extra exchange work made it 2% slower.
-    constexpr bool kLines = EPI == VITBLK_EPI_NONE && C::TN == 2;
-    if (kLines) {
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i) {
-        uint4 v[4];
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            uint32_t w[2][2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              float f[4];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                f[e] = acc[j][i][(2 * q + h) * 4 + e];
-              }
-              w[h][0] = pack_bf16x2(f[0], f[1]);
-              w[h][1] = pack_bf16x2(f[2], f[3]);
-            }
-            const auto s0 = __builtin_amdgcn_permlane32_swap(w[0][0], w[1][0], false, false);
-            const auto s1 = __builtin_amdgcn_permlane32_swap(w[0][1], w[1][1], false, false);
-            v[2 * j + q] = make_uint4(s0[0], s1[0], s0[1], s1[1]);
-          }
-        rows_to_lines(v, lane);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int64_t m = cm0 + wm * C::WTM + i * 32 + t * 8 + (lane >> 3);
-          const int64_t n = cn0 + wn * C::WTN + (lane & 7) * 8;
-          if (m < M && n < N) st_global16(Cp + m * p.ldc + n, v[t]);
-        }
-      }
-    }
     // R: the residual, or GELU's input z for the GELU-derivative epilogue.
     constexpr bool kReadsR =
         EPI == VITBLK_EPI_RESIDUAL || EPI == VITBLK_EPI_GELU_GRAD || EPI == kEpiMul;
@@ -451,9 +414,15 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
           }
       }
     }
+    // The plain and residual epilogues store each 32-row block as whole row
+    // lines (rows_to_lines): 8% faster on the fused Q|K|V projection.  The
+    // GELU epilogue keeps the direct stores: its exponentials already pace the
+    // stores, and the extra exchange work made it 2% slower.
+    constexpr bool kLines = (EPI == VITBLK_EPI_NONE || EPI == VITBLK_EPI_RESIDUAL) && C::TN == 2;
 #pragma unroll
-    for (int i = 0; i < (kLines ? 0 : C::TM); ++i) {
+    for (int i = 0; i < C::TM; ++i) {
       const int64_t m = cm0 + wm * C::WTM + i * 32 + lrow;
+      uint4 outs[C::TN][2];
 #pragma unroll
       for (int j = 0; j < C::TN; ++j) {
 #pragma unroll
@@ -526,7 +495,18 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
                             make_uint4(t0[0], t1[0], t0[1], t1[1]));
             }
           }
-          if (m < M && n < N) st_global16(Cp + m * p.ldc + n, out);
+          outs[j][q] = out;
+          if (!kLines && m < M && n < N) st_global16(Cp + m * p.ldc + n, out);
+        }
+      }
+      if (kLines) {
+        uint4 v[4] = {outs[0][0], outs[0][1], outs[C::TN - 1][0], outs[C::TN - 1][1]};
+        rows_to_lines(v, lane);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int64_t mr = cm0 + wm * C::WTM + i * 32 + t * 8 + (lane >> 3);
+          const int64_t nr = cn0 + wn * C::WTN + (lane & 7) * 8;
+          if (mr < M && nr < N) st_global16(Cp + mr * p.ldc + nr, v[t]);
         }
       }
     }
