@@ -50,13 +50,16 @@ template <> __device__ __forceinline__ void store_f32<bf16_t>(bf16_t* p, float v
 
 // GELU, tanh form: 0.5 z (1 + tanh(u)) with u = sqrt(2/pi) (z + 0.044715 z^3).
 // Uses 0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)), evaluated with the hardware
-// base-2 exponential; exact limits z -> +inf (z) and z -> -inf (-0).
+// base-2 exponential; exact limits z -> +inf (z) and z -> -inf (-0).  The
+// exponent -2 log2(e) u = z (c0 + c1 z^2) with the constants folded in double
+// precision: five VALU operations and two transcendentals per element.
 __device__ __forceinline__ float gelu_tanh_fast(float z) {
-  const float k0 = 0.7978845608028654f;        // sqrt(2/pi)
-  const float k1 = 0.044715f;
-  const float m2log2e = -2.8853900817779268f;  // -2 * log2(e)
-  float u = k0 * (z + k1 * z * z * z);
-  float e = __builtin_amdgcn_exp2f(m2log2e * u);
+  constexpr double kU0 = 0.7978845608028654;         // sqrt(2/pi)
+  constexpr double kM2Log2e = -2.8853900817779268;   // -2 * log2(e)
+  constexpr float c0 = static_cast<float>(kM2Log2e * kU0);
+  constexpr float c1 = static_cast<float>(kM2Log2e * kU0 * 0.044715);
+  const float t = __builtin_fmaf(z * z, c1, c0);
+  const float e = __builtin_amdgcn_exp2f(z * t);
   return z * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
