@@ -4,9 +4,13 @@
 // out_features) (crackedaicode.com "ViT Encoder Block", "Inputs and output").
 // The GEMM kernels want both operands contiguous along the reduction axis,
 // so each call first writes W^T once (an HBM-bound transpose of all six
-// weights, one launch).  64 x 64 tiles go through LDS so that reads and
-// writes are both coalesced; the LDS tile is padded by one element so the
-// column-wise reads fall in distinct banks.
+// weights, one launch).
+// bf16 weights whose sides are multiples of 8: each lane moves one 8 x 8
+// block, eight 16-byte row loads, an in-register transpose, eight 16-byte
+// column stores; a wave covers a 64 x 64 tile, so each group of 8 lanes
+// reads and writes whole 128-byte segments.  Other shapes and fp32: 64 x 64
+// tiles through LDS (padded by one element so the column-wise reads fall in
+// distinct banks).
 #include "device.h"
 #include "kernels.h"
 #include "vitblk.h"
@@ -45,6 +49,33 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
   }
 }
 
+// One wave per 64 x 64 tile, four tiles per workgroup; lane (br, bc) =
+// (lane / 8, lane % 8) moves rows br*8..+7, columns bc*8..+7.
+__global__ __launch_bounds__(256) void pack_blocks_kernel(PackArgs a) {
+  const PackJob& j = a.job[blockIdx.y];
+  const int64_t tc = a.tiles_c[blockIdx.y];
+  const int64_t b = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t r0 = (b / tc) * 64, c0 = (b % tc) * 64;
+  if (r0 >= j.rows) return;  // this job has fewer tiles
+  const int lane = threadIdx.x & 63;
+  const int64_t r = r0 + (lane >> 3) * 8, c = c0 + (lane & 7) * 8;
+  if (r >= j.rows || c >= j.cols) return;  // sides are multiples of 8: whole blocks
+  const bf16_t* src = static_cast<const bf16_t*>(j.src) + r * j.cols + c;
+  uint4 in[8], out[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) in[k] = ld_global16(src + k * j.cols);
+  transpose8x8_b16(in, out);
+  bf16_t* dst = static_cast<bf16_t*>(j.dst) + c * j.ldd + r;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) st_global16(dst + k * j.ldd, out[k]);
+}
+
+bool blocks_ok(const PackJob& j) {
+  return j.rows % 8 == 0 && j.cols % 8 == 0 && j.ldd % 8 == 0 &&
+         (reinterpret_cast<uintptr_t>(j.src) & 15u) == 0 &&
+         (reinterpret_cast<uintptr_t>(j.dst) & 15u) == 0;
+}
+
 }  // namespace
 
 hipError_t launch_pack(const PackJob* jobs, int njobs, int dtype, hipStream_t s) {
@@ -58,6 +89,13 @@ hipError_t launch_pack(const PackJob* jobs, int njobs, int dtype, hipStream_t s)
     max_tiles = t > max_tiles ? t : max_tiles;
   }
   if (max_tiles > 2147483647LL) return hipErrorInvalidValue;
+  bool blocks = dtype == VITBLK_BF16;
+  for (int i = 0; i < njobs; ++i) blocks = blocks && blocks_ok(jobs[i]);
+  if (blocks) {
+    const dim3 grid(static_cast<unsigned>((max_tiles + 3) / 4), static_cast<unsigned>(njobs));
+    hipLaunchKernelGGL(pack_blocks_kernel, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   const dim3 grid(static_cast<unsigned>(max_tiles), static_cast<unsigned>(njobs));
   if (dtype == VITBLK_BF16)
     hipLaunchKernelGGL(pack_kernel<bf16_t>, grid, dim3(256), 0, s, a);
