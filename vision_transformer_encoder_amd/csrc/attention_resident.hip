@@ -99,17 +99,38 @@ __global__ __launch_bounds__(64 * kMaxWaves, (DH <= 64 ? 4 : 2)) void attn_resid
 
   // Q fragments of a 32-query tile: lane (lrow, g) holds features
   // 16s + 8g .. +7 of query qt*32 + lrow (clamped to T-1), s = 0 .. DH/16-1.
+  // Each whole 64-feature group is read as full 128-byte row lines (8 lanes
+  // per query row) and regrouped into that layout (lines_to_rows); the rest
+  // (DH % 64) is read in the fragment layout directly.
+  constexpr int G64 = DH / 64;
   bf16x8 qf[DH / 16];
-  auto load_q = [&](int qt) {
+  uint4 qv[G64 > 0 ? G64 : 1][4];
+  auto issue_q = [&](int qt) {
+#pragma unroll
+    for (int gi = 0; gi < G64; ++gi)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int qq = qt * 32 + t * 8 + (lane >> 3);
+        qv[gi][t] = ld_global16(Q + (seq0 + (qq < T ? qq : T - 1)) * ld + hoff + gi * 64 +
+                                (lane & 7) * 8);
+      }
     const int q = qt * 32 + lrow;
     const bf16_t* qrow = Q + (seq0 + (q < T ? q : T - 1)) * ld + hoff + g * 8;
 #pragma unroll
-    for (int s = 0; s < DH / 16; ++s)
+    for (int s = G64 * 4; s < DH / 16; ++s)
       qf[s] = __builtin_bit_cast(bf16x8, ld_global16(qrow + s * 16));
+  };
+  auto finish_q = [&]() {
+#pragma unroll
+    for (int gi = 0; gi < G64; ++gi) {
+      lines_to_rows(qv[gi], lane);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) qf[gi * 4 + s] = __builtin_bit_cast(bf16x8, qv[gi][s]);
+    }
   };
   // The wave's first Q tile is requested together with K and V, so the
   // workgroup waits for one round of memory latency, not two.
-  if (wave < nqt) load_q(wave);
+  if (wave < nqt) issue_q(wave);
 
   // ---- K and V of this head into LDS (4 chunks of 16 B per operand in flight per thread).
   constexpr int CPR = DH / 8;  // 16-byte chunks per row
@@ -143,6 +164,7 @@ __global__ __launch_bounds__(64 * kMaxWaves, (DH <= 64 ? 4 : 2)) void attn_resid
       *reinterpret_cast<uint4*>(vs + (c / PC) * C::SV + (DH + (c % PC) * 8) * 2) =
           make_uint4(0, 0, 0, 0);
   }
+  if (wave < nqt) finish_q();
   __syncthreads();
 
   const int i16 = lane & 15, q16 = (lane >> 4) & 1;
@@ -152,7 +174,10 @@ __global__ __launch_bounds__(64 * kMaxWaves, (DH <= 64 ? 4 : 2)) void attn_resid
 
   for (int qt = wave; qt < nqt; qt += nw) {
     const int q = qt * 32 + lrow;
-    if (qt != wave) load_q(qt);
+    if (qt != wave) {
+      issue_q(qt);
+      finish_q();
+    }
     f32x16 o[C::DHP / 32];
 #pragma unroll
     for (int d = 0; d < C::DHP / 32; ++d)
@@ -257,10 +282,41 @@ __global__ __launch_bounds__(64 * kMaxWaves, (DH <= 64 ? 4 : 2)) void attn_resid
     if (k0 < T) chunk(k0, std::true_type{});
 
     const float inv = 1.0f / sum_halves(l_run);
+    // Each whole 64-feature group leaves as full row lines: the pair of
+    // 32-feature accumulator blocks is normalised, rounded, half-exchanged
+    // (v_permlane32_swap) and regrouped (rows_to_lines), 8 lanes per row.
+#pragma unroll
+    for (int gi = 0; gi < G64; ++gi) {
+      uint4 v[4];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh) {
+          uint32_t w[2][2];
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const f32x16& od = o[gi * 2 + jj];
+            const int r0 = (2 * qh + h2) * 4;
+            w[h2][0] = pack_bf16x2(od[r0 + 0] * inv, od[r0 + 1] * inv);
+            w[h2][1] = pack_bf16x2(od[r0 + 2] * inv, od[r0 + 3] * inv);
+          }
+          const auto s0 = __builtin_amdgcn_permlane32_swap(w[0][0], w[1][0], false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(w[0][1], w[1][1], false, false);
+          v[2 * jj + qh] = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+        }
+      rows_to_lines(v, lane);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int qq = qt * 32 + t * 8 + (lane >> 3);
+        if (qq < T)
+          st_global16(O + (seq0 + qq) * ldo + hoff + gi * 64 + (lane & 7) * 8, v[t]);
+      }
+    }
+    // Blocks past the whole 64-feature groups: direct 8-byte stores.
     if (q < T) {
       bf16_t* orow = O + (seq0 + q) * ldo + hoff;
 #pragma unroll
-      for (int d = 0; d < C::DHP / 32; ++d)
+      for (int d = 2 * G64; d < C::DHP / 32; ++d)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int f = d * 32 + rr * 8 + g * 4;

@@ -158,4 +158,92 @@ __device__ __forceinline__ void transpose8x8_b16(const uint4 in[8], uint4 out[8]
   }
 }
 
+// ------------------------------------------------------------- row blocks <-> whole lines
+//
+// A 32-row x 64-column bf16 block held as v[2j + q], lane l: row l & 31,
+// columns j*32 + q*16 + (l >> 5)*8 .. +7 (16 bytes) -- the layout of a
+// 32x32x16 MFMA accumulator pair after one v_permlane32_swap, and of eight
+// consecutive 16-wide k-steps of an MFMA operand.  A memory instruction in that
+// layout touches 32 rows x 32 bytes, a quarter of each row's 128-byte line.
+// rows_to_lines turns it into v[t]: rows 8t .. 8t+7, lane L row 8t + (L >> 3),
+// columns (L & 7)*8 .. +7, so each group of 8 lanes covers one row's 64
+// columns, one full line; lines_to_rows is the inverse.
+// The register index bits (j, q) trade places with the lane bits 4 and 3
+// (v_permlane16_swap swaps 16-lane rows; a row_ror:8 DPP read plus a select
+// swaps lanes l and l ^ 8), then one ds_bpermute per dword moves lane
+// (h, j, q, r2 r1 r0) to lane (r2 r1 r0, j, q, h).
+__device__ __forceinline__ void rows_to_lines(uint4 v[4], int lane) {
+  uint32_t w[4][4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    w[s][0] = v[s].x;
+    w[s][1] = v[s].y;
+    w[s][2] = v[s].z;
+    w[s][3] = v[s].w;
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const auto r = __builtin_amdgcn_permlane16_swap(w[q][d], w[2 + q][d], false, false);
+      w[q][d] = r[0];
+      w[2 + q][d] = r[1];
+    }
+  const bool hi8 = (lane >> 3) & 1;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t x = w[2 * a][d], y = w[2 * a + 1][d];
+      const uint32_t xr = __builtin_amdgcn_update_dpp(0u, x, 0x128, 0xf, 0xf, false);
+      const uint32_t yr = __builtin_amdgcn_update_dpp(0u, y, 0x128, 0xf, 0xf, false);
+      w[2 * a][d] = hi8 ? yr : x;
+      w[2 * a + 1][d] = hi8 ? y : xr;
+    }
+  const int src = ((((lane & 1) << 5) | (((lane >> 2) & 1) << 4) | (((lane >> 1) & 1) << 3) |
+                    (lane >> 3)) << 2);
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    v[t] = make_uint4(__builtin_amdgcn_ds_bpermute(src, w[t][0]),
+                      __builtin_amdgcn_ds_bpermute(src, w[t][1]),
+                      __builtin_amdgcn_ds_bpermute(src, w[t][2]),
+                      __builtin_amdgcn_ds_bpermute(src, w[t][3]));
+}
+
+// Inverse of rows_to_lines (the two exchange steps are involutions; the lane
+// permutation is undone by the inverse ds_bpermute).
+__device__ __forceinline__ void lines_to_rows(uint4 v[4], int lane) {
+  uint32_t w[4][4];
+  const int src = ((((lane & 7) << 3) | (((lane >> 4) & 1) << 2) | (((lane >> 3) & 1) << 1) |
+                    (lane >> 5)) << 2);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    w[s][0] = __builtin_amdgcn_ds_bpermute(src, v[s].x);
+    w[s][1] = __builtin_amdgcn_ds_bpermute(src, v[s].y);
+    w[s][2] = __builtin_amdgcn_ds_bpermute(src, v[s].z);
+    w[s][3] = __builtin_amdgcn_ds_bpermute(src, v[s].w);
+  }
+  const bool hi8 = (lane >> 3) & 1;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t x = w[2 * a][d], y = w[2 * a + 1][d];
+      const uint32_t xr = __builtin_amdgcn_update_dpp(0u, x, 0x128, 0xf, 0xf, false);
+      const uint32_t yr = __builtin_amdgcn_update_dpp(0u, y, 0x128, 0xf, 0xf, false);
+      w[2 * a][d] = hi8 ? yr : x;
+      w[2 * a + 1][d] = hi8 ? y : xr;
+    }
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const auto r = __builtin_amdgcn_permlane16_swap(w[q][d], w[2 + q][d], false, false);
+      w[q][d] = r[0];
+      w[2 + q][d] = r[1];
+    }
+#pragma unroll
+  for (int s = 0; s < 4; ++s) v[s] = make_uint4(w[s][0], w[s][1], w[s][2], w[s][3]);
+}
+
 }  // namespace vitblk

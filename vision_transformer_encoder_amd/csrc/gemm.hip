@@ -109,54 +109,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
                                            kBufferFlags);
 }
 
-// Output rows as whole 128-byte lines.  A 32-row x 64-column bf16 block
-// arrives as v[2j + q]: lane l holds row l & 31, columns j*32 + q*16 +
-// (l >> 5)*8 .. +7 (16 bytes), so one store instruction would write 32 rows x
-// 32 bytes, a quarter of each row's cache line.  Afterwards v[t] holds rows
-// 8t .. 8t+7, lane L row 8t + (L >> 3) and columns (L & 7)*8 .. +7: each
-// group of 8 lanes covers one row's 64 columns, one full line.
-// The register index bits (j, q) trade places with the lane bits 4 and 3
-// (v_permlane16_swap swaps 16-lane rows; a row_ror:8 DPP read plus a select
-// swaps lanes l and l ^ 8), then one ds_bpermute per dword moves lane
-// (h, j, q, r2 r1 r0) to lane (r2 r1 r0, j, q, h).
-__device__ __forceinline__ void rows_to_lines(uint4 v[4], int lane) {
-  uint32_t w[4][4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    w[s][0] = v[s].x;
-    w[s][1] = v[s].y;
-    w[s][2] = v[s].z;
-    w[s][3] = v[s].w;
-  }
-#pragma unroll
-  for (int q = 0; q < 2; ++q)
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const auto r = __builtin_amdgcn_permlane16_swap(w[q][d], w[2 + q][d], false, false);
-      w[q][d] = r[0];
-      w[2 + q][d] = r[1];
-    }
-  const bool hi8 = (lane >> 3) & 1;
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const uint32_t x = w[2 * a][d], y = w[2 * a + 1][d];
-      const uint32_t xr = __builtin_amdgcn_update_dpp(0u, x, 0x128, 0xf, 0xf, false);
-      const uint32_t yr = __builtin_amdgcn_update_dpp(0u, y, 0x128, 0xf, 0xf, false);
-      w[2 * a][d] = hi8 ? yr : x;
-      w[2 * a + 1][d] = hi8 ? y : xr;
-    }
-  const int src = ((((lane & 1) << 5) | (((lane >> 2) & 1) << 4) | (((lane >> 1) & 1) << 3) |
-                    (lane >> 3)) << 2);
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-    v[t] = make_uint4(__builtin_amdgcn_ds_bpermute(src, w[t][0]),
-                      __builtin_amdgcn_ds_bpermute(src, w[t][1]),
-                      __builtin_amdgcn_ds_bpermute(src, w[t][2]),
-                      __builtin_amdgcn_ds_bpermute(src, w[t][3]));
-}
-
 // Persistent tile order.  Workgroup b processes tiles b, b + G, b + 2G, ...
 // The hardware places workgroup b on XCD b % 8, so within each full round of
 // G tiles (G a multiple of 8) the XCD-x workgroups get the contiguous logical
