@@ -100,7 +100,12 @@ def _attention_ref(q, k, v, H):
     (20, 197, 1024, 16),  # 320 (sequence, head) items: some workgroups take two
     (80, 100, 512, 8),   # 640 items over several workgroups each; ragged last chunk
     (2, 257, 160, 2),    # d_h 80
-    (1, 1025, 64, 1),    # long sequence
+    (1, 1025, 64, 1),    # long sequence (streaming kernel from here on)
+    (2, 640, 128, 2),    # streaming, d_h 64, T a multiple of 64 (no partial chunk)
+    (1, 900, 64, 2),     # streaming, d_h 32
+    (1, 700, 160, 2),    # streaming, d_h 80
+    (1, 777, 192, 2),    # streaming, d_h 96
+    (1, 600, 256, 2),    # streaming, d_h 128
     (3, 1, 128, 2),      # single token: output = V
     (2, 33, 96, 3),      # d_h 32, one key past a 32-block
     (2, 65, 256, 2),     # d_h 128

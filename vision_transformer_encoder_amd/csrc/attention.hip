@@ -25,6 +25,7 @@
 //   scores set to -inf; 32-key blocks entirely past T are skipped.
 #include <math.h>
 
+#include "attention_tile.h"
 #include "device.h"
 #include "kernels.h"
 #include "vitblk.h"
@@ -257,6 +258,140 @@ __global__ __launch_bounds__(64 * kWaves) void attn_fwd_kernel(
   }
 }
 
+// ---------------------------------------------------------------- streaming kernel
+//
+// Sequences too long for the resident kernel (ViT at 512 px: T = 1025): keys
+// stream through LDS in 64-key chunks, two stages deep.  A workgroup is 8
+// waves over one (sequence, head) and up to 8 query tiles of 32, so each
+// K/V chunk copied into LDS serves up to 256 queries; per chunk every thread
+// requests its share of the next chunk before the tile work on the current
+// one and writes it to the other stage after, and one barrier ends the chunk.
+// The per-tile work is attention_tile.h's (the resident kernel's).
+constexpr int kStreamWaves = 8;
+
+template <int DH>
+__global__ __launch_bounds__(64 * kStreamWaves, (DH <= 64 ? 4 : 2)) void attn_stream_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    int64_t ld, bf16_t* __restrict__ O, int64_t ldo, int T, int H, int nqb, int tpb,
+    float scale_log2) {
+  using C = attn::Cfg<DH>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];  // [2][64 K rows | 64 V rows]
+  constexpr int STAGE = 64 * C::ROW;
+
+  // Workgroup -> (n, h, query block); each XCD gets a contiguous run so the
+  // query blocks of one head share its K/V in that XCD's L2.
+  const int64_t total = gridDim.x;
+  const int64_t bid = blockIdx.x;
+  const int64_t qx = total / kNumXcd, rx = total % kNumXcd;
+  const int64_t x = bid % kNumXcd;
+  const int64_t b2 = x * qx + (x < rx ? x : rx) + bid / kNumXcd;
+  const int qb = static_cast<int>(b2 % nqb);
+  const int64_t nh = b2 / nqb;
+  const int64_t seq0 = (nh / H) * static_cast<int64_t>(T);
+  const int64_t hoff = static_cast<int64_t>(nh % H) * DH;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nqt = (T + 31) / 32;
+  const int qt = qb * tpb + wave;
+  const bool active = wave < tpb && qt < nqt;  // wave-uniform
+
+  // Staging of one chunk: 64 keys x DH/8 chunks of 16 bytes per operand.
+  constexpr int CPR = DH / 8;
+  constexpr int PER = 64 * CPR;
+  constexpr int NL = (PER + 64 * kStreamWaves - 1) / (64 * kStreamWaves);
+  uint4 rk[NL], rv[NL];
+  auto fetch = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int e = tid + i * 64 * kStreamWaves;
+      if (e < PER) {
+        int t = c * 64 + e / CPR;
+        t = t < T ? t : T - 1;
+        const int64_t gofs = (seq0 + t) * ld + hoff + (e % CPR) * 8;
+        rk[i] = ld_global16(K + gofs);
+        rv[i] = ld_global16(V + gofs);
+      }
+    }
+  };
+  auto stash = [&](int st) {
+    char* const ks = smem + st * STAGE;
+    char* const vs = ks + 64 * C::SK;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int e = tid + i * 64 * kStreamWaves;
+      if (e < PER) {
+        *reinterpret_cast<uint4*>(ks + (e / CPR) * C::SK + (e % CPR) * 16) = rk[i];
+        *reinterpret_cast<uint4*>(vs + (e / CPR) * C::SV + (e % CPR) * 16) = rv[i];
+      }
+    }
+  };
+
+  attn::QLoad<DH> ql;
+  if (active) ql.issue(Q, ld, seq0, hoff, T, qt * 32, lane);
+  fetch(0);
+  if (C::DHP > DH) {  // features DH..DHP-1 of V feed only discarded output rows; keep them 0
+    constexpr int PC = (C::DHP - DH) / 8;
+    for (int e = tid; e < 2 * 64 * PC; e += 64 * kStreamWaves) {
+      const int st = e / (64 * PC), r = (e / PC) % 64;
+      *reinterpret_cast<uint4*>(smem + st * STAGE + 64 * C::SK + r * C::SV +
+                                (DH + (e % PC) * 8) * 2) = make_uint4(0, 0, 0, 0);
+    }
+  }
+  stash(0);
+  if (active) ql.finish(lane);
+  __syncthreads();
+
+  attn::Tile<DH> tile;
+  tile.init();
+  const int v_lane = attn::v_lane_offset<DH>(lane);
+  const int KF = T / 64;                 // whole 64-key chunks
+  const int KC = KF + (T % 64 != 0 ? 1 : 0);
+  for (int c = 0; c < KF; ++c) {
+    const int st = c & 1;
+    if (c + 1 < KC) fetch(c + 1);
+    if (active) {
+      const char* ks = smem + st * STAGE;
+      tile.template chunk<false>(ql.qf, ks, ks + 64 * C::SK, 64, scale_log2, lane, v_lane);
+    }
+    if (c + 1 < KC) stash(st ^ 1);
+    __syncthreads();
+  }
+  if (KC > KF && active) {  // the last, partial chunk (already in its stage)
+    const char* ks = smem + (KF & 1) * STAGE;
+    tile.template chunk<true>(ql.qf, ks, ks + 64 * C::SK, T - KF * 64, scale_log2, lane, v_lane);
+  }
+  if (active) tile.store(O, ldo, seq0, hoff, T, qt * 32, lane);
+}
+
+template <int DH>
+hipError_t launch_stream(const void* q, const void* k, const void* v, int64_t ld, void* o,
+                         int64_t ldo, int64_t N, int64_t T, int64_t H, hipStream_t s) {
+  using C = attn::Cfg<DH>;
+  constexpr size_t bytes = 2 * 64 * C::ROW;
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_stream_kernel<DH>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(bytes)) != hipSuccess) {
+      (void)hipGetLastError();
+      return hipErrorNotSupported;
+    }
+    attr_set = true;
+  }
+  const int64_t nqt = (T + 31) / 32;
+  const int64_t nqb = (nqt + kStreamWaves - 1) / kStreamWaves;
+  const int64_t tpb = (nqt + nqb - 1) / nqb;  // query tiles per workgroup, balanced
+  const int64_t blocks = N * H * nqb;
+  if (blocks > 2147483647LL) return hipErrorInvalidValue;
+  const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(DH));
+  hipLaunchKernelGGL(attn_stream_kernel<DH>, dim3(static_cast<unsigned>(blocks)),
+                     dim3(64 * kStreamWaves), bytes, s, static_cast<const bf16_t*>(q),
+                     static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), ld,
+                     static_cast<bf16_t*>(o), ldo, static_cast<int>(T), static_cast<int>(H),
+                     static_cast<int>(nqb), static_cast<int>(tpb), scale_log2);
+  return hipGetLastError();
+}
+
 template <int DH>
 hipError_t launch_dh(const void* q, const void* k, const void* v, int64_t ld, void* o,
                      int64_t ldo, int64_t N, int64_t T, int64_t H, hipStream_t s) {
@@ -281,7 +416,16 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, int64_t
   const bool fast = dtype == VITBLK_BF16 && ld % 8 == 0 && ldo % 8 == 0 && aligned16(q) &&
                     aligned16(k) && aligned16(v) && aligned16(o);
   if (fast) {
-    const hipError_t r = launch_attention_resident(q, k, v, ld, o, ldo, N, T, H, dh, s);
+    hipError_t r = launch_attention_resident(q, k, v, ld, o, ldo, N, T, H, dh, s);
+    if (r != hipErrorNotSupported) return r;
+    switch (dh) {
+      case 32: r = launch_stream<32>(q, k, v, ld, o, ldo, N, T, H, s); break;
+      case 64: r = launch_stream<64>(q, k, v, ld, o, ldo, N, T, H, s); break;
+      case 80: r = launch_stream<80>(q, k, v, ld, o, ldo, N, T, H, s); break;
+      case 96: r = launch_stream<96>(q, k, v, ld, o, ldo, N, T, H, s); break;
+      case 128: r = launch_stream<128>(q, k, v, ld, o, ldo, N, T, H, s); break;
+      default: break;
+    }
     if (r != hipErrorNotSupported) return r;
     switch (dh) {
       case 32: return launch_dh<32>(q, k, v, ld, o, ldo, N, T, H, s);
