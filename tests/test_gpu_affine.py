@@ -121,6 +121,18 @@ def test_affine_block_full_size(name):
                  f"affine {name} sequences {seqs}")
 
 
+def test_affine_block_split_k_tail_rows():
+    # As the plain block's split-K case: the MLP2 bias is added by the
+    # reduction of the tail rows' K-range partials.
+    N, T, D, H, F = 85, 197, 1024, 16, 4096
+    inp = make_block_inputs(N, T, D, F, "bf16", seed=10)
+    prm = make_affine_params(D, F, "bf16", seed=10)
+    out, _ = _run(inp, prm, H, 1e-6, "bf16")
+    seqs = [83, 84]
+    assert_close(to_host(out)[seqs], _oracle(inp, prm, H, 1e-6, seqs), "bf16",
+                 f"affine split-K tail {seqs}")
+
+
 @pytest.mark.parametrize("drop", [("b_q", "b_v"), ("ln1_gamma", "ln2_beta", "b_mlp1"),
                                   ("b_k",), tuple(oracle.AFFINE_KEYS)])
 def test_affine_block_with_some_parameters_absent(drop):

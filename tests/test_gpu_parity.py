@@ -193,6 +193,21 @@ def test_block_full_size(name):
                  f"{name} sequences {seqs}")
 
 
+def test_block_split_k_tail_rows():
+    # N*T = 16745 rows at D = 1024: the 256x256 tiles cover 16384 rows in
+    # whole rounds and the last 361 rows (ragged) go to the small tiles; the
+    # two residual products sum them over K in ranges (fp32 partials, then an
+    # in-order reduction with the residual).  Sequence 83 straddles the
+    # boundary, 84 lies wholly in the tail.
+    N, T, D, H, F = 85, 197, 1024, 16, 4096
+    inp = make_block_inputs(N, T, D, F, "bf16", seed=9)
+    out, _ = _run_block(inp, H, 1e-6, "bf16")
+    got = to_host(out)
+    assert np.all(np.isfinite(got))
+    seqs = [0, 83, 84]
+    assert_close(got[seqs], _oracle(inp, H, 1e-6, seqs), "bf16", f"split-K tail {seqs}")
+
+
 def test_tiny_workload_seed0():
     w = WORKLOADS["tiny"]
     inp = make_block_inputs(w.N, w.T, w.D, w.F, w.dtype, seed=0)

@@ -83,20 +83,24 @@ int run_block(const void* x, const void* packed, const vitblk_affine_params* prm
   // att = concat_h softmax(Q_h K_h^T / sqrt(dh)) V_h   (overwrites xn)
   VITBLK_LAUNCH(launch_attention(big, big + D * es, big + 2 * D * es, 3 * D, a, D, N, T, H,
                                  D / H, dtype, s));
-  // y = x + att @ w_o + b_o
-  VITBLK_LAUNCH(launch_gemm(linear_problem(a, pk + pl.packed.off_o, y, x, M, D, D,
-                                           VITBLK_EPI_RESIDUAL, dtype, q.b_o),
-                            s));
+  // y = x + att @ w_o + b_o   (qkv's region is free again: split-K scratch)
+  GemmProblem po = linear_problem(a, pk + pl.packed.off_o, y, x, M, D, D, VITBLK_EPI_RESIDUAL,
+                                  dtype, q.b_o);
+  po.scratch = reinterpret_cast<float*>(big);
+  po.scratch_floats = static_cast<int64_t>(pl.off_act - pl.off_big) / 4;
+  VITBLK_LAUNCH(launch_gemm(po, s));
   // LN2: yn = gamma_2 LN(y) + beta_2   (overwrites att)
   VITBLK_LAUNCH(launch_layernorm(y, D, q.ln2_gamma, q.ln2_beta, a, M, D, feps, dtype, s));
   // hidden = GELU(yn @ w_mlp1 + b_mlp1)   (overwrites qkv)
   VITBLK_LAUNCH(launch_gemm(linear_problem(a, pk + pl.packed.off_1, big, nullptr, M, D, F,
                                            VITBLK_EPI_GELU, dtype, q.b_mlp1),
                             s));
-  // out = y + hidden @ w_mlp2 + b_mlp2
-  VITBLK_LAUNCH(launch_gemm(linear_problem(big, pk + pl.packed.off_2, out, y, M, F, D,
-                                           VITBLK_EPI_RESIDUAL, dtype, q.b_mlp2),
-                            s));
+  // out = y + hidden @ w_mlp2 + b_mlp2   (yn's region is free again: split-K scratch)
+  GemmProblem p2 = linear_problem(big, pk + pl.packed.off_2, out, y, M, F, D,
+                                  VITBLK_EPI_RESIDUAL, dtype, q.b_mlp2);
+  p2.scratch = reinterpret_cast<float*>(a);
+  p2.scratch_floats = static_cast<int64_t>(pl.off_y - pl.off_act) / 4;
+  VITBLK_LAUNCH(launch_gemm(p2, s));
   return VITBLK_OK;
 }
 

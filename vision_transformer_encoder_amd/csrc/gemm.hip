@@ -139,8 +139,15 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int lrow = lane & 31, lhalf = lane >> 5;
   const int64_t M = p.M, N = p.N;
-  const int KT = static_cast<int>(p.K / C::BK);
-  const int total = mt * nt, grid = gridDim.x;
+  // Split K (kEpiPartial): the tile index runs over ksplit copies of the
+  // mt x nt tiles, copy s covering k-slices [KA * s / ksplit, KA * (s + 1) /
+  // ksplit).  Otherwise one copy and the whole of K.
+  constexpr bool kSplit = EPI == kEpiPartial;
+  const int KA = static_cast<int>(p.K / C::BK);
+  const int nsplit = kSplit ? p.ksplit : 1;
+  int KT = KA;
+  int ks = 0;  // k-range of the current tile
+  const int total = mt * nt * nsplit, grid = gridDim.x;
 
   // Tile-dependent load state: buffer resources at the tiles' first rows and
   // per-lane byte offsets of the chunks this thread loads (rows past M or N
@@ -150,11 +157,20 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
   uint32_t a_off[C::A_LOADS], b_off[C::B_LOADS];
   auto prepare = [&](int t) {
     int tm, tn;
-    tile_of(t, grid, total, mt, nt, &tm, &tn);
+    tile_of(t, grid, total, mt * nsplit, nt, &tm, &tn);
+    int64_t kbyte = 0;
+    if (kSplit) {
+      // The k-ranges are laid out as further M-tiles of the tile order.
+      ks = tm / mt;
+      tm -= ks * mt;
+      const int k0 = KA * ks / nsplit, k1 = KA * (ks + 1) / nsplit;
+      KT = k1 - k0;
+      kbyte = static_cast<int64_t>(k0) * C::BK * 2;
+    }
     m0 = static_cast<int64_t>(tm) * C::BM;
     n0 = static_cast<int64_t>(tn) * C::BN;
-    a_rs = make_rsrc(static_cast<const char*>(p.A) + m0 * p.lda * 2);
-    b_rs = make_rsrc(static_cast<const char*>(p.B) + n0 * p.ldb * 2);
+    a_rs = make_rsrc(static_cast<const char*>(p.A) + m0 * p.lda * 2 + kbyte);
+    b_rs = make_rsrc(static_cast<const char*>(p.B) + n0 * p.ldb * 2 + kbyte);
 #pragma unroll
     for (int i = 0; i < C::A_LOADS; ++i) {
       const int e = i * C::NT + tid, row = e / C::CPR;
@@ -300,6 +316,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
     // Start the next tile's first k-slices before this tile's epilogue (all
     // waves are done reading LDS once past this barrier).
     const int64_t cm0 = m0, cn0 = n0;
+    const int cks = ks;
     const int t_next = t + grid;
     const bool more = t_next < total;
     __builtin_amdgcn_s_barrier();
@@ -371,8 +388,37 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
     // GELU epilogue keeps the direct stores: its exponentials already pace the
     // stores, and the extra exchange work made it 2% slower.
     constexpr bool kLines = (EPI == VITBLK_EPI_NONE || EPI == VITBLK_EPI_RESIDUAL) && C::TN == 2;
+    if (kSplit) {
+      // Unrounded fp32 sums of this k-range: after the fp32 half exchange a
+      // lane holds 8 consecutive columns of one row (32 bytes).
+      float* P = static_cast<float*>(p.C) + static_cast<int64_t>(cks) * M * p.ldc;
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i) {
+      for (int i = 0; i < C::TM; ++i) {
+        const int64_t m = cm0 + wm * C::WTM + i * 32 + lrow;
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int64_t n = cn0 + wn * C::WTN + j * 32 + q * 16 + lhalf * 8;
+            float x[4], y[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const auto r = __builtin_amdgcn_permlane32_swap(
+                  __float_as_uint(acc[j][i][(2 * q) * 4 + e]),
+                  __float_as_uint(acc[j][i][(2 * q + 1) * 4 + e]), false, false);
+              x[e] = __uint_as_float(r[0]);
+              y[e] = __uint_as_float(r[1]);
+            }
+            if (m < M && n < N) {
+              float4* d = reinterpret_cast<float4*>(P + m * p.ldc + n);
+              d[0] = make_float4(x[0], x[1], x[2], x[3]);
+              d[1] = make_float4(y[0], y[1], y[2], y[3]);
+            }
+          }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < (kSplit ? 0 : C::TM); ++i) {
       const int64_t m = cm0 + wm * C::WTM + i * 32 + lrow;
       uint4 outs[C::TN][2];
 #pragma unroll
@@ -472,6 +518,55 @@ using BigTile = Cfg<256, 256, 2, 4, 64, 2, 3>;
 // 4 waves, 64x64 per wave, 80 KB LDS: 2 workgroups per CU.
 using SmallTile = Cfg<128, 128, 2, 2, 64, 2, 3>;
 
+// Split-K finish: C[m, n] = bf16(((sum_s P[s, m, n]) + b[n]) + R[m, n]), the
+// partials summed in order in fp32 (the same order of additions as the
+// one-pass residual epilogue: products, then bias, then residual).  One
+// thread per 8 consecutive columns; N is a multiple of 8.
+__global__ __launch_bounds__(256) void splitk_residual_kernel(const float* __restrict__ P,
+                                                              int S, int64_t M, int64_t N,
+                                                              const bf16_t* __restrict__ R,
+                                                              int64_t ldr,
+                                                              const bf16_t* __restrict__ bias,
+                                                              bf16_t* __restrict__ Cp,
+                                                              int64_t ldc) {
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t per_row = N >> 3;
+  if (g >= M * per_row) return;
+  const int64_t m = g / per_row, n = (g - m * per_row) * 8;
+  float v[8];
+  {
+    const float4* q = reinterpret_cast<const float4*>(P + m * N + n);
+    const float4 a = q[0], b = q[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  for (int sp = 1; sp < S; ++sp) {
+    const float4* q = reinterpret_cast<const float4*>(P + (sp * M + m) * N + n);
+    const float4 a = q[0], b = q[1];
+    v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
+    v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
+  }
+  if (bias != nullptr) {  // 8-byte aligned
+    const uint2 u0 = *reinterpret_cast<const uint2*>(bias + n);
+    const uint2 u1 = *reinterpret_cast<const uint2*>(bias + n + 4);
+    const uint32_t w[4] = {u0.x, u0.y, u1.x, u1.y};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] += __uint_as_float(w[e] << 16);
+      v[2 * e + 1] += __uint_as_float(w[e] & 0xffff0000u);
+    }
+  }
+  const uint4 r = ld_global16(R + m * ldr + n);
+  const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] += __uint_as_float(rw[e] << 16);
+    v[2 * e + 1] += __uint_as_float(rw[e] & 0xffff0000u);
+  }
+  st_global16(Cp + m * ldc + n, make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                           pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])));
+}
+
 // Workgroups of this kernel the device holds at once (cached per kernel).
 template <class C, int EPI, bool BIAS = false>
 int resident_workgroups() {
@@ -494,7 +589,7 @@ int resident_workgroups() {
 template <class C, int EPI, bool BIAS>
 hipError_t launch_epi(const GemmProblem& p, hipStream_t s) {
   const int64_t mt = (p.M + C::BM - 1) / C::BM, nt = (p.N + C::BN - 1) / C::BN;
-  const int64_t tiles = mt * nt;
+  const int64_t tiles = mt * nt * (EPI == kEpiPartial ? p.ksplit : 1);
   if (tiles > 2147483647LL) return hipErrorInvalidValue;
   int64_t grid = resident_workgroups<C, EPI, BIAS>();
   if (grid <= 0) return hipErrorInvalidValue;
@@ -515,6 +610,7 @@ hipError_t launch_bias(const GemmProblem& p, hipStream_t s) {
     case VITBLK_EPI_GELU_GRAD: return launch_epi<C, VITBLK_EPI_GELU_GRAD, BIAS>(p, s);
     case kEpiGeluDual: return launch_epi<C, kEpiGeluDual, BIAS>(p, s);
     case kEpiMul: return launch_epi<C, kEpiMul, BIAS>(p, s);
+    case kEpiPartial: return launch_epi<C, kEpiPartial, false>(p, s);
     default: return launch_epi<C, VITBLK_EPI_NONE, BIAS>(p, s);
   }
 }
@@ -559,6 +655,51 @@ GemmProblem row_slice(const GemmProblem& p, int64_t r0, int64_t rows) {
   return q;
 }
 
+constexpr int kMaxSplit = 8;       // k-ranges of a split-K tail
+constexpr int kMinSplitSlices = 4;  // k-slices (of 64) per range at least
+
+// The last rows of a product, left over by the big tile's whole rounds.  On
+// the small tile they are few tiles; when K is long each runs for a long time
+// while most CUs idle.  A residual product (the one kind whose result needs
+// no nonlinearity after the sum) then splits K into S ranges, as many as
+// fill the resident small-tile slots: the ranges' unrounded fp32 sums go to
+// the caller's scratch memory and a second kernel adds them in order, with
+// the bias and the residual, and rounds once.  Otherwise one small-tile
+// launch.
+hipError_t launch_tail(const GemmProblem& p, hipStream_t s) {
+  using Small = SmallTile;
+  const int64_t tiles = ((p.M + Small::BM - 1) / Small::BM) * ((p.N + Small::BN - 1) / Small::BN);
+  const int64_t ka = p.K / Small::BK;
+  int64_t S = 0;
+  if (p.epi == VITBLK_EPI_RESIDUAL && p.scratch != nullptr && p.bias[1] == nullptr &&
+      p.bias[2] == nullptr && (p.bias[0] == nullptr || p.bias_seg >= p.N) &&
+      p.ldc % 8 == 0 && (reinterpret_cast<uintptr_t>(p.scratch) & 15u) == 0) {
+    const int64_t slots = resident_workgroups<Small, kEpiPartial>();
+    S = tiles > 0 ? slots / tiles : 0;
+    if (S > kMaxSplit) S = kMaxSplit;
+    if (S > ka / kMinSplitSlices) S = ka / kMinSplitSlices;
+    while (S > 1 && S * p.M * p.N > p.scratch_floats) --S;
+  }
+  if (S < 2) return launch_cfg<Small>(p, s);
+  GemmProblem q = p;
+  q.epi = kEpiPartial;
+  q.ksplit = static_cast<int>(S);
+  q.C = p.scratch;
+  q.ldc = p.N;
+  q.R = nullptr;
+  q.bias[0] = q.bias[1] = q.bias[2] = nullptr;
+  hipError_t e = launch_epi<Small, kEpiPartial, false>(q, s);
+  if (e != hipSuccess) return e;
+  const int64_t threads = p.M * (p.N / 8);
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > 2147483647LL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(splitk_residual_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                     static_cast<const float*>(p.scratch), static_cast<int>(S), p.M, p.N,
+                     static_cast<const bf16_t*>(p.R), p.ldr,
+                     static_cast<const bf16_t*>(p.bias[0]), static_cast<bf16_t*>(p.C), p.ldc);
+  return hipGetLastError();
+}
+
 // Tile choice.  With one big-tile workgroup per CU, a tile's epilogue runs
 // with the matrix cores idle; when it also reads a residual and K is short
 // (the output projection: K = D) that share is large, and the small tile,
@@ -601,7 +742,7 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t s) {
   const int64_t rows_main = m_main * Big::BM;
   const hipError_t e = launch_cfg<Big>(row_slice(p, 0, rows_main), s);
   if (e != hipSuccess) return e;
-  return launch_cfg<Small>(row_slice(p, rows_main, p.M - rows_main), s);
+  return launch_tail(row_slice(p, rows_main, p.M - rows_main), s);
 }
 
 }  // namespace vitblk

@@ -30,6 +30,12 @@ struct GemmProblem {
   const void* bias[3];
   int64_t bias_seg;
   void* C2;  // second output of kEpiGeluDual (same layout as C), else unused
+  // kEpiPartial only: the number of k-ranges (>= 1).
+  int ksplit;
+  // Free fp32 device memory launch_gemm may use for split-K partial sums of
+  // a residual product (null: none).  Its contents are clobbered.
+  float* scratch;
+  int64_t scratch_floats;
 };
 
 // Internal epilogues of the backward (not part of the C interface):
@@ -37,6 +43,9 @@ struct GemmProblem {
 // hidden layer and its derivative, from one product); kEpiMul: C = acc * R.
 constexpr int kEpiGeluDual = 16;
 constexpr int kEpiMul = 17;
+// kEpiPartial: split K.  Tile (m, n) of k-range s of ksplit equal ranges is
+// written, unrounded, to ((float*)C)[s * M * ldc + m * ldc + n]; no bias.
+constexpr int kEpiPartial = 18;
 
 __host__ __device__ inline bool has_bias(const GemmProblem& p) {
   return p.bias[0] != nullptr || p.bias[1] != nullptr || p.bias[2] != nullptr;
