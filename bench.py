@@ -481,28 +481,56 @@ def main():
     bqkv = torch.cat([gp["b_q"], gp["b_k"], gp["b_v"]]) if affine else None
     es = 2 if w.dtype == "bf16" else 4
     wbytes = (4 * D * D + 2 * D * F) * es
+    # The packing step also sums the columns of [w_q | w_k | w_v] and w_mlp1.
+    pack_bytes = 2 * wbytes + (3 * D * D + D * F) * es + (3 * D + F) * 4
     kern = {
         "pack_weights": (lambda: vb.pack_weights(g["w_q"], g["w_k"], g["w_v"], g["w_o"],
                                                  g["w_mlp1"], g["w_mlp2"], packed=packed),
-                         "hbm", 2 * wbytes),
-        "ln1": (lambda: vb.layernorm(x2, w.eps, gamma=gq("ln1_gamma"), beta=gq("ln1_beta"),
-                                     out=xn), "hbm", 2 * M * D * es),
-        "qkv_gemm": ((lambda: vb.linear(xn, wqkv_t, vb.EPI_NONE, bias=bqkv, out=qkv)) if affine
-                     else (lambda: vb.qkv_projection(xn, wqkv_t, out=qkv)),
-                     "mfma", 2 * M * D * 3 * D),
+                         "hbm", pack_bytes),
+    }
+    if affine or w.dtype != "bf16":
+        kern.update({
+            "ln1": (lambda: vb.layernorm(x2, w.eps, gamma=gq("ln1_gamma"), beta=gq("ln1_beta"),
+                                         out=xn), "hbm", 2 * M * D * es),
+            "qkv_gemm": ((lambda: vb.linear(xn, wqkv_t, vb.EPI_NONE, bias=bqkv, out=qkv))
+                         if affine else (lambda: vb.qkv_projection(xn, wqkv_t, out=qkv)),
+                         "mfma", 2 * M * D * 3 * D),
+        })
+    else:
+        # bf16 without gains or shifts: each LayerNorm is folded into the next
+        # product (row statistics, then rstd (x @ W - mean colsum) in the
+        # product's epilogue), as vitblk_forward does.
+        cs_qkv, cs_1 = vb.packed_col_sums(packed, D, F, tdt)
+        st1 = torch.empty((M, 2), dtype=torch.float32, device=dev)
+        st2 = torch.empty_like(st1)
+        kern.update({
+            "ln1_stats": (lambda: vb.row_stats(x2, w.eps, out=st1), "hbm", M * D * es + M * 8),
+            "qkv_gemm": (lambda: vb.linear_normed(x2, wqkv_t, cs_qkv, st1, vb.EPI_NONE, out=qkv),
+                         "mfma", 2 * M * D * 3 * D),
+        })
+    kern.update({
         "attention": (lambda: vb.attention(qkv, w.N, w.T, w.H, out=att), "mfma",
                       4 * w.N * w.T * w.T * D),
         "oproj_residual": (lambda: vb.linear(att, wo_t, vb.EPI_RESIDUAL, residual=x2,
                                              bias=gq("b_o"), out=y), "mfma", 2 * M * D * D),
-        "ln2": (lambda: vb.layernorm(y, w.eps, gamma=gq("ln2_gamma"), beta=gq("ln2_beta"),
-                                     out=yn), "hbm", 2 * M * D * es),
-        "mlp1_gelu": (lambda: vb.linear(yn, w1_t, vb.EPI_GELU, bias=gq("b_mlp1"), out=hid),
-                      "mfma", 2 * M * D * F),
-        "mlp2_residual": (lambda: vb.linear(hid, w2_t, vb.EPI_RESIDUAL, residual=y,
-                                            bias=gq("b_mlp2"), out=o2), "mfma", 2 * M * F * D),
-    }
-    for name in ["ln1", "qkv_gemm", "attention", "oproj_residual", "ln2", "mlp1_gelu"]:
-        kern[name][0]()  # realistic operands for every step
+    })
+    if affine or w.dtype != "bf16":
+        kern.update({
+            "ln2": (lambda: vb.layernorm(y, w.eps, gamma=gq("ln2_gamma"), beta=gq("ln2_beta"),
+                                         out=yn), "hbm", 2 * M * D * es),
+            "mlp1_gelu": (lambda: vb.linear(yn, w1_t, vb.EPI_GELU, bias=gq("b_mlp1"), out=hid),
+                          "mfma", 2 * M * D * F),
+        })
+    else:
+        kern.update({
+            "ln2_stats": (lambda: vb.row_stats(y, w.eps, out=st2), "hbm", M * D * es + M * 8),
+            "mlp1_gelu": (lambda: vb.linear_normed(y, w1_t, cs_1, st2, vb.EPI_GELU, out=hid),
+                          "mfma", 2 * M * D * F),
+        })
+    kern["mlp2_residual"] = (lambda: vb.linear(hid, w2_t, vb.EPI_RESIDUAL, residual=y,
+                                               bias=gq("b_mlp2"), out=o2), "mfma", 2 * M * F * D)
+    for name in [k for k in kern if k not in ("pack_weights", "mlp2_residual")]:
+        kern[name][0]()  # realistic operands for every step, in block order
     if a.profile_step:
         x_copy = torch.empty(256 * 1024 * 1024, dtype=torch.bfloat16, device=dev).fill_(1.0)
         y_copy = torch.empty_like(x_copy)

@@ -95,8 +95,11 @@ const char* vitblk_status_string(int status);
  *   activations:
  *     region 0: M x max(3D, F) elements: packed Q|K|V [M, 3D], later the
  *               MLP hidden activations [M, F]
- *     region 1: M x D elements: LN(x), later the concatenated heads, later LN(y)
+ *     region 1: M x D elements: LN(x) (or, folded, its row statistics),
+ *               later the concatenated heads, later LN(y) (or its statistics)
  *     region 2: M x D elements: y = x + att @ w_o
+ *   Regions 0 and 1 also hold fp32 partial sums of the residual products'
+ *   last rows while they are otherwise unused.
  * (ViT-L/16, N = 256, bf16: about 645 MB.)  vitblk_forward_packed() needs
  * only the activations: vitblk_workspace_bytes() minus
  * vitblk_packed_weights_bytes().
@@ -113,10 +116,15 @@ size_t vitblk_workspace_bytes(int64_t N, int64_t T, int64_t D, int64_t F, int64_
  *   Wo^T   [D, D]
  *   W1^T   [F, D]   (w_mlp1 is [D, F])
  *   W2^T   [D, F]   (w_mlp2 is [F, D])
- * vitblk_packed_weights_bytes() returns the size (0 for invalid arguments;
- * host only).  vitblk_pack_weights() writes it on `stream` (one launch); the
- * buffer must not overlap a weight.  Callers that run many blocks with the
- * same weights pack once and call vitblk_forward_packed().
+ *   cs_qkv [3D]     fp32: cs_qkv[n] = sum_k Wqkv[k, n], the column sums of
+ *                   [w_q | w_k | w_v] (row sums of Wqkv^T), summed in fp32
+ *   cs_1   [F]      fp32: the column sums of w_mlp1
+ * The column sums serve the products that fold a LayerNorm in (see
+ * vitblk_linear_normed()).  vitblk_packed_weights_bytes() returns the size
+ * (0 for invalid arguments; host only).  vitblk_pack_weights() writes it on
+ * `stream` (two launches: the transposes, then the sums); the buffer must
+ * not overlap a weight.  Callers that run many blocks with the same weights
+ * pack once and call vitblk_forward_packed().
  */
 size_t vitblk_packed_weights_bytes(int64_t D, int64_t F, int dtype);
 
@@ -139,9 +147,15 @@ int vitblk_pack_weights(const void* w_q, const void* w_k, const void* w_v, const
  *          vitblk_workspace_bytes(N, T, D, F, H, dtype) bytes; its contents
  *          on entry are ignored and on return are unspecified
  *
- * Eight kernels run in order on `stream`: weight packing, LN, fused QKV
- * projection, attention, output projection + residual, LN, MLP1 + GELU,
- * MLP2 + residual.
+ * Kernels run in order on `stream`: weight packing (and the column sums),
+ * LN, fused QKV projection, attention, output projection + residual, LN,
+ * MLP1 + GELU, MLP2 + residual.  In bf16 each LN (no gain or shift) is
+ * folded into the product that follows it: only the rows' mean and
+ * 1/sqrt(var + eps) are computed, and the product's epilogue forms
+ * rstd * (x @ W - mean * colsum(W)) = LN(x) @ W (see vitblk_linear_normed()).
+ * When the last rows of a residual product would leave most of the device
+ * idle, their K range is split and a second kernel adds the partial sums
+ * (fp32, in the workspace) to the residual.
  */
 int vitblk_forward(const void* x, const void* w_q, const void* w_k, const void* w_v,
                    const void* w_o, const void* w_mlp1, const void* w_mlp2, void* out,
@@ -293,6 +307,33 @@ int vitblk_layernorm(const void* x, void* out, int64_t rows, int64_t D, double e
 int vitblk_layernorm_affine(const void* x, const void* gamma, const void* beta, void* out,
                             int64_t rows, int64_t D, double eps, int dtype,
                             vitblk_stream_t stream);
+
+/* LayerNorm statistics of each row of x [rows, D]: stats[2r] = mean,
+ * stats[2r + 1] = 1 / sqrt(var + eps) (population variance; fp32, the values
+ * vitblk_layernorm() normalises with).  stats (2 * rows floats, 8-byte
+ * aligned) must not overlap x. */
+int vitblk_row_stats(const void* x, float* stats, int64_t rows, int64_t D, double eps,
+                     int dtype, vitblk_stream_t stream);
+
+/* A product whose left operand is the LayerNorm (no gain or shift) of a,
+ * with the normalisation folded into the epilogue:
+ *
+ *   out = epilogue(LN(a) @ W + bias),  LN(a) @ W = rstd_m (a @ W - mean_m c_n)
+ *
+ * (the LayerNorm of crackedaicode.com "ViT Encoder Block", "Normalize before
+ * each stage", is (a - mean) * rstd per row; multiplied out, the mean term
+ * is the row's mean times W's column sum).  a [M, K] is the raw input (not
+ * normalised), row_stats its statistics from vitblk_row_stats(), col_sums
+ * [Nout] fp32 the column sums of W (16-byte aligned; the packed weights
+ * hold them for the QKV and MLP1 products), w_t, bias and out as for
+ * vitblk_linear_bias().  epilogue: VITBLK_EPI_NONE or VITBLK_EPI_GELU.  The
+ * difference from normalising first is rounding only: a is used as given
+ * (no rounding of LN(a) to the dtype); the fp32 subtraction adds an error
+ * of about 2^-24 sqrt(K) |mean| / std relative to the output. */
+int vitblk_linear_normed(const void* a, const void* w_t, const float* col_sums,
+                         const float* row_stats, const void* bias, void* out, int64_t M,
+                         int64_t K, int64_t Nout, int epilogue, int dtype,
+                         vitblk_stream_t stream);
 
 /* qkv = xn @ [w_q | w_k | w_v]: xn [M, D], w_qkv_t [3D, D] (the first
  * region of the packed weights), qkv [M, 3D] (one row holds a token's Q, K

@@ -13,6 +13,7 @@ from .block import (  # noqa: F401
     encoder,
     gelu_tanh,
     layer_norm,
+    layer_norm_stats,
     merge_heads,
     mlp,
     multi_head_attention,

@@ -52,6 +52,7 @@ import numpy as np
 
 __all__ = [
     "layer_norm",
+    "layer_norm_stats",
     "project",
     "split_heads",
     "merge_heads",
@@ -91,6 +92,21 @@ def layer_norm(x, eps: float) -> np.ndarray:
     dev = x - mean
     var = (dev * dev).mean(axis=-1, keepdims=True)
     return dev / np.sqrt(var + eps)
+
+
+def layer_norm_stats(x, eps: float):
+    """Each token's mean and 1 / sqrt(population variance + eps), over its last axis.
+
+    The two numbers [CAC] "Normalize before each stage" normalises a token
+    with: layer_norm(x) = (x - mean) * rstd.  [AEE] "Numerical Example" prints
+    the mean and the variance of its token.  Returns (mean, rstd), each of
+    shape x.shape[:-1].
+    """
+    x = _f64(x)
+    mean = x.mean(axis=-1)
+    dev = x - mean[..., None]
+    var = (dev * dev).mean(axis=-1)
+    return mean, 1.0 / np.sqrt(var + eps)
 
 
 def affine(t, gamma=None, beta=None) -> np.ndarray:

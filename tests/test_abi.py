@@ -51,7 +51,9 @@ def test_workspace_bytes():
     def expect(N, T, D, F, es):
         r = lambda b: (b + 255) // 256 * 256  # noqa: E731
         M = N * T
-        packed = r(3 * D * D * es) + r(D * D * es) + 2 * r(D * F * es)
+        # four weight regions, then the fp32 column sums of Wqkv [3D] and W1 [F]
+        packed = (r(3 * D * D * es) + r(D * D * es) + 2 * r(D * F * es) + r(3 * D * 4)
+                  + r(F * 4))
         assert vb.packed_weights_bytes(D, F, 1 if es == 2 else 0) == packed
         return packed + r(M * max(3 * D, F) * es) + 2 * r(M * D * es)
     assert vb.workspace_bytes(256, 197, 1024, 4096, 16, vb.VITBLK_BF16) == expect(256, 197, 1024, 4096, 2)
@@ -165,6 +167,26 @@ def test_step_entry_points_errors(lib):
     assert lib.vitblk_linear(a, b, c, c, 4, 8, 8, vb.EPI_RESIDUAL, 1, None) == ALIAS
     assert lib.vitblk_linear(a, b, None, a, 4, 8, 8, vb.EPI_NONE, 1, None) == ALIAS
     assert lib.vitblk_linear(a, b, None, c, 4, -8, 8, vb.EPI_GELU, 1, None) == INVALID
+    # row statistics (stats 8-byte aligned, 2 floats per row); every call
+    # below fails its checks before any launch
+    off = lambda p, k: ctypes.c_void_p(p.value + k)  # noqa: E731
+    assert lib.vitblk_row_stats(None, b, 4, 8, 1e-5, 1, None) == INVALID
+    assert lib.vitblk_row_stats(a, None, 4, 8, 1e-5, 1, None) == INVALID
+    assert lib.vitblk_row_stats(a, off(b, 4), 4, 8, 1e-5, 1, None) == INVALID
+    assert lib.vitblk_row_stats(a, b, 0, 8, 1e-5, 1, None) == INVALID
+    assert lib.vitblk_row_stats(a, b, 4, 8, -1.0, 1, None) == INVALID
+    assert lib.vitblk_row_stats(a, off(a, 8), 4, 8, 1e-5, 1, None) == ALIAS
+    # the LayerNorm-folded product: plain or GELU epilogue, sums 16-byte aligned
+    ln = lambda *args: lib.vitblk_linear_normed(*args)  # noqa: E731
+    assert ln(a, b, c, d, None, e, 4, 8, 8, vb.EPI_RESIDUAL, 1, None) == INVALID
+    assert ln(a, b, None, d, None, e, 4, 8, 8, vb.EPI_GELU, 1, None) == INVALID
+    assert ln(a, b, c, None, None, e, 4, 8, 8, vb.EPI_GELU, 1, None) == INVALID
+    assert ln(a, b, off(c, 8), d, None, e, 4, 8, 8, vb.EPI_GELU, 1, None) == INVALID
+    assert ln(a, b, c, off(d, 4), None, e, 4, 8, 8, vb.EPI_GELU, 1, None) == INVALID
+    assert ln(a, b, c, d, None, e, 4, 0, 8, vb.EPI_GELU, 1, None) == INVALID
+    assert ln(a, b, c, d, None, c, 4, 8, 8, vb.EPI_GELU, 1, None) == ALIAS
+    assert ln(a, b, c, d, None, d, 4, 8, 8, vb.EPI_NONE, 1, None) == ALIAS
+    assert ln(a, b, c, d, None, a, 4, 8, 8, vb.EPI_NONE, 1, None) == ALIAS
 
 
 def test_affine_entry_points_errors(lib):
@@ -313,7 +335,8 @@ def test_backward_workspace_bytes():
 
     def expect(N, T, D, F, H, es):
         M = N * T
-        packed = r(3 * D * D * es) + r(D * D * es) + 2 * r(D * F * es)
+        packed = (r(3 * D * D * es) + r(D * D * es) + 2 * r(D * F * es) + r(3 * D * 4)
+                  + r(F * 4))
         wcat = r(3 * D * D * es)
         # xn, att, y, yn, dy [M, D]; qkv [M, 3D]; z [M, max(F, 3D)]; h [M, F]
         acts = 5 * r(M * D * es) + r(M * 3 * D * es) + r(M * max(F, 3 * D) * es) + r(M * F * es)

@@ -73,6 +73,43 @@ def test_linear(dtype, epi, M, K, N):
     assert_close(got, ref, dtype, f"linear {epi} M={M} K={K} N={N}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("rows,D", [(37, 768), (64, 1024), (3, 20), (1000, 1280), (5, 4104)])
+def test_row_stats(dtype, rows, D):
+    rng = np.random.default_rng(rows * 7 + D)
+    x = _rand(rng, (rows, D), dtype, scale=2.0, offset=0.5)
+    x[0] = round_to(np.full(D, -1.25), dtype)  # constant token: rstd = 1/sqrt(eps)
+    got = to_host(vb.row_stats(to_dev(x, dtype), 1e-6)).astype(np.float64)
+    mean, rstd = oracle.layer_norm_stats(x, 1e-6)
+    # fp32 statistics: relative errors of order 2^-24 times a few terms.
+    assert np.max(np.abs(got[:, 0] - mean) / (1 + np.abs(mean))) <= 2e-6
+    assert np.max(np.abs(got[:, 1] - rstd) / rstd) <= 2e-5
+
+
+# LN(a) @ W folded into the product: the reference normalises first (float64).
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("epi", ["none", "gelu"])
+@pytest.mark.parametrize("M,K,N,bias", [(300, 256, 512, False), (129, 1024, 200, True),
+                                        (33, 40, 24, True), (70 * 256 + 77, 256, 1024, False),
+                                        (260, 1024, 4096, True)])
+def test_linear_normed(dtype, epi, M, K, N, bias):
+    if dtype == "fp32" and M > 10000:
+        pytest.skip("the big ragged case exercises the bf16 tile split only")
+    rng = np.random.default_rng(M + 3 * K + 7 * N)
+    a = _rand(rng, (M, K), dtype, scale=1.5, offset=0.75)  # a mean the fold must remove
+    w = _rand(rng, (K, N), dtype, scale=1 / math.sqrt(K))
+    b = _rand(rng, (N,), dtype, scale=0.5) if bias else None
+    da, wt = to_dev(a, dtype), to_dev(w.T, dtype)
+    cs = to_dev(w.astype(np.float64).sum(0), "fp32")  # W's column sums, an input here
+    stats = vb.row_stats(da, 1e-6)
+    got = to_host(vb.linear_normed(da, wt, cs, stats, EPIS[epi],
+                                   bias=None if b is None else to_dev(b, dtype)))
+    ref = oracle.add_bias(oracle.project(oracle.layer_norm(a, 1e-6), w), b)
+    if epi == "gelu":
+        ref = oracle.gelu_tanh(ref)
+    assert_close(got, ref, dtype, f"LN-folded {epi} M={M} K={K} N={N}")
+
+
 @pytest.mark.parametrize("epi", ["none", "residual"])
 def test_linear_with_ragged_tail_rows(epi):
     # 71 M-tiles of 256 rows (ragged): the big tile takes a whole number of
@@ -134,7 +171,8 @@ def test_pack_weights_is_an_exact_transpose(dtype, D, F):
     r = lambda b: (b + 255) // 256 * 256  # noqa: E731
     offs = [0, r(3 * D * D * es), r(3 * D * D * es) + r(D * D * es)]
     offs.append(offs[2] + r(D * F * es))
-    assert packed.numel() == offs[3] + r(D * F * es)
+    cs_off = offs[3] + r(D * F * es)
+    assert packed.numel() == cs_off + r(3 * D * 4) + r(F * 4)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
 
     def region(off, rows, cols):
@@ -145,6 +183,13 @@ def test_pack_weights_is_an_exact_transpose(dtype, D, F):
     assert torch.equal(region(offs[1], D, D), dev[3].t())
     assert torch.equal(region(offs[2], F, D), dev[4].t())
     assert torch.equal(region(offs[3], D, F), dev[5].t())
+    # Column sums of [w_q | w_k | w_v] and w_mlp1 (fp32 sums of the stored values).
+    cs_qkv, cs_1 = vb.packed_col_sums(packed, D, F, tdt)
+    for got, w in [(cs_qkv, np.concatenate([inp[k] for k in names[:3]], axis=1)),
+                   (cs_1, inp["w_mlp1"])]:
+        w = round_to(w, dtype).astype(np.float64)
+        np.testing.assert_allclose(to_host(got), w.sum(0), rtol=0,
+                                   atol=1e-6 * np.abs(w).sum(0).max())
 
 
 # ------------------------------------------------------------------ whole block

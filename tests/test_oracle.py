@@ -611,3 +611,80 @@ def test_pins_catch_planted_mistake(name, monkeypatch):
     caught_tt = _tt_max_err() > TT_TOL
     caught_brute = _brute_max_err() > 1e-9
     assert caught_tt or caught_brute, f"pins did not catch: {name}"
+
+
+# ------------------------------------------------------- LayerNorm statistics
+#
+# oracle.layer_norm_stats (each token's mean and 1 / sqrt(var + eps), the two
+# numbers a LayerNorm normalises with) is the reference of the row-statistics
+# kernel and of the products that fold the LayerNorm in.  Pins: the token of
+# [AEE] "Numerical Example" with its printed mean and variance, closed forms
+# (a constant token; a two-value token) and a scalar loop.
+
+def _stats_pins_max_err():
+    errs = []
+    g = _load("aee_hand_trace.json")["layer_norm"]
+    mean, rstd = oracle.layer_norm_stats(np.array(g["x"]), 1e-6)
+    errs.append(np.abs(mean - np.array(g["mean"])).max())
+    errs.append(np.abs(rstd - 1.0 / np.sqrt(np.array(g["variance"]) + 1e-6)).max())
+    # A constant token: mean c, variance 0, so rstd = 1 / sqrt(eps).
+    m, r = oracle.layer_norm_stats(np.full((1, 6), 2.5), 1e-6)
+    errs += [abs(m[0] - 2.5), abs(r[0] - 1.0 / math.sqrt(1e-6)) * 1e-3]
+    # Two values a, b: mean (a + b) / 2, population variance ((a - b) / 2)^2.
+    a, b = 1.75, -0.5
+    m, r = oracle.layer_norm_stats(np.array([[a, b]]), 1e-5)
+    errs += [abs(m[0] - (a + b) / 2), abs(r[0] - 1.0 / math.sqrt(((a - b) / 2) ** 2 + 1e-5))]
+    # Scalar loop over random tokens.
+    x = np.random.default_rng(3).standard_normal((5, 7)) * 2.0 + 0.3
+    m, r = oracle.layer_norm_stats(x, 1e-5)
+    for i, row in enumerate(x.tolist()):
+        mu = sum(row) / len(row)
+        var = sum((v - mu) ** 2 for v in row) / len(row)
+        errs += [abs(m[i] - mu), abs(r[i] - 1.0 / math.sqrt(var + 1e-5))]
+    return max(errs)
+
+
+def test_layer_norm_stats_pins():
+    assert _stats_pins_max_err() <= 1e-12
+
+
+def test_layer_norm_stats_give_the_layer_norm():
+    x = np.random.default_rng(4).standard_normal((3, 4, 10)) * 1.5 - 0.7
+    m, r = oracle.layer_norm_stats(x, 1e-6)
+    np.testing.assert_allclose((x - m[..., None]) * r[..., None], oracle.layer_norm(x, 1e-6),
+                               rtol=1e-13, atol=1e-13)
+
+
+def _stats_unbiased(x, eps):
+    x = np.asarray(x, dtype=np.float64)
+    return x.mean(-1), 1.0 / np.sqrt(x.var(-1, ddof=1) + eps)
+
+
+def _stats_eps_outside(x, eps):
+    x = np.asarray(x, dtype=np.float64)
+    return x.mean(-1), 1.0 / (np.sqrt(x.var(-1)) + eps)
+
+
+def _stats_not_inverted(x, eps):
+    x = np.asarray(x, dtype=np.float64)
+    return x.mean(-1), np.sqrt(x.var(-1) + eps)
+
+
+def _stats_mean_of_squares(x, eps):
+    x = np.asarray(x, dtype=np.float64)
+    return x.mean(-1), 1.0 / np.sqrt((x * x).mean(-1) + eps)
+
+
+STATS_MUTANTS = {
+    "unbiased variance": _stats_unbiased,
+    "eps outside sqrt": _stats_eps_outside,
+    "sqrt not inverted": _stats_not_inverted,
+    "uncentred second moment": _stats_mean_of_squares,
+}
+
+
+@pytest.mark.parametrize("name", sorted(STATS_MUTANTS))
+def test_layer_norm_stats_pins_catch_planted_mistake(name, monkeypatch):
+    monkeypatch.setattr(ob, "layer_norm_stats", STATS_MUTANTS[name])
+    monkeypatch.setattr(oracle, "layer_norm_stats", STATS_MUTANTS[name])
+    assert _stats_pins_max_err() > 1e-9, f"pins did not catch: {name}"

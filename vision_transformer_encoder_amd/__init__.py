@@ -31,13 +31,16 @@ from ._lib import (  # noqa: F401
     layernorm,
     layernorm_backward,
     linear,
+    linear_normed,
     load,
     pack_weights,
+    packed_col_sums,
     packed_views,
     packed_weights_bytes,
     patch_embed,
     patch_embed_workspace_bytes,
     qkv_projection,
+    row_stats,
     status_string,
     weight_grad,
     weight_grad_workspace_bytes,

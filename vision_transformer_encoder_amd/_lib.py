@@ -46,6 +46,8 @@ SIGNATURES = {
     "vitblk_forward_packed_affine": (_I, [_P, _P, _AP, _P] + [_I64] * 5 + [_D, _I, _P, _SZ, _P]),
     "vitblk_layernorm_affine": (_I, [_P] * 4 + [_I64, _I64, _D, _I, _P]),
     "vitblk_linear_bias": (_I, [_P] * 5 + [_I64, _I64, _I64, _I, _I, _P]),
+    "vitblk_row_stats": (_I, [_P, _P, _I64, _I64, _D, _I, _P]),
+    "vitblk_linear_normed": (_I, [_P] * 6 + [_I64, _I64, _I64, _I, _I, _P]),
     "vitblk_encoder_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64, _I]),
     "vitblk_patch_embed_workspace_bytes": (_SZ, [_I64] * 6 + [_I]),
     "vitblk_patch_embed": (_I, [_P] * 6 + [_I64] * 6 + [_I, _P, _SZ, _P]),
@@ -125,6 +127,18 @@ def _dev(*ts):
         if t.dtype != t0.dtype or t.device != t0.device:
             raise ValueError("vitblk tensors must share dtype and device")
     return t0
+
+
+def _dev_f32(t0, *ts):
+    """fp32 side tensors (statistics, sums) on t0's device, contiguous."""
+    torch = _torch()
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda or t.device != t0.device:
+            raise ValueError("vitblk tensors must be on the GPU, on one device")
+        if not t.is_contiguous() or t.dtype != torch.float32:
+            raise ValueError("vitblk statistics and sums are contiguous float32 tensors")
 
 
 def _stream(t, stream):
@@ -308,6 +322,20 @@ def packed_views(packed, D: int, F: int, dtype):
                  for o, (r, c) in zip(offs, shapes))
 
 
+def packed_col_sums(packed, D: int, F: int, dtype):
+    """fp32 views of the packed buffer's column sums: (cs_qkv [3D], cs_1 [F])."""
+    torch = _torch()
+    es = 2 if dtype == torch.bfloat16 else 4
+
+    def up(b):
+        return (b + 255) // 256 * 256
+
+    o = up(3 * D * D * es) + up(D * D * es) + 2 * up(D * F * es)
+    o1 = o + up(3 * D * 4)
+    return (packed[o:o + 3 * D * 4].view(torch.float32),
+            packed[o1:o1 + F * 4].view(torch.float32))
+
+
 def forward_packed(x, packed, F: int, num_heads: int, eps: float, out=None, workspace=None,
                    stream=None):
     """out = block(x) on weights packed by pack_weights()."""
@@ -416,6 +444,45 @@ def linear(a, w_t, epilogue: int = EPI_NONE, residual=None, out=None, stream=Non
                                        M, K, Nout, int(epilogue), dtype_code(a.dtype),
                                        _stream(a, stream))
         _check("vitblk_linear_bias", st)
+    return out
+
+
+def row_stats(x, eps: float, out=None, stream=None):
+    """fp32 [rows, 2]: each row's mean and 1 / sqrt(var + eps) (x [..., D])."""
+    torch = _torch()
+    _dev(x)
+    _dev_f32(x, out)
+    D = x.shape[-1]
+    rows = x.numel() // D
+    if out is None:
+        out = torch.empty((rows, 2), dtype=torch.float32, device=x.device)
+    if out.numel() != 2 * rows:
+        raise ValueError(f"stats must hold 2 floats per row ({2 * rows}), got {out.numel()}")
+    st = load().vitblk_row_stats(_ptr(x), _ptr(out), rows, D, float(eps), dtype_code(x.dtype),
+                                 _stream(x, stream))
+    _check("vitblk_row_stats", st)
+    return out
+
+
+def linear_normed(a, w_t, col_sums, stats, epilogue: int = EPI_NONE, bias=None, out=None,
+                  stream=None):
+    """out = epilogue(LN(a) @ W + bias) with the LayerNorm folded into the product:
+    a [M, K] raw rows, stats = row_stats(a), col_sums fp32 [Nout] (W's column sums),
+    W given out-major, w_t [Nout, K]."""
+    torch = _torch()
+    _dev(a, w_t, bias, out)
+    _dev_f32(a, col_sums, stats)
+    K = a.shape[-1]
+    M = a.numel() // K
+    Nout = w_t.shape[0]
+    if col_sums.numel() != Nout or stats.numel() != 2 * M:
+        raise ValueError("col_sums must hold Nout floats and stats 2 per row of a")
+    if out is None:
+        out = torch.empty((M, Nout), dtype=a.dtype, device=a.device)
+    st = load().vitblk_linear_normed(_ptr(a), _ptr(w_t), _ptr(col_sums), _ptr(stats), _ptr(bias),
+                                     _ptr(out), M, K, Nout, int(epilogue), dtype_code(a.dtype),
+                                     _stream(a, stream))
+    _check("vitblk_linear_normed", st)
     return out
 
 

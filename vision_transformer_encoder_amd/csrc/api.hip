@@ -56,6 +56,13 @@ int pack_weights(const void* w_q, const void* w_k, const void* w_v, const void* 
       {w_mlp2, F, D, base + pl.off_2, F},
   };
   VITBLK_LAUNCH(launch_pack(jobs, 6, dtype, s));
+  // Column sums of [w_q | w_k | w_v] and of w_mlp1 (row sums of the packed
+  // copies) for the products that fold in the LayerNorm.
+  const RowSumJob sums[2] = {
+      {qkv, 3 * D, D, reinterpret_cast<float*>(base + pl.off_cs_qkv)},
+      {base + pl.off_1, F, D, reinterpret_cast<float*>(base + pl.off_cs_1)},
+  };
+  VITBLK_LAUNCH(launch_row_sums(sums, 2, dtype, s));
   return VITBLK_OK;
 }
 
@@ -74,12 +81,27 @@ int run_block(const void* x, const void* packed, const vitblk_affine_params* prm
   char* y = act + pl.off_y;      // [M, D]
   const float feps = static_cast<float>(eps);
 
-  // LN1: xn = gamma_1 LN(x) + beta_1
-  VITBLK_LAUNCH(launch_layernorm(x, D, q.ln1_gamma, q.ln1_beta, a, M, D, feps, dtype, s));
-  // Q | K | V = xn @ [w_q | w_k | w_v] + [b_q | b_k | b_v]
-  VITBLK_LAUNCH(launch_gemm(linear_problem(a, pk + pl.packed.off_qkv, big, nullptr, M, D, 3 * D,
-                                           VITBLK_EPI_NONE, dtype, q.b_q, q.b_k, q.b_v, D),
-                            s));
+  // A LayerNorm without gain or shift folds into the product that follows
+  // it (bf16): LN(x) @ W = rstd (x @ W - mean 1^T W), so only the rows'
+  // statistics are computed (into region act) and the GEMM epilogue applies
+  // them with W's column sums from the packed weights.  The affine
+  // LayerNorm, and fp32, are written out.
+  float* stats = reinterpret_cast<float*>(a);
+  const bool fold1 = dtype == VITBLK_BF16 && q.ln1_gamma == nullptr && q.ln1_beta == nullptr;
+  const bool fold2 = dtype == VITBLK_BF16 && q.ln2_gamma == nullptr && q.ln2_beta == nullptr;
+
+  // LN1: xn = gamma_1 LN(x) + beta_1, then Q | K | V = xn @ [w_q | w_k | w_v] + [b_q | b_k | b_v]
+  GemmProblem pq = linear_problem(a, pk + pl.packed.off_qkv, big, nullptr, M, D, 3 * D,
+                                  VITBLK_EPI_NONE, dtype, q.b_q, q.b_k, q.b_v, D);
+  if (fold1) {
+    VITBLK_LAUNCH(launch_row_stats(x, D, stats, M, D, feps, dtype, s));
+    pq.A = x;
+    pq.row_stats = stats;
+    pq.col_sums = reinterpret_cast<const float*>(pk + pl.packed.off_cs_qkv);
+  } else {
+    VITBLK_LAUNCH(launch_layernorm(x, D, q.ln1_gamma, q.ln1_beta, a, M, D, feps, dtype, s));
+  }
+  VITBLK_LAUNCH(launch_gemm(pq, s));
   // att = concat_h softmax(Q_h K_h^T / sqrt(dh)) V_h   (overwrites xn)
   VITBLK_LAUNCH(launch_attention(big, big + D * es, big + 2 * D * es, 3 * D, a, D, N, T, H,
                                  D / H, dtype, s));
@@ -89,12 +111,19 @@ int run_block(const void* x, const void* packed, const vitblk_affine_params* prm
   po.scratch = reinterpret_cast<float*>(big);
   po.scratch_floats = static_cast<int64_t>(pl.off_act - pl.off_big) / 4;
   VITBLK_LAUNCH(launch_gemm(po, s));
-  // LN2: yn = gamma_2 LN(y) + beta_2   (overwrites att)
-  VITBLK_LAUNCH(launch_layernorm(y, D, q.ln2_gamma, q.ln2_beta, a, M, D, feps, dtype, s));
+  // LN2: yn = gamma_2 LN(y) + beta_2 (overwrites att), then
   // hidden = GELU(yn @ w_mlp1 + b_mlp1)   (overwrites qkv)
-  VITBLK_LAUNCH(launch_gemm(linear_problem(a, pk + pl.packed.off_1, big, nullptr, M, D, F,
-                                           VITBLK_EPI_GELU, dtype, q.b_mlp1),
-                            s));
+  GemmProblem p1 = linear_problem(a, pk + pl.packed.off_1, big, nullptr, M, D, F,
+                                  VITBLK_EPI_GELU, dtype, q.b_mlp1);
+  if (fold2) {
+    VITBLK_LAUNCH(launch_row_stats(y, D, stats, M, D, feps, dtype, s));
+    p1.A = y;
+    p1.row_stats = stats;
+    p1.col_sums = reinterpret_cast<const float*>(pk + pl.packed.off_cs_1);
+  } else {
+    VITBLK_LAUNCH(launch_layernorm(y, D, q.ln2_gamma, q.ln2_beta, a, M, D, feps, dtype, s));
+  }
+  VITBLK_LAUNCH(launch_gemm(p1, s));
   // out = y + hidden @ w_mlp2 + b_mlp2   (yn's region is free again: split-K scratch)
   GemmProblem p2 = linear_problem(big, pk + pl.packed.off_2, out, y, M, F, D,
                                   VITBLK_EPI_RESIDUAL, dtype, q.b_mlp2);
@@ -467,6 +496,29 @@ int vitblk_layernorm_affine(const void* x, const void* gamma, const void* beta, 
   if (st != VITBLK_OK) return st;
   VITBLK_LAUNCH(launch_layernorm(x, D, gamma, beta, out, rows, D, static_cast<float>(eps), dtype,
                                  reinterpret_cast<hipStream_t>(stream)));
+  return VITBLK_OK;
+}
+
+int vitblk_row_stats(const void* x, float* stats, int64_t rows, int64_t D, double eps,
+                     int dtype, vitblk_stream_t stream) {
+  const int st = validate_row_stats(x, stats, rows, D, eps, dtype);
+  if (st != VITBLK_OK) return st;
+  VITBLK_LAUNCH(launch_row_stats(x, D, stats, rows, D, static_cast<float>(eps), dtype,
+                                 reinterpret_cast<hipStream_t>(stream)));
+  return VITBLK_OK;
+}
+
+int vitblk_linear_normed(const void* a, const void* w_t, const float* col_sums,
+                         const float* row_stats, const void* bias, void* out, int64_t M,
+                         int64_t K, int64_t Nout, int epilogue, int dtype,
+                         vitblk_stream_t stream) {
+  const int st = validate_linear_normed(a, w_t, col_sums, row_stats, bias, out, M, K, Nout,
+                                        epilogue, dtype);
+  if (st != VITBLK_OK) return st;
+  GemmProblem p = linear_problem(a, w_t, out, nullptr, M, K, Nout, epilogue, dtype, bias);
+  p.row_stats = row_stats;
+  p.col_sums = col_sums;
+  VITBLK_LAUNCH(launch_gemm(p, reinterpret_cast<hipStream_t>(stream)));
   return VITBLK_OK;
 }
 

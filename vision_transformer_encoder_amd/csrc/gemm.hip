@@ -35,6 +35,16 @@
 //   k-slices are issued before the current tile's epilogue, so the load
 //   latency at a tile start overlaps the stores of the previous tile, and the
 //   epilogue issues all residual loads before its first store.
+// * Epilogue reads (residual, bias) are issued before the next tile's first
+//   k-slices: loads complete in issue order, so a read issued after them
+//   would hold the epilogue until those slices had landed.
+// * LayerNorm fold (row_stats set): LN(A) @ W = rstd (A @ W - mean colsum W)
+//   (crackedaicode.com "ViT Encoder Block", "Normalize before each stage":
+//   (x - mean) * rstd per token, multiplied out).  The accumulators start at
+//   -mean_m colsum_n instead of 0 and the epilogue scales by rstd_m, so LN's
+//   output never goes through memory.
+// * Split K (kEpiPartial): the tile index also runs over k-ranges whose
+//   unrounded fp32 sums are written out; a second kernel adds them in order.
 // * Tile order: workgroups are dispatched round-robin over the 8 XCDs; each
 //   XCD is given a contiguous run of tiles per round, walked in groups of 8
 //   M-tiles so that the tiles resident at once on an XCD share A and W
@@ -128,7 +138,7 @@ __device__ __forceinline__ void tile_of(int t, int grid, int total, int mt, int 
   *tn = w / gm;
 }
 
-template <class C, int EPI, bool BIAS>
+template <class C, int EPI, bool BIAS, bool NORM>
 __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p, int mt, int nt) {
   __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
   char* const a_lds = lds;                       // [stage][BM rows][BK * 2 B]
@@ -271,13 +281,51 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
   prepare(t);
   start_tile();
 
+  float rsd[C::TM];  // LayerNorm fold: rstd of the lane's rows of the current tile
   while (true) {
+    if (NORM) {
+      // LayerNorm fold, mean term: the accumulators start at -mean_m *
+      // colsum_n, so after the k loop they hold A @ W - mean colsum and the
+      // epilogue only scales by rstd_m.  The loads (L2-resident) go out
+      // before the first k-slice's wait, which they share.  A lane's rows
+      // are lrow of each 32-row block i; its columns in block j are the 4
+      // runs of 4 described for the bias below.  Rows and columns past M or
+      // N are clamped (never stored).
+      float nmu[C::TM];
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j)
+      for (int i = 0; i < C::TM; ++i) {
+        int64_t m = m0 + wm * C::WTM + i * 32 + lrow;
+        m = m < M ? m : M - 1;
+        const float2 st = *reinterpret_cast<const float2*>(p.row_stats + 2 * m);
+        nmu[i] = -st.x;
+        rsd[i] = st.y;
+      }
 #pragma unroll
-      for (int i = 0; i < C::TM; ++i)
+      for (int j = 0; j < C::TN; ++j) {
+        float cs[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.f;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          int64_t n = n0 + wn * C::WTN + j * 32 + g4 * 8 + lhalf * 4;
+          n = n < N ? n : N - 4;
+          const float4 c4 = *reinterpret_cast<const float4*>(p.col_sums + n);
+          cs[g4 * 4 + 0] = c4.x;
+          cs[g4 * 4 + 1] = c4.y;
+          cs[g4 * 4 + 2] = c4.z;
+          cs[g4 * 4 + 3] = c4.w;
+        }
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[j][i][r] = nmu[i] * cs[r];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.f;
+    }
 
     // Before computing slice kt a wave waits until its own loads of slice kt
     // have landed (newer slices may stay outstanding; vmcnt retires in issue
@@ -313,10 +361,54 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
       });
     }
 
-    // Start the next tile's first k-slices before this tile's epilogue (all
-    // waves are done reading LDS once past this barrier).
+    // The epilogue's global reads (residual, bias) go out before the next
+    // tile's first k-slices: loads complete in issue order, so a read issued
+    // after those slices would hold the epilogue until they had landed.
     const int64_t cm0 = m0, cn0 = n0;
     const int cks = ks;
+    const bf16_t* Rp = static_cast<const bf16_t*>(p.R);
+    // R: the residual, or GELU's input z for the GELU-derivative epilogue, in
+    // the lanes' store layout (below), rows and columns clamped into range.
+    constexpr bool kReadsR =
+        EPI == VITBLK_EPI_RESIDUAL || EPI == VITBLK_EPI_GELU_GRAD || EPI == kEpiMul;
+    uint4 res[C::TM][C::TN][2];
+    if (kReadsR) {
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) {
+        int64_t m = cm0 + wm * C::WTM + i * 32 + lrow;
+        m = m < M ? m : M - 1;
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            int64_t n = cn0 + wn * C::WTN + j * 32 + q * 16 + lhalf * 8;
+            n = n < N ? n : N - 8;
+            res[i][j][q] = ld_global16(Rp + m * p.ldr + n);
+          }
+      }
+    }
+    // Bias: accumulator element r of block (j, i) is column (r/4)*8 +
+    // (l/32)*4 + r%4 of the block: 4 runs of 4 columns per lane, the same for
+    // every i.  Columns past N are clamped (never stored).
+    uint2 braw[C::TN][4];
+    if (BIAS) {
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          int64_t n = cn0 + wn * C::WTN + j * 32 + g4 * 8 + lhalf * 4;
+          n = n < N ? n : N - 4;
+          const int seg = static_cast<int>(n / p.bias_seg);
+          const void* bs = seg == 0 ? p.bias[0] : (seg == 1 ? p.bias[1] : p.bias[2]);
+          braw[j][g4] = make_uint2(0u, 0u);
+          if (bs != nullptr)
+            braw[j][g4] = *reinterpret_cast<const uint2*>(
+                static_cast<const bf16_t*>(bs) + (n - static_cast<int64_t>(seg) * p.bias_seg));
+        }
+    }
+
+    // Start the next tile's first k-slices before this tile's epilogue (all
+    // waves are done reading LDS once past this barrier).
     const int t_next = t + grid;
     const bool more = t_next < total;
     __builtin_amdgcn_s_barrier();
@@ -334,25 +426,24 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
     // first store (addresses clamped into range), and added in fp32 before
     // the single rounding to bf16.
     bf16_t* Cp = static_cast<bf16_t*>(p.C);
-    const bf16_t* Rp = static_cast<const bf16_t*>(p.R);
+    // LayerNorm fold, scale term (before the bias): acc = rstd_m * acc.
+    if (NORM) {
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[j][i][r] *= rsd[i];
+    }
     // Bias, added in fp32 to the accumulators first (before GELU or the
-    // residual).  Accumulator element r of block (j, i) is column
-    // (r/4)*8 + (l/32)*4 + r%4 of the block: 4 runs of 4 columns per lane, the
-    // same for every i.  Columns past N are clamped (never stored).
+    // residual).
     if (BIAS) {
 #pragma unroll
       for (int j = 0; j < C::TN; ++j) {
         float bv[16];
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          int64_t n = cn0 + wn * C::WTN + j * 32 + g4 * 8 + lhalf * 4;
-          n = n < N ? n : N - 4;
-          const int seg = static_cast<int>(n / p.bias_seg);
-          const void* bs = seg == 0 ? p.bias[0] : (seg == 1 ? p.bias[1] : p.bias[2]);
-          uint2 u = make_uint2(0u, 0u);
-          if (bs != nullptr)
-            u = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(bs) +
-                                                (n - static_cast<int64_t>(seg) * p.bias_seg));
+          const uint2 u = braw[j][g4];
           bv[g4 * 4 + 0] = __uint_as_float(u.x << 16);
           bv[g4 * 4 + 1] = __uint_as_float(u.x & 0xffff0000u);
           bv[g4 * 4 + 2] = __uint_as_float(u.y << 16);
@@ -362,25 +453,6 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
         for (int i = 0; i < C::TM; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[j][i][r] += bv[r];
-      }
-    }
-    // R: the residual, or GELU's input z for the GELU-derivative epilogue.
-    constexpr bool kReadsR =
-        EPI == VITBLK_EPI_RESIDUAL || EPI == VITBLK_EPI_GELU_GRAD || EPI == kEpiMul;
-    uint4 res[C::TM][C::TN][2];
-    if (kReadsR) {
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i) {
-        int64_t m = cm0 + wm * C::WTM + i * 32 + lrow;
-        m = m < M ? m : M - 1;
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j)
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            int64_t n = cn0 + wn * C::WTN + j * 32 + q * 16 + lhalf * 8;
-            n = n < N ? n : N - 8;
-            res[i][j][q] = ld_global16(Rp + m * p.ldr + n);
-          }
       }
     }
     // The plain and residual epilogues store each 32-row block as whole row
@@ -568,7 +640,7 @@ __global__ __launch_bounds__(256) void splitk_residual_kernel(const float* __res
 }
 
 // Workgroups of this kernel the device holds at once (cached per kernel).
-template <class C, int EPI, bool BIAS = false>
+template <class C, int EPI, bool BIAS = false, bool NORM = false>
 int resident_workgroups() {
   static int cached = 0;
   if (cached == 0) {
@@ -576,7 +648,8 @@ int resident_workgroups() {
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&gemm_bf16_kernel<C, EPI, BIAS>), C::NT, 0) !=
+            &per_cu, reinterpret_cast<const void*>(&gemm_bf16_kernel<C, EPI, BIAS, NORM>), C::NT,
+            0) !=
             hipSuccess) {
       (void)hipGetLastError();
       return 0;
@@ -586,16 +659,16 @@ int resident_workgroups() {
   return cached;
 }
 
-template <class C, int EPI, bool BIAS>
+template <class C, int EPI, bool BIAS, bool NORM = false>
 hipError_t launch_epi(const GemmProblem& p, hipStream_t s) {
   const int64_t mt = (p.M + C::BM - 1) / C::BM, nt = (p.N + C::BN - 1) / C::BN;
   const int64_t tiles = mt * nt * (EPI == kEpiPartial ? p.ksplit : 1);
   if (tiles > 2147483647LL) return hipErrorInvalidValue;
-  int64_t grid = resident_workgroups<C, EPI, BIAS>();
+  int64_t grid = resident_workgroups<C, EPI, BIAS, NORM>();
   if (grid <= 0) return hipErrorInvalidValue;
   grid = grid / kNumXcd * kNumXcd;  // keeps the XCD-contiguous mapping exact
   if (grid <= 0 || grid > tiles) grid = tiles;
-  hipLaunchKernelGGL((gemm_bf16_kernel<C, EPI, BIAS>), dim3(static_cast<unsigned>(grid)),
+  hipLaunchKernelGGL((gemm_bf16_kernel<C, EPI, BIAS, NORM>), dim3(static_cast<unsigned>(grid)),
                      dim3(C::NT), 0, s, p, static_cast<int>(mt), static_cast<int>(nt));
   return hipGetLastError();
 }
@@ -615,8 +688,18 @@ hipError_t launch_bias(const GemmProblem& p, hipStream_t s) {
   }
 }
 
+// The LayerNorm-folded products (plain or GELU epilogue only).
+template <class C, bool BIAS>
+hipError_t launch_norm(const GemmProblem& p, hipStream_t s) {
+  if (p.epi == VITBLK_EPI_GELU) return launch_epi<C, VITBLK_EPI_GELU, BIAS, true>(p, s);
+  if (p.epi == VITBLK_EPI_NONE) return launch_epi<C, VITBLK_EPI_NONE, BIAS, true>(p, s);
+  return hipErrorInvalidValue;
+}
+
 template <class C>
 hipError_t launch_cfg(const GemmProblem& p, hipStream_t s) {
+  if (p.row_stats != nullptr)
+    return has_bias(p) ? launch_norm<C, true>(p, s) : launch_norm<C, false>(p, s);
   return has_bias(p) ? launch_bias<C, true>(p, s) : launch_bias<C, false>(p, s);
 }
 
@@ -635,6 +718,8 @@ bool gemm_fast_ok(const GemmProblem& p) {
             aligned16(p.B) && aligned16(p.C) && p.lda * 2 * 256 < (1LL << 31) &&
             p.ldb * 2 * 256 < (1LL << 31) && p.K * 2 < (1LL << 31);
   if (reads_r(p)) ok = ok && p.ldr % 8 == 0 && aligned16(p.R);
+  if (p.row_stats != nullptr)
+    ok = ok && aligned16(p.col_sums) && (reinterpret_cast<uintptr_t>(p.row_stats) & 7u) == 0;
   if (p.epi == kEpiGeluDual) ok = ok && aligned16(p.C2);
   if (has_bias(p)) {
     ok = ok && p.bias_seg > 0 && p.bias_seg % 8 == 0 && p.N <= 3 * p.bias_seg;
@@ -652,6 +737,7 @@ GemmProblem row_slice(const GemmProblem& p, int64_t r0, int64_t rows) {
   q.C = static_cast<char*>(p.C) + r0 * p.ldc * 2;
   if (p.R) q.R = static_cast<const char*>(p.R) + r0 * p.ldr * 2;
   if (p.C2) q.C2 = static_cast<char*>(p.C2) + r0 * p.ldc * 2;
+  if (p.row_stats) q.row_stats = p.row_stats + 2 * r0;
   return q;
 }
 
@@ -714,6 +800,9 @@ hipError_t launch_tail(const GemmProblem& p, hipStream_t s) {
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t s) {
   if (reads_r(p) && p.R == nullptr) return hipErrorInvalidValue;  // never launch on a null R
   if (p.epi == kEpiGeluDual && p.C2 == nullptr) return hipErrorInvalidValue;
+  if (p.row_stats != nullptr &&
+      (p.col_sums == nullptr || (p.epi != VITBLK_EPI_NONE && p.epi != VITBLK_EPI_GELU)))
+    return hipErrorInvalidValue;
   if (!gemm_fast_ok(p)) return launch_gemm_generic(p, s);
   using Big = BigTile;
   using Small = SmallTile;

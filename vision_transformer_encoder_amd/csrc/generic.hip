@@ -52,6 +52,31 @@ __global__ __launch_bounds__(kGenThreads) void ln_generic_kernel(
   }
 }
 
+// Statistics of one row per workgroup (as ln_generic_kernel): mean and
+// 1 / sqrt(var + eps).
+template <typename T>
+__global__ __launch_bounds__(kGenThreads) void row_stats_generic_kernel(const T* __restrict__ x,
+                                                                        int64_t ld_in,
+                                                                        float* __restrict__ st,
+                                                                        int64_t D, float eps) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const T* xr = x + row * ld_in;
+  float s = 0.f;
+  for (int64_t i = threadIdx.x; i < D; i += kGenThreads) s += load_f32(xr + i);
+  const float mean = block_sum_256(s, red) / static_cast<float>(D);
+  float q = 0.f;
+  for (int64_t i = threadIdx.x; i < D; i += kGenThreads) {
+    const float d = load_f32(xr + i) - mean;
+    q += d * d;
+  }
+  const float var = block_sum_256(q, red) / static_cast<float>(D);
+  if (threadIdx.x == 0) {
+    st[2 * row] = mean;
+    st[2 * row + 1] = 1.0f / sqrtf(var + eps);
+  }
+}
+
 // 64x64 output tile per workgroup, 16-deep k slices staged in LDS, 4x4
 // outputs per thread; tiles flattened into blockIdx.x.
 template <typename T, int EPI>
@@ -100,6 +125,8 @@ __global__ __launch_bounds__(kGenThreads) void gemm_generic_kernel(GemmProblem p
       const int64_t n = n0 + tx * 4 + j;
       if (n >= p.N) continue;
       float v = acc[i][j];
+      if (p.row_stats != nullptr)  // LN(A) @ W = rstd (A @ W - mean colsum)
+        v = p.row_stats[2 * m + 1] * (v - p.row_stats[2 * m] * p.col_sums[n]);
       if (has_bias(p)) {
         const int64_t seg = n / p.bias_seg;
         const void* bs = seg == 0 ? p.bias[0] : (seg == 1 ? p.bias[1] : p.bias[2]);
@@ -235,6 +262,19 @@ hipError_t launch_layernorm_generic(const void* x, int64_t ld_in, const void* ga
     hipLaunchKernelGGL(ln_generic_kernel<float>, grid, dim3(kGenThreads), 0, s,
                        static_cast<const float*>(x), ld_in, static_cast<const float*>(gamma),
                        static_cast<const float*>(beta), static_cast<float*>(y), D, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_stats_generic(const void* x, int64_t ld_in, float* stats, int64_t rows,
+                                    int64_t D, float eps, int dtype, hipStream_t s) {
+  if (rows > 2147483647LL) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(rows));
+  if (dtype == VITBLK_BF16)
+    hipLaunchKernelGGL(row_stats_generic_kernel<bf16_t>, grid, dim3(kGenThreads), 0, s,
+                       static_cast<const bf16_t*>(x), ld_in, stats, D, eps);
+  else
+    hipLaunchKernelGGL(row_stats_generic_kernel<float>, grid, dim3(kGenThreads), 0, s,
+                       static_cast<const float*>(x), ld_in, stats, D, eps);
   return hipGetLastError();
 }
 

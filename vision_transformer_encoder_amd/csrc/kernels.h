@@ -30,6 +30,14 @@ struct GemmProblem {
   const void* bias[3];
   int64_t bias_seg;
   void* C2;  // second output of kEpiGeluDual (same layout as C), else unused
+  // LayerNorm folded into a product whose left operand is LN(A) (no gain or
+  // shift): the product becomes rstd_m * (A @ W - mean_m * colsum_n), added
+  // before the bias and the epilogue, with (mean_m, rstd_m) = row_stats[2m],
+  // row_stats[2m + 1] (row m of A) and colsum_n = col_sums[n] = sum_k W[k, n]
+  // (of the operand as stored).  Both null: a plain product.  Epilogues NONE
+  // and GELU only.
+  const float* row_stats;
+  const float* col_sums;
   // kEpiPartial only: the number of k-ranges (>= 1).
   int ksplit;
   // Free fp32 device memory launch_gemm may use for split-K partial sums of
@@ -72,6 +80,24 @@ hipError_t launch_layernorm(const void* x, int64_t ld_in, const void* gamma, con
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
 
+// Whether the matrix-core kernels take p (otherwise the generic kernel does).
+bool gemm_fast_ok(const GemmProblem& p);
+
+// stats[2r], stats[2r + 1] = mean and 1 / sqrt(var + eps) of row r of x
+// (population variance, fp32, the same arithmetic as launch_layernorm's);
+// row r starts at x + r * ld_in elements.
+hipError_t launch_row_stats(const void* x, int64_t ld_in, float* stats, int64_t rows, int64_t D,
+                            float eps, int dtype, hipStream_t stream);
+
+// sums[r] = sum_c src[r * cols + c] in fp32, in a fixed order (the same
+// result on every call); up to two jobs in one launch.
+struct RowSumJob {
+  const void* src;
+  int64_t rows, cols;
+  float* sums;
+};
+hipError_t launch_row_sums(const RowSumJob* jobs, int njobs, int dtype, hipStream_t stream);
+
 // The front end: images [B, C, H, W] -> tokens [B, N (+1), D] (patch matrix,
 // embedding GEMM, token assembly); w_t, patches and embedded are workspace.
 struct PatchEmbedArgs {
@@ -111,6 +137,8 @@ hipError_t launch_layernorm_generic(const void* x, int64_t ld_in, const void* ga
                                     const void* beta, void* y, int64_t rows, int64_t D,
                                     float eps, int dtype, hipStream_t stream);
 hipError_t launch_gemm_generic(const GemmProblem& p, hipStream_t stream);
+hipError_t launch_row_stats_generic(const void* x, int64_t ld_in, float* stats, int64_t rows,
+                                    int64_t D, float eps, int dtype, hipStream_t stream);
 hipError_t launch_attention_generic(const void* q, const void* k, const void* v, int64_t ld,
                                     void* o, int64_t ldo, int64_t N, int64_t T, int64_t H,
                                     int64_t dh, int dtype, hipStream_t stream);

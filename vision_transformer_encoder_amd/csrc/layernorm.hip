@@ -10,6 +10,11 @@
 // bandwidth (2 * D * element size bytes per row).  Statistics are fp32 and
 // two-pass over the registers (mean, then the squared deviations), reduced
 // across the wave with DPP row operations and lane reads.
+//
+// The statistics-only kernel serves the products that fold a LayerNorm
+// without gain or shift into their epilogue (LN(x) @ W = rstd (x @ W -
+// mean colsum W)): it reads the row and writes its mean and rstd, half the
+// LayerNorm's traffic (D * element size + 8 bytes per row).
 #include <math.h>
 
 #include "device.h"
@@ -46,18 +51,14 @@ __device__ __forceinline__ void store8(float* p, const float v[8]) {
   *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
 
-// NCH = upper bound on 8-element chunks per lane (D <= 512 * NCH).
+// A row's statistics, the row held in registers: lane l loads chunks
+// l, l + 64, ... of 8 elements into v (NCH = upper bound on chunks per lane,
+// D <= 512 * NCH); mean and rstd = 1 / sqrt(var + eps) in fp32, two-pass.
 template <typename T, int NCH>
-__global__ __launch_bounds__(64 * kRowsPerBlock) void ln_rows_kernel(
-    const T* __restrict__ x, int64_t ld_in, const T* __restrict__ gamma,
-    const T* __restrict__ beta, T* __restrict__ y, int64_t rows, int D, float eps) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= rows) return;  // whole wave leaves; no workgroup barrier follows
+__device__ __forceinline__ void row_stats(const T* xr, int lane, int D, float eps,
+                                          float (&v)[NCH][8], float* mean_out,
+                                          float* rstd_out) {
   const int nchunks = D >> 3;
-  const T* xr = x + row * ld_in;
-  T* yr = y + row * D;
-  float v[NCH][8];
   float s = 0.f;
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
@@ -82,7 +83,22 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void ln_rows_kernel(
     }
   }
   const float var = wave_sum(q) * inv_d;
-  const float rstd = 1.0f / sqrtf(var + eps);
+  *mean_out = mean;
+  *rstd_out = 1.0f / sqrtf(var + eps);
+}
+
+template <typename T, int NCH>
+__global__ __launch_bounds__(64 * kRowsPerBlock) void ln_rows_kernel(
+    const T* __restrict__ x, int64_t ld_in, const T* __restrict__ gamma,
+    const T* __restrict__ beta, T* __restrict__ y, int64_t rows, int D, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;  // whole wave leaves; no workgroup barrier follows
+  const int nchunks = D >> 3;
+  T* yr = y + row * D;
+  float v[NCH][8];
+  float mean, rstd;
+  row_stats<T, NCH>(x + row * ld_in, lane, D, eps, v, &mean, &rstd);
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int idx = lane + 64 * c;
@@ -105,6 +121,39 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void ln_rows_kernel(
       store8(yr + idx * 8, o);
     }
   }
+}
+
+// Statistics only (for products that fold the LayerNorm into their
+// epilogue): reads the row once and writes 8 bytes.  (Four rows per wave,
+// all requested before any is reduced, measured no faster.)
+template <typename T, int NCH>
+__global__ __launch_bounds__(64 * kRowsPerBlock) void ln_stats_kernel(
+    const T* __restrict__ x, int64_t ld_in, float2* __restrict__ stats, int64_t rows, int D,
+    float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  float v[NCH][8];
+  float mean, rstd;
+  row_stats<T, NCH>(x + row * ld_in, lane, D, eps, v, &mean, &rstd);
+  if (lane == 0) stats[row] = make_float2(mean, rstd);
+}
+
+template <typename T>
+hipError_t stats_fast_typed(const T* x, int64_t ld, float2* st, int64_t rows, int D, float eps,
+                            hipStream_t s) {
+  const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  const dim3 grid(static_cast<unsigned>(blocks)), block(64 * kRowsPerBlock);
+  const int cpl = (D / 8 + 63) / 64;
+  if (cpl <= 1)
+    hipLaunchKernelGGL((ln_stats_kernel<T, 1>), grid, block, 0, s, x, ld, st, rows, D, eps);
+  else if (cpl <= 2)
+    hipLaunchKernelGGL((ln_stats_kernel<T, 2>), grid, block, 0, s, x, ld, st, rows, D, eps);
+  else if (cpl <= 4)
+    hipLaunchKernelGGL((ln_stats_kernel<T, 4>), grid, block, 0, s, x, ld, st, rows, D, eps);
+  else
+    hipLaunchKernelGGL((ln_stats_kernel<T, 8>), grid, block, 0, s, x, ld, st, rows, D, eps);
+  return hipGetLastError();
 }
 
 template <typename T>
@@ -220,6 +269,21 @@ hipError_t launch_layernorm_backward(const void* x, const void* g, const void* r
   return ln_bwd_fast_typed(static_cast<const float*>(x), static_cast<const float*>(g),
                            static_cast<const float*>(res), static_cast<float*>(dx), rows,
                            static_cast<int>(D), eps, s);
+}
+
+hipError_t launch_row_stats(const void* x, int64_t ld_in, float* stats, int64_t rows, int64_t D,
+                            float eps, int dtype, hipStream_t s) {
+  const bool fast = (D % 8 == 0) && (ld_in % 8 == 0) && (D <= 64 * 8 * 8) &&
+                    (reinterpret_cast<uintptr_t>(x) & 15u) == 0 &&
+                    (reinterpret_cast<uintptr_t>(stats) & 7u) == 0 &&
+                    (rows + kRowsPerBlock - 1) / kRowsPerBlock <= 2147483647LL;
+  if (!fast) return launch_row_stats_generic(x, ld_in, stats, rows, D, eps, dtype, s);
+  float2* st = reinterpret_cast<float2*>(stats);
+  if (dtype == VITBLK_BF16)
+    return stats_fast_typed(static_cast<const bf16_t*>(x), ld_in, st, rows, static_cast<int>(D),
+                            eps, s);
+  return stats_fast_typed(static_cast<const float*>(x), ld_in, st, rows, static_cast<int>(D), eps,
+                          s);
 }
 
 hipError_t launch_layernorm(const void* x, int64_t ld_in, const void* gamma, const void* beta,

@@ -70,6 +70,39 @@ __global__ __launch_bounds__(256) void pack_blocks_kernel(PackArgs a) {
   for (int k = 0; k < 8; ++k) st_global16(dst + k * j.ldd, out[k]);
 }
 
+// Row sums of the packed out-major weights, sums[r] = sum_c src[r][c]: the
+// column sums of the (in, out) weights that the LayerNorm fold needs.  One
+// wave per row, four rows per workgroup.  bf16 rows whose length is a
+// multiple of 8 (16-byte aligned) are read 8 elements per lane and load:
+// lane l adds chunks l, l + 64, ... in order; otherwise single elements.
+// The wave reduction is a fixed tree, so every call gives the same bits.
+struct RowSumArgs {
+  RowSumJob job[2];
+};
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(256) void row_sums_kernel(RowSumArgs a) {
+  const RowSumJob& j = a.job[blockIdx.y];
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (r >= j.rows) return;  // whole wave
+  const int lane = threadIdx.x & 63;
+  const T* src = static_cast<const T*>(j.src) + r * j.cols;
+  float s = 0.f;
+  if (VEC) {
+    for (int64_t c = lane * 8; c < j.cols; c += 512) {
+      const uint4 u = ld_global16(src + c);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        s += __uint_as_float(w[e] << 16) + __uint_as_float(w[e] & 0xffff0000u);
+    }
+  } else {
+    for (int64_t c = lane; c < j.cols; c += 64) s += load_f32(src + c);
+  }
+  s = wave_sum(s);
+  if (lane == 0) j.sums[r] = s;
+}
+
 bool blocks_ok(const PackJob& j) {
   return j.rows % 8 == 0 && j.cols % 8 == 0 && j.ldd % 8 == 0 &&
          (reinterpret_cast<uintptr_t>(j.src) & 15u) == 0 &&
@@ -101,6 +134,29 @@ hipError_t launch_pack(const PackJob* jobs, int njobs, int dtype, hipStream_t s)
     hipLaunchKernelGGL(pack_kernel<bf16_t>, grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(pack_kernel<float>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_sums(const RowSumJob* jobs, int njobs, int dtype, hipStream_t s) {
+  if (njobs < 1 || njobs > 2) return hipErrorInvalidValue;
+  RowSumArgs a{};
+  int64_t max_rows = 0;
+  for (int i = 0; i < njobs; ++i) {
+    a.job[i] = jobs[i];
+    max_rows = jobs[i].rows > max_rows ? jobs[i].rows : max_rows;
+  }
+  const int64_t blocks = (max_rows + 3) / 4;
+  if (blocks > 2147483647LL) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(njobs));
+  bool vec = dtype == VITBLK_BF16;
+  for (int i = 0; i < njobs; ++i)
+    vec = vec && jobs[i].cols % 8 == 0 && (reinterpret_cast<uintptr_t>(jobs[i].src) & 15u) == 0;
+  if (vec)
+    hipLaunchKernelGGL((row_sums_kernel<bf16_t, true>), grid, dim3(256), 0, s, a);
+  else if (dtype == VITBLK_BF16)
+    hipLaunchKernelGGL((row_sums_kernel<bf16_t, false>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((row_sums_kernel<float, false>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

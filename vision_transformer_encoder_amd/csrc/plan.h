@@ -21,6 +21,7 @@ size_t elem_size(int dtype);  // 0 for an unknown dtype
 // W2^T [D, F].
 struct PackedPlan {
   size_t off_qkv, off_o, off_1, off_2;
+  size_t off_cs_qkv, off_cs_1;  // fp32 column sums of [w_q | w_k | w_v] and of w_mlp1
   size_t total;
 };
 
@@ -29,7 +30,8 @@ struct WorkspacePlan {
   PackedPlan packed;   // at the start of the vitblk_forward workspace
   size_t act_base;     // first activation byte (0 for vitblk_forward_packed)
   size_t off_big;      // [M, max(3D, F)]: packed qkv, later the MLP hidden
-  size_t off_act;      // [M, D]: LN(x), then concatenated heads, then LN(y)
+  size_t off_act;      // [M, D]: LN(x) or its row statistics, then the concatenated
+                       // heads, then LN(y) or its row statistics
   size_t off_y;        // [M, D]: first residual output
   size_t act_total;    // bytes of the three activation regions
   size_t total;        // vitblk_forward workspace: packed.total + act_total
@@ -95,6 +97,11 @@ int validate_attention(const void* qkv, const void* att, int64_t N, int64_t T, i
                        int64_t H, int dtype);
 
 // bias may be null.
+int validate_row_stats(const void* x, const float* stats, int64_t rows, int64_t D, double eps,
+                       int dtype);
+int validate_linear_normed(const void* a, const void* w, const float* col_sums,
+                           const float* row_stats, const void* bias, const void* out, int64_t M,
+                           int64_t K, int64_t Nout, int epilogue, int dtype);
 int validate_linear(const void* a, const void* w, const void* bias, const void* residual,
                     const void* out, int64_t M, int64_t K, int64_t Nout, int epilogue,
                     int dtype);

@@ -82,7 +82,9 @@ int plan_packed(int64_t D, int64_t F, int dtype, PackedPlan* plan) {
   p.off_o = round_up(dd, kRegionAlign);             // 3 D^2 elements before
   p.off_1 = p.off_o + round_up(dd / 3, kRegionAlign);
   p.off_2 = p.off_1 + round_up(df, kRegionAlign);
-  p.total = p.off_2 + round_up(df, kRegionAlign);
+  p.off_cs_qkv = p.off_2 + round_up(df, kRegionAlign);
+  p.off_cs_1 = p.off_cs_qkv + round_up(3 * d * sizeof(float), kRegionAlign);
+  p.total = p.off_cs_1 + round_up(f * sizeof(float), kRegionAlign);
   *plan = p;
   return VITBLK_OK;
 }
@@ -345,6 +347,39 @@ int validate_linear(const void* a, const void* w, const void* bias, const void* 
     return VITBLK_ERR_ALIAS;
   if (reads_r && overlap(o, span(residual, m * n * es))) return VITBLK_ERR_ALIAS;
   if (bias != nullptr && overlap(o, span(bias, n * es))) return VITBLK_ERR_ALIAS;
+  return VITBLK_OK;
+}
+
+int validate_row_stats(const void* x, const float* stats, int64_t rows, int64_t D, double eps,
+                       int dtype) {
+  if (x == nullptr || stats == nullptr || !aligned16(x)) return VITBLK_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(stats) & 7u) != 0) return VITBLK_ERR_INVALID_ARG;
+  if (!dim_ok(rows) || !dim_ok(D)) return VITBLK_ERR_INVALID_ARG;
+  const size_t es = elem_size(dtype);
+  if (es == 0) return VITBLK_ERR_INVALID_ARG;
+  const int st = check_eps(eps);
+  if (st != VITBLK_OK) return st;
+  if (rows > kMaxDim || D > kMaxDim) return VITBLK_ERR_UNSUPPORTED;
+  const size_t r = static_cast<size_t>(rows);
+  if (overlap(span(stats, r * 2 * sizeof(float)), span(x, r * static_cast<size_t>(D) * es)))
+    return VITBLK_ERR_ALIAS;
+  return VITBLK_OK;
+}
+
+int validate_linear_normed(const void* a, const void* w, const float* col_sums,
+                           const float* row_stats, const void* bias, const void* out, int64_t M,
+                           int64_t K, int64_t Nout, int epilogue, int dtype) {
+  if (epilogue != VITBLK_EPI_NONE && epilogue != VITBLK_EPI_GELU) return VITBLK_ERR_INVALID_ARG;
+  if (col_sums == nullptr || row_stats == nullptr || !aligned16(col_sums) ||
+      (reinterpret_cast<uintptr_t>(row_stats) & 7u) != 0)
+    return VITBLK_ERR_INVALID_ARG;
+  const int st = validate_linear(a, w, bias, nullptr, out, M, K, Nout, epilogue, dtype);
+  if (st != VITBLK_OK) return st;
+  const size_t m = static_cast<size_t>(M), n = static_cast<size_t>(Nout);
+  const Span o = span(out, m * n * elem_size(dtype));
+  if (overlap(o, span(col_sums, n * sizeof(float))) ||
+      overlap(o, span(row_stats, m * 2 * sizeof(float))))
+    return VITBLK_ERR_ALIAS;
   return VITBLK_OK;
 }
 
