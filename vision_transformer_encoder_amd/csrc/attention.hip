@@ -24,16 +24,17 @@ constexpr int kNumXcd = 8;
 
 // ---------------------------------------------------------------- streaming kernel
 //
+// W waves per workgroup (kStreamWaves unless a head width says otherwise).
+constexpr int kStreamWaves = 8;
+//
 // Keys stream through LDS in 64-key chunks, two stages deep.  A workgroup is 8
 // waves over one (sequence, head) and up to 8 query tiles of 32, so each
 // K/V chunk copied into LDS serves up to 256 queries; per chunk every thread
 // requests its share of the next chunk before the tile work on the current
 // one and writes it to the other stage after, and one barrier ends the chunk.
 // The per-tile work is attention_tile.h's (the resident kernel's).
-constexpr int kStreamWaves = 8;
-
-template <int DH>
-__global__ __launch_bounds__(64 * kStreamWaves, (DH <= 64 ? 4 : 2)) void attn_stream_kernel(
+template <int DH, int W>
+__global__ __launch_bounds__(64 * W, (DH <= 64 ? 4 : 2)) void attn_stream_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     int64_t ld, bf16_t* __restrict__ O, int64_t ldo, int T, int H, int nqb, int tpb,
     float scale_log2) {
@@ -61,12 +62,12 @@ __global__ __launch_bounds__(64 * kStreamWaves, (DH <= 64 ? 4 : 2)) void attn_st
   // Staging of one chunk: 64 keys x DH/8 chunks of 16 bytes per operand.
   constexpr int CPR = DH / 8;
   constexpr int PER = 64 * CPR;
-  constexpr int NL = (PER + 64 * kStreamWaves - 1) / (64 * kStreamWaves);
+  constexpr int NL = (PER + 64 * W - 1) / (64 * W);
   uint4 rk[NL], rv[NL];
   auto fetch = [&](int c) {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      const int e = tid + i * 64 * kStreamWaves;
+      const int e = tid + i * 64 * W;
       if (e < PER) {
         int t = c * 64 + e / CPR;
         t = t < T ? t : T - 1;
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(64 * kStreamWaves, (DH <= 64 ? 4 : 2)) void attn_st
     char* const vs = ks + 64 * C::SK;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      const int e = tid + i * 64 * kStreamWaves;
+      const int e = tid + i * 64 * W;
       if (e < PER) {
         *reinterpret_cast<uint4*>(ks + (e / CPR) * C::SK + (e % CPR) * 16) = rk[i];
         *reinterpret_cast<uint4*>(vs + (e / CPR) * C::SV + (e % CPR) * 16) = rv[i];
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(64 * kStreamWaves, (DH <= 64 ? 4 : 2)) void attn_st
   fetch(0);
   if (C::DHP > DH) {  // features DH..DHP-1 of V feed only discarded output rows; keep them 0
     constexpr int PC = (C::DHP - DH) / 8;
-    for (int e = tid; e < 2 * 64 * PC; e += 64 * kStreamWaves) {
+    for (int e = tid; e < 2 * 64 * PC; e += 64 * W) {
       const int st = e / (64 * PC), r = (e / PC) % 64;
       *reinterpret_cast<uint4*>(smem + st * STAGE + 64 * C::SK + r * C::SV +
                                 (DH + (e % PC) * 8) * 2) = make_uint4(0, 0, 0, 0);
@@ -126,14 +127,14 @@ __global__ __launch_bounds__(64 * kStreamWaves, (DH <= 64 ? 4 : 2)) void attn_st
   if (active) tile.store(O, ldo, seq0, hoff, T, qt * 32, lane);
 }
 
-template <int DH>
+template <int DH, int W = kStreamWaves>
 hipError_t launch_stream(const void* q, const void* k, const void* v, int64_t ld, void* o,
                          int64_t ldo, int64_t N, int64_t T, int64_t H, hipStream_t s) {
   using C = attn::Cfg<DH>;
   constexpr size_t bytes = 2 * 64 * C::ROW;
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_stream_kernel<DH>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_stream_kernel<DH, W>),
                             hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(bytes)) != hipSuccess) {
       (void)hipGetLastError();
@@ -142,13 +143,13 @@ hipError_t launch_stream(const void* q, const void* k, const void* v, int64_t ld
     attr_set = true;
   }
   const int64_t nqt = (T + 31) / 32;
-  const int64_t nqb = (nqt + kStreamWaves - 1) / kStreamWaves;
+  const int64_t nqb = (nqt + W - 1) / W;
   const int64_t tpb = (nqt + nqb - 1) / nqb;  // query tiles per workgroup, balanced
   const int64_t blocks = N * H * nqb;
   if (blocks > 2147483647LL) return hipErrorInvalidValue;
   const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(DH));
-  hipLaunchKernelGGL(attn_stream_kernel<DH>, dim3(static_cast<unsigned>(blocks)),
-                     dim3(64 * kStreamWaves), bytes, s, static_cast<const bf16_t*>(q),
+  hipLaunchKernelGGL((attn_stream_kernel<DH, W>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(64 * W), bytes, s, static_cast<const bf16_t*>(q),
                      static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), ld,
                      static_cast<bf16_t*>(o), ldo, static_cast<int>(T), static_cast<int>(H),
                      static_cast<int>(nqb), static_cast<int>(tpb), scale_log2);

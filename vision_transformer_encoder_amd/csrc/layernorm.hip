@@ -19,6 +19,7 @@
 
 #include "device.h"
 #include "kernels.h"
+#include "row_stats.h"
 #include "vitblk.h"
 
 namespace vitblk {
@@ -26,22 +27,7 @@ namespace {
 
 constexpr int kRowsPerBlock = 4;
 
-// 8 consecutive elements <-> 8 floats.
-__device__ __forceinline__ void load8(const bf16_t* p, float v[8]) {
-  const uint4 u = ld_global16(p);
-  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = __uint_as_float(w[i] << 16);
-    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-  }
-}
-__device__ __forceinline__ void load8(const float* p, float v[8]) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
+// 8 floats -> 8 consecutive elements.
 __device__ __forceinline__ void store8(bf16_t* p, const float v[8]) {
   st_global16(p, make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
                             pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])));
@@ -49,42 +35,6 @@ __device__ __forceinline__ void store8(bf16_t* p, const float v[8]) {
 __device__ __forceinline__ void store8(float* p, const float v[8]) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
   *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
-}
-
-// A row's statistics, the row held in registers: lane l loads chunks
-// l, l + 64, ... of 8 elements into v (NCH = upper bound on chunks per lane,
-// D <= 512 * NCH); mean and rstd = 1 / sqrt(var + eps) in fp32, two-pass.
-template <typename T, int NCH>
-__device__ __forceinline__ void row_stats(const T* xr, int lane, int D, float eps,
-                                          float (&v)[NCH][8], float* mean_out,
-                                          float* rstd_out) {
-  const int nchunks = D >> 3;
-  float s = 0.f;
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const int idx = lane + 64 * c;
-    if (idx < nchunks) {
-      load8(xr + idx * 8, v[c]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s += v[c][e];
-    }
-  }
-  const float inv_d = 1.0f / static_cast<float>(D);
-  const float mean = wave_sum(s) * inv_d;
-  float q = 0.f;
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    if (lane + 64 * c < nchunks) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float d = v[c][e] - mean;
-        q += d * d;
-      }
-    }
-  }
-  const float var = wave_sum(q) * inv_d;
-  *mean_out = mean;
-  *rstd_out = 1.0f / sqrtf(var + eps);
 }
 
 template <typename T, int NCH>
@@ -133,10 +83,7 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void ln_stats_kernel(
   const int lane = threadIdx.x & 63;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;
-  float v[NCH][8];
-  float mean, rstd;
-  row_stats<T, NCH>(x + row * ld_in, lane, D, eps, v, &mean, &rstd);
-  if (lane == 0) stats[row] = make_float2(mean, rstd);
+  stats_of_row<T, NCH>(x, ld_in, stats, row, D, eps, lane);
 }
 
 template <typename T>
