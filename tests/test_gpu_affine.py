@@ -17,7 +17,7 @@ import vision_transformer_encoder_amd as vb
 from vision_transformer_encoder_amd.inputs import (WORKLOADS, make_affine_params,
                                                    make_block_inputs, round_to)
 
-from gpu_util import assert_close, to_dev, to_host
+from gpu_util import assert_close, to_dev, to_host, violation
 
 pytestmark = pytest.mark.gpu
 
@@ -119,6 +119,46 @@ def test_affine_block_full_size(name):
     seqs = sorted({0, w.N // 2, w.N - 1})
     assert_close(got[seqs], _oracle(inp, prm, w.H, w.eps, seqs), w.dtype,
                  f"affine {name} sequences {seqs}")
+
+
+def test_affine_block_large_key_bias():
+    # A large key bias adds q_i . b_k to every score of query i: some
+    # queries' scores all lie hundreds of log2 units below 0, others' far
+    # above (the output itself does not depend on b_k).  Keys of size ~40
+    # keep only bf16's precision of the per-key differences, so the input is
+    # ill-conditioned for any bf16 implementation: the block is held to the
+    # same block composed from the step entries, and must stay finite.
+    inp = make_block_inputs(2, 197, 256, 1024, "bf16", seed=14)
+    prm = make_affine_params(256, 1024, "bf16", seed=14)
+    prm["b_k"] = round_to(np.asarray(prm["b_k"]) * 400.0, "bf16")
+    ref = _oracle(inp, prm, 4, 1e-6)
+    # Per-query maximum score, in log2 units: both extremes occur.
+    xn = oracle.affine(oracle.layer_norm(inp["x"], 1e-6), prm["ln1_gamma"], prm["ln1_beta"])
+    q = oracle.add_bias(oracle.project(xn, inp["w_q"]), prm["b_q"])
+    k = oracle.add_bias(oracle.project(xn, inp["w_k"]), prm["b_k"])
+    qh, kh = oracle.split_heads(q, 4), oracle.split_heads(k, 4)
+    smax = (qh @ np.swapaxes(kh, -1, -2)).max(-1) / 8.0 * math.log2(math.e)
+    assert (smax < -96).any() and (smax > 96).any()
+
+    out, dev = _run(inp, prm, 4, 1e-6, "bf16")
+    got = to_host(out)
+    assert np.all(np.isfinite(got))
+    # The same block from the step entries.
+    import torch
+    dp = {k2: to_dev(v, "bf16") for k2, v in prm.items()}
+    x2 = dev["x"].view(-1, 256)
+    wt = {k2: dev[k2].t().contiguous() for k2 in WEIGHTS}
+    xn_d = vb.layernorm(x2, 1e-6, gamma=dp["ln1_gamma"], beta=dp["ln1_beta"])
+    wqkv = torch.cat([wt["w_q"], wt["w_k"], wt["w_v"]], 0)
+    qkv = vb.linear(xn_d, wqkv, vb.EPI_NONE, bias=torch.cat([dp["b_q"], dp["b_k"], dp["b_v"]]))
+    att = vb.attention(qkv, 2, 197, 4)
+    y = vb.linear(att, wt["w_o"], vb.EPI_RESIDUAL, residual=x2, bias=dp["b_o"])
+    yn = vb.layernorm(y, 1e-6, gamma=dp["ln2_gamma"], beta=dp["ln2_beta"])
+    h = vb.linear(yn, wt["w_mlp1"], vb.EPI_GELU, bias=dp["b_mlp1"])
+    steps = to_host(vb.linear(h, wt["w_mlp2"], vb.EPI_RESIDUAL, residual=y, bias=dp["b_mlp2"]))
+    v_block, _ = violation(got, ref)
+    v_steps, _ = violation(steps.reshape(got.shape), ref)
+    assert v_block <= v_steps * 1.1 + 1e-3, (v_block, v_steps)
 
 
 def test_affine_block_split_k_tail_rows():

@@ -16,7 +16,7 @@ import oracle
 import vision_transformer_encoder_amd as vb
 from vision_transformer_encoder_amd.inputs import WORKLOADS, make_block_inputs, round_to
 
-from gpu_util import TOL, assert_close, to_dev, to_host
+from gpu_util import TOL, assert_close, to_dev, to_host, violation
 
 pytestmark = pytest.mark.gpu
 
@@ -251,6 +251,46 @@ def test_block_split_k_tail_rows():
     assert np.all(np.isfinite(got))
     seqs = [0, 83, 84]
     assert_close(got[seqs], _oracle(inp, H, 1e-6, seqs), "bf16", f"split-K tail {seqs}")
+
+
+def _block_by_steps(dev, H, eps):
+    """The plain block composed from the step entries (LayerNorms written
+    out rather than folded into the products)."""
+    import torch
+    D = dev["x"].shape[-1]
+    x2 = dev["x"].view(-1, D)
+    wt = {k: dev[k].t().contiguous() for k in ("w_q", "w_k", "w_v", "w_o", "w_mlp1", "w_mlp2")}
+    qkv = vb.qkv_projection(vb.layernorm(x2, eps), torch.cat([wt["w_q"], wt["w_k"], wt["w_v"]], 0))
+    N, T = dev["x"].shape[0], dev["x"].shape[1]
+    y = vb.linear(vb.attention(qkv, N, T, H), wt["w_o"], vb.EPI_RESIDUAL, residual=x2)
+    h = vb.linear(vb.layernorm(y, eps), wt["w_mlp1"], vb.EPI_GELU)
+    return vb.linear(h, wt["w_mlp2"], vb.EPI_RESIDUAL, residual=y).view(dev["x"].shape)
+
+
+@pytest.mark.parametrize("gain", [6.0, 20.0])
+def test_block_large_attention_scores(gain):
+    # w_q and w_k scaled up: scores reach hundreds in log2 units, so the
+    # attention's reference maximum moves far (and its rescaling of the
+    # running sums is exercised).  Scores that large keep only bf16's
+    # precision of their differences, so the input is ill-conditioned for
+    # any bf16 implementation (the plain bar fails from gain 3 on: 0.045):
+    # the block is held to the same block composed from the step entries
+    # (LayerNorms written out instead of folded), and must stay finite.
+    inp = make_block_inputs(2, 197, 256, 1024, "bf16", seed=13)
+    for k in ("w_q", "w_k"):
+        inp[k] = round_to(inp[k] * gain, "bf16")
+    xn = oracle.layer_norm(inp["x"], 1e-6)
+    qh = oracle.split_heads(oracle.project(xn, inp["w_q"]), 4)
+    kh = oracle.split_heads(oracle.project(xn, inp["w_k"]), 4)
+    smax = (qh @ np.swapaxes(kh, -1, -2)).max(-1) / 8.0 * math.log2(math.e)
+    assert (smax > 96).any()  # scores in the hundreds
+    out, dev = _run_block(inp, 4, 1e-6, "bf16")
+    got = to_host(out)
+    assert np.all(np.isfinite(got))
+    ref = _oracle(inp, 4, 1e-6)
+    v_block, _ = violation(got, ref)
+    v_steps, _ = violation(to_host(_block_by_steps(dev, 4, 1e-6)), ref)
+    assert v_block <= v_steps * 1.1 + 1e-3, (v_block, v_steps)
 
 
 def test_tiny_workload_seed0():
