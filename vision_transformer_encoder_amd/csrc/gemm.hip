@@ -589,6 +589,11 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
 using BigTile = Cfg<256, 256, 2, 4, 64, 2, 3>;
 // 4 waves, 64x64 per wave, 80 KB LDS: 2 workgroups per CU.
 using SmallTile = Cfg<128, 128, 2, 2, 64, 2, 3>;
+// The small tile with four stages of both operands (128 KB LDS, one workgroup
+// per CU): three k-slices in flight instead of two (activations) and one
+// (weights).  For a last partial round of tiles, where each workgroup runs
+// alone on its CU and its time is the latency of its k-slices.
+using DeepTile = Cfg<128, 128, 2, 2, 64, 4, 4>;
 
 // Split-K finish: C[m, n] = bf16(((sum_s P[s, m, n]) + b[n]) + R[m, n]), the
 // partials summed in order in fp32 (the same order of additions as the
@@ -745,28 +750,33 @@ constexpr int kMaxSplit = 8;       // k-ranges of a split-K tail
 constexpr int kMinSplitSlices = 4;  // k-slices (of 64) per range at least
 
 // The last rows of a product, left over by the big tile's whole rounds.  On
-// the small tile they are few tiles; when K is long each runs for a long time
-// while most CUs idle.  A residual product (the one kind whose result needs
-// no nonlinearity after the sum) then splits K into S ranges, as many as
-// fill the resident small-tile slots: the ranges' unrounded fp32 sums go to
-// the caller's scratch memory and a second kernel adds them in order, with
-// the bias and the residual, and rounds once.  Otherwise one small-tile
-// launch.
+// the 128x128 tile they are few tiles, each alone on its CU, so they run on
+// the four-stage variant of that tile (DeepTile) when they fit in one round
+// of it (measured: 18.2 -> 17.5 us for the Q|K|V tail at ViT-L/16, 30.0 ->
+// 27.3 us for MLP2's split tail and its sum); otherwise on the two-workgroups-
+// per-CU small tile.  When K is long each tile runs for a long time while most
+// CUs idle.  A residual product (the one kind whose result needs no
+// nonlinearity after the sum) then splits K into S ranges, as many as fill the
+// resident deep-tile slots: the ranges' unrounded fp32 sums go to the caller's
+// scratch memory and a second kernel adds them in order, with the bias and the
+// residual, and rounds once.
 hipError_t launch_tail(const GemmProblem& p, hipStream_t s) {
   using Small = SmallTile;
+  static_assert(DeepTile::BM == Small::BM && DeepTile::BN == Small::BN, "same tile shape");
   const int64_t tiles = ((p.M + Small::BM - 1) / Small::BM) * ((p.N + Small::BN - 1) / Small::BN);
   const int64_t ka = p.K / Small::BK;
+  // One workgroup per CU whatever the epilogue (the LDS decides).
+  const int64_t deep_slots = resident_workgroups<DeepTile, kEpiPartial>();
   int64_t S = 0;
   if (p.epi == VITBLK_EPI_RESIDUAL && p.scratch != nullptr && p.bias[1] == nullptr &&
       p.bias[2] == nullptr && (p.bias[0] == nullptr || p.bias_seg >= p.N) &&
       p.ldc % 8 == 0 && (reinterpret_cast<uintptr_t>(p.scratch) & 15u) == 0) {
-    const int64_t slots = resident_workgroups<Small, kEpiPartial>();
-    S = tiles > 0 ? slots / tiles : 0;
+    S = tiles > 0 ? deep_slots / tiles : 0;
     if (S > kMaxSplit) S = kMaxSplit;
     if (S > ka / kMinSplitSlices) S = ka / kMinSplitSlices;
     while (S > 1 && S * p.M * p.N > p.scratch_floats) --S;
   }
-  if (S < 2) return launch_cfg<Small>(p, s);
+  if (S < 2) return tiles <= deep_slots ? launch_cfg<DeepTile>(p, s) : launch_cfg<Small>(p, s);
   GemmProblem q = p;
   q.epi = kEpiPartial;
   q.ksplit = static_cast<int>(S);
@@ -774,7 +784,7 @@ hipError_t launch_tail(const GemmProblem& p, hipStream_t s) {
   q.ldc = p.N;
   q.R = nullptr;
   q.bias[0] = q.bias[1] = q.bias[2] = nullptr;
-  hipError_t e = launch_epi<Small, kEpiPartial, false>(q, s);
+  hipError_t e = launch_epi<DeepTile, kEpiPartial, false>(q, s);
   if (e != hipSuccess) return e;
   const int64_t threads = p.M * (p.N / 8);
   const int64_t blocks = (threads + 255) / 256;
@@ -795,8 +805,8 @@ hipError_t launch_tail(const GemmProblem& p, hipStream_t s) {
 // Wave quantisation: with G resident big-tile workgroups, the last partial
 // round of tiles would run a handful of tiles for a full round's time.  The
 // big tile therefore covers the largest block of M-tiles that makes a whole
-// number of rounds, and the remaining rows run as a second launch with the
-// quarter-size tile, which finishes in a fraction of a round.
+// number of rounds, and the remaining rows run as a second launch with a
+// quarter-size tile, which finishes in a fraction of a round (launch_tail).
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t s) {
   if (reads_r(p) && p.R == nullptr) return hipErrorInvalidValue;  // never launch on a null R
   if (p.epi == kEpiGeluDual && p.C2 == nullptr) return hipErrorInvalidValue;
