@@ -122,7 +122,9 @@ size_t vitblk_workspace_bytes(int64_t N, int64_t T, int64_t D, int64_t F, int64_
  * The column sums serve the products that fold a LayerNorm in (see
  * vitblk_linear_normed()).  vitblk_packed_weights_bytes() returns the size
  * (0 for invalid arguments; host only).  vitblk_pack_weights() writes it on
- * `stream` (two launches: the transposes, then the sums); the buffer must
+ * `stream` (bf16 with every side a multiple of 8 and 16-byte aligned
+ * weights: one launch, the sums taken from the source weights; otherwise two:
+ * the transposes, then the packed copies' row sums); the buffer must
  * not overlap a weight.  Callers that run many blocks with the same weights
  * pack once and call vitblk_forward_packed().
  */
@@ -152,7 +154,9 @@ int vitblk_pack_weights(const void* w_q, const void* w_k, const void* w_v, const
  * MLP1 + GELU, MLP2 + residual.  In bf16 each LN (no gain or shift) is
  * folded into the product that follows it: only the rows' mean and
  * 1/sqrt(var + eps) are computed, and the product's epilogue forms
- * rstd * (x @ W - mean * colsum(W)) = LN(x) @ W (see vitblk_linear_normed()).
+ * rstd * (x @ W - mean * colsum(W)) = LN(x) @ W (see vitblk_linear_normed());
+ * the first LN's statistics are computed in the weight-packing launch when
+ * that launch is a single one (see vitblk_pack_weights()).
  * When the last rows of a residual product would leave most of the device
  * idle, their K range is split and a second kernel adds the partial sums
  * (fp32, in the workspace) to the residual.

@@ -215,6 +215,8 @@ SMALL_BLOCKS = [
     (2, 257, 320, 4, 1280, 1e-6, "bf16"),  # d_h 80
     (2, 65, 128, 2, 512, 1e-5, "bf16"),
     (2, 9, 24, 3, 40, 1e-6, "bf16"),       # shapes only the generic kernels take
+    (2, 7, 20, 4, 36, 1e-6, "bf16"),       # D not a multiple of 8: weights and LN1 statistics
+                                           # in separate launches
     (1, 3, 8, 8, 8, 1e-6, "bf16"),         # H = D (head width 1)
 ]
 

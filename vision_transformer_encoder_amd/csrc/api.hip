@@ -41,9 +41,12 @@ GemmProblem linear_problem(const void* a, const void* w_t, void* c, const void* 
   return p;
 }
 
+// The packed weights and, with stats non-null, a set of row statistics
+// (launch_row_stats's job) in the same launch when the layouts allow.
 int pack_weights(const void* w_q, const void* w_k, const void* w_v, const void* w_o,
                  const void* w_mlp1, const void* w_mlp2, void* packed, int64_t D, int64_t F,
-                 int dtype, const PackedPlan& pl, hipStream_t s) {
+                 int dtype, const PackedPlan& pl, hipStream_t s,
+                 const StatsJob* stats = nullptr) {
   char* base = static_cast<char*>(packed);
   const size_t es = elem_size(dtype);
   char* qkv = base + pl.off_qkv;
@@ -55,22 +58,41 @@ int pack_weights(const void* w_q, const void* w_k, const void* w_v, const void* 
       {w_mlp1, D, F, base + pl.off_1, D},
       {w_mlp2, F, D, base + pl.off_2, F},
   };
+  // Column sums of [w_q | w_k | w_v] and of w_mlp1 for the products that
+  // fold in the LayerNorm: from the source weights in the fused launch, else
+  // as the row sums of the packed copies.
+  float* cs_qkv = reinterpret_cast<float*>(base + pl.off_cs_qkv);
+  const ColSumJob cols[4] = {
+      {w_q, D, D, cs_qkv},
+      {w_k, D, D, cs_qkv + D},
+      {w_v, D, D, cs_qkv + 2 * D},
+      {w_mlp1, D, F, reinterpret_cast<float*>(base + pl.off_cs_1)},
+  };
+  const hipError_t fused = launch_prologue(jobs, 6, cols, 4, stats, dtype, s);
+  if (fused != hipErrorNotSupported) {
+    VITBLK_LAUNCH(fused);
+    return VITBLK_OK;
+  }
   VITBLK_LAUNCH(launch_pack(jobs, 6, dtype, s));
-  // Column sums of [w_q | w_k | w_v] and of w_mlp1 (row sums of the packed
-  // copies) for the products that fold in the LayerNorm.
   const RowSumJob sums[2] = {
       {qkv, 3 * D, D, reinterpret_cast<float*>(base + pl.off_cs_qkv)},
       {base + pl.off_1, F, D, reinterpret_cast<float*>(base + pl.off_cs_1)},
   };
   VITBLK_LAUNCH(launch_row_sums(sums, 2, dtype, s));
+  if (stats != nullptr)
+    VITBLK_LAUNCH(launch_row_stats(stats->x, stats->ld, stats->stats, stats->rows, stats->D,
+                                   stats->eps, dtype, s));
   return VITBLK_OK;
 }
 
 // The seven steps of the block on packed (out-major) weights.  prm: the
 // affine variant's optional gains, shifts and biases (null: none).
+// stats1_ready: the first LayerNorm's row statistics are already in place
+// (written with the packed weights; only where the block folds that
+// LayerNorm).
 int run_block(const void* x, const void* packed, const vitblk_affine_params* prm, void* out,
               int64_t N, int64_t T, int64_t D, int64_t F, int64_t H, double eps, int dtype,
-              char* act, const WorkspacePlan& pl, hipStream_t s) {
+              char* act, const WorkspacePlan& pl, hipStream_t s, bool stats1_ready = false) {
   const vitblk_affine_params none{};
   const vitblk_affine_params& q = prm != nullptr ? *prm : none;
   const int64_t M = N * T;
@@ -94,7 +116,7 @@ int run_block(const void* x, const void* packed, const vitblk_affine_params* prm
   GemmProblem pq = linear_problem(a, pk + pl.packed.off_qkv, big, nullptr, M, D, 3 * D,
                                   VITBLK_EPI_NONE, dtype, q.b_q, q.b_k, q.b_v, D);
   if (fold1) {
-    VITBLK_LAUNCH(launch_row_stats(x, D, stats, M, D, feps, dtype, s));
+    if (!stats1_ready) VITBLK_LAUNCH(launch_row_stats(x, D, stats, M, D, feps, dtype, s));
     pq.A = x;
     pq.row_stats = stats;
     pq.col_sums = reinterpret_cast<const float*>(pk + pl.packed.off_cs_qkv);
@@ -433,9 +455,17 @@ int vitblk_forward(const void* x, const void* w_q, const void* w_k, const void* 
   if (st != VITBLK_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  st = pack_weights(w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, ws, D, F, dtype, pl.packed, s);
+  // The block folds its first LayerNorm (bf16): its statistics are computed
+  // in the weights' launch, where run_block reads them (region act).
+  const bool fold1 = dtype == VITBLK_BF16;
+  const StatsJob stats1{x, D, N * T, D,
+                        reinterpret_cast<float*>(ws + pl.act_base + pl.off_act),
+                        static_cast<float>(eps)};
+  st = pack_weights(w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, ws, D, F, dtype, pl.packed, s,
+                    fold1 ? &stats1 : nullptr);
   if (st != VITBLK_OK) return st;
-  return run_block(x, ws, nullptr, out, N, T, D, F, H, eps, dtype, ws + pl.act_base, pl, s);
+  return run_block(x, ws, nullptr, out, N, T, D, F, H, eps, dtype, ws + pl.act_base, pl, s,
+                   fold1);
 }
 
 int vitblk_forward_affine(const void* x, const void* w_q, const void* w_k, const void* w_v,

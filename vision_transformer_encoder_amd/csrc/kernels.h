@@ -119,6 +119,27 @@ hipError_t launch_patch_embed(const PatchEmbedArgs& p, hipStream_t stream);
 // Transpose up to 6 weights in one launch.
 hipError_t launch_pack(const PackJob* jobs, int njobs, int dtype, hipStream_t stream);
 
+// sums[c] = sum_r src[r * cols + c] in fp32, in a fixed order: the column sums
+// of an (in, out) weight.
+struct ColSumJob {
+  const void* src;
+  int64_t rows, cols;
+  float* sums;
+};
+// Row statistics to compute alongside (launch_row_stats's job).
+struct StatsJob {
+  const void* x;
+  int64_t ld, rows, D;
+  float* stats;
+  float eps;
+};
+// One launch for the work at the start of a block call: up to 6 transposes,
+// up to 4 column sums and optionally one set of row statistics (null: none),
+// all bf16.  Returns hipErrorNotSupported, having launched nothing, when a job
+// does not meet the fused kernel's layout (then launch them one by one).
+hipError_t launch_prologue(const PackJob* jobs, int njobs, const ColSumJob* cs, int ncs,
+                           const StatsJob* stats, int dtype, hipStream_t stream);
+
 // O[n*T + t, h*dh + c] = sum_j softmax_j(Q_h K_h^T / sqrt(dh))[t, j] V[n*T + j, h*dh + c]
 // with Q, K, V row strides ld (elements) and O row stride ldo.
 hipError_t launch_attention(const void* q, const void* k, const void* v, int64_t ld,
