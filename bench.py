@@ -333,6 +333,9 @@ def bench_backward(a, w, torch, vb):
         per[name] = {"ms": round(kms, 5), "bound": bound,
                      ("tflops" if bound == "mfma" else "gbs"):
                      round(rate / (1e12 if bound == "mfma" else 1e9), 2)}
+        if name == "attention":  # both rates: its bound moves with T
+            per[name]["tflops"] = round(att_flops / (kms * 1e-3) / 1e12, 2)
+            per[name]["gbs"] = round(att_bytes / (kms * 1e-3) / 1e9, 2)
     dom = max(per, key=lambda k: per[k]["ms"])
     fn, bound, work = kern[dom]
     dms = per[dom]["ms"]
@@ -508,9 +511,15 @@ def main():
             "qkv_gemm": (lambda: vb.linear_normed(x2, wqkv_t, cs_qkv, st1, vb.EPI_NONE, out=qkv),
                          "mfma", 2 * M * D * 3 * D),
         })
+    # Attention's bound depends on T: 4 N T^2 D FLOP against 4 M D elements
+    # (Q, K, V read, O written), an intensity of about T / es FLOP per byte,
+    # below the ridge (peak FLOP/s / peak bytes/s) at ViT sequence lengths.
+    att_flops, att_bytes = 4 * w.N * w.T * w.T * D, 4 * M * D * es
+    att_bound = ("hbm" if att_flops / att_bytes < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+                 else "mfma")
     kern.update({
-        "attention": (lambda: vb.attention(qkv, w.N, w.T, w.H, out=att), "mfma",
-                      4 * w.N * w.T * w.T * D),
+        "attention": (lambda: vb.attention(qkv, w.N, w.T, w.H, out=att), att_bound,
+                      att_bytes if att_bound == "hbm" else att_flops),
         "oproj_residual": (lambda: vb.linear(att, wo_t, vb.EPI_RESIDUAL, residual=x2,
                                              bias=gq("b_o"), out=y), "mfma", 2 * M * D * D),
     })
@@ -551,6 +560,9 @@ def main():
         per[name] = {"ms": round(kms, 5), "bound": bound,
                      ("tflops" if bound == "mfma" else "gbs"):
                      round(rate / (1e12 if bound == "mfma" else 1e9), 2)}
+        if name == "attention":  # both rates: its bound moves with T
+            per[name]["tflops"] = round(att_flops / (kms * 1e-3) / 1e12, 2)
+            per[name]["gbs"] = round(att_bytes / (kms * 1e-3) / 1e9, 2)
     dom = max(per, key=lambda k: per[k]["ms"])
     fn, bound, work = kern[dom]
     dms = per[dom]["ms"]
