@@ -160,7 +160,7 @@ def test_attention(dtype, N, T, D, H):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-@pytest.mark.parametrize("D,F", [(256, 1024), (24, 40), (768, 3072), (20, 36)])
+@pytest.mark.parametrize("D,F", [(256, 1024), (24, 40), (768, 3072), (20, 36), (320, 1280)])
 def test_pack_weights_is_an_exact_transpose(dtype, D, F):
     import torch
     inp = make_block_inputs(1, 1, D, F, dtype, seed=11)
