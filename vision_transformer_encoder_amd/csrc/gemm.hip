@@ -157,6 +157,9 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
   const int nsplit = kSplit ? p.ksplit : 1;
   int KT = KA;
   int ks = 0;  // k-range of the current tile
+  // Odd rounds walk the k-slices backwards: a tile then starts on the slices
+  // its XCD's L2 touched last (the weight panels repeat from round to round).
+  bool krev = false;
   const int total = mt * nt * nsplit, grid = gridDim.x;
 
   // Tile-dependent load state: buffer resources at the tiles' first rows and
@@ -168,6 +171,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
   auto prepare = [&](int t) {
     int tm, tn;
     tile_of(t, grid, total, mt * nsplit, nt, &tm, &tn);
+    krev = ((t / grid) & 1) != 0;
     int64_t kbyte = 0;
     if (kSplit) {
       // The k-ranges are laid out as further M-tiles of the tile order.
@@ -197,13 +201,13 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
     }
   };
   auto issue_a = [&](int kt, int st) {
-    const int kb = kt * C::BK * 2;  // byte offset of the k-slice
+    const int kb = (krev ? KT - 1 - kt : kt) * C::BK * 2;  // byte offset of the k-slice
 #pragma unroll
     for (int i = 0; i < C::A_LOADS; ++i)
       load_lds16(a_rs, a_lds + st * C::A_STAGE + (i * C::NT + wave * 64) * 16, a_off[i], kb);
   };
   auto issue_b = [&](int kt, int st) {
-    const int kb = kt * C::BK * 2;
+    const int kb = (krev ? KT - 1 - kt : kt) * C::BK * 2;
 #pragma unroll
     for (int i = 0; i < C::B_LOADS; ++i)
       load_lds16(b_rs, b_lds + st * C::B_STAGE + (i * C::NT + wave * 64) * 16, b_off[i], kb);
