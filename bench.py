@@ -465,6 +465,22 @@ def main():
     t_wall = time.perf_counter() - t_wall
     ms = e0.elapsed_time(e1) / a.steps
     got = out.to("cpu", torch.float64).numpy()
+    cls_only_ms = None
+    if encoder:
+        # The same stack asked for the class tokens only: its last block then
+        # computes just their rows.
+        def cls_step():
+            vb.encoder_forward(g["x"], enc_packed, w.F, w.H, w.eps, params=enc_params,
+                               final_gamma=fg, final_beta=fb, want_tokens=False, cls_out=cls,
+                               workspace=ws_enc)
+        cls_step()
+        torch.cuda.synchronize()
+        e0.record(s)
+        for _ in range(a.steps):
+            cls_step()
+        e1.record(s)
+        torch.cuda.synchronize()
+        cls_only_ms = e0.elapsed_time(e1) / a.steps
 
     # Each step's kernel alone, on the same shapes (separate buffers per step).
     M, D, F = w.M, w.D, w.F
@@ -606,6 +622,8 @@ def main():
         "kernels": per,
         "roofline": roof,
     }
+    if cls_only_ms is not None:
+        res["cls_only_ms_per_step"] = round(cls_only_ms, 5)
     if a.cpu_seconds > 0:
         import oracle
         if encoder:

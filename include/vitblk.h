@@ -280,6 +280,15 @@ int vitblk_patch_embed(const void* images, const void* w_patch, const void* b_pa
  *           activations plus two [N*T, D] token buffers the blocks alternate
  *           between (x itself is never written)
  *
+ * With out NULL only the class tokens leave the stack (nipunbatra.github.io
+ * "Vision Transformer - optional labs and references", page 55 "Follow the
+ * CLS row from scores to weights": a CLS-only readout needs just the class
+ * query's row from the last block, with all its keys and values): the last block
+ * then computes every token's Q, K and V but attention for the first 32
+ * queries of each sequence only, and its output projection, second
+ * LayerNorm and MLP for the N class-token rows.  The values are those of the
+ * full stack up to rounding (its products' K sums may run in another order).
+ *
  * 7 L + 1 or 2 kernels on `stream`.
  */
 size_t vitblk_encoder_workspace_bytes(int64_t N, int64_t T, int64_t D, int64_t F, int64_t H,

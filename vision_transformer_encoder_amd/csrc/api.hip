@@ -89,10 +89,15 @@ int pack_weights(const void* w_q, const void* w_k, const void* w_v, const void* 
 // affine variant's optional gains, shifts and biases (null: none).
 // stats1_ready: the first LayerNorm's row statistics are already in place
 // (written with the packed weights; only where the block folds that
-// LayerNorm).
+// LayerNorm).  cls_only: only each sequence's first token (the class token)
+// leaves the block; out is then [N, D].  Every token's K and V still enter
+// attention, but only the first query tile is computed, and the output
+// projection, LN2 and the MLP run on the N class-token rows (row stride T*D
+// into the attention output and x).
 int run_block(const void* x, const void* packed, const vitblk_affine_params* prm, void* out,
               int64_t N, int64_t T, int64_t D, int64_t F, int64_t H, double eps, int dtype,
-              char* act, const WorkspacePlan& pl, hipStream_t s, bool stats1_ready = false) {
+              char* act, const WorkspacePlan& pl, hipStream_t s, bool stats1_ready = false,
+              bool cls_only = false) {
   const vitblk_affine_params none{};
   const vitblk_affine_params& q = prm != nullptr ? *prm : none;
   const int64_t M = N * T;
@@ -125,29 +130,35 @@ int run_block(const void* x, const void* packed, const vitblk_affine_params* prm
   }
   VITBLK_LAUNCH(launch_gemm(pq, s));
   // att = concat_h softmax(Q_h K_h^T / sqrt(dh)) V_h   (overwrites xn)
-  VITBLK_LAUNCH(launch_attention(big, big + D * es, big + 2 * D * es, 3 * D, a, D, N, T, H,
-                                 D / H, dtype, s));
+  if (cls_only)
+    VITBLK_LAUNCH(launch_attention_first_queries(big, big + D * es, big + 2 * D * es, 3 * D, a,
+                                                 D, N, T, H, D / H, dtype, s));
+  else
+    VITBLK_LAUNCH(launch_attention(big, big + D * es, big + 2 * D * es, 3 * D, a, D, N, T, H,
+                                   D / H, dtype, s));
   // y = x + att @ w_o + b_o   (qkv's region is free again: split-K scratch)
-  GemmProblem po = linear_problem(a, pk + pl.packed.off_o, y, x, M, D, D, VITBLK_EPI_RESIDUAL,
+  const int64_t Mo = cls_only ? N : M;  // rows from here on
+  GemmProblem po = linear_problem(a, pk + pl.packed.off_o, y, x, Mo, D, D, VITBLK_EPI_RESIDUAL,
                                   dtype, q.b_o);
+  if (cls_only) po.lda = po.ldr = T * D;  // the class-token rows of att and x
   po.scratch = reinterpret_cast<float*>(big);
   po.scratch_floats = static_cast<int64_t>(pl.off_act - pl.off_big) / 4;
   VITBLK_LAUNCH(launch_gemm(po, s));
   // LN2: yn = gamma_2 LN(y) + beta_2 (overwrites att), then
   // hidden = GELU(yn @ w_mlp1 + b_mlp1)   (overwrites qkv)
-  GemmProblem p1 = linear_problem(a, pk + pl.packed.off_1, big, nullptr, M, D, F,
+  GemmProblem p1 = linear_problem(a, pk + pl.packed.off_1, big, nullptr, Mo, D, F,
                                   VITBLK_EPI_GELU, dtype, q.b_mlp1);
   if (fold2) {
-    VITBLK_LAUNCH(launch_row_stats(y, D, stats, M, D, feps, dtype, s));
+    VITBLK_LAUNCH(launch_row_stats(y, D, stats, Mo, D, feps, dtype, s));
     p1.A = y;
     p1.row_stats = stats;
     p1.col_sums = reinterpret_cast<const float*>(pk + pl.packed.off_cs_1);
   } else {
-    VITBLK_LAUNCH(launch_layernorm(y, D, q.ln2_gamma, q.ln2_beta, a, M, D, feps, dtype, s));
+    VITBLK_LAUNCH(launch_layernorm(y, D, q.ln2_gamma, q.ln2_beta, a, Mo, D, feps, dtype, s));
   }
   VITBLK_LAUNCH(launch_gemm(p1, s));
   // out = y + hidden @ w_mlp2 + b_mlp2   (yn's region is free again: split-K scratch)
-  GemmProblem p2 = linear_problem(big, pk + pl.packed.off_2, out, y, M, F, D,
+  GemmProblem p2 = linear_problem(big, pk + pl.packed.off_2, out, y, Mo, F, D,
                                   VITBLK_EPI_RESIDUAL, dtype, q.b_mlp2);
   p2.scratch = reinterpret_cast<float*>(a);
   p2.scratch_floats = static_cast<int64_t>(pl.off_y - pl.off_act) / 4;
@@ -163,18 +174,22 @@ int run_encoder(const void* x, const void* const* packed, const vitblk_affine_pa
                 const EncoderPlan& pl, hipStream_t s) {
   char* tok[2] = {ws + pl.off_tok0, ws + pl.off_tok1};
   const void* cur = x;
+  // Only the class tokens leave the stack: the last block computes just their
+  // rows (every token's K and V still enter its attention) and writes [N, D].
+  const bool cls_last = out == nullptr && cls != nullptr && L > 0;
   for (int64_t l = 0; l < L; ++l) {
     char* dst = tok[l & 1];
     const int st = run_block(cur, packed[l], params != nullptr ? &params[l] : nullptr, dst, N, T,
-                             D, F, H, eps, dtype, ws + pl.block.act_base, pl.block, s);
+                             D, F, H, eps, dtype, ws + pl.block.act_base, pl.block, s, false,
+                             cls_last && l == L - 1);
     if (st != VITBLK_OK) return st;
     cur = dst;
   }
   const float feps = static_cast<float>(eps);
   if (out != nullptr)
     VITBLK_LAUNCH(launch_layernorm(cur, D, fg, fb, out, N * T, D, feps, dtype, s));
-  if (cls != nullptr)  // rows n*T: stride T*D
-    VITBLK_LAUNCH(launch_layernorm(cur, T * D, fg, fb, cls, N, D, feps, dtype, s));
+  if (cls != nullptr)  // rows n*T (stride T*D), or the last block's [N, D]
+    VITBLK_LAUNCH(launch_layernorm(cur, cls_last ? D : T * D, fg, fb, cls, N, D, feps, dtype, s));
   return VITBLK_OK;
 }
 

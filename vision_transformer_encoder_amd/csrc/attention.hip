@@ -127,9 +127,11 @@ __global__ __launch_bounds__(64 * W, (DH <= 64 ? 4 : 2)) void attn_stream_kernel
   if (active) tile.store(O, ldo, seq0, hoff, T, qt * 32, lane);
 }
 
+// max_qt > 0: only the first max_qt query tiles of each sequence (all keys).
 template <int DH, int W = kStreamWaves>
 hipError_t launch_stream(const void* q, const void* k, const void* v, int64_t ld, void* o,
-                         int64_t ldo, int64_t N, int64_t T, int64_t H, hipStream_t s) {
+                         int64_t ldo, int64_t N, int64_t T, int64_t H, hipStream_t s,
+                         int64_t max_qt = 0) {
   using C = attn::Cfg<DH>;
   constexpr size_t bytes = 2 * 64 * C::ROW;
   static bool attr_set = false;
@@ -142,7 +144,8 @@ hipError_t launch_stream(const void* q, const void* k, const void* v, int64_t ld
     }
     attr_set = true;
   }
-  const int64_t nqt = (T + 31) / 32;
+  int64_t nqt = (T + 31) / 32;
+  if (max_qt > 0 && nqt > max_qt) nqt = max_qt;  // the kernel then skips waves past tpb
   const int64_t nqb = (nqt + W - 1) / W;
   const int64_t tpb = (nqt + nqb - 1) / nqb;  // query tiles per workgroup, balanced
   const int64_t blocks = N * H * nqb;
@@ -160,13 +163,13 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u
 
 hipError_t launch_stream_dh(const void* q, const void* k, const void* v, int64_t ld, void* o,
                             int64_t ldo, int64_t N, int64_t T, int64_t H, int64_t dh,
-                            hipStream_t s) {
+                            hipStream_t s, int64_t max_qt = 0) {
   switch (dh) {
-    case 32: return launch_stream<32>(q, k, v, ld, o, ldo, N, T, H, s);
-    case 64: return launch_stream<64>(q, k, v, ld, o, ldo, N, T, H, s);
-    case 80: return launch_stream<80>(q, k, v, ld, o, ldo, N, T, H, s);
-    case 96: return launch_stream<96>(q, k, v, ld, o, ldo, N, T, H, s);
-    case 128: return launch_stream<128>(q, k, v, ld, o, ldo, N, T, H, s);
+    case 32: return launch_stream<32>(q, k, v, ld, o, ldo, N, T, H, s, max_qt);
+    case 64: return launch_stream<64>(q, k, v, ld, o, ldo, N, T, H, s, max_qt);
+    case 80: return launch_stream<80>(q, k, v, ld, o, ldo, N, T, H, s, max_qt);
+    case 96: return launch_stream<96>(q, k, v, ld, o, ldo, N, T, H, s, max_qt);
+    case 128: return launch_stream<128>(q, k, v, ld, o, ldo, N, T, H, s, max_qt);
     default: return hipErrorNotSupported;
   }
 }
@@ -192,6 +195,18 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, int64_t
     if (r != hipErrorNotSupported) return r;
   }
   return launch_attention_generic(q, k, v, ld, o, ldo, N, T, H, dh, dtype, s);
+}
+
+hipError_t launch_attention_first_queries(const void* q, const void* k, const void* v,
+                                          int64_t ld, void* o, int64_t ldo, int64_t N, int64_t T,
+                                          int64_t H, int64_t dh, int dtype, hipStream_t s) {
+  const bool fast = dtype == VITBLK_BF16 && ld % 8 == 0 && ldo % 8 == 0 && aligned16(q) &&
+                    aligned16(k) && aligned16(v) && aligned16(o);
+  if (fast && dh <= 64) {
+    const hipError_t r = launch_stream_dh(q, k, v, ld, o, ldo, N, T, H, dh, s, 1);
+    if (r != hipErrorNotSupported) return r;
+  }
+  return launch_attention(q, k, v, ld, o, ldo, N, T, H, dh, dtype, s);
 }
 
 }  // namespace vitblk

@@ -145,6 +145,12 @@ hipError_t launch_prologue(const PackJob* jobs, int njobs, const ColSumJob* cs, 
 hipError_t launch_attention(const void* q, const void* k, const void* v, int64_t ld,
                             void* o, int64_t ldo, int64_t N, int64_t T, int64_t H,
                             int64_t dh, int dtype, hipStream_t stream);
+// The same for at least the first 32 queries of each sequence (every key): O
+// rows n*T + t for t < min(T, 32) are written, others may not be.  For a
+// readout that needs only the class token (query 0).
+hipError_t launch_attention_first_queries(const void* q, const void* k, const void* v,
+                                          int64_t ld, void* o, int64_t ldo, int64_t N, int64_t T,
+                                          int64_t H, int64_t dh, int dtype, hipStream_t stream);
 
 // Whole-sequence-in-LDS variant (bf16); hipErrorNotSupported when it does not
 // apply (sequence too long for LDS, head width without an instantiation).
