@@ -100,6 +100,32 @@ def parse():
     return ap.parse_args()
 
 
+def time_steps(step, steps, torch):
+    """Run step() `steps` times between HIP events recorded on the launch stream
+    (one before the first step and one after each): returns (mean ms per step
+    over the whole run, per-step ms list, host wall seconds).  The events sit
+    between the steps, so the mean is the plain end-to-end time / steps."""
+    s = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ev[0].record(s)
+    for i in range(steps):
+        step()
+        ev[i + 1].record(s)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return ev[0].elapsed_time(ev[steps]) / steps, per, t_wall
+
+
+def step_stats(per):
+    """Median, minimum and maximum of the per-step times (ms)."""
+    a = np.asarray(per, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 5), "min": round(float(a.min()), 5),
+            "max": round(float(a.max()), 5)}
+
+
 def time_launches(fn, reps, torch):
     """Average duration of fn() (one kernel launch) over reps, HIP events on the launch stream."""
     s = torch.cuda.current_stream()
@@ -177,17 +203,7 @@ def bench_embed(a, w, torch, vb):
 
     for _ in range(a.warmup):
         step()
-    torch.cuda.synchronize()
-    s = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_wall = time.perf_counter()
-    e0.record(s)
-    for _ in range(a.steps):
-        step()
-    e1.record(s)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms = e0.elapsed_time(e1) / a.steps
+    ms, per_step, t_wall = time_steps(step, a.steps, torch)
     got = out.to("cpu", torch.float64).numpy()
     # The embedding GEMM alone, on the same shapes: the dominant kernel.
     Kp = (K + 63) // 64 * 64
@@ -208,6 +224,7 @@ def bench_embed(a, w, torch, vb):
         "data": "synthetic (seeded N(0,1) pixels, N(0,1/fan_in) W_patch)",
         "config": {"workload": w.name, "images": B, "image_side": side, "channels": C,
                    "patch": P, "D": D, "tokens_per_image": w.T, "variant": "embed"},
+        "step_ms": step_stats(per_step),
         "wall_s_timed": round(t_wall, 3),
         "io_gbs": round(io_bytes / (ms * 1e-3) / 1e9, 1),
         "kernels": {"embed_gemm": {"ms": round(gms, 5), "bound": "mfma",
@@ -256,17 +273,7 @@ def bench_backward(a, w, torch, vb):
 
     for _ in range(a.warmup):
         step()
-    torch.cuda.synchronize()
-    s = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_wall = time.perf_counter()
-    e0.record(s)
-    for _ in range(a.steps):
-        step()
-    e1.record(s)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms = e0.elapsed_time(e1) / a.steps
+    ms, per_step, t_wall = time_steps(step, a.steps, torch)
     got_dx = grads["dx"].to("cpu", torch.float64).numpy()
 
     # The backward's steps alone, on the same shapes and realistic operands.
@@ -364,6 +371,7 @@ def bench_backward(a, w, torch, vb):
                    "variant": "backward"},
         "block_tflops": round(tflops, 2),
         "block_frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "step_ms": step_stats(per_step),
         "wall_s_timed": round(t_wall, 3),
         "kernels": per,
         "roofline": roof,
@@ -453,34 +461,30 @@ def main():
 
     for _ in range(a.warmup):
         step()
-    torch.cuda.synchronize()
-    s = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_wall = time.perf_counter()
-    e0.record(s)
-    for _ in range(a.steps):
-        step()
-    e1.record(s)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms = e0.elapsed_time(e1) / a.steps
+    ms, per_step, t_wall = time_steps(step, a.steps, torch)
     got = out.to("cpu", torch.float64).numpy()
-    cls_only_ms = None
+    cls_only = None
     if encoder:
         # The same stack asked for the class tokens only: its last block then
-        # computes just their rows.
+        # computes just their rows.  Timed only after its output is checked
+        # against the class tokens of the full run (the same values to within
+        # the stack's bar; its smaller products may sum K in another order).
+        cls_full = cls.to("cpu", torch.float64).numpy()
+        cls_only_out = torch.empty_like(cls)
+
         def cls_step():
             vb.encoder_forward(g["x"], enc_packed, w.F, w.H, w.eps, params=enc_params,
-                               final_gamma=fg, final_beta=fb, want_tokens=False, cls_out=cls,
-                               workspace=ws_enc)
+                               final_gamma=fg, final_beta=fb, want_tokens=False,
+                               cls_out=cls_only_out, workspace=ws_enc)
         cls_step()
         torch.cuda.synchronize()
-        e0.record(s)
-        for _ in range(a.steps):
-            cls_step()
-        e1.record(s)
-        torch.cuda.synchronize()
-        cls_only_ms = e0.elapsed_time(e1) / a.steps
+        got_cls = cls_only_out.to("cpu", torch.float64).numpy()
+        dev_ratio = float((np.abs(got_cls - cls_full) / (1.0 + np.abs(cls_full))).max())
+        bar = 3e-2 * math.sqrt(L)
+        cls_only = {"agrees_with_full_run": dev_ratio, "bar": bar}
+        if np.all(np.isfinite(got_cls)) and dev_ratio <= bar:
+            cms, cper, _ = time_steps(cls_step, a.steps, torch)
+            cls_only.update({"ms_per_step": round(cms, 5), "step_ms": step_stats(cper)})
 
     # Each step's kernel alone, on the same shapes (separate buffers per step).
     M, D, F = w.M, w.D, w.F
@@ -618,12 +622,13 @@ def main():
                    **({"layers": L} if encoder else {})},
         "block_tflops": round(tflops, 2),
         "block_frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "step_ms": step_stats(per_step),
         "wall_s_timed": round(t_wall, 3),
         "kernels": per,
         "roofline": roof,
     }
-    if cls_only_ms is not None:
-        res["cls_only_ms_per_step"] = round(cls_only_ms, 5)
+    if cls_only is not None:
+        res["cls_only"] = cls_only
     if a.cpu_seconds > 0:
         import oracle
         if encoder:

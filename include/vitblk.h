@@ -366,6 +366,17 @@ int vitblk_qkv_projection(const void* xn, const void* w_qkv_t, void* qkv, int64_
 int vitblk_attention(const void* qkv, void* att, int64_t N, int64_t T, int64_t D,
                      int64_t H, int dtype, vitblk_stream_t stream);
 
+/* The same attention for the first queries of each sequence only, every key
+ * entering their softmax: rows n*T + t of att with t < min(T, 32) are
+ * written exactly as vitblk_attention() writes them; the other rows may or
+ * may not be written.  It serves a readout that needs only the class token
+ * (query 0): mlgrind.dev "E2E: Tiny Vision Transformer", "Architecture" (the
+ * class token's final state is the image's representation), with the same
+ * kernels as the class-token-only last block of vitblk_encoder_forward().
+ * Same arguments and errors as vitblk_attention(). */
+int vitblk_attention_first_queries(const void* qkv, void* att, int64_t N, int64_t T, int64_t D,
+                                   int64_t H, int dtype, vitblk_stream_t stream);
+
 /* out = epilogue(a @ W) with the weight given out-major: a [M, K],
  * w_t [Nout, K] (row n = column n of the (in, out) weight W, as in the
  * packed regions), out [M, Nout]; residual [M, Nout] is read only for

@@ -15,7 +15,6 @@ from .block import (  # noqa: F401
     layer_norm,
     layer_norm_stats,
     merge_heads,
-    mlp,
     multi_head_attention,
     project,
     softmax_rows,

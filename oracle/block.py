@@ -61,7 +61,6 @@ __all__ = [
     "attention_weights",
     "multi_head_attention",
     "gelu_tanh",
-    "mlp",
     "vit_block",
     "vit_block_stages",
     "affine",
@@ -216,11 +215,6 @@ def gelu_tanh(z) -> np.ndarray:
     """
     z = _f64(z)
     return 0.5 * z * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (z + 0.044715 * z ** 3)))
-
-
-def mlp(yn, w_mlp1, w_mlp2) -> np.ndarray:
-    """GELU(yn @ w_mlp1) @ w_mlp2, no biases ([CAC] "Feed-forward stage")."""
-    return project(gelu_tanh(project(yn, w_mlp1)), w_mlp2)
 
 
 def _params(params) -> dict:

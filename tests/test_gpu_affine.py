@@ -122,12 +122,14 @@ def test_affine_block_full_size(name):
 
 
 def test_affine_block_large_key_bias():
-    # A large key bias adds q_i . b_k to every score of query i: some
-    # queries' scores all lie hundreds of log2 units below 0, others' far
-    # above (the output itself does not depend on b_k).  Keys of size ~40
-    # keep only bf16's precision of the per-key differences, so the input is
-    # ill-conditioned for any bf16 implementation: the block is held to the
-    # same block composed from the step entries, and must stay finite.
+    # A consistency check, not a parity case: a large key bias adds q_i . b_k
+    # to every score of query i, so some queries' scores all lie hundreds of
+    # log2 units below 0 and others' far above (the output itself does not
+    # depend on b_k).  Keys of size ~40 keep only bf16's precision of the
+    # per-key differences, so the input is ill-conditioned for any bf16
+    # implementation: the block must stay finite and as close to the oracle
+    # as the same block composed from the step entries.  The attention step
+    # is held to the oracle at such scores in test_gpu_attention_extreme.py.
     inp = make_block_inputs(2, 197, 256, 1024, "bf16", seed=14)
     prm = make_affine_params(256, 1024, "bf16", seed=14)
     prm["b_k"] = round_to(np.asarray(prm["b_k"]) * 400.0, "bf16")

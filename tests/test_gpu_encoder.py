@@ -137,3 +137,41 @@ def test_encoder_class_tokens_only_vit_b16():
     _, ref_cls = oracle.encoder(x[seqs], layers, w.H, w.eps, fg, fb)
     assert_close(got[seqs], ref_cls, w.dtype, f"ViT-B/16 x{L} cls only, sequences {seqs}",
                  scale=stack_scale(L))
+
+
+def test_encoder_each_block_at_the_one_block_bar_vit_b16_depth12():
+    # Each block of a ViT-B/16 x 12 stack held to the one-block bar, given
+    # its own GPU input: the stack's blocks are chained here through
+    # vitblk_forward_packed_affine (the encoder's per-block launch sequence),
+    # checked first to reproduce the stack's output bit for bit; then the
+    # oracle runs block l on block l's GPU input, so no error carries over
+    # from earlier blocks (ai-engineer-exhaustive.pages.dev "ViT Encoder
+    # Block", "What It Is": L identical blocks in sequence).
+    import torch
+    w = WORKLOADS["vit_b16"]
+    L = 12
+    x, layers = _layers(w.N, w.T, w.D, w.F, L, w.dtype, True, seed=7)
+    fg, fb = _final(w.D, w.dtype, seed=7)
+    dev_x = to_dev(x, w.dtype)
+    packed = [vb.pack_weights(*(to_dev(lay[k], w.dtype) for k in WEIGHTS)) for lay in layers]
+    prm = [{k: to_dev(v, w.dtype) for k, v in lay["params"].items()} for lay in layers]
+    tok, _ = vb.encoder_forward(dev_x, packed, w.F, w.H, w.eps, params=prm,
+                                final_gamma=to_dev(fg, w.dtype),
+                                final_beta=to_dev(fb, w.dtype), want_cls=False)
+    chain = [dev_x]
+    for l in range(L):
+        chain.append(vb.forward_packed_affine(chain[-1], packed[l], w.F, w.H, w.eps,
+                                              params=prm[l]))
+    final = vb.layernorm(chain[-1].view(-1, w.D), w.eps, gamma=to_dev(fg, w.dtype),
+                         beta=to_dev(fb, w.dtype)).view(tok.shape)
+    assert torch.equal(final, tok)
+    seqs = [0, w.N - 1]
+    worst = 0.0
+    for l in range(L):
+        xin = to_host(chain[l])[seqs]
+        ref = oracle.vit_block(xin, *(layers[l][k] for k in WEIGHTS), w.H, w.eps,
+                               params=layers[l]["params"])
+        v, _ = assert_close(to_host(chain[l + 1])[seqs], ref, w.dtype,
+                            f"ViT-B/16 block {l} of {L}, sequences {seqs}")
+        worst = max(worst, v)
+    print(f"  worst block violation {worst:.3e} (one-block bar 3e-2)", flush=True)

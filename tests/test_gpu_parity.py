@@ -271,13 +271,15 @@ def _block_by_steps(dev, H, eps):
 
 @pytest.mark.parametrize("gain", [6.0, 20.0])
 def test_block_large_attention_scores(gain):
-    # w_q and w_k scaled up: scores reach hundreds in log2 units, so the
-    # attention's reference maximum moves far (and its rescaling of the
-    # running sums is exercised).  Scores that large keep only bf16's
-    # precision of their differences, so the input is ill-conditioned for
-    # any bf16 implementation (the plain bar fails from gain 3 on: 0.045):
-    # the block is held to the same block composed from the step entries
-    # (LayerNorms written out instead of folded), and must stay finite.
+    # A consistency check, not a parity case: w_q and w_k scaled up put the
+    # scores in the hundreds of log2 units.  Q and K are rounded to bf16
+    # after the projection, and scores that large keep only bf16's precision
+    # of their differences, so at block level the input is ill-conditioned
+    # for any bf16 implementation (the plain bar fails from gain 3 on:
+    # 0.045).  The block must stay finite and as close to the oracle as the
+    # same block composed from the step entries (LayerNorms written out
+    # instead of folded).  The attention step itself is held to the oracle
+    # at such scores, at the plain bar, in test_gpu_attention_extreme.py.
     inp = make_block_inputs(2, 197, 256, 1024, "bf16", seed=13)
     for k in ("w_q", "w_k"):
         inp[k] = round_to(inp[k] * gain, "bf16")

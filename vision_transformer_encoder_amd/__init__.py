@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     VITBLK_FP32,
     VitblkError,
     attention,
+    attention_first_queries,
     attention_backward,
     attention_backward_workspace_bytes,
     backward,

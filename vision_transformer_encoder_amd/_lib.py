@@ -41,6 +41,7 @@ SIGNATURES = {
     "vitblk_layernorm": (_I, [_P, _P, _I64, _I64, _D, _I, _P]),
     "vitblk_qkv_projection": (_I, [_P] * 3 + [_I64, _I64, _I, _P]),
     "vitblk_attention": (_I, [_P, _P, _I64, _I64, _I64, _I64, _I, _P]),
+    "vitblk_attention_first_queries": (_I, [_P, _P, _I64, _I64, _I64, _I64, _I, _P]),
     "vitblk_linear": (_I, [_P] * 4 + [_I64, _I64, _I64, _I, _I, _P]),
     "vitblk_forward_affine": (_I, [_P] * 7 + [_AP, _P] + [_I64] * 5 + [_D, _I, _P, _SZ, _P]),
     "vitblk_forward_packed_affine": (_I, [_P, _P, _AP, _P] + [_I64] * 5 + [_D, _I, _P, _SZ, _P]),
@@ -152,6 +153,61 @@ def _ptr(t):
     return ctypes.c_void_p(0 if t is None else t.data_ptr())
 
 
+# Shape checks.  The C interface receives bare pointers, so a tensor of the
+# wrong size would be read or written out of bounds on the device; every
+# entry point below checks the shapes it relies on before anything reaches
+# the library.
+
+def _shape(t, shape, name):
+    """t (if given) must have exactly this shape."""
+    if t is not None and tuple(t.shape) != tuple(int(d) for d in shape):
+        raise ValueError(f"{name} must have shape {tuple(int(d) for d in shape)}, "
+                         f"got {tuple(t.shape)}")
+
+
+def _rank(t, ndim, name):
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _buffer(t, ref, need, name):
+    """A caller-supplied byte buffer (workspace, packed weights): on ref's
+    GPU, contiguous, and at least `need` bytes."""
+    if t is None:
+        return
+    if _nbytes(t) < need:
+        raise ValueError(f"{name} holds {_nbytes(t)} bytes, needs at least {need}")
+    if ref is None:  # size only
+        return
+    if not t.is_cuda or t.device != ref.device:
+        raise ValueError(f"{name} must be on the same GPU as the inputs")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _params_shapes(params, D, F):
+    """Each affine parameter is one value per feature: [F] for b_mlp1, else [D]."""
+    if params is None:
+        return
+    for k, v in params.items():
+        _shape(v, (F,) if k == "b_mlp1" else (D,), k)
+
+
+def _block_weights(w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, D):
+    """The six (in, out) weights of a block of width D; returns F."""
+    _rank(w_mlp1, 2, "w_mlp1")
+    F = w_mlp1.shape[1]
+    for name, w in (("w_q", w_q), ("w_k", w_k), ("w_v", w_v), ("w_o", w_o)):
+        _shape(w, (D, D), name)
+    _shape(w_mlp1, (D, F), "w_mlp1")
+    _shape(w_mlp2, (F, D), "w_mlp2")
+    return F
+
+
 def workspace_bytes(N, T, D, F, H, dtype) -> int:
     code = dtype if isinstance(dtype, int) else dtype_code(dtype)
     return int(load().vitblk_workspace_bytes(N, T, D, F, H, code))
@@ -166,13 +222,16 @@ def forward(x, w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, num_heads: int, eps: float,
             out=None, workspace=None, stream=None):
     """out = block(x) for x [N, T, D]; returns out (allocated if not given)."""
     torch = _torch()
-    _dev(x, w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, out)
+    _rank(x, 3, "x")
     N, T, D = x.shape
-    F = w_mlp1.shape[1]
+    F = _block_weights(w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, D)
+    _shape(out, x.shape, "out")
     code = dtype_code(x.dtype)
+    need = workspace_bytes(N, T, D, F, num_heads, code)
+    _buffer(workspace, x, need, "workspace")
+    _dev(x, w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, out)
     if out is None:
         out = torch.empty_like(x)
-    need = workspace_bytes(N, T, D, F, num_heads, code)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     st = load().vitblk_forward(_ptr(x), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(w_o),
@@ -184,13 +243,14 @@ def forward(x, w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, num_heads: int, eps: float,
     return out
 
 
-def _affine(params, ref):
+def _affine(params, ref, D, F):
     """AffineParams from a {name: tensor or None} dict (None: no parameters)."""
     if params is None:
         return None
     unknown = set(params) - set(AFFINE_KEYS)
     if unknown:
         raise ValueError(f"unknown block parameters: {sorted(unknown)}")
+    _params_shapes(params, D, F)
     ts = [params.get(k) for k in AFFINE_KEYS]
     _dev(ref, *ts)
     return AffineParams(*[0 if t is None else t.data_ptr() for t in ts])
@@ -200,14 +260,18 @@ def forward_affine(x, w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, num_heads: int, eps: f
                    params=None, out=None, workspace=None, stream=None):
     """The affine block: params maps AFFINE_KEYS names to [D] (b_mlp1: [F]) tensors."""
     torch = _torch()
-    _dev(x, w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, out)
+    _rank(x, 3, "x")
     N, T, D = x.shape
-    F = w_mlp1.shape[1]
+    F = _block_weights(w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, D)
+    _shape(out, x.shape, "out")
+    _params_shapes(params, D, F)
     code = dtype_code(x.dtype)
-    ap = _affine(params, x)
+    need = workspace_bytes(N, T, D, F, num_heads, code)
+    _buffer(workspace, x, need, "workspace")
+    _dev(x, w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, out)
+    ap = _affine(params, x, D, F)
     if out is None:
         out = torch.empty_like(x)
-    need = workspace_bytes(N, T, D, F, num_heads, code)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     st = load().vitblk_forward_affine(_ptr(x), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(w_o),
@@ -229,14 +293,24 @@ def patch_embed(images, w_patch, patch: int, b_patch=None, cls_token=None, pos_e
                 out=None, workspace=None, stream=None):
     """Tokens [B, N (+1), D] from images [B, C, H, W] (see vitblk_patch_embed)."""
     torch = _torch()
-    _dev(images, w_patch, b_patch, cls_token, pos_emb, out)
+    _rank(images, 4, "images")
+    _rank(w_patch, 2, "w_patch")
     B, C, H, W = images.shape
     D = w_patch.shape[1]
-    code = dtype_code(images.dtype)
+    if patch <= 0 or H % patch or W % patch:
+        raise ValueError(f"the patch side {patch} must divide the image sides {H} x {W}")
     T = (H // patch) * (W // patch) + (1 if cls_token is not None else 0)
+    _shape(w_patch, (patch * patch * C, D), "w_patch")
+    _shape(b_patch, (D,), "b_patch")
+    _shape(cls_token, (D,), "cls_token")
+    _shape(pos_emb, (T, D), "pos_emb")
+    _shape(out, (B, T, D), "out")
+    code = dtype_code(images.dtype)
+    need = patch_embed_workspace_bytes(B, C, H, W, patch, D, code)
+    _buffer(workspace, images, need, "workspace")
+    _dev(images, w_patch, b_patch, cls_token, pos_emb, out)
     if out is None:
         out = torch.empty((B, T, D), dtype=images.dtype, device=images.device)
-    need = patch_embed_workspace_bytes(B, C, H, W, patch, D, code)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=images.device)
     st = load().vitblk_patch_embed(_ptr(images), _ptr(w_patch), _ptr(b_patch), _ptr(cls_token),
@@ -261,10 +335,24 @@ def encoder_forward(x, packed, F: int, num_heads: int, eps: float, params=None,
     (tokens [N, T, D] or None, cls [N, D] or None).
     """
     torch = _torch()
-    _dev(x, final_gamma, final_beta, out, cls_out)
+    _rank(x, 3, "x")
     N, T, D = x.shape
     L = len(packed)
+    _shape(final_gamma, (D,), "final_gamma")
+    _shape(final_beta, (D,), "final_beta")
+    _shape(out, x.shape, "out")
+    _shape(cls_out, (N, D), "cls_out")
+    if params is not None:
+        for p in params:
+            _params_shapes(p, D, F)
     code = dtype_code(x.dtype)
+    pw = packed_weights_bytes(D, F, code)
+    for i, p in enumerate(packed):  # every size first, then every device
+        _buffer(p, None, pw, f"packed[{i}]")
+    for i, p in enumerate(packed):
+        _buffer(p, x, pw, f"packed[{i}]")
+    _buffer(workspace, x, encoder_workspace_bytes(N, T, D, F, num_heads, code), "workspace")
+    _dev(x, final_gamma, final_beta, out, cls_out)
     if want_tokens and out is None:
         out = torch.empty_like(x)
     if want_cls and cls_out is None:
@@ -274,8 +362,9 @@ def encoder_forward(x, packed, F: int, num_heads: int, eps: float, params=None,
     if params is not None:
         if len(params) != L:
             raise ValueError("one parameter dict per block")
-        aps = (AffineParams * L)(*[_affine(p, x) or AffineParams() for p in params])
+        aps = (AffineParams * L)(*[_affine(p, x, D, F) or AffineParams() for p in params])
     need = encoder_workspace_bytes(N, T, D, F, num_heads, code)
+    _buffer(workspace, x, need, "workspace")
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     st = load().vitblk_encoder_forward(
@@ -290,9 +379,12 @@ def encoder_forward(x, packed, F: int, num_heads: int, eps: float, params=None,
 def pack_weights(w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, packed=None, stream=None):
     """Out-major copies of the six weights in one buffer (uint8 tensor)."""
     torch = _torch()
-    _dev(w_q, w_k, w_v, w_o, w_mlp1, w_mlp2)
-    D, F = w_mlp1.shape
+    _rank(w_q, 2, "w_q")
+    D = w_q.shape[0]
+    F = _block_weights(w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, D)
     code = dtype_code(w_q.dtype)
+    _buffer(packed, w_q, packed_weights_bytes(D, F, code), "packed")
+    _dev(w_q, w_k, w_v, w_o, w_mlp1, w_mlp2)
     if packed is None:
         packed = torch.empty(max(packed_weights_bytes(D, F, code), 1), dtype=torch.uint8,
                              device=w_q.device)
@@ -340,12 +432,16 @@ def forward_packed(x, packed, F: int, num_heads: int, eps: float, out=None, work
                    stream=None):
     """out = block(x) on weights packed by pack_weights()."""
     torch = _torch()
-    _dev(x, out)
+    _rank(x, 3, "x")
     N, T, D = x.shape
+    _shape(out, x.shape, "out")
     code = dtype_code(x.dtype)
+    _buffer(packed, x, packed_weights_bytes(D, F, code), "packed")
+    need = workspace_bytes(N, T, D, F, num_heads, code) - packed_weights_bytes(D, F, code)
+    _buffer(workspace, x, need, "workspace")
+    _dev(x, out)
     if out is None:
         out = torch.empty_like(x)
-    need = workspace_bytes(N, T, D, F, num_heads, code) - packed_weights_bytes(D, F, code)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     st = load().vitblk_forward_packed(_ptr(x), _ptr(packed), _ptr(out), N, T, D, F, num_heads,
@@ -360,13 +456,18 @@ def forward_packed_affine(x, packed, F: int, num_heads: int, eps: float, params=
                           out=None, workspace=None, stream=None):
     """The affine block on weights packed by pack_weights()."""
     torch = _torch()
-    _dev(x, out)
+    _rank(x, 3, "x")
     N, T, D = x.shape
+    _shape(out, x.shape, "out")
+    _params_shapes(params, D, F)
     code = dtype_code(x.dtype)
-    ap = _affine(params, x)
+    _buffer(packed, x, packed_weights_bytes(D, F, code), "packed")
+    need = workspace_bytes(N, T, D, F, num_heads, code) - packed_weights_bytes(D, F, code)
+    _buffer(workspace, x, need, "workspace")
+    _dev(x, out)
+    ap = _affine(params, x, D, F)
     if out is None:
         out = torch.empty_like(x)
-    need = workspace_bytes(N, T, D, F, num_heads, code) - packed_weights_bytes(D, F, code)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     st = load().vitblk_forward_packed_affine(_ptr(x), _ptr(packed),
@@ -382,9 +483,12 @@ def forward_packed_affine(x, packed, F: int, num_heads: int, eps: float, params=
 def layernorm(x, eps: float, gamma=None, beta=None, out=None, stream=None):
     """Row-wise LN over the last axis of a contiguous tensor, optionally * gamma + beta."""
     torch = _torch()
-    _dev(x, gamma, beta, out)
     D = x.shape[-1]
     rows = x.numel() // D
+    _shape(gamma, (D,), "gamma")
+    _shape(beta, (D,), "beta")
+    _shape(out, x.shape, "out")
+    _dev(x, gamma, beta, out)
     if out is None:
         out = torch.empty_like(x)
     if gamma is None and beta is None:
@@ -401,9 +505,11 @@ def layernorm(x, eps: float, gamma=None, beta=None, out=None, stream=None):
 def qkv_projection(xn, w_qkv_t, out=None, stream=None):
     """Packed [M, 3D] = xn [M, D] @ [w_q | w_k | w_v], weight given out-major [3D, D]."""
     torch = _torch()
-    _dev(xn, w_qkv_t, out)
     D = xn.shape[-1]
     M = xn.numel() // D
+    _shape(w_qkv_t, (3 * D, D), "w_qkv_t")
+    _shape(out, (M, 3 * D), "out")
+    _dev(xn, w_qkv_t, out)
     if out is None:
         out = torch.empty((M, 3 * D), dtype=xn.dtype, device=xn.device)
     st = load().vitblk_qkv_projection(_ptr(xn), _ptr(w_qkv_t), _ptr(out), M, D,
@@ -415,8 +521,11 @@ def qkv_projection(xn, w_qkv_t, out=None, stream=None):
 def attention(qkv, N: int, T: int, num_heads: int, out=None, stream=None):
     """Concatenated head outputs [N*T, D] from packed qkv [N*T, 3D]."""
     torch = _torch()
-    _dev(qkv, out)
+    _rank(qkv, 2, "qkv")
     D = qkv.shape[-1] // 3
+    _shape(qkv, (N * T, 3 * D), "qkv")
+    _shape(out, (N * T, D), "out")
+    _dev(qkv, out)
     if out is None:
         out = torch.empty((N * T, D), dtype=qkv.dtype, device=qkv.device)
     st = load().vitblk_attention(_ptr(qkv), _ptr(out), N, T, D, num_heads,
@@ -425,14 +534,38 @@ def attention(qkv, N: int, T: int, num_heads: int, out=None, stream=None):
     return out
 
 
+def attention_first_queries(qkv, N: int, T: int, num_heads: int, out=None, stream=None):
+    """attention() for the first min(T, 32) queries of each sequence (all keys):
+    those rows of out [N*T, D] are written, the others may not be."""
+    torch = _torch()
+    _rank(qkv, 2, "qkv")
+    D = qkv.shape[-1] // 3
+    _shape(qkv, (N * T, 3 * D), "qkv")
+    _shape(out, (N * T, D), "out")
+    _dev(qkv, out)
+    if out is None:
+        out = torch.empty((N * T, D), dtype=qkv.dtype, device=qkv.device)
+    st = load().vitblk_attention_first_queries(_ptr(qkv), _ptr(out), N, T, D, num_heads,
+                                               dtype_code(qkv.dtype), _stream(qkv, stream))
+    _check("vitblk_attention_first_queries", st)
+    return out
+
+
 def linear(a, w_t, epilogue: int = EPI_NONE, residual=None, out=None, stream=None,
            bias=None):
     """out = epilogue(a [M, K] @ W + bias) (+ residual), W given out-major, w_t [Nout, K]."""
     torch = _torch()
-    _dev(a, w_t, residual, bias, out)
     K = a.shape[-1]
     M = a.numel() // K
+    _rank(w_t, 2, "w_t")
     Nout = w_t.shape[0]
+    _shape(w_t, (Nout, K), "w_t")
+    _shape(residual, (M, Nout), "residual")
+    _shape(bias, (Nout,), "bias")
+    _shape(out, (M, Nout), "out")
+    if epilogue == EPI_RESIDUAL and residual is None:
+        raise ValueError("the residual epilogue needs a residual")
+    _dev(a, w_t, residual, bias, out)
     if out is None:
         out = torch.empty((M, Nout), dtype=a.dtype, device=a.device)
     if bias is None:
@@ -470,13 +603,17 @@ def linear_normed(a, w_t, col_sums, stats, epilogue: int = EPI_NONE, bias=None, 
     a [M, K] raw rows, stats = row_stats(a), col_sums fp32 [Nout] (W's column sums),
     W given out-major, w_t [Nout, K]."""
     torch = _torch()
-    _dev(a, w_t, bias, out)
-    _dev_f32(a, col_sums, stats)
     K = a.shape[-1]
     M = a.numel() // K
+    _rank(w_t, 2, "w_t")
     Nout = w_t.shape[0]
+    _shape(w_t, (Nout, K), "w_t")
+    _shape(bias, (Nout,), "bias")
+    _shape(out, (M, Nout), "out")
     if col_sums.numel() != Nout or stats.numel() != 2 * M:
         raise ValueError("col_sums must hold Nout floats and stats 2 per row of a")
+    _dev(a, w_t, bias, out)
+    _dev_f32(a, col_sums, stats)
     if out is None:
         out = torch.empty((M, Nout), dtype=a.dtype, device=a.device)
     st = load().vitblk_linear_normed(_ptr(a), _ptr(w_t), _ptr(col_sums), _ptr(stats), _ptr(bias),
@@ -498,16 +635,26 @@ def backward(x, w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, dout, num_heads: int, eps: f
     """Gradients of sum(dout * block(x)): dict keyed by GRAD_KEYS (allocated if not given)."""
     torch = _torch()
     ws_ = (w_q, w_k, w_v, w_o, w_mlp1, w_mlp2)
-    _dev(x, dout, *ws_)
+    _rank(x, 3, "x")
     N, T, D = x.shape
-    F = w_mlp1.shape[1]
+    F = _block_weights(*ws_, D)
+    _shape(dout, x.shape, "dout")
+    if grads is not None:
+        missing = set(GRAD_KEYS) - set(grads)
+        if missing:
+            raise ValueError(f"grads lacks {sorted(missing)}")
+        _shape(grads["dx"], x.shape, "dx")
+        for k, w in zip(GRAD_KEYS[1:], ws_):
+            _shape(grads[k], w.shape, k)
     code = dtype_code(x.dtype)
+    need = backward_workspace_bytes(N, T, D, F, num_heads, code)
+    _buffer(workspace, x, need, "workspace")
+    _dev(x, dout, *ws_)
     if grads is None:
         grads = {"dx": torch.empty_like(x)}
         for k, w in zip(GRAD_KEYS[1:], ws_):
             grads[k] = torch.empty_like(w)
-    _dev(*grads.values())
-    need = backward_workspace_bytes(N, T, D, F, num_heads, code)
+    _dev(x, *(grads[k] for k in GRAD_KEYS))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     st = load().vitblk_backward(_ptr(x), *[_ptr(w) for w in ws_], _ptr(dout),
@@ -525,11 +672,13 @@ def weight_grad_workspace_bytes(M, I, J) -> int:
 def weight_grad(a, b, out=None, workspace=None, stream=None):
     """out [I, J] = a^T b for a [M, I], b [M, J] (sum over the M token rows)."""
     torch = _torch()
-    _dev(a, b, out)
     I, J = a.shape[-1], b.shape[-1]
     M = a.numel() // I
     if b.numel() // J != M:
         raise ValueError("a and b must have the same number of rows")
+    _shape(out, (I, J), "out")
+    _buffer(workspace, a, weight_grad_workspace_bytes(M, I, J), "workspace")
+    _dev(a, b, out)
     if out is None:
         out = torch.empty((I, J), dtype=a.dtype, device=a.device)
     if workspace is None:
@@ -545,9 +694,12 @@ def weight_grad(a, b, out=None, workspace=None, stream=None):
 def layernorm_backward(x, g, eps: float, residual=None, out=None, stream=None):
     """dx = residual + LN'(x)^T g, row by row over the last axis."""
     torch = _torch()
-    _dev(x, g, residual, out)
     D = x.shape[-1]
     rows = x.numel() // D
+    _shape(g, x.shape, "g")
+    _shape(residual, x.shape, "residual")
+    _shape(out, x.shape, "out")
+    _dev(x, g, residual, out)
     if out is None:
         out = torch.empty_like(x)
     st = load().vitblk_layernorm_backward(_ptr(x), _ptr(g), _ptr(residual), _ptr(out), rows, D,
@@ -564,8 +716,12 @@ def attention_backward(qkv, datt, N: int, T: int, num_heads: int, out=None, work
                        stream=None):
     """dqkv [N*T, 3D] from the forward's qkv [N*T, 3D] and datt [N*T, D]."""
     torch = _torch()
-    _dev(qkv, datt, out)
     D = datt.shape[-1]
+    _shape(qkv, (N * T, 3 * D), "qkv")
+    _shape(datt, (N * T, D), "datt")
+    _shape(out, (N * T, 3 * D), "out")
+    _buffer(workspace, qkv, attention_backward_workspace_bytes(N, T, D, num_heads), "workspace")
+    _dev(qkv, datt, out)
     if out is None:
         out = torch.empty((N * T, 3 * D), dtype=qkv.dtype, device=qkv.device)
     if workspace is None:

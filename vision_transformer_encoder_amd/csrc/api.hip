@@ -588,6 +588,18 @@ int vitblk_attention(const void* qkv, void* att, int64_t N, int64_t T, int64_t D
   return VITBLK_OK;
 }
 
+int vitblk_attention_first_queries(const void* qkv, void* att, int64_t N, int64_t T, int64_t D,
+                                   int64_t H, int dtype, vitblk_stream_t stream) {
+  const int st = validate_attention(qkv, att, N, T, D, H, dtype);
+  if (st != VITBLK_OK) return st;
+  const char* base = static_cast<const char*>(qkv);
+  const size_t es = elem_size(dtype);
+  VITBLK_LAUNCH(launch_attention_first_queries(base, base + D * es, base + 2 * D * es, 3 * D, att,
+                                               D, N, T, H, D / H, dtype,
+                                               reinterpret_cast<hipStream_t>(stream)));
+  return VITBLK_OK;
+}
+
 int vitblk_linear(const void* a, const void* w_t, const void* residual, void* out, int64_t M,
                   int64_t K, int64_t Nout, int epilogue, int dtype, vitblk_stream_t stream) {
   return vitblk_linear_bias(a, w_t, nullptr, residual, out, M, K, Nout, epilogue, dtype, stream);
