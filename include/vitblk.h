@@ -222,6 +222,32 @@ int vitblk_forward_packed(const void* x, const void* packed, void* out, int64_t 
                           int64_t D, int64_t F, int64_t H, double eps, int dtype,
                           void* workspace, size_t workspace_bytes, vitblk_stream_t stream);
 
+/*
+ * vitblk_forward_packed() for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the activations live in a scratch array inside the library (a
+ * file-scope __device__ array of VITBLK_NOALLOC_SCRATCH_BYTES bytes, one per
+ * GPU the library runs on, held until the process ends) instead of a caller
+ * workspace.  The call allocates nothing.  The caller still owns x, packed
+ * and out (device pointers on the GPU that `stream` belongs to).
+ *
+ * Limit: vitblk_workspace_bytes(N, T, D, F, H, dtype) -
+ * vitblk_packed_weights_bytes(D, F, dtype) must not exceed
+ * VITBLK_NOALLOC_SCRATCH_BYTES (e.g. ViT-L/16 width: up to 27 sequences of
+ * 197 tokens); larger sizes return VITBLK_ERR_WORKSPACE and launch nothing.
+ * Every call on one GPU uses that GPU's single scratch array, which keeps
+ * the last call's contents (nothing in it needs to start at zero): calls
+ * that overlap in time on one GPU (other host threads, or streams that run
+ * concurrently) race, and the caller must order them.  The results are
+ * those of vitblk_forward_packed() on the same inputs, bit for bit.
+ * Other errors as vitblk_forward_packed(); VITBLK_ERR_HIP if the scratch
+ * array's address cannot be resolved on the stream's device.
+ */
+#define VITBLK_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int vitblk_forward_packed_noalloc(const void* x, const void* packed, void* out, int64_t N,
+                                  int64_t T, int64_t D, int64_t F, int64_t H, double eps,
+                                  int dtype, vitblk_stream_t stream);
+
 /* vitblk_forward_packed() with the affine variant's parameters (may be NULL). */
 int vitblk_forward_packed_affine(const void* x, const void* packed,
                                  const vitblk_affine_params* params, void* out, int64_t N,

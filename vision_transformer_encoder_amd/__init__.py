@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     GRAD_KEYS,
     EPI_NONE,
     EPI_RESIDUAL,
+    NOALLOC_SCRATCH_BYTES,
     VITBLK_BF16,
     VITBLK_FP32,
     VitblkError,
@@ -29,6 +30,7 @@ from ._lib import (  # noqa: F401
     forward_affine,
     forward_packed,
     forward_packed_affine,
+    forward_packed_noalloc,
     layernorm,
     layernorm_backward,
     linear,

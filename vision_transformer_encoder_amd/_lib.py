@@ -38,6 +38,7 @@ SIGNATURES = {
     "vitblk_pack_weights": (_I, [_P] * 7 + [_I64, _I64, _I, _P]),
     "vitblk_forward": (_I, [_P] * 8 + [_I64] * 5 + [_D, _I, _P, _SZ, _P]),
     "vitblk_forward_packed": (_I, [_P] * 3 + [_I64] * 5 + [_D, _I, _P, _SZ, _P]),
+    "vitblk_forward_packed_noalloc": (_I, [_P] * 3 + [_I64] * 5 + [_D, _I, _P]),
     "vitblk_layernorm": (_I, [_P, _P, _I64, _I64, _D, _I, _P]),
     "vitblk_qkv_projection": (_I, [_P] * 3 + [_I64, _I64, _I, _P]),
     "vitblk_attention": (_I, [_P, _P, _I64, _I64, _I64, _I64, _I, _P]),
@@ -449,6 +450,28 @@ def forward_packed(x, packed, F: int, num_heads: int, eps: float, out=None, work
                                       workspace.numel() * workspace.element_size(),
                                       _stream(x, stream))
     _check("vitblk_forward_packed", st)
+    return out
+
+
+# Bytes of the library's own scratch array (VITBLK_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def forward_packed_noalloc(x, packed, F: int, num_heads: int, eps: float, out, stream=None):
+    """forward_packed() with the activations in the library's scratch array:
+    no workspace, nothing allocated (out must be given).  Calls that overlap
+    on one GPU race (they share that GPU's array)."""
+    _rank(x, 3, "x")
+    N, T, D = x.shape
+    if out is None:
+        raise ValueError("out must be given: this entry point allocates nothing")
+    _shape(out, x.shape, "out")
+    code = dtype_code(x.dtype)
+    _buffer(packed, x, packed_weights_bytes(D, F, code), "packed")
+    _dev(x, out)
+    st = load().vitblk_forward_packed_noalloc(_ptr(x), _ptr(packed), _ptr(out), N, T, D, F,
+                                              num_heads, float(eps), code, _stream(x, stream))
+    _check("vitblk_forward_packed_noalloc", st)
     return out
 
 

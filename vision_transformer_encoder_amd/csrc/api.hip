@@ -2,6 +2,8 @@
 // launch sequence of one pre-LN encoder block forward.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "kernels.h"
 #include "plan.h"
 #include "vitblk.h"
@@ -511,6 +513,70 @@ int vitblk_forward_packed(const void* x, const void* packed, void* out, int64_t 
   return run_block(x, packed, nullptr, out, N, T, D, F, H, eps, dtype,
                    static_cast<char*>(workspace) + pl.act_base, pl,
                    reinterpret_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------- no-allocation entry
+
+namespace {
+
+// The activations of vitblk_forward_packed_noalloc: one array per GPU (the
+// code object's global), never allocated or freed by the library.  In host
+// code `scratch` names a host-side stand-in, not device memory; its device
+// address on each GPU comes from hipGetSymbolAddress (scratch_ptr) and only
+// that address is ever passed to kernels.
+__device__ __align__(256) char scratch[VITBLK_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_addr[kMaxDevices] = {};
+
+// scratch's address on the device `stream` runs on, resolved once per device
+// with that device current (the caller's current device is restored).
+int scratch_ptr(hipStream_t stream, void** out) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return VITBLK_ERR_HIP;
+  int dev = cur;
+  if (stream != nullptr && hipStreamGetDevice(stream, &dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return VITBLK_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return VITBLK_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (scratch_addr[dev] == nullptr) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return VITBLK_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return VITBLK_ERR_HIP;
+    }
+    scratch_addr[dev] = p;
+  }
+  *out = scratch_addr[dev];
+  return VITBLK_OK;
+}
+
+}  // namespace
+
+int vitblk_forward_packed_noalloc(const void* x, const void* packed, void* out, int64_t N,
+                                  int64_t T, int64_t D, int64_t F, int64_t H, double eps,
+                                  int dtype, vitblk_stream_t stream) {
+  // Sizes first (host only): a block whose activations exceed the scratch
+  // array is rejected before any HIP call.
+  WorkspacePlan pl;
+  int st = plan_workspace(N, T, D, F, H, dtype, &pl);
+  if (st != VITBLK_OK) return st;
+  if (pl.act_total > VITBLK_NOALLOC_SCRATCH_BYTES) return VITBLK_ERR_WORKSPACE;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  st = scratch_ptr(s, &ws);
+  if (st != VITBLK_OK) return st;
+  st = validate_forward_packed(x, packed, out, N, T, D, F, H, eps, dtype, ws,
+                               VITBLK_NOALLOC_SCRATCH_BYTES, &pl);
+  if (st != VITBLK_OK) return st;
+  return run_block(x, packed, nullptr, out, N, T, D, F, H, eps, dtype,
+                   static_cast<char*>(ws) + pl.act_base, pl, s);
 }
 
 int vitblk_forward_packed_affine(const void* x, const void* packed,
