@@ -145,13 +145,29 @@ int run_block(const void* x, const void* packed, const vitblk_affine_params* prm
   if (cls_only) po.lda = po.ldr = T * D;  // the class-token rows of att and x
   po.scratch = reinterpret_cast<float*>(big);
   po.scratch_floats = static_cast<int64_t>(pl.off_act - pl.off_big) / 4;
+  // With LN2 folded, the product's epilogue also writes each row's partial
+  // statistics over every 64 columns of y (into qkv's region, dead now) and
+  // a small kernel combines them: y is not read again for its statistics.
+  if (fold2) {
+    po.row_partials = reinterpret_cast<float2*>(big);
+    if (gemm_row_partials_ok(po)) {
+      po.epi = kEpiResidualStats;
+      po.scratch = nullptr;
+    } else {
+      po.row_partials = nullptr;
+    }
+  }
   VITBLK_LAUNCH(launch_gemm(po, s));
   // LN2: yn = gamma_2 LN(y) + beta_2 (overwrites att), then
   // hidden = GELU(yn @ w_mlp1 + b_mlp1)   (overwrites qkv)
   GemmProblem p1 = linear_problem(a, pk + pl.packed.off_1, big, nullptr, Mo, D, F,
                                   VITBLK_EPI_GELU, dtype, q.b_mlp1);
   if (fold2) {
-    VITBLK_LAUNCH(launch_row_stats(y, D, stats, Mo, D, feps, dtype, s));
+    if (po.row_partials != nullptr)
+      VITBLK_LAUNCH(launch_row_stats_from_partials(po.row_partials, D / kStatsStrip, stats, Mo, D,
+                                                   feps, s));
+    else
+      VITBLK_LAUNCH(launch_row_stats(y, D, stats, Mo, D, feps, dtype, s));
     p1.A = y;
     p1.row_stats = stats;
     p1.col_sums = reinterpret_cast<const float*>(pk + pl.packed.off_cs_1);

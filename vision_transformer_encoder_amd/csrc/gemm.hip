@@ -373,8 +373,8 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
     const bf16_t* Rp = static_cast<const bf16_t*>(p.R);
     // R: the residual, or GELU's input z for the GELU-derivative epilogue, in
     // the lanes' store layout (below), rows and columns clamped into range.
-    constexpr bool kReadsR =
-        EPI == VITBLK_EPI_RESIDUAL || EPI == VITBLK_EPI_GELU_GRAD || EPI == kEpiMul;
+    constexpr bool kReadsR = EPI == VITBLK_EPI_RESIDUAL || EPI == VITBLK_EPI_GELU_GRAD ||
+                             EPI == kEpiMul || EPI == kEpiResidualStats;
     uint4 res[C::TM][C::TN][2];
     if (kReadsR) {
 #pragma unroll
@@ -463,7 +463,9 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
     // lines (rows_to_lines): 8% faster on the fused Q|K|V projection.  The
     // GELU epilogue keeps the direct stores: its exponentials already pace the
     // stores, and the extra exchange work made it 2% slower.
-    constexpr bool kLines = (EPI == VITBLK_EPI_NONE || EPI == VITBLK_EPI_RESIDUAL) && C::TN == 2;
+    constexpr bool kLines =
+        (EPI == VITBLK_EPI_NONE || EPI == VITBLK_EPI_RESIDUAL || EPI == kEpiResidualStats) &&
+        C::TN == 2;
     if (kSplit) {
       // Unrounded fp32 sums of this k-range: after the fp32 half exchange a
       // lane holds 8 consecutive columns of one row (32 bytes).
@@ -571,6 +573,48 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
           }
           outs[j][q] = out;
           if (!kLines && m < M && n < N) st_global16(Cp + m * p.ldc + n, out);
+        }
+      }
+      if constexpr (EPI == kEpiResidualStats) {
+        // Row m's statistics over this wave's WTN columns, from the values as
+        // stored (bf16): the lane's 16 * TN values as a sum and a sum of
+        // squares (v_dot2_f32_bf16 of each packed pair with (1, 1) and with
+        // itself: the bf16 products are exact in fp32), the lane's M2 = S2 -
+        // S1^2 / n (relative error about n 2^-24 (1 + mean^2 / var)), then
+        // the two lane halves combined (Chan et al.'s pairwise update).
+        static_assert(C::WTN == kStatsStrip, "one partial per wave strip");
+        constexpr float kCnt = 16.0f * C::TN;
+        constexpr bf16x2_t kOne2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+        float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const uint32_t w[4] = {outs[j][q].x, outs[j][q].y, outs[j][q].z, outs[j][q].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const bf16x2_t pr = __builtin_bit_cast(bf16x2_t, w[e]);
+              s1 = __builtin_amdgcn_fdot2_f32_bf16(pr, kOne2, s1, false);
+              s2 = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, s2, false);
+            }
+          }
+        const float mu = s1 * (1.0f / kCnt);
+        const float m2 = fmaxf(fmaf(-s1, mu, s2), 0.0f);
+        const auto ms = __builtin_amdgcn_permlane32_swap(__float_as_uint(mu), __float_as_uint(mu),
+                                                         false, false);
+        const auto qs = __builtin_amdgcn_permlane32_swap(__float_as_uint(m2), __float_as_uint(m2),
+                                                         false, false);
+        const float ma = __uint_as_float(ms[0]), mb = __uint_as_float(ms[1]);
+        const float delta = mb - ma;
+        const float mean = 0.5f * (ma + mb);
+        const float m2t = __uint_as_float(qs[0]) + __uint_as_float(qs[1]) +
+                          delta * delta * (0.5f * kCnt);
+        // A strip lies wholly inside or outside N (N is a multiple of it).
+        const int64_t n_strip = cn0 + wn * C::WTN;
+        if (lhalf == 0 && m < M && n_strip < N) {
+          const int64_t strips = N / kStatsStrip;
+          const int64_t strip = n_strip / kStatsStrip;
+          p.row_partials[m * strips + strip] = make_float2(mean, m2t);
         }
       }
       if (kLines) {
@@ -693,6 +737,7 @@ hipError_t launch_bias(const GemmProblem& p, hipStream_t s) {
     case kEpiGeluDual: return launch_epi<C, kEpiGeluDual, BIAS>(p, s);
     case kEpiMul: return launch_epi<C, kEpiMul, BIAS>(p, s);
     case kEpiPartial: return launch_epi<C, kEpiPartial, false>(p, s);
+    case kEpiResidualStats: return launch_epi<C, kEpiResidualStats, false>(p, s);
     default: return launch_epi<C, VITBLK_EPI_NONE, BIAS>(p, s);
   }
 }
@@ -736,6 +781,15 @@ bool gemm_fast_ok(const GemmProblem& p) {
       ok = ok && (reinterpret_cast<uintptr_t>(b) & 7u) == 0;
   }
   return ok;
+}
+
+// The row partials ride on the two-workgroups-per-CU 128x128 tile, the one
+// the output projection (a residual product with K = D) takes anyway; no bias.
+bool gemm_row_partials_ok(const GemmProblem& p) {
+  GemmProblem q = p;
+  q.epi = kEpiResidualStats;
+  return gemm_fast_ok(q) && p.row_partials != nullptr && p.N % kStatsStrip == 0 &&
+         (reinterpret_cast<uintptr_t>(p.row_partials) & 7u) == 0 && !has_bias(p);
 }
 
 // Rows [r0, r0 + rows) of p as a problem of its own.
@@ -817,6 +871,10 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t s) {
   if (p.row_stats != nullptr &&
       (p.col_sums == nullptr || (p.epi != VITBLK_EPI_NONE && p.epi != VITBLK_EPI_GELU)))
     return hipErrorInvalidValue;
+  if (p.epi == kEpiResidualStats) {
+    if (!gemm_row_partials_ok(p)) return hipErrorInvalidValue;
+    return launch_cfg<SmallTile>(p, s);
+  }
   if (!gemm_fast_ok(p)) return launch_gemm_generic(p, s);
   using Big = BigTile;
   using Small = SmallTile;

@@ -44,6 +44,10 @@ struct GemmProblem {
   // a residual product (null: none).  Its contents are clobbered.
   float* scratch;
   int64_t scratch_floats;
+  // kEpiResidualStats only: row_partials[m * (N / 64) + n / 64] = (mean, M2)
+  // of the stored (rounded) outputs of row m over columns [n, n + 64), n a
+  // multiple of 64 (M2 = the sum of squared deviations from that mean).
+  float2* row_partials;
 };
 
 // Internal epilogues of the backward (not part of the C interface):
@@ -54,6 +58,11 @@ constexpr int kEpiMul = 17;
 // kEpiPartial: split K.  Tile (m, n) of k-range s of ksplit equal ranges is
 // written, unrounded, to ((float*)C)[s * M * ldc + m * ldc + n]; no bias.
 constexpr int kEpiPartial = 18;
+// kEpiResidualStats: the residual epilogue, plus the row partials above (the
+// next LayerNorm's statistics, combined by launch_row_stats_from_partials).
+constexpr int kEpiResidualStats = 19;
+// Columns per row partial of kEpiResidualStats (every tile's wave strip).
+constexpr int kStatsStrip = 64;
 
 __host__ __device__ inline bool has_bias(const GemmProblem& p) {
   return p.bias[0] != nullptr || p.bias[1] != nullptr || p.bias[2] != nullptr;
@@ -61,7 +70,8 @@ __host__ __device__ inline bool has_bias(const GemmProblem& p) {
 
 // Epilogues that read R (the residual, or GELU's input for its derivative).
 __host__ __device__ inline bool reads_r(const GemmProblem& p) {
-  return p.epi == VITBLK_EPI_RESIDUAL || p.epi == VITBLK_EPI_GELU_GRAD || p.epi == kEpiMul;
+  return p.epi == VITBLK_EPI_RESIDUAL || p.epi == VITBLK_EPI_GELU_GRAD || p.epi == kEpiMul ||
+         p.epi == kEpiResidualStats;
 }
 
 // One (in, out) weight to write out-major: dst[c * ldd + r] = src[r * cols + c].
@@ -79,6 +89,15 @@ hipError_t launch_layernorm(const void* x, int64_t ld_in, const void* gamma, con
                             hipStream_t stream);
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
+
+// Whether the residual product p can also write its rows' partial statistics
+// (kEpiResidualStats) on the matrix-core kernel.
+bool gemm_row_partials_ok(const GemmProblem& p);
+
+// stats[2r], stats[2r + 1] = mean and 1 / sqrt(M2 / D + eps) of row r from its
+// nstrips = D / kStatsStrip partials (kEpiResidualStats), combined in order.
+hipError_t launch_row_stats_from_partials(const float2* partials, int64_t nstrips, float* stats,
+                                          int64_t rows, int64_t D, float eps, hipStream_t stream);
 
 // Whether the matrix-core kernels take p (otherwise the generic kernel does).
 bool gemm_fast_ok(const GemmProblem& p);

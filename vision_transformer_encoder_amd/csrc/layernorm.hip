@@ -233,6 +233,42 @@ hipError_t launch_row_stats(const void* x, int64_t ld_in, float* stats, int64_t 
                           s);
 }
 
+// A row's statistics from its per-strip partials (count, mean, M2), every
+// strip kStatsStrip values: folded left to right with Chan et al.'s update
+// (n_ab = n_a + n_b, mean_ab = mean_a + d n_b / n_ab, M2_ab = M2_a + M2_b +
+// d^2 n_a n_b / n_ab, d = mean_b - mean_a), then rstd = 1 / sqrt(M2 / D + eps)
+// (population variance, eps inside the root).  One thread per row.
+__global__ __launch_bounds__(256) void stats_from_partials_kernel(
+    const float2* __restrict__ P, int nstrips, float2* __restrict__ stats, int64_t rows,
+    float eps) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (r >= rows) return;
+  const float2* pr = P + r * nstrips;
+  const float nb = static_cast<float>(kStatsStrip);
+  float2 a = pr[0];
+  float n = nb, mean = a.x, m2 = a.y;
+  for (int k = 1; k < nstrips; ++k) {
+    const float2 b = pr[k];
+    const float nn = n + nb;
+    const float d = b.x - mean;
+    mean += d * (nb / nn);
+    m2 += b.y + d * d * (n * nb / nn);
+    n = nn;
+  }
+  stats[r] = make_float2(mean, 1.0f / sqrtf(m2 / n + eps));
+}
+
+hipError_t launch_row_stats_from_partials(const float2* partials, int64_t nstrips, float* stats,
+                                          int64_t rows, int64_t D, float eps, hipStream_t s) {
+  if (nstrips < 1 || nstrips * kStatsStrip != D || rows < 1) return hipErrorInvalidValue;
+  const int64_t blocks = (rows + 255) / 256;
+  if (blocks > 2147483647LL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(stats_from_partials_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256),
+                     0, s, partials, static_cast<int>(nstrips), reinterpret_cast<float2*>(stats),
+                     rows, eps);
+  return hipGetLastError();
+}
+
 hipError_t launch_layernorm(const void* x, int64_t ld_in, const void* gamma, const void* beta,
                             void* y, int64_t rows, int64_t D, float eps, int dtype,
                             hipStream_t s) {
