@@ -3,9 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload vit_l16]
                     [--variant plain|affine|encoder|embed|backward] [--layers L]
 
-A step is one full block forward (8 kernels through vitblk_forward: weight packing
-and the seven steps of the block) over one
-batch of synthetic inputs already resident in HBM.  Prints ONE JSON line:
+A step is one full block forward (vitblk_forward: the weights' packing with the
+first LayerNorm's statistics, then the block's steps, 11 launches at ViT-L/16) over
+one batch of synthetic inputs already resident in HBM.  Prints ONE JSON line:
 tokens/s for the whole job, ms per step, the block's achieved TFLOP/s and
 fraction of the bf16 dense MFMA peak, per-kernel times (each step's kernel
 timed alone with HIP events on the launch stream), the roofline of the
@@ -94,6 +94,8 @@ def parse():
                          "the front end, or the block backward")
     ap.add_argument("--layers", type=int, default=0,
                     help="encoder depth (default: 12 / 24 / 32 for ViT-B / L / H)")
+    ap.add_argument("--no-vendor-ref", action="store_true",
+                    help="skip the torch.mm (hipBLASLt) reference timings of the GEMM shapes")
     ap.add_argument("--profile-step", default=None,
                     help="run only a 512 MiB copy (counter calibration) and 3 launches of this "
                          "step's kernel, for rocprofv3 --pmc; prints no JSON")
@@ -537,22 +539,25 @@ def main():
     att_flops, att_bytes = 4 * w.N * w.T * w.T * D, 4 * M * D * es
     att_bound = ("hbm" if att_flops / att_bytes < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
                  else "mfma")
-    kern.update({
-        "attention": (lambda: vb.attention(qkv, w.N, w.T, w.H, out=att), att_bound,
-                      att_bytes if att_bound == "hbm" else att_flops),
-        "oproj_residual": (lambda: vb.linear(att, wo_t, vb.EPI_RESIDUAL, residual=x2,
-                                             bias=gq("b_o"), out=y), "mfma", 2 * M * D * D),
-    })
+    kern["attention"] = (lambda: vb.attention(qkv, w.N, w.T, w.H, out=att), att_bound,
+                         att_bytes if att_bound == "hbm" else att_flops)
     if affine or w.dtype != "bf16":
         kern.update({
+            "oproj_residual": (lambda: vb.linear(att, wo_t, vb.EPI_RESIDUAL, residual=x2,
+                                                 bias=gq("b_o"), out=y), "mfma", 2 * M * D * D),
             "ln2": (lambda: vb.layernorm(y, w.eps, gamma=gq("ln2_gamma"), beta=gq("ln2_beta"),
                                          out=yn), "hbm", 2 * M * D * es),
             "mlp1_gelu": (lambda: vb.linear(yn, w1_t, vb.EPI_GELU, bias=gq("b_mlp1"), out=hid),
                           "mfma", 2 * M * D * F),
         })
     else:
+        # The output projection writes the LN2 row statistics' partials from
+        # its epilogue and one small kernel combines them, as in the block.
+        ows = torch.empty(vb.linear_residual_row_stats_workspace_bytes(M, D), dtype=torch.uint8,
+                          device=dev)
         kern.update({
-            "ln2_stats": (lambda: vb.row_stats(y, w.eps, out=st2), "hbm", M * D * es + M * 8),
+            "oproj_residual_ln2_stats": (lambda: vb.linear_residual_row_stats(
+                att, wo_t, x2, w.eps, out=y, stats=st2, workspace=ows), "mfma", 2 * M * D * D),
             "mlp1_gelu": (lambda: vb.linear_normed(y, w1_t, cs_1, st2, vb.EPI_GELU, out=hid),
                           "mfma", 2 * M * D * F),
         })
@@ -583,6 +588,21 @@ def main():
         if name == "attention":  # both rates: its bound moves with T
             per[name]["tflops"] = round(att_flops / (kms * 1e-3) / 1e12, 2)
             per[name]["gbs"] = round(att_bytes / (kms * 1e-3) / 1e9, 2)
+    vendor = None
+    if w.dtype == "bf16" and not a.no_vendor_ref:
+        # Reference only, never on the product path: torch.mm (hipBLASLt) on
+        # operands of the four products' shapes, plain products without the
+        # fused epilogues -- what the vendor library reaches on these shapes.
+        vendor = {}
+        for vname, (kk, nn) in {"qkv": (D, 3 * D), "oproj": (D, D), "mlp1": (D, F),
+                                "mlp2": (F, D)}.items():
+            va = torch.randn(M, kk, device=dev).to(tdt)
+            vw = (torch.randn(kk, nn, device=dev) / math.sqrt(kk)).to(tdt).contiguous()
+            vo = torch.empty(M, nn, device=dev, dtype=tdt)
+            vms = time_launches(lambda: torch.mm(va, vw, out=vo), a.kernel_reps, torch)
+            vendor[vname] = {"ms": round(vms, 5),
+                             "tflops": round(2 * M * kk * nn / (vms * 1e-3) / 1e12, 2)}
+            del va, vw, vo
     dom = max(per, key=lambda k: per[k]["ms"])
     fn, bound, work = kern[dom]
     dms = per[dom]["ms"]
@@ -629,6 +649,8 @@ def main():
     }
     if cls_only is not None:
         res["cls_only"] = cls_only
+    if vendor is not None:
+        res["vendor_gemm_ref"] = vendor
     if a.cpu_seconds > 0:
         import oracle
         if encoder:

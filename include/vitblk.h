@@ -374,6 +374,28 @@ int vitblk_linear_normed(const void* a, const void* w_t, const float* col_sums,
                          int64_t K, int64_t Nout, int epilogue, int dtype,
                          vitblk_stream_t stream);
 
+/* The output projection with the first residual and the second LayerNorm's
+ * statistics: out = residual + a @ W (a [M, K], w_t [Nout, K] out-major as
+ * for vitblk_linear(), residual and out [M, Nout]), then row_stats[2m],
+ * row_stats[2m + 1] = mean and 1 / sqrt(var + eps) of row m of out as stored
+ * (population variance), the pair vitblk_linear_normed() takes.
+ * crackedaicode.com "ViT Encoder Block", "Multi-head attention" (y = x +
+ * attention @ w_o) and "Feed-forward stage" (LN of y).  In bf16 with Nout a
+ * multiple of 64 the product's epilogue writes each row's (mean, M2) over
+ * every 64 columns into the workspace and one small kernel combines them
+ * (the raw second moment of 32 values per lane: relative error of the
+ * variance about 2^-19 (1 + mean^2 / var)); otherwise the plain product is
+ * followed by vitblk_row_stats()'s kernel.  workspace: at least
+ * vitblk_linear_residual_row_stats_workspace_bytes(M, Nout) bytes, 16-byte
+ * aligned, its contents clobbered.  row_stats is fp32, 8-byte aligned; no
+ * output may overlap an input, the other output or the workspace. */
+size_t vitblk_linear_residual_row_stats_workspace_bytes(int64_t M, int64_t Nout);
+
+int vitblk_linear_residual_row_stats(const void* a, const void* w_t, const void* residual,
+                                     void* out, float* row_stats, int64_t M, int64_t K,
+                                     int64_t Nout, double eps, int dtype, void* workspace,
+                                     size_t workspace_bytes, vitblk_stream_t stream);
+
 /* qkv = xn @ [w_q | w_k | w_v]: xn [M, D], w_qkv_t [3D, D] (the first
  * region of the packed weights), qkv [M, 3D] (one row holds a token's Q, K
  * and V, each as H consecutive head chunks).  crackedaicode.com "ViT Encoder

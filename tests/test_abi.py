@@ -187,6 +187,23 @@ def test_step_entry_points_errors(lib):
     assert ln(a, b, c, d, None, c, 4, 8, 8, vb.EPI_GELU, 1, None) == ALIAS
     assert ln(a, b, c, d, None, d, 4, 8, 8, vb.EPI_NONE, 1, None) == ALIAS
     assert ln(a, b, c, d, None, a, 4, 8, 8, vb.EPI_NONE, 1, None) == ALIAS
+    # the output projection with the next LayerNorm's statistics: residual
+    # required, stats 8-byte aligned, a workspace of one pair per 64 columns
+    rs = lambda *args: lib.vitblk_linear_residual_row_stats(*args)  # noqa: E731
+    need = lib.vitblk_linear_residual_row_stats_workspace_bytes(4, 128)
+    assert need == 4 * 2 * 8
+    assert lib.vitblk_linear_residual_row_stats_workspace_bytes(4, 130) == 4 * 3 * 8
+    assert lib.vitblk_linear_residual_row_stats_workspace_bytes(0, 128) == 0
+    ws = _addr(9)
+    assert rs(a, b, None, c, d, 4, 8, 128, 1e-6, 1, ws, need, None) == INVALID
+    assert rs(a, b, e, c, None, 4, 8, 128, 1e-6, 1, ws, need, None) == INVALID
+    assert rs(a, b, e, c, off(d, 4), 4, 8, 128, 1e-6, 1, ws, need, None) == INVALID
+    assert rs(a, b, e, c, d, 4, 8, 128, -1.0, 1, ws, need, None) == INVALID
+    assert rs(a, b, e, c, d, 4, 8, 128, 1e-6, 1, ws, need - 1, None) == WORKSPACE
+    assert rs(a, b, e, c, d, 4, 8, 128, 1e-6, 1, None, need, None) == WORKSPACE
+    assert rs(a, b, e, c, c, 4, 8, 128, 1e-6, 1, ws, need, None) == ALIAS
+    assert rs(a, b, e, c, d, 4, 8, 128, 1e-6, 1, c, need, None) == ALIAS
+    assert rs(a, b, e, c, d, 4, 8, 128, 1e-6, 1, e, need, None) == ALIAS
 
 
 def test_affine_entry_points_errors(lib):

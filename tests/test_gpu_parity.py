@@ -125,6 +125,37 @@ def test_linear_with_ragged_tail_rows(epi):
     assert_close(got, ref, "bf16", f"linear {epi} M={M}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("M,K,N,offset", [(300, 256, 512, 0.0), (2000, 1024, 1024, 1.5),
+                                          (70 * 256 + 77, 256, 1024, 4.0), (129, 320, 320, 0.5),
+                                          (50, 40, 24, 0.0), (7, 64, 136, 2.0)])
+def test_linear_residual_row_stats(dtype, M, K, N, offset):
+    # The output projection with the first residual and the second
+    # LayerNorm's row statistics of the stored y ([CAC] "Multi-head
+    # attention", "Feed-forward stage").  bf16 with N a multiple of 64 takes
+    # the fused epilogue partials; other shapes and fp32 the plain product and
+    # the statistics kernel.  The statistics are held to the float64 oracle's
+    # of the same stored values; the residual rows carry a mean offset of
+    # `offset` standard deviations.
+    if dtype == "fp32" and M > 10000:
+        pytest.skip("the big ragged case exercises the bf16 tile split only")
+    rng = np.random.default_rng(M + 5 * K + 11 * N)
+    a = _rand(rng, (M, K), dtype)
+    w = _rand(rng, (K, N), dtype, scale=1 / math.sqrt(K))
+    r = _rand(rng, (M, N), dtype, scale=1.0, offset=offset)
+    y, st = vb.linear_residual_row_stats(to_dev(a, dtype), to_dev(w.T, dtype), to_dev(r, dtype),
+                                         1e-6)
+    y = to_host(y)
+    assert_close(y, r + oracle.project(a, w), dtype, f"y M={M} K={K} N={N}")
+    mean, rstd = oracle.layer_norm_stats(y, 1e-6)  # of the values as stored
+    got = to_host(st)
+    std = 1.0 / rstd
+    dm = np.max(np.abs(got[:, 0] - mean) / (np.abs(mean) + std))
+    dr = np.max(np.abs(got[:, 1] / rstd - 1.0))
+    print(f"  stats: mean {dm:.2e} (of |mean| + std), rstd {dr:.2e} (relative)", flush=True)
+    assert dm <= 2e-6 and dr <= 1e-4
+
+
 def _attention_ref(q, k, v, H):
     a = oracle.softmax_rows(oracle.attention_scores(oracle.split_heads(q, H),
                                                     oracle.split_heads(k, H)))

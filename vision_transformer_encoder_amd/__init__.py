@@ -35,6 +35,8 @@ from ._lib import (  # noqa: F401
     layernorm_backward,
     linear,
     linear_normed,
+    linear_residual_row_stats,
+    linear_residual_row_stats_workspace_bytes,
     load,
     pack_weights,
     packed_col_sums,

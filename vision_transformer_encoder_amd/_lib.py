@@ -50,6 +50,8 @@ SIGNATURES = {
     "vitblk_linear_bias": (_I, [_P] * 5 + [_I64, _I64, _I64, _I, _I, _P]),
     "vitblk_row_stats": (_I, [_P, _P, _I64, _I64, _D, _I, _P]),
     "vitblk_linear_normed": (_I, [_P] * 6 + [_I64, _I64, _I64, _I, _I, _P]),
+    "vitblk_linear_residual_row_stats_workspace_bytes": (_SZ, [_I64, _I64]),
+    "vitblk_linear_residual_row_stats": (_I, [_P] * 5 + [_I64] * 3 + [_D, _I, _P, _SZ, _P]),
     "vitblk_encoder_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64, _I]),
     "vitblk_patch_embed_workspace_bytes": (_SZ, [_I64] * 6 + [_I]),
     "vitblk_patch_embed": (_I, [_P] * 6 + [_I64] * 6 + [_I, _P, _SZ, _P]),
@@ -644,6 +646,41 @@ def linear_normed(a, w_t, col_sums, stats, epilogue: int = EPI_NONE, bias=None, 
                                      _stream(a, stream))
     _check("vitblk_linear_normed", st)
     return out
+
+
+def linear_residual_row_stats_workspace_bytes(M, Nout) -> int:
+    return int(load().vitblk_linear_residual_row_stats_workspace_bytes(M, Nout))
+
+
+def linear_residual_row_stats(a, w_t, residual, eps: float, out=None, stats=None,
+                              workspace=None, stream=None):
+    """(out, stats): out = residual + a @ W (W out-major, w_t [Nout, K]) and each
+    row's (mean, 1 / sqrt(var + eps)) of out as stored, fp32 [M, 2]."""
+    torch = _torch()
+    K = a.shape[-1]
+    M = a.numel() // K
+    _rank(w_t, 2, "w_t")
+    Nout = w_t.shape[0]
+    _shape(w_t, (Nout, K), "w_t")
+    _shape(residual, (M, Nout), "residual")
+    _shape(out, (M, Nout), "out")
+    _shape(stats, (M, 2), "stats")
+    need = linear_residual_row_stats_workspace_bytes(M, Nout)
+    _buffer(workspace, a, need, "workspace")
+    _dev(a, w_t, residual, out)
+    _dev_f32(a, stats)
+    if out is None:
+        out = torch.empty((M, Nout), dtype=a.dtype, device=a.device)
+    if stats is None:
+        stats = torch.empty((M, 2), dtype=torch.float32, device=a.device)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=a.device)
+    st = load().vitblk_linear_residual_row_stats(
+        _ptr(a), _ptr(w_t), _ptr(residual), _ptr(out), _ptr(stats), M, K, Nout, float(eps),
+        dtype_code(a.dtype), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(a, stream))
+    _check("vitblk_linear_residual_row_stats", st)
+    return out, stats
 
 
 # ------------------------------------------------------------------ backward

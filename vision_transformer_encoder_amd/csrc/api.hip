@@ -649,6 +649,34 @@ int vitblk_linear_normed(const void* a, const void* w_t, const float* col_sums,
   return VITBLK_OK;
 }
 
+size_t vitblk_linear_residual_row_stats_workspace_bytes(int64_t M, int64_t Nout) {
+  return linear_stats_workspace_bytes(M, Nout);
+}
+
+int vitblk_linear_residual_row_stats(const void* a, const void* w_t, const void* residual,
+                                     void* out, float* row_stats, int64_t M, int64_t K,
+                                     int64_t Nout, double eps, int dtype, void* workspace,
+                                     size_t workspace_bytes, vitblk_stream_t stream) {
+  const int st = validate_linear_residual_stats(a, w_t, residual, out, row_stats, M, K, Nout, eps,
+                                                dtype, workspace, workspace_bytes);
+  if (st != VITBLK_OK) return st;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const float feps = static_cast<float>(eps);
+  GemmProblem p = linear_problem(a, w_t, out, residual, M, K, Nout, VITBLK_EPI_RESIDUAL, dtype);
+  p.row_partials = static_cast<float2*>(workspace);
+  if (gemm_row_partials_ok(p)) {
+    p.epi = kEpiResidualStats;
+    VITBLK_LAUNCH(launch_gemm(p, s));
+    VITBLK_LAUNCH(launch_row_stats_from_partials(p.row_partials, Nout / kStatsStrip, row_stats, M,
+                                                 Nout, feps, s));
+    return VITBLK_OK;
+  }
+  p.row_partials = nullptr;
+  VITBLK_LAUNCH(launch_gemm(p, s));
+  VITBLK_LAUNCH(launch_row_stats(out, Nout, row_stats, M, Nout, feps, dtype, s));
+  return VITBLK_OK;
+}
+
 int vitblk_qkv_projection(const void* xn, const void* w_qkv_t, void* qkv, int64_t M, int64_t D,
                           int dtype, vitblk_stream_t stream) {
   const int st = validate_qkv(xn, w_qkv_t, qkv, M, D, dtype);

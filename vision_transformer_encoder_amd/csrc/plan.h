@@ -102,6 +102,15 @@ int validate_row_stats(const void* x, const float* stats, int64_t rows, int64_t 
 int validate_linear_normed(const void* a, const void* w, const float* col_sums,
                            const float* row_stats, const void* bias, const void* out, int64_t M,
                            int64_t K, int64_t Nout, int epilogue, int dtype);
+// Workspace of vitblk_linear_residual_row_stats: one (mean, M2) pair per row
+// and 64 columns.  0 for invalid sizes.
+size_t linear_stats_workspace_bytes(int64_t M, int64_t Nout);
+
+int validate_linear_residual_stats(const void* a, const void* w, const void* residual,
+                                   const void* out, const float* stats, int64_t M, int64_t K,
+                                   int64_t Nout, double eps, int dtype, const void* workspace,
+                                   size_t workspace_bytes);
+
 int validate_linear(const void* a, const void* w, const void* bias, const void* residual,
                     const void* out, int64_t M, int64_t K, int64_t Nout, int epilogue,
                     int dtype);

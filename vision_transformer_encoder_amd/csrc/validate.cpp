@@ -350,6 +350,38 @@ int validate_linear(const void* a, const void* w, const void* bias, const void* 
   return VITBLK_OK;
 }
 
+size_t linear_stats_workspace_bytes(int64_t M, int64_t Nout) {
+  if (!dim_ok(M) || !dim_ok(Nout) || M > kMaxDim || Nout > kMaxDim) return 0;
+  const size_t strips = (static_cast<size_t>(Nout) + 63) / 64;
+  return static_cast<size_t>(M) * strips * 2 * sizeof(float);
+}
+
+int validate_linear_residual_stats(const void* a, const void* w, const void* residual,
+                                   const void* out, const float* stats, int64_t M, int64_t K,
+                                   int64_t Nout, double eps, int dtype, const void* workspace,
+                                   size_t workspace_bytes) {
+  int st = validate_linear(a, w, nullptr, residual, out, M, K, Nout, VITBLK_EPI_RESIDUAL, dtype);
+  if (st != VITBLK_OK) return st;
+  if (stats == nullptr || (reinterpret_cast<uintptr_t>(stats) & 7u) != 0)
+    return VITBLK_ERR_INVALID_ARG;
+  st = check_eps(eps);
+  if (st != VITBLK_OK) return st;
+  const size_t need = linear_stats_workspace_bytes(M, Nout);
+  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need)
+    return VITBLK_ERR_WORKSPACE;
+  const size_t es = elem_size(dtype);
+  const size_t m = static_cast<size_t>(M), k = static_cast<size_t>(K);
+  const size_t n = static_cast<size_t>(Nout);
+  const Span so = span(stats, m * 2 * sizeof(float)), ws = span(workspace, need);
+  const Span o = span(out, m * n * es), sa = span(a, m * k * es), sw = span(w, k * n * es),
+             sr = span(residual, m * n * es);
+  if (overlap(so, o) || overlap(so, sa) || overlap(so, sw) || overlap(so, sr) ||
+      overlap(so, ws) || overlap(ws, o) || overlap(ws, sa) || overlap(ws, sw) ||
+      overlap(ws, sr))
+    return VITBLK_ERR_ALIAS;
+  return VITBLK_OK;
+}
+
 int validate_row_stats(const void* x, const float* stats, int64_t rows, int64_t D, double eps,
                        int dtype) {
   if (x == nullptr || stats == nullptr || !aligned16(x)) return VITBLK_ERR_INVALID_ARG;
