@@ -26,9 +26,15 @@
  * ---------------------------------------
  * - Pointers named x, w_*, out, qkv, ... are DEVICE pointers (HIP global
  *   memory) on the current device, owned by the caller.  The library never
- *   allocates, frees or retains memory, holds no state between calls, and is
- *   re-entrant.  Calls enqueue on `stream` (0 = the null stream) and return
- *   without synchronising; the caller synchronises before reading results.
+ *   allocates or frees memory and keeps no caller data between calls; the
+ *   only exception to "no device memory of its own" is the scratch array of
+ *   vitblk_forward_packed_noalloc() (see there).  Its only host state is
+ *   per-process launch configuration computed on first use (each kernel's
+ *   resident workgroup count and dynamic-LDS attribute, the scratch array's
+ *   address per device): written once with the same value by whichever call
+ *   comes first, so concurrent calls from several threads are safe.  Calls
+ *   enqueue on `stream` (0 = the null stream) and return without
+ *   synchronising; the caller synchronises before reading results.
  * - All tensors are dense, row-major and contiguous in the element type given
  *   by `dtype` (VITBLK_FP32: IEEE float; VITBLK_BF16: bfloat16 stored as its
  *   16-bit pattern).  Device pointers must be aligned to 16 bytes.

@@ -12,6 +12,8 @@
 // T-1 when loaded (finite values) and their scores set to -inf.
 #include <math.h>
 
+#include <atomic>
+
 #include "attention_tile.h"
 #include "device.h"
 #include "kernels.h"
@@ -134,15 +136,15 @@ hipError_t launch_stream(const void* q, const void* k, const void* v, int64_t ld
                          int64_t max_qt = 0) {
   using C = attn::Cfg<DH>;
   constexpr size_t bytes = 2 * 64 * C::ROW;
-  static bool attr_set = false;
-  if (!attr_set) {
+  static std::atomic<bool> attr_set{false};  // set once, idempotent
+  if (!attr_set.load(std::memory_order_relaxed)) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_stream_kernel<DH, W>),
                             hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(bytes)) != hipSuccess) {
       (void)hipGetLastError();
       return hipErrorNotSupported;
     }
-    attr_set = true;
+    attr_set.store(true, std::memory_order_relaxed);
   }
   int64_t nqt = (T + 31) / 32;
   if (max_qt > 0 && nqt > max_qt) nqt = max_qt;  // the kernel then skips waves past tpb

@@ -38,6 +38,8 @@
 // a one-key row gets P = 1 exactly.
 #include <math.h>
 
+#include <atomic>
+
 #include "device.h"
 #include "kernels.h"
 #include "vitblk.h"
@@ -365,8 +367,8 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, int64_t ld, c
   const int64_t bytes_dq = 2 * T_pad * C::SR + slack;
   const int64_t bytes_dkv = 2 * T_pad * C::SR + T_pad * 16 + slack;
   if (bytes_dq > kLds || bytes_dkv > kLds) return hipErrorNotSupported;
-  static bool attr_set = false;
-  if (!attr_set) {
+  static std::atomic<bool> attr_set{false};  // set once, idempotent
+  if (!attr_set.load(std::memory_order_relaxed)) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<DH>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLds) != hipSuccess ||
         hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dkv_kernel<DH>),
@@ -374,7 +376,7 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, int64_t ld, c
       (void)hipGetLastError();
       return hipErrorNotSupported;
     }
-    attr_set = true;
+    attr_set.store(true, std::memory_order_relaxed);
   }
   const int64_t tiles = T_pad / 32;
   const int per_wave = static_cast<int>((tiles + kMaxWaves - 1) / kMaxWaves);

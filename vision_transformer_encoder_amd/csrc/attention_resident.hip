@@ -15,6 +15,8 @@
 // T-1 (finite values) and their scores are set to -inf.
 #include <math.h>
 
+#include <atomic>
+
 #include "attention_tile.h"
 #include "device.h"
 #include "kernels.h"
@@ -111,8 +113,8 @@ hipError_t launch_res(const void* q, const void* k, const void* v, int64_t ld, v
   const int64_t T_pad = (T + 31) / 32 * 32;
   const int64_t bytes = T_pad * C::ROW;
   if (bytes > kLdsBytes) return hipErrorNotSupported;
-  static bool attr_set = false;
-  if (!attr_set) {
+  static std::atomic<bool> attr_set{false};  // set once, idempotent
+  if (!attr_set.load(std::memory_order_relaxed)) {
     const hipError_t e = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&attn_resident_kernel<DH>),
         hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
@@ -120,7 +122,7 @@ hipError_t launch_res(const void* q, const void* k, const void* v, int64_t ld, v
       (void)hipGetLastError();  // clear it: the caller falls back to the streaming kernel
       return hipErrorNotSupported;
     }
-    attr_set = true;
+    attr_set.store(true, std::memory_order_relaxed);
   }
   const int64_t nqt = T_pad / 32;
   const int per_wave = static_cast<int>((nqt + kMaxWaves - 1) / kMaxWaves);

@@ -49,6 +49,8 @@
 //   XCD is given a contiguous run of tiles per round, walked in groups of 8
 //   M-tiles so that the tiles resident at once on an XCD share A and W
 //   panels in its L2.
+#include <atomic>
+
 #include "device.h"
 #include "kernels.h"
 #include "vitblk.h"
@@ -695,8 +697,9 @@ __global__ __launch_bounds__(256) void splitk_residual_kernel(const float* __res
 // Workgroups of this kernel the device holds at once (cached per kernel).
 template <class C, int EPI, bool BIAS = false, bool NORM = false>
 int resident_workgroups() {
-  static int cached = 0;
-  if (cached == 0) {
+  static std::atomic<int> cached{0};  // computed once, the same value by any thread
+  int value = cached.load(std::memory_order_relaxed);
+  if (value == 0) {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -707,9 +710,10 @@ int resident_workgroups() {
       (void)hipGetLastError();
       return 0;
     }
-    cached = cus * (per_cu > 0 ? per_cu : 1);
+    value = cus * (per_cu > 0 ? per_cu : 1);
+    cached.store(value, std::memory_order_relaxed);
   }
-  return cached;
+  return value;
 }
 
 template <class C, int EPI, bool BIAS, bool NORM = false>
