@@ -44,6 +44,8 @@ if ROOT not in sys.path:
 METRIC = "encoder-block fwd tokens/sec + % bf16 MFMA peak, ViT-L/16 shape N=256"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector (published; counts packed FMA, which this
+                            # build does not emit, so its fp32 kernels top out at half)
 # Measured HBM traffic of the dominant step (rocprofv3 FETCH_SIZE / WRITE_SIZE,
 # calibrated on a plain copy); used only while the kernel source is unchanged.
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "vit_l16_mlp1_gelu_traffic.json")
@@ -94,6 +96,9 @@ def parse():
                          "the front end, or the block backward")
     ap.add_argument("--layers", type=int, default=0,
                     help="encoder depth (default: 12 / 24 / 32 for ViT-B / L / H)")
+    ap.add_argument("--dtype", choices=["bf16", "fp32"], default=None,
+                    help="element type (default: the workload's own; fp32 runs the generic "
+                         "VALU kernels, a correctness path whose speed is reported, not tuned)")
     ap.add_argument("--no-vendor-ref", action="store_true",
                     help="skip the torch.mm (hipBLASLt) reference timings of the GEMM shapes")
     ap.add_argument("--profile-step", default=None,
@@ -407,6 +412,9 @@ def main():
     if a.profile_step:  # counters only: one untimed block, then the step alone
         a.warmup, a.steps, a.cpu_seconds = 0, 1, 0
     w = WORKLOADS[a.workload]
+    if a.dtype and a.dtype != w.dtype:
+        # The same shapes in another element type (fp32: the generic VALU kernels).
+        w = w.with_(dtype=a.dtype)
     if a.variant == "embed":
         torch.cuda.set_device(torch.device("cuda:0"))
         return bench_embed(a, w, torch, vb)
@@ -537,8 +545,10 @@ def main():
     # (Q, K, V read, O written), an intensity of about T / es FLOP per byte,
     # below the ridge (peak FLOP/s / peak bytes/s) at ViT sequence lengths.
     att_flops, att_bytes = 4 * w.N * w.T * w.T * D, 4 * M * D * es
-    att_bound = ("hbm" if att_flops / att_bytes < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-                 else "mfma")
+    att_peak, att_unit = ((PEAK_BF16_TFLOPS, "mfma") if w.dtype == "bf16"
+                          else (PEAK_FP32_TFLOPS, "alu"))
+    att_bound = ("hbm" if att_flops / att_bytes < att_peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+                 else att_unit)
     kern["attention"] = (lambda: vb.attention(qkv, w.N, w.T, w.H, out=att), att_bound,
                          att_bytes if att_bound == "hbm" else att_flops)
     if affine or w.dtype != "bf16":
@@ -578,13 +588,17 @@ def main():
         print(f"profiled {a.profile_step}", file=sys.stderr)
         return
 
+    if w.dtype == "fp32":
+        # fp32 products run on the VALU (generic kernels).
+        kern = {k: (fn, "alu" if bound == "mfma" else bound, work)
+                for k, (fn, bound, work) in kern.items()}
     per = {}
     for name, (fn, bound, work) in kern.items():
         kms = time_launches(fn, a.kernel_reps, torch)
         rate = work / (kms * 1e-3)
         per[name] = {"ms": round(kms, 5), "bound": bound,
-                     ("tflops" if bound == "mfma" else "gbs"):
-                     round(rate / (1e12 if bound == "mfma" else 1e9), 2)}
+                     ("gbs" if bound == "hbm" else "tflops"):
+                     round(rate / (1e9 if bound == "hbm" else 1e12), 2)}
         if name == "attention":  # both rates: its bound moves with T
             per[name]["tflops"] = round(att_flops / (kms * 1e-3) / 1e12, 2)
             per[name]["gbs"] = round(att_bytes / (kms * 1e-3) / 1e9, 2)
@@ -606,12 +620,14 @@ def main():
     dom = max(per, key=lambda k: per[k]["ms"])
     fn, bound, work = kern[dom]
     dms = per[dom]["ms"]
-    if bound == "mfma":
+    if bound in ("mfma", "alu"):
         ach = work / (dms * 1e-3) / 1e12
-        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                "traffic": None if affine else recorded_traffic(dom, w.name),
+        pk = PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_FP32_TFLOPS
+        roof = {"kernel": dom, "bound": bound, "achieved": round(ach, 2),
+                "peak": pk, "unit": "TFLOP/s",
+                "frac": round(ach / pk, 4),
+                "traffic": (None if affine or w.dtype != "bf16"
+                            else recorded_traffic(dom, w.name)),
                 "work_per_launch": f"{work / 1e9:.2f} GFLOP"}
     else:
         ach = work / (dms * 1e-3) / 1e9
@@ -623,8 +639,10 @@ def main():
     flops = L * block_flops(w.N, w.T, w.D, w.F)
     tflops = flops / (ms * 1e-3) / 1e12
     res = {
-        "metric": METRIC if not encoder else
-        f"encoder-stack fwd tokens/sec ({L} blocks + final LN), {w.name} shape N={w.N}",
+        "metric": (f"encoder-stack fwd tokens/sec ({L} blocks + final LN), {w.name} shape N={w.N}"
+                   if encoder else METRIC if w.dtype == "bf16" and w.name == "vit_l16" and
+                   not affine else f"encoder-block fwd tokens/sec, {w.name} shape N={w.N}, "
+                   f"{w.dtype}{', affine' if affine else ''}"),
         "value": round(w.M / (ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -647,6 +665,8 @@ def main():
         "kernels": per,
         "roofline": roof,
     }
+    if w.dtype == "fp32":
+        res["block_frac_fp32_vector_peak"] = round(tflops / PEAK_FP32_TFLOPS, 4)
     if cls_only is not None:
         res["cls_only"] = cls_only
     if vendor is not None:
