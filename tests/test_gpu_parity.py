@@ -178,8 +178,11 @@ def _attention_ref(q, k, v, H):
     (2, 33, 96, 3),      # d_h 32, one key past a 32-block
     (2, 65, 256, 2),     # d_h 128
     (2, 96, 192, 2),     # d_h 96, T a multiple of 32 but not 64
-    (2, 50, 24, 3),      # d_h 8 (generic kernel)
-    (1, 7, 48, 1),       # d_h 48 (generic kernel)
+    (2, 50, 24, 3),      # d_h 8 (tiled VALU kernel)
+    (1, 7, 48, 1),       # d_h 48 (tiled VALU kernel)
+    (1, 300, 40, 1),     # d_h 40: two query blocks, ragged last key chunk (tiled VALU)
+    (2, 40, 36, 3),      # d_h 12: no tiled instantiation (one query per wave)
+    (1, 70, 320, 2),     # d_h 160: no tiled instantiation (one query per wave)
 ])
 def test_attention(dtype, N, T, D, H):
     rng = np.random.default_rng(N * 100000 + T * 100 + D)

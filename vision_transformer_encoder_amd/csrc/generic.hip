@@ -2,7 +2,7 @@
 //
 // They serve fp32 tensors (the fp32 tolerance rules out bf16 products) and
 // bf16 shapes the MFMA kernels do not tile (D or F not a multiple of 64,
-// odd head widths).  Simple, bounds-checked, not tuned.
+// odd head widths).  Bounds-checked; only attention is tiled for speed.
 #include <math.h>
 
 #include "device.h"
@@ -213,6 +213,167 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(const T* __restrict__ 
   }
 }
 
+// Tiled attention on the VALU, fp32 arithmetic (fp32 tensors; bf16 head widths
+// the matrix-core kernels do not take).  One workgroup of 256 threads per
+// (sequence, head, block of 256 / G queries); G threads per query, each
+// holding DH / G features of the query (pre-scaled by log2(e) / sqrt(dh)) and
+// of its output row.  Keys pass in chunks of kVKeys through two LDS stages
+// (fp32), read as broadcasts (every thread of a pair group reads the same
+// key row); each thread's share of the next chunk is requested before the
+// work on the current one and written to the other stage after, one barrier
+// per chunk.  Online softmax per query, key by key: a running maximum and
+// sum, the sum and the accumulators rescaled when a key's score exceeds the
+// maximum (exp2 of the pre-scaled scores); keys past T are not visited.
+constexpr int kVKeys = 32;
+constexpr int kVThreads = 256;
+
+template <typename T, int DH, int G>
+__global__ __launch_bounds__(kVThreads) void attn_valu_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, int64_t ld,
+    T* __restrict__ o, int64_t ldo, int T_, int H, int qblocks, float scale_log2) {
+  constexpr int DL = DH / G;                  // features per thread
+  constexpr int QPB = kVThreads / G;          // queries per workgroup
+  constexpr int PER = kVKeys * DH / kVThreads;  // chunk elements per thread and operand
+  static_assert(DH % G == 0 && DL % 4 == 0 && (kVKeys * DH) % kVThreads == 0, "layout");
+  static_assert(G == 1 || G == 2, "one or two threads per query");
+  extern __shared__ __attribute__((aligned(16))) float kvs[];  // [2 stages][K | V][kVKeys][DH]
+  constexpr int STAGE = 2 * kVKeys * DH;
+
+  const int tid = threadIdx.x;
+  int64_t b = blockIdx.x;
+  const int qb = static_cast<int>(b % qblocks);
+  b /= qblocks;
+  const int h = static_cast<int>(b % H);
+  const int64_t base = (b / H) * static_cast<int64_t>(T_);
+  const int tq = qb * QPB + tid / G;  // this thread's query
+  const int foff = (tid % G) * DL;    // its features
+  const int tqc = tq < T_ ? tq : T_ - 1;
+
+  float qr[DL], acc[DL];
+  const T* qrow = q + (base + tqc) * ld + static_cast<int64_t>(h) * DH + foff;
+#pragma unroll
+  for (int c = 0; c < DL; ++c) {
+    qr[c] = load_f32(qrow + c) * scale_log2;
+    acc[c] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+
+  float rk[PER], rv[PER];
+  auto fetch = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + i * kVThreads;
+      int key = c0 + e / DH;
+      key = key < T_ ? key : T_ - 1;
+      const int64_t g = (base + key) * ld + static_cast<int64_t>(h) * DH + e % DH;
+      rk[i] = load_f32(k + g);
+      rv[i] = load_f32(v + g);
+    }
+  };
+  auto stash = [&](int st) {
+    float* ks = kvs + st * STAGE;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + i * kVThreads;
+      ks[e] = rk[i];
+      ks[kVKeys * DH + e] = rv[i];
+    }
+  };
+
+  const int nchunks = (T_ + kVKeys - 1) / kVKeys;
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int c = 0; c < nchunks; ++c) {
+    if (c + 1 < nchunks) fetch((c + 1) * kVKeys);
+    const float* ks = kvs + (c & 1) * STAGE;
+    const float* vs = ks + kVKeys * DH;
+    int nvalid = T_ - c * kVKeys;  // keys of this chunk below T (>= 1)
+    nvalid = nvalid < kVKeys ? nvalid : kVKeys;
+#pragma unroll 2
+    for (int j = 0; j < nvalid; ++j) {
+      const float4* kr = reinterpret_cast<const float4*>(ks + j * DH + foff);
+      float d = 0.f;
+#pragma unroll
+      for (int c4 = 0; c4 < DL / 4; ++c4) {
+        const float4 kk = kr[c4];
+        d = fmaf(qr[4 * c4 + 0], kk.x, d);
+        d = fmaf(qr[4 * c4 + 1], kk.y, d);
+        d = fmaf(qr[4 * c4 + 2], kk.z, d);
+        d = fmaf(qr[4 * c4 + 3], kk.w, d);
+      }
+      if (G == 2) d += __shfl_xor(d, 1);
+      // A new maximum rescales the running sum and the accumulators (the
+      // first key always does: m starts at -inf).
+      if (d > m) {
+        const float alpha = exp2f(m - d);
+        l *= alpha;
+#pragma unroll
+        for (int c2 = 0; c2 < DL; ++c2) acc[c2] *= alpha;
+        m = d;
+      }
+      const float p = exp2f(d - m);
+      l += p;
+      const float4* vr = reinterpret_cast<const float4*>(vs + j * DH + foff);
+#pragma unroll
+      for (int c4 = 0; c4 < DL / 4; ++c4) {
+        const float4 vv = vr[c4];
+        acc[4 * c4 + 0] = fmaf(p, vv.x, acc[4 * c4 + 0]);
+        acc[4 * c4 + 1] = fmaf(p, vv.y, acc[4 * c4 + 1]);
+        acc[4 * c4 + 2] = fmaf(p, vv.z, acc[4 * c4 + 2]);
+        acc[4 * c4 + 3] = fmaf(p, vv.w, acc[4 * c4 + 3]);
+      }
+    }
+    if (c + 1 < nchunks) stash((c + 1) & 1);
+    __syncthreads();
+  }
+  if (tq < T_) {
+    const float inv = 1.0f / l;
+    T* orow = o + (base + tq) * ldo + static_cast<int64_t>(h) * DH + foff;
+#pragma unroll
+    for (int c = 0; c < DL; ++c) store_f32(orow + c, acc[c] * inv);
+  }
+}
+
+template <typename E, int DH, int G>
+hipError_t launch_attn_valu(const void* q, const void* k, const void* v, int64_t ld, void* o,
+                            int64_t ldo, int64_t N, int64_t T, int64_t H, hipStream_t s) {
+  constexpr int QPB = kVThreads / G;
+  constexpr size_t bytes = 2 * 2 * kVKeys * DH * sizeof(float);
+  const int64_t qblocks = (T + QPB - 1) / QPB;
+  const int64_t blocks = N * H * qblocks;
+  if (blocks > 2147483647LL || T > 2147483647LL || H > 2147483647LL) return hipErrorInvalidValue;
+  const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(DH));
+  hipLaunchKernelGGL((attn_valu_kernel<E, DH, G>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(kVThreads), bytes, s, static_cast<const E*>(q),
+                     static_cast<const E*>(k), static_cast<const E*>(v), ld, static_cast<E*>(o),
+                     ldo, static_cast<int>(T), static_cast<int>(H), static_cast<int>(qblocks),
+                     scale_log2);
+  return hipGetLastError();
+}
+
+// The tiled VALU kernel for the head widths it is instantiated for (multiples
+// of 8 up to 64 with one thread per query, 80, 96 and 128 with two);
+// hipErrorNotSupported otherwise.
+template <typename E>
+hipError_t attn_valu_dh(const void* q, const void* k, const void* v, int64_t ld, void* o,
+                        int64_t ldo, int64_t N, int64_t T, int64_t H, int64_t dh, hipStream_t s) {
+  switch (dh) {
+    case 8: return launch_attn_valu<E, 8, 1>(q, k, v, ld, o, ldo, N, T, H, s);
+    case 16: return launch_attn_valu<E, 16, 1>(q, k, v, ld, o, ldo, N, T, H, s);
+    case 24: return launch_attn_valu<E, 24, 1>(q, k, v, ld, o, ldo, N, T, H, s);
+    case 32: return launch_attn_valu<E, 32, 1>(q, k, v, ld, o, ldo, N, T, H, s);
+    case 40: return launch_attn_valu<E, 40, 1>(q, k, v, ld, o, ldo, N, T, H, s);
+    case 48: return launch_attn_valu<E, 48, 1>(q, k, v, ld, o, ldo, N, T, H, s);
+    case 56: return launch_attn_valu<E, 56, 1>(q, k, v, ld, o, ldo, N, T, H, s);
+    case 64: return launch_attn_valu<E, 64, 1>(q, k, v, ld, o, ldo, N, T, H, s);
+    case 80: return launch_attn_valu<E, 80, 2>(q, k, v, ld, o, ldo, N, T, H, s);
+    case 96: return launch_attn_valu<E, 96, 2>(q, k, v, ld, o, ldo, N, T, H, s);
+    case 128: return launch_attn_valu<E, 128, 2>(q, k, v, ld, o, ldo, N, T, H, s);
+    default: return hipErrorNotSupported;
+  }
+}
+
 template <typename T>
 hipError_t gemm_generic_typed(const GemmProblem& p, hipStream_t s) {
   const int64_t mt = (p.M + 63) / 64, nt = (p.N + 63) / 64;
@@ -288,6 +449,12 @@ hipError_t launch_gemm_generic(const GemmProblem& p, hipStream_t s) {
 hipError_t launch_attention_generic(const void* q, const void* k, const void* v, int64_t ld,
                                     void* o, int64_t ldo, int64_t N, int64_t T, int64_t H,
                                     int64_t dh, int dtype, hipStream_t s) {
+  // Tiled kernel where the head width has an instantiation; the one-query-per-
+  // wave kernel below for every other width.
+  const hipError_t r = dtype == VITBLK_BF16
+                           ? attn_valu_dh<bf16_t>(q, k, v, ld, o, ldo, N, T, H, dh, s)
+                           : attn_valu_dh<float>(q, k, v, ld, o, ldo, N, T, H, dh, s);
+  if (r != hipErrorNotSupported) return r;
   if (dh > 64 * kMaxDhPerLane) return hipErrorInvalidValue;
   const int64_t blocks = N * H * T;
   if (blocks > 2147483647LL) return hipErrorInvalidValue;
