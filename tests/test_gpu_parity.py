@@ -73,6 +73,23 @@ def test_linear(dtype, epi, M, K, N):
     assert_close(got, ref, dtype, f"linear {epi} M={M} K={K} N={N}")
 
 
+@pytest.mark.parametrize("epi", ["none", "gelu"])
+def test_linear_with_near_round_split(epi):
+    # 50 M-tiles x 12 N-tiles of 256 (ViT-B/16's MLP1 rows and width): no
+    # row split gives whole rounds of the 256 resident big-tile workgroups,
+    # so the big tile takes 42 M-tiles (504 tiles, two nearly full rounds)
+    # and the 128x128 tile the last 1856 rows.
+    M, K, N = 64 * 197, 128, 3072
+    rng = np.random.default_rng(37)
+    a = _rand(rng, (M, K), "bf16")
+    w = _rand(rng, (K, N), "bf16", scale=1 / math.sqrt(K))
+    got = to_host(vb.linear(to_dev(a, "bf16"), to_dev(w.T, "bf16"), EPIS[epi]))
+    ref = oracle.project(a, w)
+    if epi == "gelu":
+        ref = oracle.gelu_tanh(ref)
+    assert_close(got, ref, "bf16", f"linear {epi} M={M} near-round split")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("rows,D", [(37, 768), (64, 1024), (3, 20), (1000, 1280), (5, 4104)])
 def test_row_stats(dtype, rows, D):

@@ -901,9 +901,29 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t s) {
     g = b;
     b = r;
   }
-  const int64_t step = grid / g;           // M-tiles per whole number of rounds
-  const int64_t m_main = mt / step * step;  // M-tiles done with the big tile
-  if (m_main == 0 || m_main == mt || (mt * nt) % grid == 0) return launch_cfg<Big>(p, s);
+  const int64_t step = grid / g;     // M-tiles per whole number of rounds
+  int64_t m_main = mt / step * step;  // M-tiles done with the big tile
+  if ((mt * nt) % grid == 0) return launch_cfg<Big>(p, s);
+  if (m_main == 0) {
+    // No row split gives whole rounds (nt shares few factors with the grid):
+    // the big tile takes the rows of floor(tiles / grid) nearly full rounds
+    // and the small tile the rest, when that is estimated to be shorter than
+    // a last partial round of big tiles.  A round of the small tile (a
+    // quarter of the work per tile, two workgroups per CU) is counted as half
+    // a big-tile round.
+    const int64_t rounds = mt * nt / grid;
+    const int64_t m_try = rounds * grid / nt;
+    if (m_try > 0 && m_try < mt) {
+      const int64_t small_tiles = ((p.M - m_try * Big::BM + SmallTile::BM - 1) / SmallTile::BM) *
+                                  ((p.N + SmallTile::BN - 1) / SmallTile::BN);
+      int64_t small_slots = resident_workgroups<SmallTile, VITBLK_EPI_NONE>();
+      if (small_slots <= 0) small_slots = 2 * grid;
+      const int64_t small_rounds = (small_tiles + small_slots - 1) / small_slots;
+      const int64_t whole_rounds = (mt * nt + grid - 1) / grid;
+      if (2 * ((m_try * nt + grid - 1) / grid) + small_rounds < 2 * whole_rounds) m_main = m_try;
+    }
+  }
+  if (m_main == 0 || m_main == mt) return launch_cfg<Big>(p, s);
   const int64_t rows_main = m_main * Big::BM;
   const hipError_t e = launch_cfg<Big>(row_slice(p, 0, rows_main), s);
   if (e != hipSuccess) return e;
