@@ -66,33 +66,16 @@ __global__ __launch_bounds__(64 * W, (DH <= 64 ? 4 : 2)) void attn_stream_kernel
   constexpr int PER = 64 * CPR;
   constexpr int NL = (PER + 64 * W - 1) / (64 * W);
   uint4 rk[NL], rv[NL];
-  // Chunk e of a stage: row and 16-byte column of K and of V.  Head width
-  // 64 with 8 waves: each 16-lane write phase covers two whole rows, 8 rows
-  // apart for K (row stride 9 x 16 B) and 2 apart for V (12 x 16 B), so the
-  // 16 stores of a phase land on distinct bank groups; the 8 lanes of a row
-  // still read its 128 bytes from global memory together.
-  auto krow = [&](int e) {
-    if (DH == 64 && W == 8) return (e >> 6) + 8 * ((e & 63) >> 3);
-    return e / CPR;
-  };
-  auto vrow = [&](int e) {
-    if (DH == 64 && W == 8) {
-      const int j = (e & 63) >> 3;  // 0..7 -> 0, 2, 1, 3, 4, 6, 5, 7
-      return 8 * (e >> 6) + (j & 4) + ((j & 1) << 1) + ((j >> 1) & 1);
-    }
-    return e / CPR;
-  };
   auto fetch = [&](int c) {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int e = tid + i * 64 * W;
       if (e < PER) {
-        int tk = c * 64 + krow(e), tv = c * 64 + vrow(e);
-        tk = tk < T ? tk : T - 1;
-        tv = tv < T ? tv : T - 1;
-        const int64_t col = hoff + (e % CPR) * 8;
-        rk[i] = ld_global16(K + (seq0 + tk) * ld + col);
-        rv[i] = ld_global16(V + (seq0 + tv) * ld + col);
+        int t = c * 64 + e / CPR;
+        t = t < T ? t : T - 1;
+        const int64_t gofs = (seq0 + t) * ld + hoff + (e % CPR) * 8;
+        rk[i] = ld_global16(K + gofs);
+        rv[i] = ld_global16(V + gofs);
       }
     }
   };
@@ -103,8 +86,8 @@ __global__ __launch_bounds__(64 * W, (DH <= 64 ? 4 : 2)) void attn_stream_kernel
     for (int i = 0; i < NL; ++i) {
       const int e = tid + i * 64 * W;
       if (e < PER) {
-        *reinterpret_cast<uint4*>(ks + krow(e) * C::SK + (e % CPR) * 16) = rk[i];
-        *reinterpret_cast<uint4*>(vs + vrow(e) * C::SV + (e % CPR) * 16) = rv[i];
+        *reinterpret_cast<uint4*>(ks + (e / CPR) * C::SK + (e % CPR) * 16) = rk[i];
+        *reinterpret_cast<uint4*>(vs + (e / CPR) * C::SV + (e % CPR) * 16) = rv[i];
       }
     }
   };
