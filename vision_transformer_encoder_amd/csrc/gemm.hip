@@ -14,7 +14,8 @@
 //   of one row; lanes l and l+32 swap halves so each lane stores 16 bytes.
 // * Both tiles go straight from global memory into LDS with
 //   buffer_load_dwordx4 ... lds (no staging registers): each load instruction
-//   fills 1 KB of LDS, 16 bytes per lane at consecutive addresses.  The
+//   fills 1 KB of LDS, 16 bytes per lane at consecutive addresses.  In the
+//   256x256 tile only one wave per SIMD issues them (see kSpec).  The
 //   buffer resource (SGPRs) points at the tile's first row, each lane keeps
 //   one 32-bit offset per load, and the k offset is scalar.  LDS rows are
 //   BK k-values; the 16-byte chunk index is XOR-swizzled per row (see
@@ -170,6 +171,16 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
   int64_t m0 = 0, n0 = 0;
   __amdgpu_buffer_rsrc_t a_rs, b_rs;
   uint32_t a_off[C::A_LOADS], b_off[C::B_LOADS];
+  // Big tile: the waves of the first half (one per SIMD) issue every
+  // global->LDS load, their own chunks and those of wave + NT/128; the second
+  // half issue none.  A wave stalls while its LDS-DMA loads are accepted, so
+  // with every wave loading, both waves of a SIMD stalled together after each
+  // barrier and the matrix core idled; this way the other wave keeps issuing
+  // MFMAs meanwhile (measured: MLP1 444.7 -> 422.3 us, Q|K|V 311.4 -> 295.0
+  // us at ViT-L/16).
+  constexpr bool kSpec = C::NSA > C::NS && C::BM == 256;
+  constexpr int HW = C::NT / 128;  // waves per half
+  uint32_t a_off2[kSpec ? C::A_LOADS : 1], b_off2[kSpec ? C::B_LOADS : 1];
   auto prepare = [&](int t) {
     int tm, tn;
     tile_of(t, grid, total, mt * nsplit, nt, &tm, &tn);
@@ -193,6 +204,12 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
       const int c = (e % C::CPR) ^ swz_key<C::CPR>(row);
       const int64_t r = (m0 + row < M) ? row : (M - 1 - m0);
       a_off[i] = static_cast<uint32_t>(r * p.lda * 2 + c * 16);
+      if (kSpec) {
+        const int e2 = e + HW * 64, row2 = e2 / C::CPR;
+        const int c2 = (e2 % C::CPR) ^ swz_key<C::CPR>(row2);
+        const int64_t r2 = (m0 + row2 < M) ? row2 : (M - 1 - m0);
+        a_off2[kSpec ? i : 0] = static_cast<uint32_t>(r2 * p.lda * 2 + c2 * 16);
+      }
     }
 #pragma unroll
     for (int i = 0; i < C::B_LOADS; ++i) {
@@ -200,16 +217,44 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
       const int c = (e % C::CPR) ^ swz_key<C::CPR>(row);
       const int64_t r = (n0 + row < N) ? row : (N - 1 - n0);
       b_off[i] = static_cast<uint32_t>(r * p.ldb * 2 + c * 16);
+      if (kSpec) {
+        const int e2 = e + HW * 64, row2 = e2 / C::CPR;
+        const int c2 = (e2 % C::CPR) ^ swz_key<C::CPR>(row2);
+        const int64_t r2 = (n0 + row2 < N) ? row2 : (N - 1 - n0);
+        b_off2[kSpec ? i : 0] = static_cast<uint32_t>(r2 * p.ldb * 2 + c2 * 16);
+      }
     }
   };
   auto issue_a = [&](int kt, int st) {
     const int kb = (krev ? KT - 1 - kt : kt) * C::BK * 2;  // byte offset of the k-slice
+    if (kSpec) {
+      if (wave < HW) {
+#pragma unroll
+        for (int i = 0; i < C::A_LOADS; ++i) {
+          load_lds16(a_rs, a_lds + st * C::A_STAGE + (i * C::NT + wave * 64) * 16, a_off[i], kb);
+          load_lds16(a_rs, a_lds + st * C::A_STAGE + (i * C::NT + (wave + HW) * 64) * 16,
+                     a_off2[kSpec ? i : 0], kb);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < C::A_LOADS; ++i)
       load_lds16(a_rs, a_lds + st * C::A_STAGE + (i * C::NT + wave * 64) * 16, a_off[i], kb);
   };
   auto issue_b = [&](int kt, int st) {
     const int kb = (krev ? KT - 1 - kt : kt) * C::BK * 2;
+    if (kSpec) {
+      if (wave < HW) {
+#pragma unroll
+        for (int i = 0; i < C::B_LOADS; ++i) {
+          load_lds16(b_rs, b_lds + st * C::B_STAGE + (i * C::NT + wave * 64) * 16, b_off[i], kb);
+          load_lds16(b_rs, b_lds + st * C::B_STAGE + (i * C::NT + (wave + HW) * 64) * 16,
+                     b_off2[kSpec ? i : 0], kb);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < C::B_LOADS; ++i)
       load_lds16(b_rs, b_lds + st * C::B_STAGE + (i * C::NT + wave * 64) * 16, b_off[i], kb);
@@ -341,11 +386,12 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
     for (int kt = 0; kt < KT; ++kt) {
       if (C::NSA > C::NS) {
         // Iteration j issues W(j+1) then A(j+2); at the top of iteration kt
-        // only A(kt+1) is newer than W(kt) (and A(kt) is older).  Loads
-        // retire in issue order; at kt = 0 the previous tile's stores are
-        // pending too, so wait for everything.
+        // only A(kt+1) is newer than W(kt) (and A(kt) is older); a loading
+        // wave of the big tile issues twice the A loads.  Loads retire in
+        // issue order; at kt = 0 the previous tile's stores are pending too,
+        // so wait for everything.
         if (kt > 0 && kt + 1 < KT)
-          wait_vmcnt<C::A_LOADS>();
+          wait_vmcnt<(kSpec ? 2 : 1) * C::A_LOADS>();
         else
           wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
