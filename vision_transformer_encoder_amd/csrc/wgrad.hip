@@ -126,12 +126,17 @@ __global__ __launch_bounds__(NT, 1) void wgrad_mfma_kernel(WgradArgs p) {
   // Per-lane byte offsets of its chunks within a slice (chunks past the
   // feature range are clamped to the last valid chunk: their products reach
   // only outputs that are never stored).
-  uint32_t a_off[LOADS], b_off[LOADS];
+  // Waves 0..3 (one per SIMD) issue every global->LDS load, their own chunks
+  // and those of wave + 4; waves 4..7 issue none, so each SIMD always has a
+  // wave that is not stalled on LDS-DMA issue and keeps the matrix core busy.
+  constexpr int HW = NT / 128;
+  const bool loader = wave < HW;
+  uint32_t a_off[2 * LOADS], b_off[2 * LOADS];
   const int a_last = static_cast<int>((p.I - i0 < BI ? p.I - i0 : BI) / 8) - 1;
   const int b_last = static_cast<int>((p.J - j0 < BJ ? p.J - j0 : BJ) / 8) - 1;
 #pragma unroll
-  for (int u = 0; u < LOADS; ++u) {
-    const int e = u * NT + tid, row = e / CPR;
+  for (int u = 0; u < 2 * LOADS; ++u) {
+    const int e = (u % LOADS) * NT + tid + (u / LOADS) * HW * 64, row = e / CPR;
     const int c = (e % CPR) ^ swz(row);
     a_off[u] = static_cast<uint32_t>(row * p.lda * 2 + (c < a_last ? c : a_last) * 16);
     b_off[u] = static_cast<uint32_t>(row * p.ldb * 2 + (c < b_last ? c : b_last) * 16);
@@ -139,14 +144,18 @@ __global__ __launch_bounds__(NT, 1) void wgrad_mfma_kernel(WgradArgs p) {
   const int a_step = static_cast<int>(BK * p.lda * 2);  // bytes per slice
   const int b_step = static_cast<int>(BK * p.ldb * 2);
   auto issue_a = [&](int kt, int st) {
+    if (!loader) return;
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u)
-      dma16(a_rs, a_lds + st * STAGE + (u * NT + wave * 64) * 16, a_off[u], kt * a_step);
+    for (int u = 0; u < 2 * LOADS; ++u)
+      dma16(a_rs, a_lds + st * STAGE + ((u % LOADS) * NT + (wave + (u / LOADS) * HW) * 64) * 16,
+            a_off[u], kt * a_step);
   };
   auto issue_b = [&](int kt, int st) {
+    if (!loader) return;
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u)
-      dma16(b_rs, b_lds + st * STAGE + (u * NT + wave * 64) * 16, b_off[u], kt * b_step);
+    for (int u = 0; u < 2 * LOADS; ++u)
+      dma16(b_rs, b_lds + st * STAGE + ((u % LOADS) * NT + (wave + (u / LOADS) * HW) * 64) * 16,
+            b_off[u], kt * b_step);
   };
 
   // Fragment read offsets.  For MFMA block `blk` of a wave tile starting at
@@ -186,9 +195,10 @@ __global__ __launch_bounds__(NT, 1) void wgrad_mfma_kernel(WgradArgs p) {
   }
   for (int kt = 0; kt < KT; ++kt) {
     // Issue order: W(kt+1) then A(kt+2) per iteration, so at the top of
-    // iteration kt only A(kt+1) is newer than slice kt's loads.
+    // iteration kt only A(kt+1) (2 * LOADS per loading wave) is newer than
+    // slice kt's loads.
     if (kt > 0 && kt + 1 < KT)
-      wait_vmcnt<LOADS>();
+      wait_vmcnt<2 * LOADS>();
     else
       wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
