@@ -26,8 +26,10 @@ HIP_SOURCES = ["api.hip", "layernorm.hip", "gemm.hip", "attention.hip",
                "backward.hip", "wgrad.hip", "attention_bwd.hip"]
 HOST_SOURCES = ["validate.cpp"]
 
-# Packed-fp32 instructions are disabled for all device code.
+# Packed-fp32 instructions are disabled for all device code; a variable read
+# before it is set (e.g. a local initialised from itself) is an error.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+             "-Werror=uninitialized", "-Werror=sometimes-uninitialized",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wall", "-Wno-unused-function"]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall"]
