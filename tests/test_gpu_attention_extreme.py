@@ -12,10 +12,10 @@ well conditioned (scores are exact products of the given values summed in
 fp32; each probability is rounded once), so it is held to the plain bar,
 3e-2 (1 + |o|) elementwise, against the float64 oracle.
 
-Covered: the streaming kernel (head width 64 at every T, head width 80 at
-T = 1025), the resident kernel (head width 80 at T = 197 and 257), the
-first-queries entry used by the class-token readout, and one fp32 case on
-the generic kernel at the fp32 bar.
+Covered: the streaming kernel (head widths 64 and 80 at every T: eight- and
+four-wave workgroups), the resident kernel (head widths 96 and 128 at T = 257
+and 197), the first-queries entry used by the class-token readout, and one
+fp32 case on the generic kernel at the fp32 bar.
 """
 
 import math
@@ -88,9 +88,12 @@ def _case(kind, N, T, D, H, dtype, seed):
         # 64 keys.  Even heads' queries carry +16 there (their maxima rise by
         # ~60 natural units per chunk), odd heads' -24 (every score of theirs
         # lies ~90 or more natural units below 0, the maximum in the first chunk).
+        # Heads wider than 80 scale those query values by sqrt(dh / 80) so the
+        # 1 / sqrt(dh) score scale leaves the same ranges.
         bias = 40.0 + 30.0 * (np.arange(T) // 64) + 10.0 * np.sin(np.arange(T) * 0.37)
+        amp = max(1.0, math.sqrt(dh / 80.0))
         for h in range(H):
-            q[:, :, h * dh] = 16.0 if h % 2 == 0 else -24.0
+            q[:, :, h * dh] = (16.0 if h % 2 == 0 else -24.0) * amp
             k[:, :, h * dh] = bias[None, :]
     else:
         raise ValueError(kind)
@@ -99,14 +102,16 @@ def _case(kind, N, T, D, H, dtype, seed):
 
 KINDS = ["growing", "shrinking", "late_key", "tail_key", "key_bias"]
 SHAPES = [
-    # (N, T, D, H): head width 64 streams at every T; 80 is resident at 197
-    # and 257 and streams at 1025.
+    # (N, T, D, H): head widths 64 and 80 stream at every T; 96 and 128 are
+    # resident while the sequence fits in LDS.
     (2, 197, 128, 2),
     (2, 257, 128, 2),
     (1, 1025, 128, 2),
     (2, 197, 160, 2),
     (2, 257, 160, 2),
     (1, 1025, 160, 2),
+    (2, 257, 192, 2),
+    (2, 197, 256, 2),
 ]
 
 
@@ -140,7 +145,8 @@ def test_attention_first_queries_extreme_scores(kind, N, T, D, H):
     assert_close(got[:, :nq], ref, "bf16", f"first queries {kind} N={N} T={T} D={D}")
 
 
-@pytest.mark.parametrize("N,T,D,H", [(2, 197, 128, 2), (3, 40, 96, 3), (2, 1, 128, 2)])
+@pytest.mark.parametrize("N,T,D,H", [(2, 197, 128, 2), (3, 40, 96, 3), (2, 1, 128, 2),
+                                     (2, 257, 160, 2)])
 def test_attention_first_queries_matches_attention(N, T, D, H):
     # Ordinary inputs: the written rows are bit for bit those of the full step.
     import torch

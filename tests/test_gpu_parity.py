@@ -184,7 +184,7 @@ def _attention_ref(q, k, v, H):
     (2, 197, 128, 2),    # d_h 64, ViT token count
     (20, 197, 1024, 16),  # 320 (sequence, head) items: some workgroups take two
     (80, 100, 512, 8),   # 640 items over several workgroups each; ragged last chunk
-    (2, 257, 160, 2),    # d_h 80
+    (2, 257, 160, 2),    # d_h 80 (four-wave streaming workgroups)
     (1, 1025, 64, 1),    # long sequence (streaming kernel from here on)
     (2, 640, 128, 2),    # streaming, d_h 64, T a multiple of 64 (no partial chunk)
     (1, 900, 64, 2),     # streaming, d_h 32

@@ -169,7 +169,7 @@ hipError_t launch_stream_dh(const void* q, const void* k, const void* v, int64_t
   switch (dh) {
     case 32: return launch_stream<32>(q, k, v, ld, o, ldo, N, T, H, s, max_qt);
     case 64: return launch_stream<64>(q, k, v, ld, o, ldo, N, T, H, s, max_qt);
-    case 80: return launch_stream<80>(q, k, v, ld, o, ldo, N, T, H, s, max_qt);
+    case 80: return launch_stream<80, 4>(q, k, v, ld, o, ldo, N, T, H, s, max_qt);
     case 96: return launch_stream<96>(q, k, v, ld, o, ldo, N, T, H, s, max_qt);
     case 128: return launch_stream<128>(q, k, v, ld, o, ldo, N, T, H, s, max_qt);
     default: return hipErrorNotSupported;
@@ -178,12 +178,14 @@ hipError_t launch_stream_dh(const void* q, const void* k, const void* v, int64_t
 
 }  // namespace
 
-// Kernel choice (bf16): head widths up to 64 take the streaming kernel at every
+// Kernel choice (bf16): head widths up to 80 take the streaming kernel at every
 // T (measured at ViT-B/16 and ViT-L/16: its chunk-by-chunk copies overlap the
-// tile work, 8-9% faster than holding the whole sequence); wider heads need
-// more registers per wave, so they take the resident kernel while the
-// sequence fits in LDS (ViT-H/14: 158 vs 181 us) and stream beyond.  Other
-// dtypes and shapes: the generic kernel.
+// tile work, 8-9% faster than holding the whole sequence).  Width 80 needs
+// about 150 registers per wave, so it streams with 4-wave workgroups, three
+// per CU (ViT-H/14: 123 us, against 159 on the resident kernel and 181 with
+// 8-wave workgroups, one per CU).  Wider heads take the resident kernel while
+// the sequence fits in LDS and stream beyond.  Other dtypes and shapes: the
+// generic kernel.
 hipError_t launch_attention(const void* q, const void* k, const void* v, int64_t ld, void* o,
                             int64_t ldo, int64_t N, int64_t T, int64_t H, int64_t dh, int dtype,
                             hipStream_t s) {
@@ -191,7 +193,7 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, int64_t
                     aligned16(k) && aligned16(v) && aligned16(o);
   if (fast) {
     hipError_t r = hipErrorNotSupported;
-    if (dh <= 64) r = launch_stream_dh(q, k, v, ld, o, ldo, N, T, H, dh, s);
+    if (dh <= 80) r = launch_stream_dh(q, k, v, ld, o, ldo, N, T, H, dh, s);
     if (r == hipErrorNotSupported) r = launch_attention_resident(q, k, v, ld, o, ldo, N, T, H, dh, s);
     if (r == hipErrorNotSupported) r = launch_stream_dh(q, k, v, ld, o, ldo, N, T, H, dh, s);
     if (r != hipErrorNotSupported) return r;
