@@ -90,6 +90,32 @@ def test_linear_with_near_round_split(epi):
     assert_close(got, ref, "bf16", f"linear {epi} M={M} near-round split")
 
 
+@pytest.mark.parametrize("epi", ["none", "residual", "gelu"])
+@pytest.mark.parametrize("M,K,N", [
+    (1000, 192, 200),    # 192-row tiles: 6 x 1, last M-tile 40 rows, N ragged
+    (64 * 197, 128, 768),  # ViT-B/16's MLP2 grid: 50 x 3 big tiles or 66 x 3 of 192 rows
+    (65 * 256 - 100, 128, 768),  # 195 big tiles in one partial round (261 of 192 rows: too many)
+])
+def test_linear_under_one_round(epi, M, K, N):
+    # Products with fewer big tiles than resident workgroups: the 192 x 256
+    # tile when its tiles also fit in one round, else the big tile.  Residual
+    # products with K <= 1024 take the 128 x 128 tile, so theirs get K + 1024.
+    if epi == "residual":
+        K += 1024
+    rng = np.random.default_rng(M + K + N)
+    a = _rand(rng, (M, K), "bf16")
+    w = _rand(rng, (K, N), "bf16", scale=1 / math.sqrt(K))
+    r = _rand(rng, (M, N), "bf16")
+    got = to_host(vb.linear(to_dev(a, "bf16"), to_dev(w.T, "bf16"), EPIS[epi],
+                            residual=to_dev(r, "bf16") if epi == "residual" else None))
+    ref = oracle.project(a, w)
+    if epi == "residual":
+        ref = r + ref
+    elif epi == "gelu":
+        ref = oracle.gelu_tanh(ref)
+    assert_close(got, ref, "bf16", f"linear {epi} M={M} K={K} N={N} under one round")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("rows,D", [(37, 768), (64, 1024), (3, 20), (1000, 1280), (5, 4104)])
 def test_row_stats(dtype, rows, D):

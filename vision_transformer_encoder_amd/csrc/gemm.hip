@@ -171,14 +171,14 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
   int64_t m0 = 0, n0 = 0;
   __amdgpu_buffer_rsrc_t a_rs, b_rs;
   uint32_t a_off[C::A_LOADS], b_off[C::B_LOADS];
-  // Big tile: the waves of the first half (one per SIMD) issue every
+  // 8-wave tiles: the waves of the first half (one per SIMD) issue every
   // global->LDS load, their own chunks and those of wave + NT/128; the second
   // half issue none.  A wave stalls while its LDS-DMA loads are accepted, so
   // with every wave loading, both waves of a SIMD stalled together after each
   // barrier and the matrix core idled; this way the other wave keeps issuing
   // MFMAs meanwhile (measured: MLP1 444.7 -> 422.3 us, Q|K|V 311.4 -> 295.0
   // us at ViT-L/16).
-  constexpr bool kSpec = C::NSA > C::NS && C::BM == 256;
+  constexpr bool kSpec = C::NSA > C::NS && C::NT == 512;
   constexpr int HW = C::NT / 128;  // waves per half
   uint32_t a_off2[kSpec ? C::A_LOADS : 1], b_off2[kSpec ? C::B_LOADS : 1];
   auto prepare = [&](int t) {
@@ -685,6 +685,10 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
 using BigTile = Cfg<256, 256, 2, 4, 64, 2, 3>;
 // 4 waves, 64x64 per wave, 80 KB LDS: 2 workgroups per CU.
 using SmallTile = Cfg<128, 128, 2, 2, 64, 2, 3>;
+// 8 waves, 96x64 per wave, 3 A stages + 2 W stages: 136 KB LDS, one workgroup
+// per CU.  Three quarters of a big tile's work, for products whose big tiles
+// leave CUs idle in their only round.
+using MidTile = Cfg<192, 256, 2, 4, 64, 2, 3>;
 // The small tile with four stages of both operands (128 KB LDS, one workgroup
 // per CU): three k-slices in flight instead of two (activations) and one
 // (weights).  For a last partial round of tiles, where each workgroup runs
@@ -940,6 +944,13 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t s) {
     default: grid = resident_workgroups<Big, VITBLK_EPI_NONE>(); break;
   }
   grid = grid / kNumXcd * kNumXcd;
+  if (grid > 0 && mt * nt < grid) {
+    // Fewer big tiles than CUs: each CU holds at most one tile, so the time
+    // is one tile's; 192-row tiles take 3/4 of it when they too fit in one
+    // round (ViT-B/16's MLP2: 150 big tiles or 198 of these, 72.3 -> 60.3 us).
+    const int64_t mt_mid = (p.M + MidTile::BM - 1) / MidTile::BM;
+    if (mt_mid * nt <= grid) return launch_cfg<MidTile>(p, s);
+  }
   if (grid <= 0 || mt * nt <= grid) return launch_cfg<Big>(p, s);
   int64_t g = grid, b = nt;  // gcd(grid, nt)
   while (b) {
