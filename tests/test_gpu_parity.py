@@ -116,6 +116,19 @@ def test_linear_under_one_round(epi, M, K, N):
     assert_close(got, ref, "bf16", f"linear {epi} M={M} K={K} N={N} under one round")
 
 
+def test_linear_residual_short_k_one_round():
+    # A residual product with K <= 1024 whose 128 x 128 tiles need more than
+    # one round while 192 x 256 tiles fit in one: the latter.
+    M, K, N = 64 * 197 - 61, 512, 768
+    rng = np.random.default_rng(41)
+    a = _rand(rng, (M, K), "bf16")
+    w = _rand(rng, (K, N), "bf16", scale=1 / math.sqrt(K))
+    r = _rand(rng, (M, N), "bf16")
+    got = to_host(vb.linear(to_dev(a, "bf16"), to_dev(w.T, "bf16"), EPIS["residual"],
+                            residual=to_dev(r, "bf16")))
+    assert_close(got, r + oracle.project(a, w), "bf16", f"residual M={M} K={K} one round")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("rows,D", [(37, 768), (64, 1024), (3, 20), (1000, 1280), (5, 4104)])
 def test_row_stats(dtype, rows, D):
@@ -171,13 +184,15 @@ def test_linear_with_ragged_tail_rows(epi):
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("M,K,N,offset", [(300, 256, 512, 0.0), (2000, 1024, 1024, 1.5),
                                           (70 * 256 + 77, 256, 1024, 4.0), (129, 320, 320, 0.5),
-                                          (50, 40, 24, 0.0), (7, 64, 136, 2.0)])
+                                          (50, 40, 24, 0.0), (7, 64, 136, 2.0),
+                                          (64 * 197 - 61, 256, 768, 1.0)])
 def test_linear_residual_row_stats(dtype, M, K, N, offset):
     # The output projection with the first residual and the second
     # LayerNorm's row statistics of the stored y ([CAC] "Multi-head
     # attention", "Feed-forward stage").  bf16 with N a multiple of 64 takes
     # the fused epilogue partials; other shapes and fp32 the plain product and
-    # the statistics kernel.  The statistics are held to the float64 oracle's
+    # the statistics kernel.  M = 12547, N = 768: 594 small tiles for 512
+    # slots, 198 of 192 rows in one round (the 192 x 256 tile).  The statistics are held to the float64 oracle's
     # of the same stored values; the residual rows carry a mean offset of
     # `offset` standard deviations.
     if dtype == "fp32" and M > 10000:

@@ -837,8 +837,8 @@ bool gemm_fast_ok(const GemmProblem& p) {
   return ok;
 }
 
-// The row partials ride on the two-workgroups-per-CU 128x128 tile, the one
-// the output projection (a residual product with K = D) takes anyway; no bias.
+// The row partials ride on the tiles the output projection (a residual
+// product with K = D) takes anyway, whose waves cover 64 columns each; no bias.
 bool gemm_row_partials_ok(const GemmProblem& p) {
   GemmProblem q = p;
   q.epi = kEpiResidualStats;
@@ -908,6 +908,20 @@ hipError_t launch_tail(const GemmProblem& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The residual products with K <= 1024 (the output projection) take the small
+// tile, except when its tiles need more than one round and the 192-row tiles
+// fit in one (ViT-B/16: 594 small tiles for 512 slots, or 198 of 192 rows:
+// 29.8 -> 27.8 us with the LayerNorm partials).
+bool mid_fits_one_round(const GemmProblem& p) {
+  const int64_t nt = (p.N + MidTile::BN - 1) / MidTile::BN;
+  const int64_t mid = (p.M + MidTile::BM - 1) / MidTile::BM * nt;
+  const int64_t small = ((p.M + SmallTile::BM - 1) / SmallTile::BM) *
+                        ((p.N + SmallTile::BN - 1) / SmallTile::BN);
+  const int64_t mid_slots = resident_workgroups<MidTile, VITBLK_EPI_NONE>() / kNumXcd * kNumXcd;
+  const int64_t small_slots = resident_workgroups<SmallTile, VITBLK_EPI_NONE>();
+  return mid_slots > 0 && small_slots > 0 && small > small_slots && mid <= mid_slots;
+}
+
 // Tile choice.  With one big-tile workgroup per CU, a tile's epilogue runs
 // with the matrix cores idle; when it also reads a residual and K is short
 // (the output projection: K = D) that share is large, and the small tile,
@@ -927,12 +941,13 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t s) {
     return hipErrorInvalidValue;
   if (p.epi == kEpiResidualStats) {
     if (!gemm_row_partials_ok(p)) return hipErrorInvalidValue;
-    return launch_cfg<SmallTile>(p, s);
+    return mid_fits_one_round(p) ? launch_cfg<MidTile>(p, s) : launch_cfg<SmallTile>(p, s);
   }
   if (!gemm_fast_ok(p)) return launch_gemm_generic(p, s);
   using Big = BigTile;
   using Small = SmallTile;
-  if (p.epi == VITBLK_EPI_RESIDUAL && p.K <= 1024) return launch_cfg<Small>(p, s);
+  if (p.epi == VITBLK_EPI_RESIDUAL && p.K <= 1024)
+    return mid_fits_one_round(p) ? launch_cfg<MidTile>(p, s) : launch_cfg<Small>(p, s);
   const int64_t mt = (p.M + Big::BM - 1) / Big::BM, nt = (p.N + Big::BN - 1) / Big::BN;
   int64_t grid = 0;
   switch (p.epi) {
