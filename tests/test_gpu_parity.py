@@ -196,7 +196,7 @@ def test_linear_residual_row_stats(dtype, M, K, N, offset):
     # of the same stored values; the residual rows carry a mean offset of
     # `offset` standard deviations.
     if dtype == "fp32" and M > 10000:
-        pytest.skip("the big ragged case exercises the bf16 tile split only")
+        pytest.skip("the large cases exercise the bf16 tile choice only")
     rng = np.random.default_rng(M + 5 * K + 11 * N)
     a = _rand(rng, (M, K), dtype)
     w = _rand(rng, (K, N), dtype, scale=1 / math.sqrt(K))
