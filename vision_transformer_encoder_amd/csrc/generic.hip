@@ -442,8 +442,9 @@ hipError_t launch_row_stats_generic(const void* x, int64_t ld_in, float* stats, 
 hipError_t launch_gemm_generic(const GemmProblem& p, hipStream_t s) {
   if (reads_r(p) && p.R == nullptr) return hipErrorInvalidValue;
   if (p.epi == kEpiGeluDual && p.C2 == nullptr) return hipErrorInvalidValue;
-  return p.dtype == VITBLK_BF16 ? gemm_generic_typed<bf16_t>(p, s)
-                                : gemm_generic_typed<float>(p, s);
+  if (p.dtype == VITBLK_BF16) return gemm_generic_typed<bf16_t>(p, s);
+  const hipError_t r = launch_gemm_f32_mfma(p, s);  // aligned fp32: the matrix cores
+  return r != hipErrorNotSupported ? r : gemm_generic_typed<float>(p, s);
 }
 
 hipError_t launch_attention_generic(const void* q, const void* k, const void* v, int64_t ld,

@@ -183,6 +183,9 @@ hipError_t launch_layernorm_generic(const void* x, int64_t ld_in, const void* ga
                                     const void* beta, void* y, int64_t rows, int64_t D,
                                     float eps, int dtype, hipStream_t stream);
 hipError_t launch_gemm_generic(const GemmProblem& p, hipStream_t stream);
+// fp32 on the matrix cores (gemm_f32.hip); hipErrorNotSupported (nothing
+// launched) for shapes, alignments or epilogues it does not take.
+hipError_t launch_gemm_f32_mfma(const GemmProblem& p, hipStream_t stream);
 hipError_t launch_row_stats_generic(const void* x, int64_t ld_in, float* stats, int64_t rows,
                                     int64_t D, float eps, int dtype, hipStream_t stream);
 hipError_t launch_attention_generic(const void* q, const void* k, const void* v, int64_t ld,
