@@ -14,8 +14,8 @@ fp32; each probability is rounded once), so it is held to the plain bar,
 
 Covered: the streaming kernel (head widths 64 and 80 at every T: eight- and
 four-wave workgroups), the resident kernel (head widths 96 and 128 at T = 257
-and 197), the first-queries entry used by the class-token readout, and one
-fp32 case on the generic kernel at the fp32 bar.
+and 197), the first-queries entry used by the class-token readout, and fp32
+cases (the fp32 matrix-core kernel and the VALU kernel) at the fp32 bar.
 """
 
 import math
@@ -159,9 +159,10 @@ def test_attention_first_queries_matches_attention(N, T, D, H):
     assert torch.equal(full[:, :nq], first[:, :nq])
 
 
-def test_attention_extreme_scores_fp32_generic():
-    N, T, D, H = 2, 197, 128, 2
+@pytest.mark.parametrize("N,T,D,H", [(2, 197, 128, 2), (2, 257, 160, 2), (2, 197, 96, 2)])
+def test_attention_extreme_scores_fp32(N, T, D, H):
+    # Head widths 64 and 80: the fp32 matrix-core kernel; 48: the VALU kernel.
     q, k, v = _case("late_key", N, T, D, H, "fp32", seed=23)
     qkv = np.concatenate([q, k, v], axis=-1).reshape(N * T, 3 * D)
     got = to_host(vb.attention(to_dev(qkv, "fp32"), N, T, H)).reshape(N, T, D)
-    assert_close(got, _attention_ref(q, k, v, H), "fp32", "attention fp32 late key")
+    assert_close(got, _attention_ref(q, k, v, H), "fp32", f"attention fp32 late key D={D} H={H}")

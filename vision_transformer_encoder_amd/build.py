@@ -21,7 +21,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libvitblk.so")
 
 ARCH = os.environ.get("VITBLK_OFFLOAD_ARCH", "gfx950")
-HIP_SOURCES = ["api.hip", "layernorm.hip", "gemm.hip", "gemm_f32.hip", "attention.hip",
+HIP_SOURCES = ["api.hip", "layernorm.hip", "gemm.hip", "gemm_f32.hip", "attention.hip", "attention_f32.hip",
                "attention_resident.hip", "patch.hip", "generic.hip", "pack.hip",
                "backward.hip", "wgrad.hip", "attention_bwd.hip"]
 HOST_SOURCES = ["validate.cpp"]

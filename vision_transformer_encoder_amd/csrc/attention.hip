@@ -184,8 +184,9 @@ hipError_t launch_stream_dh(const void* q, const void* k, const void* v, int64_t
 // about 150 registers per wave, so it streams with 4-wave workgroups, three
 // per CU (ViT-H/14: 123 us, against 159 on the resident kernel and 181 with
 // 8-wave workgroups, one per CU).  Wider heads take the resident kernel while
-// the sequence fits in LDS and stream beyond.  Other dtypes and shapes: the
-// generic kernel.
+// the sequence fits in LDS and stream beyond.  fp32 with the same head widths:
+// the fp32 matrix-core kernel (attention_f32.hip).  Other shapes: the generic
+// kernel.
 hipError_t launch_attention(const void* q, const void* k, const void* v, int64_t ld, void* o,
                             int64_t ldo, int64_t N, int64_t T, int64_t H, int64_t dh, int dtype,
                             hipStream_t s) {
@@ -196,6 +197,10 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, int64_t
     if (dh <= 80) r = launch_stream_dh(q, k, v, ld, o, ldo, N, T, H, dh, s);
     if (r == hipErrorNotSupported) r = launch_attention_resident(q, k, v, ld, o, ldo, N, T, H, dh, s);
     if (r == hipErrorNotSupported) r = launch_stream_dh(q, k, v, ld, o, ldo, N, T, H, dh, s);
+    if (r != hipErrorNotSupported) return r;
+  }
+  if (dtype == VITBLK_FP32) {
+    const hipError_t r = launch_attention_f32_mfma(q, k, v, ld, o, ldo, N, T, H, dh, s);
     if (r != hipErrorNotSupported) return r;
   }
   return launch_attention_generic(q, k, v, ld, o, ldo, N, T, H, dh, dtype, s);

@@ -171,6 +171,13 @@ hipError_t launch_attention_first_queries(const void* q, const void* k, const vo
                                           int64_t ld, void* o, int64_t ldo, int64_t N, int64_t T,
                                           int64_t H, int64_t dh, int dtype, hipStream_t stream);
 
+// fp32 on the matrix cores (attention_f32.hip) for head widths 32, 64, 80, 96,
+// 128 and 16-byte-aligned rows; hipErrorNotSupported (nothing launched)
+// otherwise.
+hipError_t launch_attention_f32_mfma(const void* q, const void* k, const void* v, int64_t ld,
+                                     void* o, int64_t ldo, int64_t N, int64_t T, int64_t H,
+                                     int64_t dh, hipStream_t stream);
+
 // Whole-sequence-in-LDS variant (bf16); hipErrorNotSupported when it does not
 // apply (sequence too long for LDS, head width without an instantiation).
 hipError_t launch_attention_resident(const void* q, const void* k, const void* v, int64_t ld,
