@@ -57,8 +57,10 @@ EPIS = {"none": vb.EPI_NONE, "residual": vb.EPI_RESIDUAL, "gelu": vb.EPI_GELU}
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("epi", sorted(EPIS))
 @pytest.mark.parametrize("M,K,N", [(300, 256, 512), (129, 1024, 200), (33, 40, 24),
-                                   (600, 4096, 256)])
+                                   (600, 4096, 256), (45, 37, 26)])
 def test_linear(dtype, epi, M, K, N):
+    # K = 37, N = 26: no MFMA kernel takes them (fp32 needs multiples of 4,
+    # bf16 of 64 and 8), so both dtypes run the any-shape VALU kernel.
     rng = np.random.default_rng(M * 7 + K * 3 + N)
     a = _rand(rng, (M, K), dtype)
     w = _rand(rng, (K, N), dtype, scale=1 / math.sqrt(K))
