@@ -34,8 +34,10 @@ EMBEDS = [
     (2, 3, 8, 8, 4, 16, "fp32"),        # the tiny model's front end
     (3, 1, 8, 12, 4, 24, "fp32"),       # non-square image, one channel
     (4, 3, 224, 224, 16, 768, "bf16"),  # ViT-B/16
+    (128, 3, 224, 224, 16, 768, "bf16"),  # 25088 patch rows: big tile + 128x128 tail, token rows
     (2, 3, 224, 224, 14, 1280, "bf16"),  # ViT-H/14: patch width 588 -> padded to 640
     (2, 3, 32, 48, 8, 100, "bf16"),     # D not a multiple of 8: generic GEMM, scalar token rows
+    (2, 3, 12, 20, 4, 32, "bf16"),      # image rows not whole 16-byte vectors: per-vector gather
 ]
 
 

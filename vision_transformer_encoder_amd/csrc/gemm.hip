@@ -152,6 +152,17 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int lrow = lane & 31, lhalf = lane >> 5;
   const int64_t M = p.M, N = p.N;
+  // Row of C and of R for product row m (kEpiEmbed: token rows and position
+  // rows; otherwise m itself).
+  auto c_row = [&](int64_t m) -> int64_t {
+    if (EPI != kEpiEmbed) return m;
+    const int64_t gr = p.row_base + m;
+    return gr + p.row_skip * (gr / p.row_group + 1);
+  };
+  auto r_row = [&](int64_t m) -> int64_t {
+    if (EPI != kEpiEmbed) return m;
+    return p.row_skip + (p.row_base + m) % p.row_group;
+  };
   // Split K (kEpiPartial): the tile index runs over ksplit copies of the
   // mt x nt tiles, copy s covering k-slices [KA * s / ksplit, KA * (s + 1) /
   // ksplit).  Otherwise one copy and the whole of K.
@@ -422,7 +433,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
     // R: the residual, or GELU's input z for the GELU-derivative epilogue, in
     // the lanes' store layout (below), rows and columns clamped into range.
     constexpr bool kReadsR = EPI == VITBLK_EPI_RESIDUAL || EPI == VITBLK_EPI_GELU_GRAD ||
-                             EPI == kEpiMul || EPI == kEpiResidualStats;
+                             EPI == kEpiMul || EPI == kEpiResidualStats || EPI == kEpiEmbed;
     uint4 res[C::TM][C::TN][2];
     if (kReadsR) {
 #pragma unroll
@@ -435,7 +446,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
           for (int q = 0; q < 2; ++q) {
             int64_t n = cn0 + wn * C::WTN + j * 32 + q * 16 + lhalf * 8;
             n = n < N ? n : N - 8;
-            res[i][j][q] = ld_global16(Rp + m * p.ldr + n);
+            res[i][j][q] = ld_global16(Rp + r_row(m) * p.ldr + n);
           }
       }
     }
@@ -511,9 +522,9 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
     // lines (rows_to_lines): 8% faster on the fused Q|K|V projection.  The
     // GELU epilogue keeps the direct stores: its exponentials already pace the
     // stores, and the extra exchange work made it 2% slower.
-    constexpr bool kLines =
-        (EPI == VITBLK_EPI_NONE || EPI == VITBLK_EPI_RESIDUAL || EPI == kEpiResidualStats) &&
-        C::TN == 2;
+    constexpr bool kLines = (EPI == VITBLK_EPI_NONE || EPI == VITBLK_EPI_RESIDUAL ||
+                             EPI == kEpiResidualStats || EPI == kEpiEmbed) &&
+                            C::TN == 2;
     if (kSplit) {
       // Unrounded fp32 sums of this k-range: after the fp32 half exchange a
       // lane holds 8 consecutive columns of one row (32 bytes).
@@ -620,7 +631,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
             }
           }
           outs[j][q] = out;
-          if (!kLines && m < M && n < N) st_global16(Cp + m * p.ldc + n, out);
+          if (!kLines && m < M && n < N) st_global16(Cp + c_row(m) * p.ldc + n, out);
         }
       }
       if constexpr (EPI == kEpiResidualStats) {
@@ -672,7 +683,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
         for (int t = 0; t < 4; ++t) {
           const int64_t mr = cm0 + wm * C::WTM + i * 32 + t * 8 + (lane >> 3);
           const int64_t nr = cn0 + wn * C::WTN + (lane & 7) * 8;
-          if (mr < M && nr < N) st_global16(Cp + mr * p.ldc + nr, v[t]);
+          if (mr < M && nr < N) st_global16(Cp + c_row(mr) * p.ldc + nr, v[t]);
         }
       }
     }
@@ -792,6 +803,7 @@ hipError_t launch_bias(const GemmProblem& p, hipStream_t s) {
     case kEpiMul: return launch_epi<C, kEpiMul, BIAS>(p, s);
     case kEpiPartial: return launch_epi<C, kEpiPartial, false>(p, s);
     case kEpiResidualStats: return launch_epi<C, kEpiResidualStats, false>(p, s);
+    case kEpiEmbed: return launch_epi<C, kEpiEmbed, BIAS>(p, s);
     default: return launch_epi<C, VITBLK_EPI_NONE, BIAS>(p, s);
   }
 }
@@ -851,6 +863,10 @@ GemmProblem row_slice(const GemmProblem& p, int64_t r0, int64_t rows) {
   GemmProblem q = p;
   q.M = rows;
   q.A = static_cast<const char*>(p.A) + r0 * p.lda * 2;
+  if (p.epi == kEpiEmbed) {  // C and R rows follow from the absolute product row
+    q.row_base = p.row_base + r0;
+    return q;
+  }
   q.C = static_cast<char*>(p.C) + r0 * p.ldc * 2;
   if (p.R) q.R = static_cast<const char*>(p.R) + r0 * p.ldr * 2;
   if (p.C2) q.C2 = static_cast<char*>(p.C2) + r0 * p.ldc * 2;
@@ -943,6 +959,8 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t s) {
     if (!gemm_row_partials_ok(p)) return hipErrorInvalidValue;
     return mid_fits_one_round(p) ? launch_cfg<MidTile>(p, s) : launch_cfg<SmallTile>(p, s);
   }
+  if (p.epi == kEpiEmbed && (!gemm_fast_ok(p) || p.row_group <= 0 || p.row_skip < 0))
+    return hipErrorInvalidValue;  // the token-row epilogue exists on the MFMA kernel only
   if (!gemm_fast_ok(p)) return launch_gemm_generic(p, s);
   using Big = BigTile;
   using Small = SmallTile;

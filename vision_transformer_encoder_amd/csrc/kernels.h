@@ -48,6 +48,12 @@ struct GemmProblem {
   // of the stored (rounded) outputs of row m over columns [n, n + 64), n a
   // multiple of 64 (M2 = the sum of squared deviations from that mean).
   float2* row_partials;
+  // kEpiEmbed only: product row g = row_base + m (m the row within this
+  // launch) is token cell = g % row_group of image g / row_group; it goes to
+  // C row g + row_skip * (g / row_group + 1) and adds R row row_skip + cell
+  // (C and R are not offset by row_base).
+  int64_t row_group, row_base;
+  int64_t row_skip;
 };
 
 // Internal epilogues of the backward (not part of the C interface):
@@ -61,6 +67,10 @@ constexpr int kEpiPartial = 18;
 // kEpiResidualStats: the residual epilogue, plus the row partials above (the
 // next LayerNorm's statistics, combined by launch_row_stats_from_partials).
 constexpr int kEpiResidualStats = 19;
+// kEpiEmbed: the patch-embedding product written straight into the token
+// rows with the position embedding added (fields row_group, row_base,
+// row_skip above; bf16 MFMA kernel only).
+constexpr int kEpiEmbed = 20;
 // Columns per row partial of kEpiResidualStats (every tile's wave strip).
 constexpr int kStatsStrip = 64;
 
@@ -71,7 +81,7 @@ __host__ __device__ inline bool has_bias(const GemmProblem& p) {
 // Epilogues that read R (the residual, or GELU's input for its derivative).
 __host__ __device__ inline bool reads_r(const GemmProblem& p) {
   return p.epi == VITBLK_EPI_RESIDUAL || p.epi == VITBLK_EPI_GELU_GRAD || p.epi == kEpiMul ||
-         p.epi == kEpiResidualStats;
+         p.epi == kEpiResidualStats || p.epi == kEpiEmbed;
 }
 
 // One (in, out) weight to write out-major: dst[c * ldd + r] = src[r * cols + c].
