@@ -38,6 +38,7 @@ EMBEDS = [
     (2, 3, 224, 224, 14, 1280, "bf16"),  # ViT-H/14: patch width 588 -> padded to 640
     (2, 3, 32, 48, 8, 100, "bf16"),     # D not a multiple of 8: generic GEMM, scalar token rows
     (2, 3, 12, 20, 4, 32, "bf16"),      # image rows not whole 16-byte vectors: per-vector gather
+    (1, 3, 32, 32, 8, 64, "bf16"),      # one image: the token rows take a separate pass
 ]
 
 

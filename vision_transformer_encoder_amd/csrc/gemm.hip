@@ -152,16 +152,35 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int lrow = lane & 31, lhalf = lane >> 5;
   const int64_t M = p.M, N = p.N;
-  // Row of C and of R for product row m (kEpiEmbed: token rows and position
-  // rows; otherwise m itself).
-  auto c_row = [&](int64_t m) -> int64_t {
+  // kEpiEmbed: product row m = first + delta (first: the first row of a
+  // wave's 32-row block, whose quotient and remainder by row_group, q0 and r0,
+  // are taken once per block) goes to C row g + row_skip * (g / row_group + 1)
+  // and reads R row row_skip + g % row_group, g = row_base + m (32-bit: the
+  // launcher keeps row_base + M below 2^31).  Other epilogues: row m itself.
+  auto c_row = [&](int64_t m, uint32_t q0, uint32_t r0, int delta) -> int64_t {
     if (EPI != kEpiEmbed) return m;
-    const int64_t gr = p.row_base + m;
-    return gr + p.row_skip * (gr / p.row_group + 1);
+    const uint32_t n32 = static_cast<uint32_t>(p.row_group);
+    uint32_t idx = r0 + static_cast<uint32_t>(delta), q = q0;
+    while (idx >= n32) {  // delta < 32: at most 32 / row_group + 1 steps
+      idx -= n32;
+      ++q;
+    }
+    return p.row_base + m + p.row_skip * static_cast<int64_t>(q + 1);
   };
-  auto r_row = [&](int64_t m) -> int64_t {
+  auto r_row = [&](int64_t m, uint32_t r0, int delta) -> int64_t {
     if (EPI != kEpiEmbed) return m;
-    return p.row_skip + (p.row_base + m) % p.row_group;
+    const uint32_t n32 = static_cast<uint32_t>(p.row_group);
+    uint32_t idx = r0 + static_cast<uint32_t>(delta);
+    while (idx >= n32) idx -= n32;
+    return p.row_skip + static_cast<int64_t>(idx);
+  };
+  // q0, r0 of the 32-row block starting at product row first.
+  auto block_div = [&](int64_t first, uint32_t* q0, uint32_t* r0) {
+    if (EPI != kEpiEmbed) return;
+    const uint32_t g = static_cast<uint32_t>(p.row_base + first);
+    const uint32_t n32 = static_cast<uint32_t>(p.row_group);
+    *q0 = g / n32;
+    *r0 = g - *q0 * n32;
   };
   // Split K (kEpiPartial): the tile index runs over ksplit copies of the
   // mt x nt tiles, copy s covering k-slices [KA * s / ksplit, KA * (s + 1) /
@@ -435,10 +454,19 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
     constexpr bool kReadsR = EPI == VITBLK_EPI_RESIDUAL || EPI == VITBLK_EPI_GELU_GRAD ||
                              EPI == kEpiMul || EPI == kEpiResidualStats || EPI == kEpiEmbed;
     uint4 res[C::TM][C::TN][2];
+    // kEpiEmbed: each wave block's quotient and remainder (see c_row).
+    uint32_t bq[C::TM], br[C::TM];
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) {
+      bq[i] = br[i] = 0;
+      block_div(cm0 + wm * C::WTM + i * 32, &bq[i], &br[i]);
+    }
     if (kReadsR) {
 #pragma unroll
       for (int i = 0; i < C::TM; ++i) {
         int64_t m = cm0 + wm * C::WTM + i * 32 + lrow;
+        // A row past M reads the block's first row (its product is never stored).
+        const int rdelta = m < M ? lrow : 0;
         m = m < M ? m : M - 1;
 #pragma unroll
         for (int j = 0; j < C::TN; ++j)
@@ -446,7 +474,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
           for (int q = 0; q < 2; ++q) {
             int64_t n = cn0 + wn * C::WTN + j * 32 + q * 16 + lhalf * 8;
             n = n < N ? n : N - 8;
-            res[i][j][q] = ld_global16(Rp + r_row(m) * p.ldr + n);
+            res[i][j][q] = ld_global16(Rp + r_row(m, br[i], rdelta) * p.ldr + n);
           }
       }
     }
@@ -631,7 +659,8 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
             }
           }
           outs[j][q] = out;
-          if (!kLines && m < M && n < N) st_global16(Cp + c_row(m) * p.ldc + n, out);
+          if (!kLines && m < M && n < N)
+            st_global16(Cp + c_row(m, bq[i], br[i], lrow) * p.ldc + n, out);
         }
       }
       if constexpr (EPI == kEpiResidualStats) {
@@ -683,7 +712,8 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
         for (int t = 0; t < 4; ++t) {
           const int64_t mr = cm0 + wm * C::WTM + i * 32 + t * 8 + (lane >> 3);
           const int64_t nr = cn0 + wn * C::WTN + (lane & 7) * 8;
-          if (mr < M && nr < N) st_global16(Cp + c_row(mr) * p.ldc + nr, v[t]);
+          if (mr < M && nr < N)
+            st_global16(Cp + c_row(mr, bq[i], br[i], t * 8 + (lane >> 3)) * p.ldc + nr, v[t]);
         }
       }
     }
@@ -959,7 +989,8 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t s) {
     if (!gemm_row_partials_ok(p)) return hipErrorInvalidValue;
     return mid_fits_one_round(p) ? launch_cfg<MidTile>(p, s) : launch_cfg<SmallTile>(p, s);
   }
-  if (p.epi == kEpiEmbed && (!gemm_fast_ok(p) || p.row_group <= 0 || p.row_skip < 0))
+  if (p.epi == kEpiEmbed && (!gemm_fast_ok(p) || p.row_group <= 0 || p.row_skip < 0 ||
+                             p.row_base < 0 || p.row_base + p.M > 2147483647LL))
     return hipErrorInvalidValue;  // the token-row epilogue exists on the MFMA kernel only
   if (!gemm_fast_ok(p)) return launch_gemm_generic(p, s);
   using Big = BigTile;

@@ -10,9 +10,9 @@
 // the GEMM (bias epilogue) then embeds them into [B*N, D]; tokens_kernel
 // writes the sequences [B, N (+1), D]: the class token (if any) as token 0,
 // then the embedded patches, each plus its position embedding (if any).  With
-// position embeddings and the MFMA GEMM, the GEMM's token epilogue writes the
-// patch tokens (position embedding added) and tokens_kernel only the class
-// tokens.
+// position embeddings and the MFMA GEMM, pos_bias_kernel writes the class
+// tokens and a table of position embedding plus bias, and the GEMM's token
+// epilogue writes the patch tokens with that table added.
 // All three are HBM-bound except the GEMM (MFMA).
 #include "device.h"
 #include "kernels.h"
@@ -122,24 +122,21 @@ __global__ __launch_bounds__(256) void zero_pad_kernel(T* __restrict__ w, int64_
 }
 
 // Token rows: out[b, t, :] = (t < HC ? cls : emb[b * N + t - HC]) + pos[t], for
-// t < t_end (N + HC: every row; HC: the class-token rows only, when the
-// embedding product wrote the others), VEC consecutive features per thread
-// (VEC = 8 needs D % 8 == 0).
+// VEC consecutive features per thread (VEC = 8 needs D % 8 == 0).
 template <typename T, int VEC>
 __global__ __launch_bounds__(256) void tokens_kernel(const T* __restrict__ emb,
                                                      const T* __restrict__ cls,
                                                      const T* __restrict__ pos,
                                                      T* __restrict__ out, int64_t B, int N,
-                                                     int HC, int D, int t_end) {
+                                                     int HC, int D) {
   const int Tn = N + HC;
   const int per_row = D / VEC;
   const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (e >= B * t_end * per_row) return;
-  const int64_t r = e / per_row;
-  const int d0 = static_cast<int>(e - r * per_row) * VEC;
-  const int64_t b = r / t_end;
-  const int t = static_cast<int>(r - b * t_end);
-  const int64_t row = b * Tn + t;
+  if (e >= B * Tn * per_row) return;
+  const int64_t row = e / per_row;
+  const int d0 = static_cast<int>(e - row * per_row) * VEC;
+  const int64_t b = row / Tn;
+  const int t = static_cast<int>(row - b * Tn);
   const T* src = t < HC ? cls + d0 : emb + (b * N + t - HC) * D + d0;
   float v[VEC];
 #pragma unroll
@@ -150,6 +147,46 @@ __global__ __launch_bounds__(256) void tokens_kernel(const T* __restrict__ emb,
   }
 #pragma unroll
   for (int i = 0; i < VEC; ++i) store_f32(out + row * D + d0 + i, v[i]);
+}
+
+// Before the fused embedding product (bf16, D % 8 == 0, one 16-byte vector
+// per thread): the position embedding plus patch bias, rounded once, pb[t] =
+// pos[t] + b (b null: pos) for t < rows, and, if cls is given, the class-token
+// rows out[i * Tn] = cls + pos[0] of the B images.
+__global__ __launch_bounds__(256) void pos_bias_kernel(const bf16_t* __restrict__ pos,
+                                                       const bf16_t* __restrict__ b,
+                                                       bf16_t* __restrict__ pb, int64_t rows,
+                                                       int D, const bf16_t* __restrict__ cls,
+                                                       bf16_t* __restrict__ out, int64_t B,
+                                                       int64_t Tn) {
+  int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int per_row = D / 8;
+  if (e >= rows * per_row) {  // a class-token row
+    e -= rows * per_row;
+    if (cls == nullptr || e >= B * per_row) return;
+    const int64_t i = e / per_row;
+    const int d0 = static_cast<int>(e - i * per_row) * 8;
+    const uint4 cv = ld_global16(cls + d0), pv = ld_global16(pos + d0);
+    const uint32_t cw[4] = {cv.x, cv.y, cv.z, cv.w}, pw[4] = {pv.x, pv.y, pv.z, pv.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      o[k] = pack_bf16x2(__uint_as_float(cw[k] << 16) + __uint_as_float(pw[k] << 16),
+                         __uint_as_float(cw[k] & 0xffff0000u) + __uint_as_float(pw[k] & 0xffff0000u));
+    st_global16(out + i * Tn * D + d0, make_uint4(o[0], o[1], o[2], o[3]));
+    return;
+  }
+  const int64_t t = e / per_row;
+  const int d0 = static_cast<int>(e - t * per_row) * 8;
+  const uint4 pv = ld_global16(pos + t * D + d0);
+  const uint4 bv = b != nullptr ? ld_global16(b + d0) : make_uint4(0, 0, 0, 0);
+  const uint32_t pw[4] = {pv.x, pv.y, pv.z, pv.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = pack_bf16x2(__uint_as_float(pw[i] << 16) + __uint_as_float(bw[i] << 16),
+                       __uint_as_float(pw[i] & 0xffff0000u) + __uint_as_float(bw[i] & 0xffff0000u));
+  st_global16(pb + t * D + d0, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
 unsigned blocks_for(int64_t n) { return static_cast<unsigned>((n + 255) / 256); }
@@ -203,31 +240,45 @@ hipError_t launch_typed(const PatchEmbedArgs& p, hipStream_t s) {
   g.bias_seg = p.D;
   const int HC = p.cls != nullptr ? 1 : 0;
   // With position embeddings on the MFMA kernel, the product writes the patch
-  // tokens itself (each row into its token row, the position embedding added
-  // before the one rounding) and only the class-token rows remain.
+  // tokens itself (each row into its token row) and only the class-token rows
+  // remain.  Its epilogue adds one bf16 table, the position embeddings plus
+  // the patch bias (their sum rounded once, into the then unused embedding
+  // buffer, which holds it when B*N >= N + HC rows), so it carries no bias.
   GemmProblem gt = g;
   gt.epi = kEpiEmbed;
   gt.C = p.tokens;
-  gt.R = p.pos;
+  gt.R = p.embedded;
   gt.ldr = p.D;
+  gt.bias[0] = nullptr;
   gt.row_group = N;
   gt.row_base = 0;
   gt.row_skip = HC;
-  const bool fused = p.pos != nullptr && gemm_fast_ok(gt);
-  if ((e = launch_gemm(fused ? gt : g, s)) != hipSuccess) return e;
-  const int t_end = fused ? HC : N + HC;
-  if (t_end == 0) return hipSuccess;
-  const int64_t toks = p.B * t_end;
+  const bool fused = p.dtype == VITBLK_BF16 && p.pos != nullptr && p.D % 8 == 0 &&
+                     rows >= N + HC && gemm_fast_ok(gt) &&
+                     (reinterpret_cast<uintptr_t>(p.pos) & 15u) == 0 &&
+                     (reinterpret_cast<uintptr_t>(p.b_patch) & 15u) == 0;
+  if (fused) {  // the table, and the class-token rows (they do not need the product)
+    hipLaunchKernelGGL(pos_bias_kernel, dim3(blocks_for((N + HC + HC * p.B) * (p.D / 8))),
+                       dim3(256), 0, s, static_cast<const bf16_t*>(p.pos),
+                       static_cast<const bf16_t*>(p.b_patch), static_cast<bf16_t*>(p.embedded),
+                       static_cast<int64_t>(N + HC), static_cast<int>(p.D),
+                       static_cast<const bf16_t*>(p.cls), static_cast<bf16_t*>(p.tokens), p.B,
+                       static_cast<int64_t>(N + HC));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return launch_gemm(gt, s);
+  }
+  if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+  const int64_t toks = p.B * (N + HC);
   if (p.D % 8 == 0)
     hipLaunchKernelGGL((tokens_kernel<T, 8>), dim3(blocks_for(toks * (p.D / 8))), dim3(256), 0,
                        s, static_cast<const T*>(p.embedded), static_cast<const T*>(p.cls),
                        static_cast<const T*>(p.pos), static_cast<T*>(p.tokens), p.B, N, HC,
-                       static_cast<int>(p.D), t_end);
+                       static_cast<int>(p.D));
   else
     hipLaunchKernelGGL((tokens_kernel<T, 1>), dim3(blocks_for(toks * p.D)), dim3(256), 0, s,
                        static_cast<const T*>(p.embedded), static_cast<const T*>(p.cls),
                        static_cast<const T*>(p.pos), static_cast<T*>(p.tokens), p.B, N, HC,
-                       static_cast<int>(p.D), t_end);
+                       static_cast<int>(p.D));
   return hipGetLastError();
 }
 
