@@ -38,7 +38,9 @@
 //   epilogue issues all residual loads before its first store.
 // * Epilogue reads (residual, bias) are issued before the next tile's first
 //   k-slices: loads complete in issue order, so a read issued after them
-//   would hold the epilogue until those slices had landed.
+//   would hold the epilogue until those slices had landed.  A bias without
+//   the LayerNorm fold is no epilogue work at all: the accumulators start at
+//   it (fp32; the products are then added to it).
 // * LayerNorm fold (row_stats set): LN(A) @ W = rstd (A @ W - mean colsum W)
 //   (crackedaicode.com "ViT Encoder Block", "Normalize before each stage":
 //   (x - mean) * rstd per token, multiplied out).  The accumulators start at
@@ -399,6 +401,33 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[j][i][r] = nmu[i] * cs[r];
       }
+    } else if (BIAS) {
+      // Bias without the fold: the accumulators start at the bias, so the
+      // epilogue has nothing to add.  Element r of block (j, i) is column
+      // (r/4)*8 + (l/32)*4 + r%4 of block j (columns past N clamped).
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        float bv[16];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          int64_t n = n0 + wn * C::WTN + j * 32 + g4 * 8 + lhalf * 4;
+          n = n < N ? n : N - 4;
+          const int seg = static_cast<int>(n / p.bias_seg);
+          const void* bs = seg == 0 ? p.bias[0] : (seg == 1 ? p.bias[1] : p.bias[2]);
+          uint2 u = make_uint2(0u, 0u);
+          if (bs != nullptr)
+            u = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(bs) +
+                                                (n - static_cast<int64_t>(seg) * p.bias_seg));
+          bv[g4 * 4 + 0] = __uint_as_float(u.x << 16);
+          bv[g4 * 4 + 1] = __uint_as_float(u.x & 0xffff0000u);
+          bv[g4 * 4 + 2] = __uint_as_float(u.y << 16);
+          bv[g4 * 4 + 3] = __uint_as_float(u.y & 0xffff0000u);
+        }
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[j][i][r] = bv[r];
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < C::TN; ++j)
@@ -482,7 +511,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
     // (l/32)*4 + r%4 of the block: 4 runs of 4 columns per lane, the same for
     // every i.  Columns past N are clamped (never stored).
     uint2 braw[C::TN][4];
-    if (BIAS) {
+    if (BIAS && NORM) {
 #pragma unroll
       for (int j = 0; j < C::TN; ++j)
 #pragma unroll
@@ -526,9 +555,9 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[j][i][r] *= rsd[i];
     }
-    // Bias, added in fp32 to the accumulators first (before GELU or the
-    // residual).
-    if (BIAS) {
+    // Bias after the fold's scale, added in fp32 (before GELU or the
+    // residual); without the fold the accumulators started at the bias.
+    if (BIAS && NORM) {
 #pragma unroll
       for (int j = 0; j < C::TN; ++j) {
         float bv[16];
