@@ -5,7 +5,10 @@
 // accumulation.  It carries the block's four products: the packed Q|K|V
 // projection, the output projection + first residual, MLP1 + GELU and
 // MLP2 + second residual (crackedaicode.com "ViT Encoder Block",
-// "Multi-head attention" and "Feed-forward stage").
+// "Multi-head attention" and "Feed-forward stage"); also the backward's
+// data-gradient products and the patch embedding (whose token-row epilogue
+// writes each product row into its token row with the position embedding
+// added, kEpiEmbed).
 //
 // Design (gfx950, wave64):
 // * v_mfma_f32_32x32x16_bf16.  Each wave owns a (32*TN) x (32*TM) block of
@@ -48,6 +51,11 @@
 //   output never goes through memory.
 // * Split K (kEpiPartial): the tile index also runs over k-ranges whose
 //   unrounded fp32 sums are written out; a second kernel adds them in order.
+// * Tiles: 256x256 (8 waves, the default), 192x256 (8 waves, when a product
+//   has fewer big tiles than CUs and these fit in one round), 128x128 (4
+//   waves, two workgroups per CU: the output projection and the rows past
+//   the big tile's whole rounds) and its four-stage variant (one per CU,
+//   for a last partial round); launch_gemm chooses.
 // * Tile order: workgroups are dispatched round-robin over the 8 XCDs; each
 //   XCD is given a contiguous run of tiles per round, walked in groups of 8
 //   M-tiles so that the tiles resident at once on an XCD share A and W
