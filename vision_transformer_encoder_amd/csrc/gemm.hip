@@ -39,11 +39,11 @@
 //   k-slices are issued before the current tile's epilogue, so the load
 //   latency at a tile start overlaps the stores of the previous tile, and the
 //   epilogue issues all residual loads before its first store.
-// * Epilogue reads (residual, bias) are issued before the next tile's first
+// * Epilogue reads (residual) are issued before the next tile's first
 //   k-slices: loads complete in issue order, so a read issued after them
-//   would hold the epilogue until those slices had landed.  A bias without
-//   the LayerNorm fold is no epilogue work at all: the accumulators start at
-//   it (fp32; the products are then added to it).
+//   would hold the epilogue until those slices had landed.  A bias is no
+//   epilogue work at all: the accumulators start at it (fp32; the products
+//   are then added to it), with the LayerNorm fold at b / rstd (below).
 // * LayerNorm fold (row_stats set): LN(A) @ W = rstd (A @ W - mean colsum W)
 //   (crackedaicode.com "ViT Encoder Block", "Normalize before each stage":
 //   (x - mean) * rstd per token, multiplied out).  The accumulators start at
@@ -374,15 +374,35 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
 
   float rsd[C::TM];  // LayerNorm fold: rstd of the lane's rows of the current tile
   while (true) {
+    // The bias of block j's columns for this lane: element r of block (j, i)
+    // is column (r/4)*8 + (l/32)*4 + r%4 of block j (columns past N clamped).
+    auto bias_run = [&](int j, float* bv) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        int64_t n = n0 + wn * C::WTN + j * 32 + g4 * 8 + lhalf * 4;
+        n = n < N ? n : N - 4;
+        const int seg = static_cast<int>(n / p.bias_seg);
+        const void* bs = seg == 0 ? p.bias[0] : (seg == 1 ? p.bias[1] : p.bias[2]);
+        uint2 u = make_uint2(0u, 0u);
+        if (bs != nullptr)
+          u = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(bs) +
+                                              (n - static_cast<int64_t>(seg) * p.bias_seg));
+        bv[g4 * 4 + 0] = __uint_as_float(u.x << 16);
+        bv[g4 * 4 + 1] = __uint_as_float(u.x & 0xffff0000u);
+        bv[g4 * 4 + 2] = __uint_as_float(u.y << 16);
+        bv[g4 * 4 + 3] = __uint_as_float(u.y & 0xffff0000u);
+      }
+    };
     if (NORM) {
       // LayerNorm fold, mean term: the accumulators start at -mean_m *
       // colsum_n, so after the k loop they hold A @ W - mean colsum and the
-      // epilogue only scales by rstd_m.  The loads (L2-resident) go out
+      // epilogue only scales by rstd_m.  With a bias they start at
+      // -mean_m colsum_n + b_n / rstd_m, so the same scale also yields the
+      // bias (rstd (A @ W - mean colsum) + b).  The loads (L2-resident) go out
       // before the first k-slice's wait, which they share.  A lane's rows
-      // are lrow of each 32-row block i; its columns in block j are the 4
-      // runs of 4 described for the bias below.  Rows and columns past M or
-      // N are clamped (never stored).
-      float nmu[C::TM];
+      // are lrow of each 32-row block i.  Rows and columns past M or N are
+      // clamped (never stored).
+      float nmu[C::TM], sig[C::TM];
 #pragma unroll
       for (int i = 0; i < C::TM; ++i) {
         int64_t m = m0 + wm * C::WTM + i * 32 + lrow;
@@ -390,10 +410,11 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
         const float2 st = *reinterpret_cast<const float2*>(p.row_stats + 2 * m);
         nmu[i] = -st.x;
         rsd[i] = st.y;
+        sig[i] = BIAS ? 1.0f / st.y : 0.f;
       }
 #pragma unroll
       for (int j = 0; j < C::TN; ++j) {
-        float cs[16];
+        float cs[16], bv[16];
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           int64_t n = n0 + wn * C::WTN + j * 32 + g4 * 8 + lhalf * 4;
@@ -404,33 +425,20 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
           cs[g4 * 4 + 2] = c4.z;
           cs[g4 * 4 + 3] = c4.w;
         }
+        if (BIAS) bias_run(j, bv);
 #pragma unroll
         for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[j][i][r] = nmu[i] * cs[r];
+          for (int r = 0; r < 16; ++r)
+            acc[j][i][r] = BIAS ? __builtin_fmaf(sig[i], bv[r], nmu[i] * cs[r]) : nmu[i] * cs[r];
       }
     } else if (BIAS) {
       // Bias without the fold: the accumulators start at the bias, so the
-      // epilogue has nothing to add.  Element r of block (j, i) is column
-      // (r/4)*8 + (l/32)*4 + r%4 of block j (columns past N clamped).
+      // epilogue has nothing to add.
 #pragma unroll
       for (int j = 0; j < C::TN; ++j) {
         float bv[16];
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          int64_t n = n0 + wn * C::WTN + j * 32 + g4 * 8 + lhalf * 4;
-          n = n < N ? n : N - 4;
-          const int seg = static_cast<int>(n / p.bias_seg);
-          const void* bs = seg == 0 ? p.bias[0] : (seg == 1 ? p.bias[1] : p.bias[2]);
-          uint2 u = make_uint2(0u, 0u);
-          if (bs != nullptr)
-            u = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(bs) +
-                                                (n - static_cast<int64_t>(seg) * p.bias_seg));
-          bv[g4 * 4 + 0] = __uint_as_float(u.x << 16);
-          bv[g4 * 4 + 1] = __uint_as_float(u.x & 0xffff0000u);
-          bv[g4 * 4 + 2] = __uint_as_float(u.y << 16);
-          bv[g4 * 4 + 3] = __uint_as_float(u.y & 0xffff0000u);
-        }
+        bias_run(j, bv);
 #pragma unroll
         for (int i = 0; i < C::TM; ++i)
 #pragma unroll
@@ -515,25 +523,6 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
           }
       }
     }
-    // Bias: accumulator element r of block (j, i) is column (r/4)*8 +
-    // (l/32)*4 + r%4 of the block: 4 runs of 4 columns per lane, the same for
-    // every i.  Columns past N are clamped (never stored).
-    uint2 braw[C::TN][4];
-    if (BIAS && NORM) {
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          int64_t n = cn0 + wn * C::WTN + j * 32 + g4 * 8 + lhalf * 4;
-          n = n < N ? n : N - 4;
-          const int seg = static_cast<int>(n / p.bias_seg);
-          const void* bs = seg == 0 ? p.bias[0] : (seg == 1 ? p.bias[1] : p.bias[2]);
-          braw[j][g4] = make_uint2(0u, 0u);
-          if (bs != nullptr)
-            braw[j][g4] = *reinterpret_cast<const uint2*>(
-                static_cast<const bf16_t*>(bs) + (n - static_cast<int64_t>(seg) * p.bias_seg));
-        }
-    }
 
     // Start the next tile's first k-slices before this tile's epilogue (all
     // waves are done reading LDS once past this barrier).
@@ -554,7 +543,8 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
     // first store (addresses clamped into range), and added in fp32 before
     // the single rounding to bf16.
     bf16_t* Cp = static_cast<bf16_t*>(p.C);
-    // LayerNorm fold, scale term (before the bias): acc = rstd_m * acc.
+    // LayerNorm fold, scale term: acc = rstd_m * acc (the bias, if any, was
+    // in the accumulators' start value).
     if (NORM) {
 #pragma unroll
       for (int i = 0; i < C::TM; ++i)
@@ -562,26 +552,6 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
         for (int j = 0; j < C::TN; ++j)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[j][i][r] *= rsd[i];
-    }
-    // Bias after the fold's scale, added in fp32 (before GELU or the
-    // residual); without the fold the accumulators started at the bias.
-    if (BIAS && NORM) {
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) {
-        float bv[16];
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const uint2 u = braw[j][g4];
-          bv[g4 * 4 + 0] = __uint_as_float(u.x << 16);
-          bv[g4 * 4 + 1] = __uint_as_float(u.x & 0xffff0000u);
-          bv[g4 * 4 + 2] = __uint_as_float(u.y << 16);
-          bv[g4 * 4 + 3] = __uint_as_float(u.y & 0xffff0000u);
-        }
-#pragma unroll
-        for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[j][i][r] += bv[r];
-      }
     }
     // The plain and residual epilogues store each 32-row block as whole row
     // lines (rows_to_lines): 8% faster on the fused Q|K|V projection.  The
