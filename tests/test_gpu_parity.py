@@ -312,6 +312,11 @@ SMALL_BLOCKS = [
     (2, 7, 20, 4, 36, 1e-6, "bf16"),       # D not a multiple of 8: weights and LN1 statistics
                                            # in separate launches
     (1, 3, 8, 8, 8, 1e-6, "bf16"),         # H = D (head width 1)
+    (1, 1, 64, 1, 128, 1e-6, "bf16"),      # one token: attention returns V
+    (3, 1, 32, 2, 64, 1e-5, "fp32"),       # one token per sequence, fp32
+    (2, 70, 128, 1, 256, 1e-6, "bf16"),    # H = 1 (head width 128: the resident kernel)
+    (2, 40, 192, 2, 384, 1e-6, "bf16"),    # head width 96
+    (2, 97, 256, 4, 512, 1e-6, "fp32"),    # fp32 matrix-core products and attention
 ]
 
 
