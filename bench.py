@@ -133,12 +133,26 @@ def step_stats(per):
             "max": round(float(a.max()), 5)}
 
 
+_QUEUE_AHEAD = {}
+
+
 def time_launches(fn, reps, torch):
-    """Average duration of fn() (one kernel launch) over reps, HIP events on the launch stream."""
+    """Average duration of fn() (one kernel launch) over reps, HIP events on the launch stream.
+
+    A few untimed products run first, long enough for the host to enqueue
+    every timed launch behind them: a launch shorter than its host-side call
+    (argument checks, marshalling) would otherwise be timed at the host's rate.
+    """
     s = torch.cuda.current_stream()
     fn()
+    if "a" not in _QUEUE_AHEAD:
+        _QUEUE_AHEAD["a"] = torch.ones((4096, 4096), dtype=torch.bfloat16, device="cuda")
+        _QUEUE_AHEAD["c"] = torch.empty_like(_QUEUE_AHEAD["a"])
+    qa, qc = _QUEUE_AHEAD["a"], _QUEUE_AHEAD["c"]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    for _ in range(2 + reps // 4):  # about 0.15 ms each
+        torch.mm(qa, qa, out=qc)
     e0.record(s)
     for _ in range(reps):
         fn()
@@ -521,7 +535,7 @@ def main():
                                                  g["w_mlp1"], g["w_mlp2"], packed=packed),
                          "hbm", pack_bytes),
     }
-    if affine or w.dtype != "bf16":
+    if w.dtype != "bf16":
         kern.update({
             "ln1": (lambda: vb.layernorm(x2, w.eps, gamma=gq("ln1_gamma"), beta=gq("ln1_beta"),
                                          out=xn), "hbm", 2 * M * D * es),
@@ -530,17 +544,29 @@ def main():
                          "mfma", 2 * M * D * 3 * D),
         })
     else:
-        # bf16 without gains or shifts: each LayerNorm is folded into the next
-        # product (row statistics, then rstd (x @ W - mean colsum) in the
-        # product's epilogue), as vitblk_forward does.
+        # bf16: each LayerNorm is folded into the next product (row
+        # statistics, then rstd (x @ W - mean colsum) in the product), as the
+        # block does; with a gain and shift the product takes the fold's
+        # scaled weight copy, its column sums and bias + beta @ W (one launch
+        # per call, the fold step below).
         cs_qkv, cs_1 = vb.packed_col_sums(packed, D, F, tdt)
         st1 = torch.empty((M, 2), dtype=torch.float32, device=dev)
         st2 = torch.empty_like(st1)
-        kern.update({
-            "ln1_stats": (lambda: vb.row_stats(x2, w.eps, out=st1), "hbm", M * D * es + M * 8),
-            "qkv_gemm": (lambda: vb.linear_normed(x2, wqkv_t, cs_qkv, st1, vb.EPI_NONE, out=qkv),
-                         "mfma", 2 * M * D * 3 * D),
-        })
+        kern["ln1_stats"] = (lambda: vb.row_stats(x2, w.eps, out=st1), "hbm", M * D * es + M * 8)
+        if affine:
+            f1 = vb.affine_fold(wqkv_t, gq("ln1_gamma"), gq("ln1_beta"), bqkv)
+            f2 = vb.affine_fold(w1_t, gq("ln2_gamma"), gq("ln2_beta"), gq("b_mlp1"))
+            fold_bytes = lambda n: 2 * n * D * es + 2 * D * es + n * (4 + 2 * es)  # noqa: E731
+            kern.update({
+                "ln1_fold": (lambda: vb.affine_fold(wqkv_t, gq("ln1_gamma"), gq("ln1_beta"), bqkv,
+                                                    out=f1), "hbm", fold_bytes(3 * D)),
+                "qkv_gemm": (lambda: vb.linear_normed(x2, f1[0], f1[1], st1, vb.EPI_NONE,
+                                                      bias=f1[2], out=qkv),
+                             "mfma", 2 * M * D * 3 * D),
+            })
+        else:
+            kern["qkv_gemm"] = (lambda: vb.linear_normed(x2, wqkv_t, cs_qkv, st1, vb.EPI_NONE,
+                                                         out=qkv), "mfma", 2 * M * D * 3 * D)
     # Attention's bound depends on T: 4 N T^2 D FLOP against 4 M D elements
     # (Q, K, V read, O written), an intensity of about T / es FLOP per byte,
     # below the ridge (peak FLOP/s / peak bytes/s) at ViT sequence lengths.
@@ -551,7 +577,7 @@ def main():
                  else att_unit)
     kern["attention"] = (lambda: vb.attention(qkv, w.N, w.T, w.H, out=att), att_bound,
                          att_bytes if att_bound == "hbm" else att_flops)
-    if affine or w.dtype != "bf16":
+    if w.dtype != "bf16":
         kern.update({
             "oproj_residual": (lambda: vb.linear(att, wo_t, vb.EPI_RESIDUAL, residual=x2,
                                                  bias=gq("b_o"), out=y), "mfma", 2 * M * D * D),
@@ -562,15 +588,24 @@ def main():
         })
     else:
         # The output projection writes the LN2 row statistics' partials from
-        # its epilogue and one small kernel combines them, as in the block.
+        # its epilogue and one small kernel combines them, as in the block
+        # (this step entry takes no bias: the affine block's b_o starts in the
+        # accumulators and costs no epilogue work).
         ows = torch.empty(vb.linear_residual_row_stats_workspace_bytes(M, D), dtype=torch.uint8,
                           device=dev)
-        kern.update({
-            "oproj_residual_ln2_stats": (lambda: vb.linear_residual_row_stats(
-                att, wo_t, x2, w.eps, out=y, stats=st2, workspace=ows), "mfma", 2 * M * D * D),
-            "mlp1_gelu": (lambda: vb.linear_normed(y, w1_t, cs_1, st2, vb.EPI_GELU, out=hid),
-                          "mfma", 2 * M * D * F),
-        })
+        kern["oproj_residual_ln2_stats"] = (lambda: vb.linear_residual_row_stats(
+            att, wo_t, x2, w.eps, out=y, stats=st2, workspace=ows), "mfma", 2 * M * D * D)
+        if affine:
+            kern.update({
+                "ln2_fold": (lambda: vb.affine_fold(w1_t, gq("ln2_gamma"), gq("ln2_beta"),
+                                                    gq("b_mlp1"), out=f2), "hbm", fold_bytes(F)),
+                "mlp1_gelu": (lambda: vb.linear_normed(y, f2[0], f2[1], st2, vb.EPI_GELU,
+                                                       bias=f2[2], out=hid),
+                              "mfma", 2 * M * D * F),
+            })
+        else:
+            kern["mlp1_gelu"] = (lambda: vb.linear_normed(y, w1_t, cs_1, st2, vb.EPI_GELU,
+                                                          out=hid), "mfma", 2 * M * D * F)
     kern["mlp2_residual"] = (lambda: vb.linear(hid, w2_t, vb.EPI_RESIDUAL, residual=y,
                                                bias=gq("b_mlp2"), out=o2), "mfma", 2 * M * F * D)
     for name in [k for k in kern if k not in ("pack_weights", "mlp2_residual")]:

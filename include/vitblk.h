@@ -208,9 +208,13 @@ typedef struct {
 
 /*
  * vitblk_forward() with the affine variant's parameters (may be NULL).  The
- * same eight kernels: the gains and shifts are applied by the LayerNorm
- * kernel, the biases in the GEMM epilogues (before GELU and before the
- * residual add, in fp32).  Same workspace and errors as vitblk_forward().
+ * biases enter the products in fp32 (before GELU and before the residual
+ * add).  In bf16 each LayerNorm with a gain or shift is folded into the
+ * product after it as the plain block's are (vitblk_affine_fold()'s scaled
+ * weight copy, column sums and bias, per call, in workspace regions that are
+ * dead at that point) when those regions hold the copy (N T >= 3 D and
+ * about N T >= F); otherwise, and in fp32, the LayerNorm kernel applies the
+ * gain and shift.  Same workspace and errors as vitblk_forward().
  */
 int vitblk_forward_affine(const void* x, const void* w_q, const void* w_k, const void* w_v,
                           const void* w_o, const void* w_mlp1, const void* w_mlp2,
@@ -379,6 +383,26 @@ int vitblk_linear_normed(const void* a, const void* w_t, const float* col_sums,
                          const float* row_stats, const void* bias, void* out, int64_t M,
                          int64_t K, int64_t Nout, int epilogue, int dtype,
                          vitblk_stream_t stream);
+
+/* The affine LayerNorm folded into the product after it (bf16 only).  For
+ * the LayerNorm gain gamma [K] and shift beta [K]
+ * (ai-engineer-exhaustive.pages.dev "ViT Encoder Block", "Key Equations",
+ * steps 1 and 4), W given out-major (w_t [Nout, K]) and the product's bias
+ * [Nout]:
+ *
+ *   w_scaled[n, k] = bf16(gamma_k * w_t[n, k])
+ *   col_sums[n]    = sum_k w_scaled[n, k]              (fp32, fixed order)
+ *   bias_out[n]    = bf16(bias_n + sum_k beta_k * w_t[n, k])
+ *
+ * so that vitblk_linear_normed(a, w_scaled, col_sums, row_stats(a), bias_out)
+ * is (LN(a) * gamma + beta) @ W + bias up to rounding (LN(a) * gamma @ W =
+ * rstd (a @ diag(gamma) W - mean colsum(diag(gamma) W))).  gamma, beta and
+ * bias may each be NULL (ones, zeros, zeros).  K a multiple of 8; w_t,
+ * w_scaled, gamma, beta and col_sums 16-byte aligned; the three outputs must
+ * not overlap the inputs or each other.  Other dtypes: VITBLK_ERR_UNSUPPORTED. */
+int vitblk_affine_fold(const void* w_t, const void* gamma, const void* beta, const void* bias,
+                       void* w_scaled, float* col_sums, void* bias_out, int64_t Nout, int64_t K,
+                       int dtype, vitblk_stream_t stream);
 
 /* The output projection with the first residual and the second LayerNorm's
  * statistics: out = residual + a @ W (a [M, K], w_t [Nout, K] out-major as

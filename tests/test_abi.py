@@ -187,6 +187,27 @@ def test_step_entry_points_errors(lib):
     assert ln(a, b, c, d, None, c, 4, 8, 8, vb.EPI_GELU, 1, None) == ALIAS
     assert ln(a, b, c, d, None, d, 4, 8, 8, vb.EPI_NONE, 1, None) == ALIAS
     assert ln(a, b, c, d, None, a, 4, 8, 8, vb.EPI_NONE, 1, None) == ALIAS
+    # the affine LayerNorm fold: bf16 only, K a multiple of 8, outputs clear
+    # of the inputs and of each other (w_t a, gamma b, beta c, bias d;
+    # outputs e, col sums at _addr(6), bias_out at _addr(7))
+    fo = lambda *args: lib.vitblk_affine_fold(*args)  # noqa: E731
+    cs, bo = _addr(6), _addr(7)
+    assert fo(None, b, c, d, e, cs, bo, 8, 16, 1, None) == INVALID
+    assert fo(a, b, c, d, None, cs, bo, 8, 16, 1, None) == INVALID
+    assert fo(a, b, c, d, e, None, bo, 8, 16, 1, None) == INVALID
+    assert fo(a, b, c, d, e, cs, None, 8, 16, 1, None) == INVALID
+    assert fo(a, off(b, 8), c, d, e, cs, bo, 8, 16, 1, None) == INVALID
+    assert fo(a, b, c, d, e, off(cs, 4), bo, 8, 16, 1, None) == INVALID
+    assert fo(a, b, c, off(d, 1), e, cs, bo, 8, 16, 1, None) == INVALID
+    assert fo(a, b, c, d, e, cs, bo, 0, 16, 1, None) == INVALID
+    assert fo(a, b, c, d, e, cs, bo, 8, 16, 9, None) == INVALID
+    assert fo(a, b, c, d, e, cs, bo, 8, 16, 0, None) == UNSUPPORTED  # fp32
+    assert fo(a, b, c, d, e, cs, bo, 8, 12, 1, None) == UNSUPPORTED  # K % 8
+    assert fo(a, b, c, d, off(a, 64), cs, bo, 8, 16, 1, None) == ALIAS
+    assert fo(a, b, c, d, e, off(b, 16), bo, 8, 16, 1, None) == ALIAS
+    assert fo(a, b, c, d, e, cs, off(d, 2), 8, 16, 1, None) == ALIAS
+    assert fo(a, b, c, d, e, cs, off(e, 64), 8, 16, 1, None) == ALIAS
+    assert fo(a, None, None, None, e, cs, off(cs, 16), 8, 16, 1, None) == ALIAS
     # the output projection with the next LayerNorm's statistics: residual
     # required, stats 8-byte aligned, a workspace of one pair per 64 columns
     rs = lambda *args: lib.vitblk_linear_residual_row_stats(*args)  # noqa: E731

@@ -71,6 +71,57 @@ def test_linear_bias(dtype, epi, M, K, N):
     assert_close(got, ref, dtype, f"linear+bias {epi} M={M} K={K} N={N}")
 
 
+# ------------------------------------------------------------------ the fold
+
+@pytest.mark.parametrize("Nout,K", [(768, 256), (40, 16), (3072, 1024), (24, 2056)])
+@pytest.mark.parametrize("which", ["all", "gamma", "beta", "bias", "none"])
+def test_affine_fold_step(Nout, K, which):
+    # w_scaled = bf16(gamma_k w[n, k]): the product of two bf16 values is
+    # exact in fp32, so one rounding, bit for bit; the column sums are fp32
+    # sums of those values; bias_out = bf16(b + beta @ W) within one bf16 ulp
+    # (fp32 against float64 accumulation may land on either side of a tie).
+    import torch
+    rng = np.random.default_rng(Nout * 7 + K)
+    w_t = _rand(rng, (Nout, K), "bf16", scale=1 / math.sqrt(K))
+    g = _rand(rng, (K,), "bf16", scale=0.5, offset=1.0) if which in ("all", "gamma") else None
+    be = _rand(rng, (K,), "bf16", scale=0.5) if which in ("all", "beta") else None
+    b = _rand(rng, (Nout,), "bf16", scale=0.5) if which in ("all", "bias") else None
+    dev = lambda a: None if a is None else to_dev(a, "bf16")  # noqa: E731
+    ws, cs, bo = vb.affine_fold(dev(w_t), dev(g), dev(be), dev(b))
+    torch.cuda.synchronize()
+    ref_ws = round_to(w_t * (1.0 if g is None else g[None, :]), "bf16")
+    assert np.array_equal(to_host(ws), ref_ws)
+    got_cs = cs.cpu().double().numpy()
+    assert np.all(np.abs(got_cs - ref_ws.sum(1)) <= 1e-6 * np.abs(ref_ws).sum(1) + 1e-30)
+    ref_b = (0.0 if b is None else b) + (0.0 if be is None else w_t @ be)
+    ref_b = np.broadcast_to(np.asarray(ref_b, dtype=np.float64), (Nout,))
+    got_b = to_host(bo)
+    assert np.all(np.abs(got_b - ref_b) <= 2.0 ** -7 * np.abs(ref_b) + 1e-30), \
+        np.max(np.abs(got_b - ref_b))
+
+
+@pytest.mark.parametrize("M,K,N,epi", [(300, 256, 512, "gelu"), (517, 1024, 768, "none"),
+                                       (33, 64, 24, "none")])
+def test_affine_fold_then_normed_product(M, K, N, epi):
+    # The fold's operands in vitblk_linear_normed give (LN(a) gamma + beta) @ W
+    # + b of the oracle's LayerNorm, gain and shift, and product.
+    rng = np.random.default_rng(M + K + N)
+    a = _rand(rng, (M, K), "bf16", scale=2.0, offset=0.5)
+    w = _rand(rng, (K, N), "bf16", scale=1 / math.sqrt(K))
+    g = _rand(rng, (K,), "bf16", scale=0.3, offset=1.0)
+    be = _rand(rng, (K,), "bf16", scale=0.5)
+    b = _rand(rng, (N,), "bf16", scale=0.5)
+    da = to_dev(a, "bf16")
+    ws, cs, bo = vb.affine_fold(to_dev(w.T, "bf16"), to_dev(g, "bf16"), to_dev(be, "bf16"),
+                                to_dev(b, "bf16"))
+    st = vb.row_stats(da, 1e-6)
+    got = to_host(vb.linear_normed(da, ws, cs, st, EPIS[epi], bias=bo))
+    ref = oracle.add_bias(oracle.project(oracle.affine(oracle.layer_norm(a, 1e-6), g, be), w), b)
+    if epi == "gelu":
+        ref = oracle.gelu_tanh(ref)
+    assert_close(got, ref, "bf16", f"fold + normed product {epi} M={M} K={K} N={N}")
+
+
 # ------------------------------------------------------------------ the block
 
 def _run(inp, prm, H, eps, dtype, packed=False, drop=()):
@@ -186,6 +237,54 @@ def test_affine_block_with_some_parameters_absent(drop):
                  f"affine block without {drop}")
 
 
+# Sizes where both affine LayerNorms fold into the products after them (bf16):
+# the gain-scaled weight copy of Q|K|V ([3D, D]) fits in the token-sized region
+# y (M >= 3D) and that of MLP1 ([F, D]) beside the row statistics in another
+# (8 M + 2 F D + 6 F bytes, each part rounded up to 256, <= 2 M D).  The
+# smaller blocks above (M < 3D) write their LayerNorms out.
+FOLDED = (4, 197, 128, 2, 512)
+
+
+def _folds(N, T, D, F):
+    M = N * T
+    up = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    f1 = up(up(3 * D * D * 2) + 3 * D * 4) + 3 * D * 2
+    f2 = up(up(up(8 * M) + F * D * 2) + F * 4) + F * 2
+    return f1 <= M * D * 2 and f2 <= M * D * 2
+
+
+@pytest.mark.parametrize("drop", [(), ("ln1_gamma",), ("ln1_beta",), ("ln2_gamma", "b_mlp1"),
+                                  ("ln2_beta", "b_q", "b_v"), ("ln1_gamma", "ln2_gamma"),
+                                  ("ln1_beta", "ln2_beta", "b_o")])
+def test_affine_block_folded(drop):
+    # The folded path: diag(gamma) W, its column sums and b + beta @ W, per
+    # call, with either of gain and shift absent, and the output projection's
+    # bias on the LN2 row-partials epilogue.
+    N, T, D, H, F = FOLDED
+    assert _folds(N, T, D, F)
+    inp = make_block_inputs(N, T, D, F, "bf16", seed=21)
+    prm = make_affine_params(D, F, "bf16", seed=21)
+    out, _ = _run(inp, prm, H, 1e-6, "bf16", drop=drop)
+    assert_close(to_host(out), _oracle(inp, prm, H, 1e-6, drop=drop), "bf16",
+                 f"folded affine block without {drop}")
+
+
+def test_affine_block_folded_large_gains():
+    # Gains far from 1 (N(0, 1): near 0 and of both signs) and unit shifts:
+    # the scaled copy is rounded to bf16 once, as the written-out LayerNorm's
+    # output is.  (Much larger gains scale the attention scores by gamma^2 and
+    # leave any bf16 block outside the bar: at 3 N(0, 1) a CPU emulation of
+    # the written-out path's roundings is off by 0.38, the fold's by 0.30.)
+    N, T, D, H, F = FOLDED
+    rng = np.random.default_rng(22)
+    inp = make_block_inputs(N, T, D, F, "bf16", seed=22)
+    prm = make_affine_params(D, F, "bf16", seed=22)
+    for k in ("ln1_gamma", "ln2_gamma", "ln1_beta", "ln2_beta"):
+        prm[k] = round_to(rng.standard_normal(D), "bf16")
+    out, _ = _run(inp, prm, H, 1e-6, "bf16")
+    assert_close(to_host(out), _oracle(inp, prm, H, 1e-6), "bf16", "folded, large gains")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_affine_without_parameters_is_the_plain_block(dtype):
     import torch
@@ -198,12 +297,13 @@ def test_affine_without_parameters_is_the_plain_block(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-def test_affine_packed_matches_unpacked(dtype):
+@pytest.mark.parametrize("N,T,D,H,F", [(2, 197, 256, 4, 1024), FOLDED])
+def test_affine_packed_matches_unpacked(dtype, N, T, D, H, F):
     import torch
-    inp = make_block_inputs(2, 197, 256, 1024, dtype, seed=3)
-    prm = make_affine_params(256, 1024, dtype, seed=3)
-    a, _ = _run(inp, prm, 4, 1e-6, dtype)
-    b, _ = _run(inp, prm, 4, 1e-6, dtype, packed=True)
+    inp = make_block_inputs(N, T, D, F, dtype, seed=3)
+    prm = make_affine_params(D, F, dtype, seed=3)
+    a, _ = _run(inp, prm, H, 1e-6, dtype)
+    b, _ = _run(inp, prm, H, 1e-6, dtype, packed=True)
     assert torch.equal(a, b)
 
 

@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     attention_first_queries,
     attention_backward,
     attention_backward_workspace_bytes,
+    affine_fold,
     backward,
     backward_workspace_bytes,
     encoder_forward,

@@ -50,6 +50,7 @@ SIGNATURES = {
     "vitblk_linear_bias": (_I, [_P] * 5 + [_I64, _I64, _I64, _I, _I, _P]),
     "vitblk_row_stats": (_I, [_P, _P, _I64, _I64, _D, _I, _P]),
     "vitblk_linear_normed": (_I, [_P] * 6 + [_I64, _I64, _I64, _I, _I, _P]),
+    "vitblk_affine_fold": (_I, [_P] * 4 + [_P] * 3 + [_I64, _I64, _I, _P]),
     "vitblk_linear_residual_row_stats_workspace_bytes": (_SZ, [_I64, _I64]),
     "vitblk_linear_residual_row_stats": (_I, [_P] * 5 + [_I64] * 3 + [_D, _I, _P, _SZ, _P]),
     "vitblk_encoder_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64, _I]),
@@ -646,6 +647,37 @@ def linear_normed(a, w_t, col_sums, stats, epilogue: int = EPI_NONE, bias=None, 
                                      _stream(a, stream))
     _check("vitblk_linear_normed", st)
     return out
+
+
+def affine_fold(w_t, gamma=None, beta=None, bias=None, out=None, stream=None):
+    """The affine LayerNorm folded into the product after it (bf16):
+    (w_scaled [Nout, K], col_sums fp32 [Nout], bias_out [Nout]) with
+    w_scaled = gamma * w_t (per column k), col_sums its row sums and
+    bias_out = bias + w_t @ beta, the operands vitblk_linear_normed takes for
+    (LN(a) * gamma + beta) @ W + bias.  w_t [Nout, K] is W out-major.
+    out: optional preallocated triple."""
+    torch = _torch()
+    _rank(w_t, 2, "w_t")
+    Nout, K = w_t.shape
+    _shape(gamma, (K,), "gamma")
+    _shape(beta, (K,), "beta")
+    _shape(bias, (Nout,), "bias")
+    _dev(w_t, gamma, beta, bias)
+    if out is None:
+        out = (torch.empty_like(w_t), torch.empty(Nout, dtype=torch.float32, device=w_t.device),
+               torch.empty(Nout, dtype=w_t.dtype, device=w_t.device))
+    ws, cs, bo = out
+    _shape(ws, (Nout, K), "w_scaled")
+    _shape(bo, (Nout,), "bias_out")
+    _dev(w_t, ws, bo)
+    _dev_f32(w_t, cs)
+    if cs.numel() != Nout:
+        raise ValueError("col_sums must hold Nout floats")
+    st = load().vitblk_affine_fold(_ptr(w_t), _ptr(gamma), _ptr(beta), _ptr(bias), _ptr(ws),
+                                   _ptr(cs), _ptr(bo), Nout, K, dtype_code(w_t.dtype),
+                                   _stream(w_t, stream))
+    _check("vitblk_affine_fold", st)
+    return ws, cs, bo
 
 
 def linear_residual_row_stats_workspace_bytes(M, Nout) -> int:

@@ -87,6 +87,57 @@ int pack_weights(const void* w_q, const void* w_k, const void* w_v, const void* 
   return VITBLK_OK;
 }
 
+// Where an affine LayerNorm (gain and/or shift) folds into the product after
+// it (bf16): the gain-scaled weight copy, its column sums and the folded bias
+// (launch_affine_fold) go to a region that is dead while that product runs,
+// at these offsets from the region's start: LN1's into region y (written only
+// by the output projection, after the fused Q|K|V product), LN2's into region
+// act after the row statistics (its concatenated heads are dead once the
+// output projection has run).  The block writes such a LayerNorm out where
+// the copy does not fit (M < 3D or about M < F) or an operand is misaligned.
+struct FoldCopy {
+  size_t w, cs, b, end;
+};
+
+FoldCopy fold_copy(size_t start, int64_t nout, int64_t K) {
+  const auto up = [](size_t v) { return (v + kRegionAlign - 1) / kRegionAlign * kRegionAlign; };
+  FoldCopy f;
+  f.w = up(start);
+  f.cs = up(f.w + static_cast<size_t>(nout) * static_cast<size_t>(K) * 2);
+  f.b = up(f.cs + static_cast<size_t>(nout) * 4);
+  f.end = f.b + static_cast<size_t>(nout) * 2;
+  return f;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Which LayerNorms the block folds.  fold: the product applies the row
+// statistics; affine: with the gain/shift fold's copy (region offsets f).
+struct FoldPlan {
+  bool fold1, affine1, fold2, affine2;
+  FoldCopy f1, f2;
+};
+
+FoldPlan plan_folds(const vitblk_affine_params& q, const char* pk, const char* act,
+                    const WorkspacePlan& pl, int64_t Mo, int64_t D, int64_t F, int dtype) {
+  FoldPlan fp{};
+  if (dtype != VITBLK_BF16) return fp;
+  const bool has1 = q.ln1_gamma != nullptr || q.ln1_beta != nullptr;
+  const bool has2 = q.ln2_gamma != nullptr || q.ln2_beta != nullptr;
+  const char* a = act + pl.off_act;
+  const char* y = act + pl.off_y;
+  fp.f1 = fold_copy(0, 3 * D, D);
+  fp.f2 = fold_copy(static_cast<size_t>(Mo) * 8, F, D);  // after Mo rows' (mean, rstd)
+  const bool ok = D % 8 == 0 && aligned16(a) && aligned16(y);
+  fp.affine1 = has1 && ok && aligned16(pk + pl.packed.off_qkv) &&
+               fp.f1.end <= pl.act_total - pl.off_y;
+  fp.affine2 = has2 && ok && aligned16(pk + pl.packed.off_1) &&
+               fp.f2.end <= pl.off_y - pl.off_act;
+  fp.fold1 = !has1 || fp.affine1;
+  fp.fold2 = !has2 || fp.affine2;
+  return fp;
+}
+
 // The seven steps of the block on packed (out-major) weights.  prm: the
 // affine variant's optional gains, shifts and biases (null: none).
 // stats1_ready: the first LayerNorm's row statistics are already in place
@@ -110,23 +161,44 @@ int run_block(const void* x, const void* packed, const vitblk_affine_params* prm
   char* y = act + pl.off_y;      // [M, D]
   const float feps = static_cast<float>(eps);
 
-  // A LayerNorm without gain or shift folds into the product that follows
-  // it (bf16): LN(x) @ W = rstd (x @ W - mean 1^T W), so only the rows'
-  // statistics are computed (into region act) and the GEMM epilogue applies
-  // them with W's column sums from the packed weights.  The affine
-  // LayerNorm, and fp32, are written out.
+  // A LayerNorm folds into the product that follows it (bf16): LN(x) @ W =
+  // rstd (x @ W - mean 1^T W), so only the rows' statistics are computed
+  // (into region act) and the product applies them with W's column sums from
+  // the packed weights.  With a gain and shift the product takes the
+  // launch_affine_fold copy instead (diag(gamma) W, its column sums, the bias
+  // plus beta @ W).  fp32, and an affine LayerNorm whose copy has no room,
+  // are written out.
   float* stats = reinterpret_cast<float*>(a);
-  const bool fold1 = dtype == VITBLK_BF16 && q.ln1_gamma == nullptr && q.ln1_beta == nullptr;
-  const bool fold2 = dtype == VITBLK_BF16 && q.ln2_gamma == nullptr && q.ln2_beta == nullptr;
+  const int64_t Mo = cls_only ? N : M;  // rows after attention
+  const FoldPlan fp = plan_folds(q, pk, act, pl, Mo, D, F, dtype);
 
   // LN1: xn = gamma_1 LN(x) + beta_1, then Q | K | V = xn @ [w_q | w_k | w_v] + [b_q | b_k | b_v]
   GemmProblem pq = linear_problem(a, pk + pl.packed.off_qkv, big, nullptr, M, D, 3 * D,
                                   VITBLK_EPI_NONE, dtype, q.b_q, q.b_k, q.b_v, D);
-  if (fold1) {
-    if (!stats1_ready) VITBLK_LAUNCH(launch_row_stats(x, D, stats, M, D, feps, dtype, s));
+  if (fp.fold1) {
+    bool stats_done = stats1_ready;
     pq.A = x;
     pq.row_stats = stats;
     pq.col_sums = reinterpret_cast<const float*>(pk + pl.packed.off_cs_qkv);
+    if (fp.affine1) {
+      const AffineFoldJob j{pk + pl.packed.off_qkv, q.ln1_gamma, q.ln1_beta,
+                            {q.b_q, q.b_k, q.b_v},   D, 3 * D, D, y + fp.f1.w,
+                            reinterpret_cast<float*>(y + fp.f1.cs), y + fp.f1.b};
+      const FoldSide side{x, D, nullptr, 0, stats, M, D, feps};
+      const hipError_t e = launch_affine_fold(j, stats_done ? nullptr : &side, s);
+      if (e != hipErrorNotSupported) {
+        VITBLK_LAUNCH(e);
+        stats_done = true;
+      } else {
+        VITBLK_LAUNCH(launch_affine_fold(j, nullptr, s));
+      }
+      pq.B = y + fp.f1.w;
+      pq.col_sums = reinterpret_cast<const float*>(y + fp.f1.cs);
+      pq.bias[0] = y + fp.f1.b;
+      pq.bias[1] = pq.bias[2] = nullptr;
+      pq.bias_seg = 3 * D;
+    }
+    if (!stats_done) VITBLK_LAUNCH(launch_row_stats(x, D, stats, M, D, feps, dtype, s));
   } else {
     VITBLK_LAUNCH(launch_layernorm(x, D, q.ln1_gamma, q.ln1_beta, a, M, D, feps, dtype, s));
   }
@@ -139,7 +211,6 @@ int run_block(const void* x, const void* packed, const vitblk_affine_params* prm
     VITBLK_LAUNCH(launch_attention(big, big + D * es, big + 2 * D * es, 3 * D, a, D, N, T, H,
                                    D / H, dtype, s));
   // y = x + att @ w_o + b_o   (qkv's region is free again: split-K scratch)
-  const int64_t Mo = cls_only ? N : M;  // rows from here on
   GemmProblem po = linear_problem(a, pk + pl.packed.off_o, y, x, Mo, D, D, VITBLK_EPI_RESIDUAL,
                                   dtype, q.b_o);
   if (cls_only) po.lda = po.ldr = T * D;  // the class-token rows of att and x
@@ -148,7 +219,7 @@ int run_block(const void* x, const void* packed, const vitblk_affine_params* prm
   // With LN2 folded, the product's epilogue also writes each row's partial
   // statistics over every 64 columns of y (into qkv's region, dead now) and
   // a small kernel combines them: y is not read again for its statistics.
-  if (fold2) {
+  if (fp.fold2) {
     po.row_partials = reinterpret_cast<float2*>(big);
     if (gemm_row_partials_ok(po)) {
       po.epi = kEpiResidualStats;
@@ -162,15 +233,37 @@ int run_block(const void* x, const void* packed, const vitblk_affine_params* prm
   // hidden = GELU(yn @ w_mlp1 + b_mlp1)   (overwrites qkv)
   GemmProblem p1 = linear_problem(a, pk + pl.packed.off_1, big, nullptr, Mo, D, F,
                                   VITBLK_EPI_GELU, dtype, q.b_mlp1);
-  if (fold2) {
-    if (po.row_partials != nullptr)
-      VITBLK_LAUNCH(launch_row_stats_from_partials(po.row_partials, D / kStatsStrip, stats, Mo, D,
-                                                   feps, s));
-    else
-      VITBLK_LAUNCH(launch_row_stats(y, D, stats, Mo, D, feps, dtype, s));
+  if (fp.fold2) {
+    // The statistics from the row partials ride in the fold's launch.
+    bool stats_done = false;
     p1.A = y;
     p1.row_stats = stats;
     p1.col_sums = reinterpret_cast<const float*>(pk + pl.packed.off_cs_1);
+    if (fp.affine2) {
+      const AffineFoldJob j{pk + pl.packed.off_1, q.ln2_gamma, q.ln2_beta,
+                            {q.b_mlp1, nullptr, nullptr},   F, F, D, a + fp.f2.w,
+                            reinterpret_cast<float*>(a + fp.f2.cs), a + fp.f2.b};
+      const FoldSide side{nullptr, 0, po.row_partials, D / kStatsStrip, stats, Mo, D, feps};
+      const hipError_t e =
+          launch_affine_fold(j, po.row_partials != nullptr ? &side : nullptr, s);
+      if (e != hipErrorNotSupported) {
+        VITBLK_LAUNCH(e);
+        stats_done = po.row_partials != nullptr;
+      } else {
+        VITBLK_LAUNCH(launch_affine_fold(j, nullptr, s));
+      }
+      p1.B = a + fp.f2.w;
+      p1.col_sums = reinterpret_cast<const float*>(a + fp.f2.cs);
+      p1.bias[0] = a + fp.f2.b;
+      p1.bias_seg = F;
+    }
+    if (!stats_done) {
+      if (po.row_partials != nullptr)
+        VITBLK_LAUNCH(launch_row_stats_from_partials(po.row_partials, D / kStatsStrip, stats, Mo,
+                                                     D, feps, s));
+      else
+        VITBLK_LAUNCH(launch_row_stats(y, D, stats, Mo, D, feps, dtype, s));
+    }
   } else {
     VITBLK_LAUNCH(launch_layernorm(y, D, q.ln2_gamma, q.ln2_beta, a, Mo, D, feps, dtype, s));
   }
@@ -514,9 +607,18 @@ int vitblk_forward_affine(const void* x, const void* w_q, const void* w_k, const
   if (st != VITBLK_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  st = pack_weights(w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, ws, D, F, dtype, pl.packed, s);
+  const vitblk_affine_params none{};
+  const bool fold1 = plan_folds(params != nullptr ? *params : none, ws, ws + pl.act_base, pl,
+                                N * T, D, F, dtype)
+                         .fold1;
+  const StatsJob stats1{x, D, N * T, D,
+                        reinterpret_cast<float*>(ws + pl.act_base + pl.off_act),
+                        static_cast<float>(eps)};
+  st = pack_weights(w_q, w_k, w_v, w_o, w_mlp1, w_mlp2, ws, D, F, dtype, pl.packed, s,
+                    fold1 ? &stats1 : nullptr);
   if (st != VITBLK_OK) return st;
-  return run_block(x, ws, params, out, N, T, D, F, H, eps, dtype, ws + pl.act_base, pl, s);
+  return run_block(x, ws, params, out, N, T, D, F, H, eps, dtype, ws + pl.act_base, pl, s,
+                   fold1);
 }
 
 int vitblk_forward_packed(const void* x, const void* packed, void* out, int64_t N, int64_t T,
@@ -646,6 +748,18 @@ int vitblk_linear_normed(const void* a, const void* w_t, const float* col_sums,
   p.row_stats = row_stats;
   p.col_sums = col_sums;
   VITBLK_LAUNCH(launch_gemm(p, reinterpret_cast<hipStream_t>(stream)));
+  return VITBLK_OK;
+}
+
+int vitblk_affine_fold(const void* w_t, const void* gamma, const void* beta, const void* bias,
+                       void* w_scaled, float* col_sums, void* bias_out, int64_t Nout, int64_t K,
+                       int dtype, vitblk_stream_t stream) {
+  const int st = validate_affine_fold(w_t, gamma, beta, bias, w_scaled, col_sums, bias_out, Nout,
+                                      K, dtype);
+  if (st != VITBLK_OK) return st;
+  const AffineFoldJob j{w_t, gamma, beta, {bias, nullptr, nullptr}, Nout, Nout, K,
+                        w_scaled, col_sums, bias_out};
+  VITBLK_LAUNCH(launch_affine_fold(j, nullptr, reinterpret_cast<hipStream_t>(stream)));
   return VITBLK_OK;
 }
 

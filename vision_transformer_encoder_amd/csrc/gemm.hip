@@ -375,18 +375,46 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
   float rsd[C::TM];  // LayerNorm fold: rstd of the lane's rows of the current tile
   while (true) {
     // The bias of block j's columns for this lane: element r of block (j, i)
-    // is column (r/4)*8 + (l/32)*4 + r%4 of block j (columns past N clamped).
+    // is column (r/4)*8 + (l/32)*4 + r%4 of block j.  One segment (bias_seg
+    // >= N: every bias but the three separate Q, K, V vectors): each run of 4
+    // columns is one 8-byte raw buffer load at a 32-bit offset, columns past
+    // N read as zero by the buffer's range check.  Otherwise at most three
+    // segments (N <= 3 bias_seg), the segment by comparison, columns past N
+    // clamped.
+    const bool one_seg = p.bias_seg >= N;  // uniform
     auto bias_run = [&](int j, float* bv) {
+      if (one_seg) {
+        uint2 u[4] = {};
+        if (p.bias[0] != nullptr) {
+          const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+              const_cast<void*>(p.bias[0]), 0, static_cast<int>(static_cast<uint32_t>(N * 2)),
+              kBufferFlags);
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const uint32_t n = static_cast<uint32_t>(n0) + wn * C::WTN + j * 32 + g4 * 8 + lhalf * 4;
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(brs, n * 2, 0, 0);
+            u[g4] = make_uint2(v[0], v[1]);
+          }
+        }
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          bv[g4 * 4 + 0] = __uint_as_float(u[g4].x << 16);
+          bv[g4 * 4 + 1] = __uint_as_float(u[g4].x & 0xffff0000u);
+          bv[g4 * 4 + 2] = __uint_as_float(u[g4].y << 16);
+          bv[g4 * 4 + 3] = __uint_as_float(u[g4].y & 0xffff0000u);
+        }
+        return;
+      }
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         int64_t n = n0 + wn * C::WTN + j * 32 + g4 * 8 + lhalf * 4;
         n = n < N ? n : N - 4;
-        const int seg = static_cast<int>(n / p.bias_seg);
-        const void* bs = seg == 0 ? p.bias[0] : (seg == 1 ? p.bias[1] : p.bias[2]);
+        const bool s1 = n >= p.bias_seg, s2 = n >= 2 * p.bias_seg;
+        const void* bs = s2 ? p.bias[2] : (s1 ? p.bias[1] : p.bias[0]);
+        const int64_t off = n - (s2 ? 2 * p.bias_seg : (s1 ? p.bias_seg : 0));
         uint2 u = make_uint2(0u, 0u);
         if (bs != nullptr)
-          u = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(bs) +
-                                              (n - static_cast<int64_t>(seg) * p.bias_seg));
+          u = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(bs) + off);
         bv[g4 * 4 + 0] = __uint_as_float(u.x << 16);
         bv[g4 * 4 + 1] = __uint_as_float(u.x & 0xffff0000u);
         bv[g4 * 4 + 2] = __uint_as_float(u.y << 16);
@@ -396,13 +424,12 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
     if (NORM) {
       // LayerNorm fold, mean term: the accumulators start at -mean_m *
       // colsum_n, so after the k loop they hold A @ W - mean colsum and the
-      // epilogue only scales by rstd_m.  With a bias they start at
-      // -mean_m colsum_n + b_n / rstd_m, so the same scale also yields the
-      // bias (rstd (A @ W - mean colsum) + b).  The loads (L2-resident) go out
+      // epilogue only scales by rstd_m (and, with a bias, adds it in the same
+      // fma: rstd (A @ W - mean colsum) + b).  The loads (L2-resident) go out
       // before the first k-slice's wait, which they share.  A lane's rows
       // are lrow of each 32-row block i.  Rows and columns past M or N are
       // clamped (never stored).
-      float nmu[C::TM], sig[C::TM];
+      float nmu[C::TM];
 #pragma unroll
       for (int i = 0; i < C::TM; ++i) {
         int64_t m = m0 + wm * C::WTM + i * 32 + lrow;
@@ -410,11 +437,10 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
         const float2 st = *reinterpret_cast<const float2*>(p.row_stats + 2 * m);
         nmu[i] = -st.x;
         rsd[i] = st.y;
-        sig[i] = BIAS ? 1.0f / st.y : 0.f;
       }
 #pragma unroll
       for (int j = 0; j < C::TN; ++j) {
-        float cs[16], bv[16];
+        float cs[16];
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           int64_t n = n0 + wn * C::WTN + j * 32 + g4 * 8 + lhalf * 4;
@@ -425,12 +451,10 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
           cs[g4 * 4 + 2] = c4.z;
           cs[g4 * 4 + 3] = c4.w;
         }
-        if (BIAS) bias_run(j, bv);
 #pragma unroll
         for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            acc[j][i][r] = BIAS ? __builtin_fmaf(sig[i], bv[r], nmu[i] * cs[r]) : nmu[i] * cs[r];
+          for (int r = 0; r < 16; ++r) acc[j][i][r] = nmu[i] * cs[r];
       }
     } else if (BIAS) {
       // Bias without the fold: the accumulators start at the bias, so the
@@ -499,6 +523,13 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
     constexpr bool kReadsR = EPI == VITBLK_EPI_RESIDUAL || EPI == VITBLK_EPI_GELU_GRAD ||
                              EPI == kEpiMul || EPI == kEpiResidualStats || EPI == kEpiEmbed;
     uint4 res[C::TM][C::TN][2];
+    // With the LayerNorm fold the bias enters in the epilogue's rstd scale
+    // (an fma instead of the multiply): read with the other epilogue operands.
+    float bve[C::TN][16];
+    if (NORM && BIAS) {
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) bias_run(j, bve[j]);
+    }
     // kEpiEmbed: each wave block's quotient and remainder (see c_row).
     uint32_t bq[C::TM], br[C::TM];
 #pragma unroll
@@ -543,15 +574,16 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
     // first store (addresses clamped into range), and added in fp32 before
     // the single rounding to bf16.
     bf16_t* Cp = static_cast<bf16_t*>(p.C);
-    // LayerNorm fold, scale term: acc = rstd_m * acc (the bias, if any, was
-    // in the accumulators' start value).
+    // LayerNorm fold, scale term: acc = rstd_m * acc (+ b_n).
     if (NORM) {
 #pragma unroll
       for (int i = 0; i < C::TM; ++i)
 #pragma unroll
         for (int j = 0; j < C::TN; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[j][i][r] *= rsd[i];
+          for (int r = 0; r < 16; ++r)
+            acc[j][i][r] = BIAS ? __builtin_fmaf(acc[j][i][r], rsd[i], bve[j][r])
+                                : acc[j][i][r] * rsd[i];
     }
     // The plain and residual epilogues store each 32-row block as whole row
     // lines (rows_to_lines): 8% faster on the fused Q|K|V projection.  The
@@ -839,7 +871,7 @@ hipError_t launch_bias(const GemmProblem& p, hipStream_t s) {
     case kEpiGeluDual: return launch_epi<C, kEpiGeluDual, BIAS>(p, s);
     case kEpiMul: return launch_epi<C, kEpiMul, BIAS>(p, s);
     case kEpiPartial: return launch_epi<C, kEpiPartial, false>(p, s);
-    case kEpiResidualStats: return launch_epi<C, kEpiResidualStats, false>(p, s);
+    case kEpiResidualStats: return launch_epi<C, kEpiResidualStats, BIAS>(p, s);
     case kEpiEmbed: return launch_epi<C, kEpiEmbed, BIAS>(p, s);
     default: return launch_epi<C, VITBLK_EPI_NONE, BIAS>(p, s);
   }
@@ -887,12 +919,12 @@ bool gemm_fast_ok(const GemmProblem& p) {
 }
 
 // The row partials ride on the tiles the output projection (a residual
-// product with K = D) takes anyway, whose waves cover 64 columns each; no bias.
+// product with K = D) takes anyway, whose waves cover 64 columns each.
 bool gemm_row_partials_ok(const GemmProblem& p) {
   GemmProblem q = p;
   q.epi = kEpiResidualStats;
   return gemm_fast_ok(q) && p.row_partials != nullptr && p.N % kStatsStrip == 0 &&
-         (reinterpret_cast<uintptr_t>(p.row_partials) & 7u) == 0 && !has_bias(p);
+         (reinterpret_cast<uintptr_t>(p.row_partials) & 7u) == 0;
 }
 
 // Rows [r0, r0 + rows) of p as a problem of its own.

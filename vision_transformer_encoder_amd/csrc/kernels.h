@@ -169,6 +169,40 @@ struct StatsJob {
 hipError_t launch_prologue(const PackJob* jobs, int njobs, const ColSumJob* cs, int ncs,
                            const StatsJob* stats, int dtype, hipStream_t stream);
 
+// The affine LayerNorm's fold into the product after it (bf16): for the
+// out-major weight w_t [N, K], w_scaled[n, k] = bf16(gamma_k w_t[n, k]),
+// col_sums[n] = sum_k w_scaled[n, k] (fp32, fixed order) and bias_out[n] =
+// bf16(b_n + sum_k beta_k w_t[n, k]), b in segments of bias_seg columns (each
+// null: zeros).  gamma, beta null: ones, zeros.  K a multiple of 8, w_t,
+// w_scaled, gamma and beta 16-byte aligned.
+struct AffineFoldJob {
+  const void* w_t;
+  const void* gamma;
+  const void* beta;
+  const void* bias[3];
+  int64_t bias_seg;
+  int64_t N, K;
+  void* w_scaled;
+  float* col_sums;
+  void* bias_out;
+};
+// Row statistics computed in the same launch (the product's other operand):
+// stats[2r], stats[2r + 1] = mean and rstd of row r, from the bf16 rows x
+// (row stride ld; launch_row_stats's job) or, with partials non-null, from
+// nstrips = D / kStatsStrip row partials (launch_row_stats_from_partials's).
+struct FoldSide {
+  const void* x;
+  int64_t ld;
+  const float2* partials;
+  int64_t nstrips;
+  float* stats;
+  int64_t rows, D;
+  float eps;
+};
+// side may be null.  hipErrorNotSupported, with nothing launched: the side
+// job does not meet the kernel's layout (launch it on its own instead).
+hipError_t launch_affine_fold(const AffineFoldJob& job, const FoldSide* side, hipStream_t stream);
+
 // O[n*T + t, h*dh + c] = sum_j softmax_j(Q_h K_h^T / sqrt(dh))[t, j] V[n*T + j, h*dh + c]
 // with Q, K, V row strides ld (elements) and O row stride ldo.
 hipError_t launch_attention(const void* q, const void* k, const void* v, int64_t ld,

@@ -238,11 +238,9 @@ hipError_t launch_row_stats(const void* x, int64_t ld_in, float* stats, int64_t 
 // (n_ab = n_a + n_b, mean_ab = mean_a + d n_b / n_ab, M2_ab = M2_a + M2_b +
 // d^2 n_a n_b / n_ab, d = mean_b - mean_a), then rstd = 1 / sqrt(M2 / D + eps)
 // (population variance, eps inside the root).  One thread per row.
-__global__ __launch_bounds__(256) void stats_from_partials_kernel(
-    const float2* __restrict__ P, int nstrips, float2* __restrict__ stats, int64_t rows,
-    float eps) {
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (r >= rows) return;
+__device__ __forceinline__ void combine_partials(const float2* __restrict__ P, int nstrips,
+                                                 float2* __restrict__ stats, int64_t r,
+                                                 float eps) {
   const float2* pr = P + r * nstrips;
   const float nb = static_cast<float>(kStatsStrip);
   float2 a = pr[0];
@@ -256,6 +254,13 @@ __global__ __launch_bounds__(256) void stats_from_partials_kernel(
     n = nn;
   }
   stats[r] = make_float2(mean, 1.0f / sqrtf(m2 / n + eps));
+}
+
+__global__ __launch_bounds__(256) void stats_from_partials_kernel(
+    const float2* __restrict__ P, int nstrips, float2* __restrict__ stats, int64_t rows,
+    float eps) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (r < rows) combine_partials(P, nstrips, stats, r, eps);
 }
 
 hipError_t launch_row_stats_from_partials(const float2* partials, int64_t nstrips, float* stats,
@@ -283,6 +288,177 @@ hipError_t launch_layernorm(const void* x, int64_t ld_in, const void* gamma, con
   return ln_fast_typed(static_cast<const float*>(x), ld_in, static_cast<const float*>(gamma),
                        static_cast<const float*>(beta), static_cast<float*>(y), rows,
                        static_cast<int>(D), eps, s);
+}
+
+
+// ------------------------------------------------------------- affine fold
+
+// The affine LayerNorm folded into the product after it (bf16).  With
+// xn = gamma * LN(x) + beta (ai-engineer-exhaustive.pages.dev "ViT Encoder
+// Block", "Key Equations", steps 1 and 4) and LN(x) = rstd (x - mean):
+//   xn @ W + b = rstd (x @ W' - mean colsum(W')) + b',
+//   W' = diag(gamma) W,  b' = b + beta @ W,
+// so the product runs on x itself with the LayerNorm fold's row statistics.
+// One wave per output column n (a row of the out-major W^T), four per
+// workgroup: the lane's 8-element runs of the row scaled and rounded to bf16
+// (W'), their fp32 sum (colsum(W') of the rounded values, as the product
+// uses them) and the fp32 sum of beta_k W[k, n], then the wave sums and
+// b'_n = bf16(b_n + sum).  Reads W^T once and writes W'^T once.  The launch
+// is short and latency-bound, so the row statistics the product also needs
+// (of x, or combined from row partials) ride in it as a second role.
+namespace {
+
+// One 8-element run of W^T row n at column k (wv, with the gains gv and
+// shifts bv of those columns): W' stored, sums accumulated.
+__device__ __forceinline__ void fold_run(const uint4& wv, const uint4& gv, const uint4& bv,
+                                         int64_t k, bf16_t* ws, float& cs, float& bb) {
+  const uint32_t wu[4] = {wv.x, wv.y, wv.z, wv.w};
+  const uint32_t gu[4] = {gv.x, gv.y, gv.z, gv.w};
+  const uint32_t bu[4] = {bv.x, bv.y, bv.z, bv.w};
+  uint32_t out[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float w0 = __uint_as_float(wu[e] << 16), w1 = __uint_as_float(wu[e] & 0xffff0000u);
+    const float g0 = __uint_as_float(gu[e] << 16), g1 = __uint_as_float(gu[e] & 0xffff0000u);
+    const float b0 = __uint_as_float(bu[e] << 16), b1 = __uint_as_float(bu[e] & 0xffff0000u);
+    out[e] = pack_bf16x2(g0 * w0, g1 * w1);
+    cs += __uint_as_float(out[e] << 16);
+    cs += __uint_as_float(out[e] & 0xffff0000u);
+    bb = fmaf(b0, w0, bb);
+    bb = fmaf(b1, w1, bb);
+  }
+  st_global16(ws + k, make_uint4(out[0], out[1], out[2], out[3]));
+}
+
+constexpr uint32_t kOnes = 0x3f803f80u;  // two bf16 1.0
+__device__ __forceinline__ uint4 load_or(const bf16_t* p, int64_t k, uint32_t fill) {
+  return p != nullptr ? ld_global16(p + k) : make_uint4(fill, fill, fill, fill);
+}
+
+// Rows up to 2048 wide: all of the lane's (at most four) runs, with their
+// gains and shifts, are requested before any is used.
+constexpr int kFoldRuns = 4;
+
+__device__ __forceinline__ void fold_row(const AffineFoldJob& j, int64_t n, int lane) {
+  const bf16_t* w = static_cast<const bf16_t*>(j.w_t) + n * j.K;
+  bf16_t* ws = static_cast<bf16_t*>(j.w_scaled) + n * j.K;
+  const bf16_t* g = static_cast<const bf16_t*>(j.gamma);
+  const bf16_t* be = static_cast<const bf16_t*>(j.beta);
+  // b_n, requested with the runs (used by lane 0 at the end).
+  const int seg = static_cast<int>(n >= j.bias_seg) + static_cast<int>(n >= 2 * j.bias_seg);
+  const bf16_t* bs = static_cast<const bf16_t*>(j.bias[seg]);
+  const float b = bs != nullptr && lane == 0 ? bf16_to_f32(bs[n - seg * j.bias_seg]) : 0.f;
+  float cs = 0.f, bb = 0.f;
+  if (j.K <= kFoldRuns * 64 * 8) {
+    uint4 wv[kFoldRuns], gv[kFoldRuns], bv[kFoldRuns];
+#pragma unroll
+    for (int r = 0; r < kFoldRuns; ++r) {
+      const int64_t k = (r * 64 + lane) * 8;
+      const bool in = k < j.K;
+      wv[r] = in ? ld_global16(w + k) : make_uint4(0u, 0u, 0u, 0u);
+      gv[r] = in ? load_or(g, k, kOnes) : make_uint4(0u, 0u, 0u, 0u);
+      bv[r] = in ? load_or(be, k, 0u) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int r = 0; r < kFoldRuns; ++r) {
+      const int64_t k = (r * 64 + lane) * 8;
+      if (k < j.K) fold_run(wv[r], gv[r], bv[r], k, ws, cs, bb);
+    }
+  } else {
+    for (int64_t k = lane * 8; k < j.K; k += 64 * 8)
+      fold_run(ld_global16(w + k), load_or(g, k, kOnes), load_or(be, k, 0u), k, ws, cs, bb);
+  }
+  cs = wave_sum(cs);
+  bb = wave_sum(bb);
+  if (lane == 0) {
+    j.col_sums[n] = cs;
+    static_cast<bf16_t*>(j.bias_out)[n] = f32_to_bf16(b + bb);
+  }
+}
+
+// The launch's second role: 0 none, 1 the row statistics of x (a wave per
+// row, as ln_stats_kernel), 2 row statistics combined from row partials (a
+// thread per row, as stats_from_partials_kernel).
+struct FoldSideArgs {
+  int kind;
+  const bf16_t* x;
+  int64_t ld;
+  const float2* partials;
+  int nstrips;
+  float2* stats;
+  int64_t rows;
+  int D;
+  float eps;
+};
+
+template <int NCH>
+__global__ __launch_bounds__(256) void affine_fold_kernel(AffineFoldJob j, int64_t fold_blocks,
+                                                          FoldSideArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t b = blockIdx.x;
+  if (b < fold_blocks) {
+    const int64_t n = b * 4 + wave;
+    if (n < j.N) fold_row(j, n, lane);
+    return;
+  }
+  const int64_t sb = b - fold_blocks;
+  if (a.kind == 1) {
+    const int64_t row = sb * 4 + wave;
+    if (row < a.rows) stats_of_row<bf16_t, NCH>(a.x, a.ld, a.stats, row, a.D, a.eps, lane);
+  } else if (a.kind == 2) {
+    const int64_t r = sb * 256 + threadIdx.x;
+    if (r < a.rows) combine_partials(a.partials, a.nstrips, a.stats, r, a.eps);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_affine_fold(const AffineFoldJob& j, const FoldSide* side, hipStream_t s) {
+  const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  if (j.N <= 0 || j.K <= 0 || j.K % 8 != 0 || j.bias_seg <= 0 || j.N > 3 * j.bias_seg ||
+      j.w_t == nullptr || j.w_scaled == nullptr || j.col_sums == nullptr ||
+      j.bias_out == nullptr || !a16(j.w_t) || !a16(j.w_scaled) || !a16(j.gamma) ||
+      !a16(j.beta))
+    return hipErrorInvalidValue;
+  const int64_t fold_blocks = (j.N + 3) / 4;
+  FoldSideArgs a{};
+  int64_t side_blocks = 0;
+  int cpl = 1;
+  if (side != nullptr && side->rows > 0) {
+    if ((reinterpret_cast<uintptr_t>(side->stats) & 7u) != 0 || side->D < 1)
+      return hipErrorNotSupported;
+    a.stats = reinterpret_cast<float2*>(side->stats);
+    a.rows = side->rows;
+    a.D = static_cast<int>(side->D);
+    a.eps = side->eps;
+    if (side->partials != nullptr) {
+      if (side->nstrips < 1 || side->nstrips * kStatsStrip != side->D) return hipErrorNotSupported;
+      a.kind = 2;
+      a.partials = side->partials;
+      a.nstrips = static_cast<int>(side->nstrips);
+      side_blocks = (side->rows + 255) / 256;
+    } else {
+      if (side->D % 8 != 0 || side->ld % 8 != 0 || side->D > 64 * 8 * 8 || !a16(side->x))
+        return hipErrorNotSupported;
+      a.kind = 1;
+      a.x = static_cast<const bf16_t*>(side->x);
+      a.ld = side->ld;
+      side_blocks = (side->rows + 3) / 4;
+      cpl = static_cast<int>((side->D / 8 + 63) / 64);
+    }
+  }
+  const int64_t blocks = fold_blocks + side_blocks;
+  if (blocks > 2147483647LL) return side != nullptr ? hipErrorNotSupported : hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+  if (cpl <= 1)
+    hipLaunchKernelGGL(affine_fold_kernel<1>, grid, block, 0, s, j, fold_blocks, a);
+  else if (cpl <= 2)
+    hipLaunchKernelGGL(affine_fold_kernel<2>, grid, block, 0, s, j, fold_blocks, a);
+  else if (cpl <= 4)
+    hipLaunchKernelGGL(affine_fold_kernel<4>, grid, block, 0, s, j, fold_blocks, a);
+  else
+    hipLaunchKernelGGL(affine_fold_kernel<8>, grid, block, 0, s, j, fold_blocks, a);
+  return hipGetLastError();
 }
 
 }  // namespace vitblk

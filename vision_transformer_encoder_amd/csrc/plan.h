@@ -102,6 +102,10 @@ int validate_row_stats(const void* x, const float* stats, int64_t rows, int64_t 
 int validate_linear_normed(const void* a, const void* w, const float* col_sums,
                            const float* row_stats, const void* bias, const void* out, int64_t M,
                            int64_t K, int64_t Nout, int epilogue, int dtype);
+// gamma, beta and bias may be null.
+int validate_affine_fold(const void* w_t, const void* gamma, const void* beta, const void* bias,
+                         const void* w_scaled, const float* col_sums, const void* bias_out,
+                         int64_t Nout, int64_t K, int dtype);
 // Workspace of vitblk_linear_residual_row_stats: one (mean, M2) pair per row
 // and 64 columns.  0 for invalid sizes.
 size_t linear_stats_workspace_bytes(int64_t M, int64_t Nout);

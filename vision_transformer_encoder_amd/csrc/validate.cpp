@@ -415,6 +415,35 @@ int validate_linear_normed(const void* a, const void* w, const float* col_sums,
   return VITBLK_OK;
 }
 
+int validate_affine_fold(const void* w_t, const void* gamma, const void* beta, const void* bias,
+                         const void* w_scaled, const float* col_sums, const void* bias_out,
+                         int64_t Nout, int64_t K, int dtype) {
+  if (w_t == nullptr || w_scaled == nullptr || col_sums == nullptr || bias_out == nullptr)
+    return VITBLK_ERR_INVALID_ARG;
+  if (!aligned16(w_t) || !aligned16(w_scaled) || !aligned16(gamma) || !aligned16(beta) ||
+      !aligned16(col_sums) || (reinterpret_cast<uintptr_t>(bias) & 1u) != 0 ||
+      (reinterpret_cast<uintptr_t>(bias_out) & 1u) != 0)
+    return VITBLK_ERR_INVALID_ARG;
+  if (!dim_ok(Nout) || !dim_ok(K)) return VITBLK_ERR_INVALID_ARG;
+  const size_t es = elem_size(dtype);
+  if (es == 0) return VITBLK_ERR_INVALID_ARG;
+  if (dtype != VITBLK_BF16 || K % 8 != 0 || Nout > kMaxDim || K > kMaxDim)
+    return VITBLK_ERR_UNSUPPORTED;
+  const size_t n = static_cast<size_t>(Nout), k = static_cast<size_t>(K);
+  const Span outs[3] = {span(w_scaled, n * k * es), span(col_sums, n * sizeof(float)),
+                        span(bias_out, n * es)};
+  const Span ins[4] = {span(w_t, n * k * es), span(gamma, gamma != nullptr ? k * es : 0),
+                       span(beta, beta != nullptr ? k * es : 0),
+                       span(bias, bias != nullptr ? n * es : 0)};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 4; ++j)
+      if (overlap(outs[i], ins[j])) return VITBLK_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j])) return VITBLK_ERR_ALIAS;
+  }
+  return VITBLK_OK;
+}
+
 int validate_encoder(const void* x, const void* const* packed, const vitblk_affine_params* params,
                      int64_t L, const void* final_gamma, const void* final_beta,
                      const void* out, const void* cls_out, int64_t N, int64_t T, int64_t D,
