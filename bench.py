@@ -29,6 +29,7 @@ GPU tests).
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import math
 import os
@@ -114,6 +115,11 @@ def time_steps(step, steps, torch):
     between the steps, so the mean is the plain end-to-end time / steps."""
     s = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    # Python's cyclic garbage collector off while the steps are enqueued (as
+    # timeit does): a collection pause on the host would otherwise show up as
+    # an idle GPU gap wherever the host is only a few short steps ahead.
+    gc_was_on = gc.isenabled()
+    gc.disable()
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     ev[0].record(s)
@@ -122,6 +128,8 @@ def time_steps(step, steps, torch):
         ev[i + 1].record(s)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
+    if gc_was_on:
+        gc.enable()
     per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
     return ev[0].elapsed_time(ev[steps]) / steps, per, t_wall
 

@@ -269,6 +269,19 @@ def test_affine_block_folded(drop):
                  f"folded affine block without {drop}")
 
 
+@pytest.mark.parametrize("N,T,D,H,F", [(2, 197, 72, 2, 288), (3, 97, 64, 4, 128)])
+def test_affine_block_folded_other_kernels(N, T, D, H, F):
+    # Folded with products outside the matrix-core kernel's shapes (K = 72:
+    # the any-shape kernel, with the LN2 statistics from their own pass) and
+    # with a narrow F (MLP1's copy beside the statistics of 291 rows).
+    assert _folds(N, T, D, F)
+    inp = make_block_inputs(N, T, D, F, "bf16", seed=23)
+    prm = make_affine_params(D, F, "bf16", seed=23)
+    out, _ = _run(inp, prm, H, 1e-6, "bf16")
+    assert_close(to_host(out), _oracle(inp, prm, H, 1e-6), "bf16",
+                 f"folded affine block N={N} T={T} D={D} F={F}")
+
+
 def test_affine_block_folded_large_gains():
     # Gains far from 1 (N(0, 1): near 0 and of both signs) and unit shifts:
     # the scaled copy is rounded to bf16 once, as the written-out LayerNorm's

@@ -592,6 +592,30 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
     constexpr bool kLines = (EPI == VITBLK_EPI_NONE || EPI == VITBLK_EPI_RESIDUAL ||
                              EPI == kEpiResidualStats || EPI == kEpiEmbed) &&
                             C::TN == 2;
+    // C stores: raw buffer stores at 32-bit offsets from the tile's first
+    // row; a lane outside M or N gets an offset past the buffer's range, so
+    // the hardware drops its store.  With no branch per store the epilogue
+    // is one block the scheduler can interleave (ViT-L/16 Q|K|V 298.8 ->
+    // 295.0 us, MLP1 427.5 -> 425.0 us).  Not for the token-row epilogue (its
+    // rows are remapped), nor where the big tile would then spill registers:
+    // with a bias, and the GELU-derivative and row-statistics epilogues.
+    constexpr bool kBufStore =
+        EPI != kEpiEmbed && !kSplit && !BIAS &&
+        !(C::BM == 256 && (EPI == VITBLK_EPI_GELU_GRAD || EPI == kEpiResidualStats));
+    const int64_t c_rows = M - cm0 < C::BM ? M - cm0 : C::BM;
+    auto c_rsrc = [&](void* base) {
+      return __builtin_amdgcn_make_buffer_rsrc(static_cast<bf16_t*>(base) + cm0 * p.ldc, 0,
+                                               static_cast<int>(c_rows * p.ldc * 2),
+                                               kBufferFlags);
+    };
+    const __amdgpu_buffer_rsrc_t c_rs = c_rsrc(p.C);
+    auto store_c = [&](const __amdgpu_buffer_rsrc_t& rs, int64_t m, int64_t n, const uint4& v) {
+      const uint32_t off = (m < M && n < N) ? static_cast<uint32_t>(((m - cm0) * p.ldc + n) * 2)
+                                            : 0x80000000u;
+      typedef unsigned v4u __attribute__((ext_vector_type(4)));
+      const v4u d = {v.x, v.y, v.z, v.w};
+      __builtin_amdgcn_raw_buffer_store_b128(d, rs, off, 0, 0);
+    };
     if (kSplit) {
       // Unrounded fp32 sums of this k-range: after the fp32 half exchange a
       // lane holds 8 consecutive columns of one row (32 bytes).
@@ -692,14 +716,20 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
             if (EPI == kEpiGeluDual) {
               const auto t0 = __builtin_amdgcn_permlane32_swap(w2[0][0], w2[1][0], false, false);
               const auto t1 = __builtin_amdgcn_permlane32_swap(w2[0][1], w2[1][1], false, false);
-              if (m < M && n < N)
-                st_global16(static_cast<bf16_t*>(p.C2) + m * p.ldc + n,
-                            make_uint4(t0[0], t1[0], t0[1], t1[1]));
+              const uint4 d2 = make_uint4(t0[0], t1[0], t0[1], t1[1]);
+              if constexpr (kBufStore)
+                store_c(c_rsrc(p.C2), m, n, d2);
+              else if (m < M && n < N)
+                st_global16(static_cast<bf16_t*>(p.C2) + m * p.ldc + n, d2);
             }
           }
           outs[j][q] = out;
-          if (!kLines && m < M && n < N)
-            st_global16(Cp + c_row(m, bq[i], br[i], lrow) * p.ldc + n, out);
+          if constexpr (!kLines) {
+            if constexpr (kBufStore)
+              store_c(c_rs, m, n, out);
+            else if (m < M && n < N)
+              st_global16(Cp + c_row(m, bq[i], br[i], lrow) * p.ldc + n, out);
+          }
         }
       }
       if constexpr (EPI == kEpiResidualStats) {
@@ -751,7 +781,9 @@ __global__ __launch_bounds__(C::NT, C::WPE) void gemm_bf16_kernel(GemmProblem p,
         for (int t = 0; t < 4; ++t) {
           const int64_t mr = cm0 + wm * C::WTM + i * 32 + t * 8 + (lane >> 3);
           const int64_t nr = cn0 + wn * C::WTN + (lane & 7) * 8;
-          if (mr < M && nr < N)
+          if constexpr (kBufStore)
+            store_c(c_rs, mr, nr, v[t]);
+          else if (mr < M && nr < N)
             st_global16(Cp + c_row(mr, bq[i], br[i], t * 8 + (lane >> 3)) * p.ldc + nr, v[t]);
         }
       }
@@ -897,15 +929,16 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u
 }  // namespace
 
 // The MFMA kernel needs bf16, K a multiple of 64, N a multiple of 8, 16-byte
-// aligned rows, and a 256-row panel of either operand to span < 2 GiB (its
-// buffer offsets are 32-bit); a bias in segments of a multiple of 8 columns
+// aligned rows, and a 256-row panel of either operand and of the output to
+// span < 2 GiB (its buffer offsets are 32-bit); a bias in segments of a multiple of 8 columns
 // (so no lane's run of columns straddles two segments), 8-byte aligned.
 // Everything else takes the generic kernel.
 bool gemm_fast_ok(const GemmProblem& p) {
   bool ok = p.dtype == VITBLK_BF16 && p.K % 64 == 0 && p.N % 8 == 0 && p.N >= 8 &&
             p.lda % 8 == 0 && p.ldb % 8 == 0 && p.ldc % 8 == 0 && aligned16(p.A) &&
             aligned16(p.B) && aligned16(p.C) && p.lda * 2 * 256 < (1LL << 31) &&
-            p.ldb * 2 * 256 < (1LL << 31) && p.K * 2 < (1LL << 31);
+            p.ldb * 2 * 256 < (1LL << 31) && p.ldc * 2 * 256 < (1LL << 31) &&
+            p.K * 2 < (1LL << 31);
   if (reads_r(p)) ok = ok && p.ldr % 8 == 0 && aligned16(p.R);
   if (p.row_stats != nullptr)
     ok = ok && aligned16(p.col_sums) && (reinterpret_cast<uintptr_t>(p.row_stats) & 7u) == 0;
