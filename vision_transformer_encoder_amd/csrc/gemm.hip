@@ -43,7 +43,8 @@
 //   k-slices: loads complete in issue order, so a read issued after them
 //   would hold the epilogue until those slices had landed.  A bias is no
 //   epilogue work at all: the accumulators start at it (fp32; the products
-//   are then added to it), with the LayerNorm fold at b / rstd (below).
+//   are then added to it), or with the LayerNorm fold the epilogue's rstd
+//   scale adds it in the same fma (below).
 // * LayerNorm fold (row_stats set): LN(A) @ W = rstd (A @ W - mean colsum W)
 //   (crackedaicode.com "ViT Encoder Block", "Normalize before each stage":
 //   (x - mean) * rstd per token, multiplied out).  The accumulators start at
