@@ -182,7 +182,7 @@ int run_block(const void* x, const void* packed, const vitblk_affine_params* prm
     pq.col_sums = reinterpret_cast<const float*>(pk + pl.packed.off_cs_qkv);
     if (fp.affine1) {
       const AffineFoldJob j{pk + pl.packed.off_qkv, q.ln1_gamma, q.ln1_beta,
-                            {q.b_q, q.b_k, q.b_v},   D, 3 * D, D, y + fp.f1.w,
+                            {q.b_q, q.b_k, q.b_v}, D, 3 * D, D, y + fp.f1.w,
                             reinterpret_cast<float*>(y + fp.f1.cs), y + fp.f1.b};
       const FoldSide side{x, D, nullptr, 0, stats, M, D, feps};
       const hipError_t e = launch_affine_fold(j, stats_done ? nullptr : &side, s);
@@ -241,7 +241,7 @@ int run_block(const void* x, const void* packed, const vitblk_affine_params* prm
     p1.col_sums = reinterpret_cast<const float*>(pk + pl.packed.off_cs_1);
     if (fp.affine2) {
       const AffineFoldJob j{pk + pl.packed.off_1, q.ln2_gamma, q.ln2_beta,
-                            {q.b_mlp1, nullptr, nullptr},   F, F, D, a + fp.f2.w,
+                            {q.b_mlp1, nullptr, nullptr}, F, F, D, a + fp.f2.w,
                             reinterpret_cast<float*>(a + fp.f2.cs), a + fp.f2.b};
       const FoldSide side{nullptr, 0, po.row_partials, D / kStatsStrip, stats, Mo, D, feps};
       const hipError_t e =
